@@ -1,0 +1,319 @@
+"""CPU oracle for the INT4 / ternary-INT2 weight matmul (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use this module. It shares no code with the HIP library and
+imports nothing from it.
+
+Sources (cited by page title and section):
+
+* [INT4 page] "Accelerating LLM inference with CUDA Graph and INT4
+  quantization" (基于CUDA Graph 和 INT4 量化加速大语言模型推理过程), Part 1:
+  step 1 weight quantization (symmetric scale from the largest magnitude,
+  round, clip, two 4-bit values per byte), step 2 activation quantization
+  (dynamic scale, round), step 3 the INT4 GEMM dataflow (unpack, 8-bit dot
+  products into INT32, multiply by the scales, optional bias), step 4
+  dequantization (INT32 result times weight_scale * activation_scale).
+* [BitBLAS page] "BitBLAS practical guide: mixed-precision matmul in vLLM"
+  (BitBLAS实战指南：在vLLM中集成混合精度计算，降低70%内存使用): section
+  "What is BitBLAS" (the problem statement C[M,N] = A[M,K] x W[N,K], layout
+  "nt"), the data-type table (FP16 x INT4, INT8 x INT2), the memory-saving
+  list (INT4 saves 75 %, INT2 87.5 % against FP16), "Advanced features 2:
+  weight group quantization" (group_size 128, with scaling, with zeros,
+  zeros_mode "original"), and the BitNet-b1.58 case (ternary weights).
+
+Readings taken where the pages are silent or contradict themselves (each is
+listed again in the design notes):
+
+1. INT4 symmetric range is [-7, 7] with scale = max|w| / 7. The INT4 page
+   prints 127, which it itself calls the INT8 range; 127 is kept for the INT8
+   activations only. Code -8 is never produced.
+2. Scales are per output channel (one per row n of W) for the symmetric
+   scheme; the page's formula takes the max over "the weight tensor".
+3. round() is round-half-to-even; divisions are IEEE float32 divisions
+   (the precision the kernels decide codes in).
+4. Nibble order: element 2j of a row goes to the low nibble of byte j, 2j+1
+   to the high nibble. Crumbs (2-bit) are little-endian within a byte.
+   Signed values are stored as two's complement.
+5. Group quantization (asymmetric uINT4, zeros_mode "original"): over each
+   group of 128 consecutive k, s16 = fp16((max - min) / 15), every later
+   step uses the fp16-rounded scale, z = clip(rint(-min / s), 0, 15),
+   q = clip(rint(w / s) + z, 0, 15), and w is reconstructed as (q - z) * s.
+   A group with s == 0 gets q = z = 0.
+6. Accumulation for FP16 x INT4 is float32 in the kernels (the BitBLAS
+   example names fp16; fp16 accumulation over K = 11008 would not meet the
+   output tolerance); the oracle accumulates in float64.
+7. Activations are quantized per token (row m), dynamically, to [-127, 127].
+8. Ternary codes are inputs; their per-tensor scale is fp16(mean |src|) of
+   the float32 source, summed in float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "quantize_w4_sym",
+    "quantize_w4_group",
+    "pack_int4",
+    "unpack_int4",
+    "pack_int2",
+    "unpack_int2",
+    "ternary_scale",
+    "quantize_a8",
+    "int_accumulate",
+    "int_accumulate_entries",
+    "dequant_epilogue",
+    "w4a8_gemm",
+    "w2a8_gemm",
+    "w4a16_gemm",
+    "w4a16_entries",
+    "OUT_F16",
+    "OUT_F32",
+    "OUT_I32",
+]
+
+OUT_F16, OUT_F32, OUT_I32 = "f16", "f32", "i32"
+
+_F32 = np.float32
+
+
+# ----------------------------------------------------------------------------
+# weight quantization
+# ----------------------------------------------------------------------------
+def quantize_w4_sym(W):
+    """Symmetric per-output-channel INT4 codes and float32 scales.
+
+    INT4 page, Part 1 step 1: scale = largest magnitude / Q, code =
+    round(w / scale), clipped to the symmetric range; Q = 7 for INT4
+    (reading 1). One scale per row n (reading 2). Returns (q int8 [N,K] in
+    [-7,7], s float32 [N]).
+    """
+    W = np.ascontiguousarray(W, dtype=_F32)
+    amax = np.max(np.abs(W), axis=1)              # exact in float32
+    s = (amax / _F32(7.0)).astype(_F32)           # IEEE float32 division
+    q = np.zeros(W.shape, dtype=np.int8)
+    live = s > 0
+    if np.any(live):
+        r = np.rint(W[live] / s[live, None])       # float32 divide, half-even
+        q[live] = np.clip(r, -7, 7).astype(np.int8)
+    return q, s
+
+
+def quantize_w4_group(W, group_size=128):
+    """Asymmetric uINT4 codes with fp16 group scales and uint8 zeros.
+
+    BitBLAS page, "Advanced features 2: weight group quantization"
+    (group_size=128, with_scaling, with_zeros, zeros_mode "original"), with
+    the min/max asymmetric scheme of reading 5. Returns (q uint8 [N,K] in
+    [0,15], s float16 [N,K/g], z uint8 [N,K/g]).
+    """
+    W = np.ascontiguousarray(W, dtype=_F32)
+    N, K = W.shape
+    if K % group_size:
+        raise ValueError("K must be a multiple of group_size")
+    G = K // group_size
+    Wg = W.reshape(N, G, group_size)
+    mn = Wg.min(axis=2)
+    mx = Wg.max(axis=2)
+    s16 = ((mx - mn) / _F32(15.0)).astype(np.float16)   # fp32 op, then RNE to fp16
+    sf = s16.astype(_F32)
+    z = np.zeros((N, G), dtype=np.uint8)
+    q = np.zeros((N, G, group_size), dtype=np.uint8)
+    live = sf > 0
+    if np.any(live):
+        zl = np.clip(np.rint(-mn[live] / sf[live]), 0, 15)
+        ql = np.clip(np.rint(Wg[live] / sf[live][:, None]) + zl[:, None], 0, 15)
+        z[live] = zl.astype(np.uint8)
+        q[live] = ql.astype(np.uint8)
+    return q.reshape(N, K), s16, z
+
+
+def ternary_scale(src):
+    """Per-tensor fp16 scale of a ternary weight: fp16(mean |src|).
+
+    BitBLAS page, BitNet-b1.58 case (ternary weights); the absmean scale is
+    reading 8. The sum is taken in float64 over the float32 source.
+    """
+    src = np.asarray(src, dtype=_F32)
+    mean = np.abs(src.astype(np.float64)).sum() / src.size
+    return np.float16(mean)
+
+
+# ----------------------------------------------------------------------------
+# packing
+# ----------------------------------------------------------------------------
+def pack_int4(q):
+    """Two 4-bit codes per byte: element 2j -> low nibble, 2j+1 -> high.
+
+    INT4 page, Part 1 step 1 ("storage": two INT4 weights in one byte);
+    nibble order is reading 4. Accepts signed [-8,7] or unsigned [0,15]
+    codes; returns uint8 [N, K/2].
+    """
+    q = np.asarray(q)
+    if q.shape[-1] % 2:
+        raise ValueError("K must be even")
+    u = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(b, signed):
+    """Inverse of pack_int4; signed=True gives two's-complement [-8,7]."""
+    b = np.asarray(b, dtype=np.uint8)
+    lo = (b & 0xF).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    if signed:
+        lo = np.where(lo >= 8, lo - 16, lo)
+        hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int16)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out.astype(np.int8 if signed else np.uint8)
+
+
+def pack_int2(c):
+    """Four 2-bit two's-complement codes per byte, element 4j+i at bits 2i.
+
+    BitBLAS page data-type table (INT8 x INT2) and memory list (INT2 is one
+    eighth of FP16); crumb order is reading 4.
+    """
+    c = np.asarray(c)
+    if c.shape[-1] % 4:
+        raise ValueError("K must be a multiple of 4")
+    u = (c.astype(np.int16) & 0x3).astype(np.uint8)
+    return (u[..., 0::4] | (u[..., 1::4] << 2) | (u[..., 2::4] << 4)
+            | (u[..., 3::4] << 6)).astype(np.uint8)
+
+
+def unpack_int2(b):
+    """Inverse of pack_int2: 2-bit two's complement -> int8 in [-2, 1]."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (4 * b.shape[-1],), dtype=np.int16)
+    for i in range(4):
+        v = ((b >> (2 * i)) & 0x3).astype(np.int16)
+        out[..., i::4] = np.where(v >= 2, v - 4, v)
+    return out.astype(np.int8)
+
+
+# ----------------------------------------------------------------------------
+# activations
+# ----------------------------------------------------------------------------
+def quantize_a8(A):
+    """Per-token dynamic INT8 activations.
+
+    INT4 page, Part 1 step 2: quantized = round(activation / scale), with a
+    dynamic scale; per token and symmetric [-127, 127] (reading 7), scale =
+    max|a| / 127 in float32. fp16 inputs widen exactly to float32. Returns
+    (qa int8 [M,K], sa float32 [M], rowsum int32 [M] = sum_k qa).
+    """
+    A32 = np.ascontiguousarray(A).astype(_F32)
+    amax = np.max(np.abs(A32), axis=1) if A32.shape[1] else np.zeros(A32.shape[0], _F32)
+    sa = (amax / _F32(127.0)).astype(_F32)
+    qa = np.zeros(A32.shape, dtype=np.int8)
+    live = sa > 0
+    if np.any(live):
+        r = np.rint(A32[live] / sa[live, None])
+        qa[live] = np.clip(r, -127, 127).astype(np.int8)
+    rowsum = qa.astype(np.int64).sum(axis=1).astype(np.int32)
+    return qa, sa, rowsum
+
+
+# ----------------------------------------------------------------------------
+# matmul
+# ----------------------------------------------------------------------------
+def int_accumulate(qa, qw):
+    """INT32 accumulators acc[m,n] = sum_k qa[m,k] * qw[n,k] ("nt").
+
+    BitBLAS page "What is BitBLAS": C[M,N] = A[M,K] x W[N,K], both operands
+    K-contiguous. INT4 page Part 1 step 3: 8-bit products summed into INT32.
+    Computed exactly in int64 and checked to fit int32.
+    """
+    acc = np.asarray(qa, np.int64) @ np.asarray(qw, np.int64).T
+    if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -(2**31)):
+        raise OverflowError("accumulator exceeds int32")
+    return acc
+
+
+def int_accumulate_entries(qa, qw, rows, cols):
+    """The same sums for selected (rows[i], cols[i]) entries only."""
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    a = np.asarray(qa, np.int64)[rows]
+    w = np.asarray(qw, np.int64)[cols]
+    return np.einsum("ik,ik->i", a, w)
+
+
+def dequant_epilogue(acc, ws, sa, bias, out):
+    """Scale INT32 accumulators back to real numbers.
+
+    INT4 page, Part 1 steps 3-4: multiply the INT32 result by
+    weight_scale * activation_scale, optionally add a bias, convert to the
+    output precision (or hand back the INT32 result). ``acc`` is [M,N] (or
+    a flat vector of entries with matching ``ws``/``sa``/``bias``). The
+    product is formed in float64 and rounded once to the output type.
+    """
+    acc = np.asarray(acc, np.int64)
+    if out == OUT_I32:
+        return acc.astype(np.int32)
+    v = acc.astype(np.float64) * np.asarray(ws, np.float64) * np.asarray(sa, np.float64)
+    if bias is not None:
+        v = v + np.asarray(bias, np.float64)
+    if out == OUT_F32:
+        return v.astype(_F32)
+    if out == OUT_F16:
+        return v.astype(np.float16)
+    raise ValueError(out)
+
+
+def w4a8_gemm(qa, sa, qw, ws, bias=None, out=OUT_F16):
+    """W4A8: INT8 activations x symmetric INT4 weights -> out.
+
+    ``qa`` int8 [M,K], ``sa`` float32 [M], ``qw`` int8 codes [N,K] in
+    [-7,7] (unpacked), ``ws`` float32 [N], ``bias`` fp16 [N] or None.
+    """
+    acc = int_accumulate(qa, qw)
+    return dequant_epilogue(acc, np.asarray(ws, np.float32)[None, :],
+                            np.asarray(sa, np.float32)[:, None],
+                            None if bias is None else np.asarray(bias)[None, :], out)
+
+
+def w2a8_gemm(qa, sa, codes, scale16, bias=None, out=OUT_F16):
+    """W2A8: INT8 activations x ternary codes with one fp16 tensor scale."""
+    acc = int_accumulate(qa, codes)
+    ws = np.float64(np.float16(scale16))
+    return dequant_epilogue(acc, ws, np.asarray(sa, np.float32)[:, None],
+                            None if bias is None else np.asarray(bias)[None, :], out)
+
+
+def _dequant_group(q, s16, z, group_size):
+    """(q - z) * s per element in float64 (zeros_mode "original")."""
+    N, K = q.shape
+    G = K // group_size
+    d = (q.reshape(N, G, group_size).astype(np.float64)
+         - z.astype(np.float64)[:, :, None]) * s16.astype(np.float64)[:, :, None]
+    return d.reshape(N, K)
+
+
+def w4a16_gemm(A16, q, s16, z, group_size=128, bias=None):
+    """W4A16: fp16 activations x group-quantized uINT4 weights -> fp16.
+
+    BitBLAS page data-type table row FP16 x INT4 and "Advanced features 2"
+    (group scales and zeros). C[m,n] = fp16(sum_k a[m,k] * (q[n,k] - z) * s
+    + bias[n]), with the sum in float64 (reading 6).
+    """
+    Wd = _dequant_group(np.asarray(q), np.asarray(s16), np.asarray(z), group_size)
+    C = np.asarray(A16).astype(np.float64) @ Wd.T
+    if bias is not None:
+        C = C + np.asarray(bias).astype(np.float64)[None, :]
+    return C.astype(np.float16)
+
+
+def w4a16_entries(A16, q, s16, z, rows, cols, group_size=128, bias=None):
+    """The W4A16 result for selected (rows[i], cols[i]) entries only."""
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    Wd = _dequant_group(np.asarray(q)[cols], np.asarray(s16)[cols],
+                        np.asarray(z)[cols], group_size)
+    a = np.asarray(A16)[rows].astype(np.float64)
+    v = np.einsum("ik,ik->i", a, Wd)
+    if bias is not None:
+        v = v + np.asarray(bias).astype(np.float64)[cols]
+    return v.astype(np.float16)
