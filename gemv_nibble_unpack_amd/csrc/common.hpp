@@ -1,0 +1,113 @@
+// Shared helpers for the gfx950 kernels and the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gemv_nibble_unpack.h"
+
+namespace w4 {
+
+// ---------------------------------------------------------------------------
+// vector types used by the MFMA builtins and 16-byte memory operations
+// ---------------------------------------------------------------------------
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef int i4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// prepacked layout geometry
+//
+// Weights are cut into tiles of 16 output rows (n) x TILE_K reduction
+// elements (k). Every tile is 1 KiB: 64 lanes x 16 bytes, so one
+// global_load_dwordx4 per lane of a wave moves one whole tile. Lane l of a
+// tile holds row n = 16*t + (l & 15) and the (l >> 4)-th quarter of the
+// tile's k range, i.e. 16 consecutive bytes of that row in the canonical
+// packed order, re-ordered inside each 4-byte word so that the unpack in
+// registers is a handful of AND/OR/shift operations (see the unpack_*
+// helpers). Tiles are stored n-tile-major: tile (t, kt) at (t*KT + kt) KiB.
+//
+// The W4A16 layout appends the group scales (fp16) and zeros (uint8) in the
+// same n-tile order, four consecutive groups per (tile row, quad) so a lane
+// fetches its row's four scales with one 8-byte load and its four zeros
+// with one 4-byte load.
+// ---------------------------------------------------------------------------
+constexpr int TILE_N = 16;
+constexpr int TILE_BYTES = 1024;
+
+struct Geometry {
+  int NT;          // n tiles
+  int KT;          // k tiles
+  int KQ;          // k quads (groups of four k tiles)
+  int tile_k;      // k extent of one tile
+  size_t w_bytes;  // bytes of the code section
+  size_t s_off;    // byte offset of the scale section (W4A16)
+  size_t z_off;    // byte offset of the zero section (W4A16)
+  size_t total;    // prepacked bytes
+};
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__host__ __device__ inline Geometry geometry(int layout, int N, int K) {
+  Geometry g{};
+  g.tile_k = layout == W4_LAYOUT_W2A8 ? 256 : 128;
+  g.NT = ceil_div(N, TILE_N);
+  g.KT = ceil_div(K, g.tile_k);
+  g.KQ = ceil_div(g.KT, 4);
+  g.w_bytes = (size_t)g.NT * g.KT * TILE_BYTES;
+  g.s_off = g.w_bytes;
+  g.z_off = g.w_bytes;
+  g.total = g.w_bytes;
+  if (layout == W4_LAYOUT_W4A16) {
+    g.z_off = g.s_off + (size_t)g.NT * g.KQ * TILE_N * 4 * sizeof(uint16_t);
+    g.total = g.z_off + (size_t)g.NT * g.KQ * TILE_N * 4;
+  }
+  return g;
+}
+
+// ---------------------------------------------------------------------------
+// host-side validation helpers
+// ---------------------------------------------------------------------------
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+// Wave-wide reductions (64 lanes) through cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// fp16 bit pattern <-> float
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+}
+
+}  // namespace w4

@@ -1,0 +1,168 @@
+// C-ABI matmul entry points: argument validation, launch planning, dispatch
+// between the decode kernel (M <= 16) and the prefill GEMM kernel.
+
+#include "gemm.hpp"
+#include "gemv.hpp"
+
+namespace w4 {
+
+constexpr int GEMV_WAVES = 8;
+constexpr int GEMV_U = 4;
+constexpr int TARGET_BLOCKS = 256;  // one block per compute unit
+
+struct Plan {
+  bool gemm;        // prefill kernel instead of the decode kernel
+  int tn, ksplit, kts, mtiles, ngroups;
+  size_t counters_bytes, ws_bytes;
+};
+
+inline int kind_layout(int kind) {
+  return kind == KIND_W4A8 ? W4_LAYOUT_W4A8 : kind == KIND_W4A16 ? W4_LAYOUT_W4A16 : W4_LAYOUT_W2A8;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Deterministic in (kind, M, N, K): w4_workspace_bytes and the launch agree.
+inline Plan make_plan(int kind, int M, int N, int K) {
+  const Geometry g = geometry(kind_layout(kind), N, K);
+  Plan P{};
+  P.gemm = use_gemm(kind, M);
+  if (P.gemm) {
+    P.ws_bytes = gemm_workspace_bytes(kind, M, N, K);
+    return P;
+  }
+  P.tn = 1;
+  P.mtiles = ceil_div(M, 16);
+  P.ngroups = ceil_div(g.NT, P.tn);
+  const int blocks = P.ngroups * P.mtiles;
+  int ks = 1;
+  // split K across blocks until the chip has a block per CU, keeping at
+  // least GEMV_WAVES k tiles per split so no wave of a block idles
+  while (blocks * ks < TARGET_BLOCKS && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ks *= 2;
+  P.kts = ceil_div(g.KT, ks);
+  P.ksplit = ceil_div(g.KT, P.kts);
+  if (P.ksplit > 1) {
+    P.counters_bytes = align256((size_t)P.mtiles * P.ngroups * sizeof(unsigned));
+    P.ws_bytes = P.counters_bytes + (size_t)P.mtiles * P.ksplit * P.ngroups * P.tn * 256 * 4;
+  }
+  return P;
+}
+
+template <int KIND>
+int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream) {
+  p.ksplit = P.ksplit;
+  p.kts = P.kts;
+  p.counters = reinterpret_cast<unsigned*>(ws);
+  p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + P.counters_bytes : nullptr;
+  const dim3 grid(P.ngroups, P.ksplit, P.mtiles);
+  hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, 1, GEMV_U>), grid, dim3(GEMV_WAVES * 64), 0,
+                     stream, p);
+  return launch_status();
+}
+
+template <int KIND>
+int run(MMParams p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const Plan P = make_plan(KIND, p.M, p.N, p.K);
+  if (P.ws_bytes) {
+    if (!ws || ws_bytes < P.ws_bytes) return W4_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return W4_ERR_ALIGN;
+  }
+  const Geometry g = geometry(kind_layout(KIND), p.N, p.K);
+  p.NT = g.NT;
+  p.KT = g.KT;
+  p.KQ = g.KQ;
+  if (P.gemm) return launch_gemm<KIND>(p, ws, stream);
+  return launch_gemv<KIND>(P, p, ws, stream);
+}
+
+inline int check_common(int M, int N, int K, int kmult) {
+  if (M < 0 || N < 1 || K < kmult || K > W4_MAX_K || K % kmult) return W4_ERR_SHAPE;
+  return W4_OK;
+}
+
+inline bool out_aligned(const void* C, int out_dtype) {
+  return aligned(C, out_dtype == W4_OUT_F16 ? 2 : 4);
+}
+
+}  // namespace w4
+
+using namespace w4;
+
+extern "C" size_t w4_workspace_bytes(int layout, int M, int N, int K) {
+  int kind;
+  if (layout == W4_LAYOUT_W4A8) kind = KIND_W4A8;
+  else if (layout == W4_LAYOUT_W4A16) kind = KIND_W4A16;
+  else if (layout == W4_LAYOUT_W2A8) kind = KIND_W2A8;
+  else return 0;
+  if (check_common(M, N, K, kind == KIND_W4A16 ? W4_GROUP_SIZE : 16) != W4_OK || M == 0) return 0;
+  return make_plan(kind, M, N, K).ws_bytes;
+}
+
+static int a8_common(int kind, const int8_t* Aq, const float* a_scale, const uint8_t* Wp,
+                     const void* scale, const uint16_t* bias, void* C, int out_dtype, int M, int N,
+                     int K, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (out_dtype != W4_OUT_F16 && out_dtype != W4_OUT_F32 && out_dtype != W4_OUT_I32)
+    return W4_ERR_ARG;
+  const int st = check_common(M, N, K, 16);
+  if (st != W4_OK) return st;
+  if (M == 0) return W4_OK;
+  if (!Aq || !a_scale || !Wp || !scale || !C) return W4_ERR_NULL;
+  if (!aligned(Aq, 16) || !aligned(Wp, 16) || !aligned(a_scale, 4) || !out_aligned(C, out_dtype) ||
+      (bias && !aligned(bias, 2)) || !aligned(scale, kind == KIND_W4A8 ? 4 : 2))
+    return W4_ERR_ALIGN;
+  MMParams p{};
+  p.A = Aq;
+  p.a_scale = a_scale;
+  p.Wt = Wp;
+  p.w_scale = kind == KIND_W4A8 ? (const float*)scale : nullptr;
+  p.w_scale16 = kind == KIND_W2A8 ? (const uint16_t*)scale : nullptr;
+  p.bias = out_dtype == W4_OUT_I32 ? nullptr : bias;
+  p.C = C;
+  p.out_dtype = out_dtype;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return kind == KIND_W4A8 ? run<KIND_W4A8>(p, ws, ws_bytes, stream)
+                           : run<KIND_W2A8>(p, ws, ws_bytes, stream);
+}
+
+extern "C" int w4a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp,
+                         const float* w_scale, const uint16_t* bias, void* C, int out_dtype, int M,
+                         int N, int K, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return a8_common(KIND_W4A8, Aq, a_scale, Wp, w_scale, bias, C, out_dtype, M, N, K, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" int w2a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp,
+                         const uint16_t* w_scale16, const uint16_t* bias, void* C, int out_dtype,
+                         int M, int N, int K, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return a8_common(KIND_W2A8, Aq, a_scale, Wp, w_scale16, bias, C, out_dtype, M, N, K, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size,
+                          const uint16_t* bias, uint16_t* C, int M, int N, int K, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (group_size != W4_GROUP_SIZE) return W4_ERR_ARG;
+  const int st = check_common(M, N, K, W4_GROUP_SIZE);
+  if (st != W4_OK) return st;
+  if (M == 0) return W4_OK;
+  if (!A || !Wp || !C) return W4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(Wp, 16) || !aligned(C, 2) || (bias && !aligned(bias, 2)))
+    return W4_ERR_ALIGN;
+  const Geometry g = geometry(W4_LAYOUT_W4A16, N, K);
+  MMParams p{};
+  p.A = A;
+  p.Wt = Wp;
+  p.St = reinterpret_cast<const uint16_t*>(Wp + g.s_off);
+  p.Zt = Wp + g.z_off;
+  p.bias = bias;
+  p.C = C;
+  p.out_dtype = W4_OUT_F16;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return run<KIND_W4A16>(p, workspace, workspace_bytes, stream);
+}

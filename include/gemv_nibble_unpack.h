@@ -1,0 +1,212 @@
+/*
+ * gemv_nibble_unpack.h -- C ABI of the MI355X (gfx950) low-bit-weight matmul
+ * library.
+ *
+ * The library computes the mixed-precision product stated on the BitBLAS
+ * practical-guide page, section "What is BitBLAS":
+ *
+ *     C[M,N] = A[M,K] x W[N,K]^T          (layout "nt": both K-contiguous)
+ *
+ * with W stored as 4-bit codes, two per byte (INT4 quantization page, Part 1
+ * step 1 "storage"), or as 2-bit ternary codes, four per byte (BitBLAS page,
+ * data-type table row INT8 x INT2 and the BitNet-b1.58 case), and A either
+ * INT8 with a per-token scale (INT4 page, Part 1 steps 2-4: INT32 accumulate,
+ * then multiply by weight_scale * activation_scale) or fp16 (BitBLAS page,
+ * table row FP16 x INT4 with the group scales and zeros of "Advanced
+ * features 2").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers unless stated otherwise, owned by
+ *   the caller, row-major and dense. fp16 data is passed as uint16_t holding
+ *   IEEE binary16 bit patterns.
+ * - Every call is asynchronous on `stream` (NULL = the default stream). The
+ *   library never allocates device memory, never synchronises, and holds no
+ *   state besides its code objects.
+ * - Every call validates its arguments before touching the GPU and returns
+ *   W4_OK (0) or a negative status; nothing is launched when it fails.
+ *   W4_ERR_HIP means the launch itself failed (hipGetLastError).
+ * - Large buffers (W, Wq, Wp, A, Aq, C, codes, workspace) must be 16-byte
+ *   aligned; small vectors (scales, zeros, bias, a_scale, rowsum) need their
+ *   natural alignment.
+ * - Sizes: N >= 1, K >= 1, M >= 1 (M = 0 is accepted by the matmul entry
+ *   points and returns W4_OK without a launch). K is limited to 131072 so that
+ *   INT32 accumulators cannot overflow.
+ */
+#ifndef GEMV_NIBBLE_UNPACK_H
+#define GEMV_NIBBLE_UNPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define W4_OK             0
+#define W4_ERR_NULL      -1   /* a required pointer is NULL                   */
+#define W4_ERR_SHAPE     -2   /* a size is out of range / breaks a multiple   */
+#define W4_ERR_ALIGN     -3   /* a pointer is not aligned as required         */
+#define W4_ERR_ARG       -4   /* an enumerated argument has an unknown value  */
+#define W4_ERR_WORKSPACE -5   /* workspace NULL or smaller than required      */
+#define W4_ERR_HIP       -6   /* the HIP runtime rejected the launch          */
+
+/* ---- enumerations -------------------------------------------------------- */
+/* weight schemes for quantize_pack_w4 */
+#define W4_SYM_PER_CHANNEL 0  /* INT4 in [-7,7], float32 scale per row n      */
+#define W4_ASYM_GROUP      1  /* uINT4 in [0,15], fp16 scale + uint8 zero per
+                                 row n and group of 128 consecutive k         */
+/* matmul output types */
+#define W4_OUT_F16 0
+#define W4_OUT_F32 1
+#define W4_OUT_I32 2          /* the raw INT32 accumulators (A8 paths only)  */
+/* activation input types for quantize_a8 */
+#define W4_IN_F16 0
+#define W4_IN_F32 1
+/* prepacked weight layouts (what the matmul kernels read) */
+#define W4_LAYOUT_W4A8  0     /* INT4 codes for the INT8-activation kernels   */
+#define W4_LAYOUT_W4A16 1     /* uINT4 codes + group scales/zeros, fp16 acts  */
+#define W4_LAYOUT_W2A8  2     /* ternary 2-bit codes, INT8 activations        */
+
+#define W4_GROUP_SIZE 128
+#define W4_MAX_K 131072
+
+/* Human-readable text for a status code (static string, never NULL). */
+const char* w4_status_string(int status);
+
+/* ---- offline weight preparation ------------------------------------------ */
+
+/*
+ * quantize_pack_w4 -- quantize float32 weights to 4-bit codes and pack them.
+ *
+ * W4_SYM_PER_CHANNEL (INT4 page, Part 1 step 1, with the INT4 range):
+ *   s[n] = max_k |W[n,k]| / 7 (float32 division), q = clip(rint(W / s[n]),
+ *   -7, 7) with round-half-to-even; s[n] == 0 gives q = 0.
+ *   `scales` is float32[N]; `zeros` must be NULL; group_size must be -1.
+ * W4_ASYM_GROUP (BitBLAS page, "Advanced features 2", zeros_mode original):
+ *   per group g of 128 consecutive k: s = fp16((max - min) / 15), then with
+ *   sf = float(s): z = clip(rint(-min / sf), 0, 15), q = clip(rint(W / sf) + z,
+ *   0, 15); sf == 0 gives q = z = 0. Reconstruction is (q - z) * s.
+ *   `scales` is fp16[N, K/128]; `zeros` is uint8[N, K/128]; group_size = 128;
+ *   K must be a multiple of 128.
+ * Packing (both): Wq[n, j] = (q[n,2j] & 15) | (q[n,2j+1] & 15) << 4, i.e.
+ *   even k in the low nibble, signed codes as two's complement. Wq is
+ *   uint8[N, K/2]; K must be even. W must be finite.
+ */
+int quantize_pack_w4(const float* W, int N, int K, int scheme, int group_size,
+                     uint8_t* Wq, void* scales, uint8_t* zeros, hipStream_t stream);
+
+/*
+ * quantize_pack_w2 -- pack ternary codes four per byte (BitBLAS page,
+ * data-type table row INT8 x INT2; BitNet-b1.58 case).
+ *   Wq[n, j] = sum_i (codes[n,4j+i] & 3) << 2i (2-bit two's complement:
+ *   1 -> 01, 0 -> 00, -1 -> 11). codes is int8[N,K] with values in [-2,1];
+ *   Wq is uint8[N, K/4]; K must be a multiple of 4.
+ */
+int quantize_pack_w2(const int8_t* codes, int N, int K, uint8_t* Wq, hipStream_t stream);
+
+/*
+ * ternary_scale_f16 -- per-tensor scale of a ternary weight: fp16 of the mean
+ * absolute value of the float32 source (summed in float64, rounded once to
+ * fp16, half-to-even). Writes one fp16 value to the DEVICE pointer scale.
+ * count >= 1.
+ */
+int ternary_scale_f16(const float* src, int64_t count, uint16_t* scale, hipStream_t stream);
+
+/*
+ * prepack_bytes -- size in bytes of the prepacked buffer for a layout, or 0 if
+ * the arguments are invalid. The prepacked buffer is opaque: it holds the
+ * codes in the order the kernels stream them (16 rows x 128 k per 1 KiB tile
+ * for 4-bit codes, 16 rows x 256 k for 2-bit), padded with zero codes to whole
+ * tiles, and for W4_LAYOUT_W4A16 also the group scales and zeros.
+ * This is the offline "compressed format" of the BitBLAS page (performance
+ * advice 2): the weight is transformed once so no work is spent at run time.
+ */
+size_t prepack_bytes(int layout, int N, int K);
+
+/*
+ * prepack_w -- canonical packed codes -> prepacked buffer Wp.
+ *   W4_LAYOUT_W4A8 : Wq uint8[N,K/2] (signed INT4); scales, zeros unused
+ *                    (pass NULL); K multiple of 16.
+ *   W4_LAYOUT_W4A16: Wq uint8[N,K/2] (uINT4), scales fp16[N,K/128], zeros
+ *                    uint8[N,K/128]; K multiple of 128.
+ *   W4_LAYOUT_W2A8 : Wq uint8[N,K/4]; scales, zeros unused; K multiple of 16.
+ * Wp must hold prepack_bytes(layout, N, K) bytes.
+ */
+int prepack_w(int layout, const uint8_t* Wq, const void* scales, const uint8_t* zeros,
+              int N, int K, uint8_t* Wp, hipStream_t stream);
+
+/* unprepack_w -- exact inverse of prepack_w (for checking a layout). */
+int unprepack_w(int layout, const uint8_t* Wp, int N, int K, uint8_t* Wq, void* scales,
+                uint8_t* zeros, hipStream_t stream);
+
+/* ---- per-call activation quantization ------------------------------------- */
+
+/*
+ * quantize_a8 -- per-token dynamic INT8 activations (INT4 page, Part 1 step 2):
+ *   a_scale[m] = max_k |A[m,k]| / 127 (float32; fp16 input widened exactly),
+ *   Aq = clip(rint(A / a_scale[m]), -127, 127) (half-to-even; a_scale == 0
+ *   gives 0), rowsum[m] = sum_k Aq[m,k] (int32; pass NULL to skip).
+ *   A is fp16 or float32 [M,K] per in_dtype; Aq is int8[M,K]; K multiple of 8.
+ */
+int quantize_a8(const void* A, int in_dtype, int M, int K, int8_t* Aq, float* a_scale,
+                int32_t* rowsum, hipStream_t stream);
+
+/* ---- the matmul ------------------------------------------------------------ */
+
+/*
+ * w4_workspace_bytes -- device workspace a matmul call needs (0 if none).
+ * The workspace must be zero-filled once before its first use; every call
+ * leaves the part it relies on zero again, so the same buffer can be reused
+ * by later calls on the same stream. Calls that overlap in time must not
+ * share a workspace.
+ */
+size_t w4_workspace_bytes(int layout, int M, int N, int K);
+
+/*
+ * w4a8_gemm -- INT8 activations x symmetric INT4 weights (INT4 page, Part 1
+ * steps 3-4):
+ *   acc[m,n] = sum_k Aq[m,k] * q[n,k]  (exact INT32),
+ *   W4_OUT_I32: C = acc (int32[M,N]);
+ *   W4_OUT_F32: C = acc * w_scale[n] * a_scale[m] (float32[M,N]);
+ *   W4_OUT_F16: C = fp16(acc * w_scale[n] * a_scale[m] + bias[n]) (fp16[M,N]).
+ *   Aq int8[M,K]; a_scale float32[M]; Wp from prepack_w(W4_LAYOUT_W4A8);
+ *   w_scale float32[N]; bias fp16[N] or NULL (ignored for W4_OUT_I32).
+ *   K multiple of 16. M <= 16 runs the decode GEMV kernel, larger M the
+ *   LDS-tiled MFMA GEMM kernel.
+ */
+int w4a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp, const float* w_scale,
+              const uint16_t* bias, void* C, int out_dtype, int M, int N, int K,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * w2a8_gemm -- INT8 activations x ternary 2-bit weights with one per-tensor
+ * fp16 scale (device pointer w_scale16, e.g. from ternary_scale_f16). Same
+ * outputs as w4a8_gemm with w_scale[n] replaced by the tensor scale. Wp from
+ * prepack_w(W4_LAYOUT_W2A8). K multiple of 16.
+ */
+int w2a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp,
+              const uint16_t* w_scale16, const uint16_t* bias, void* C, int out_dtype,
+              int M, int N, int K, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/*
+ * w4a16_gemm -- fp16 activations x group-128 uINT4 weights (BitBLAS page,
+ * table row FP16 x INT4; "Advanced features 2"):
+ *   C[m,n] = fp16( sum_g s[n,g] * sum_{k in g} A[m,k] * (q[n,k] - z[n,g])
+ *                  + bias[n] ),
+ *   accumulated in float32. A fp16[M,K]; Wp from prepack_w(W4_LAYOUT_W4A16)
+ *   (it carries the scales and zeros); group_size must be 128; bias fp16[N]
+ *   or NULL; C fp16[M,N]. K multiple of 128.
+ */
+int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size, const uint16_t* bias,
+               uint16_t* C, int M, int N, int K, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMV_NIBBLE_UNPACK_H */

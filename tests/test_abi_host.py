@@ -1,0 +1,104 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+the header declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemv_nibble_unpack_amd as G
+from gemv_nibble_unpack_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gemv_nibble_unpack.h")
+
+# fake, 256-aligned device addresses: validation must fail before any use
+P = ctypes.c_void_p(0x7F0000000000)
+P2 = ctypes.c_void_p(0x7F0000100000)
+MIS = ctypes.c_void_p(0x7F0000000002)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_library_agree():
+    lib = G.load()
+    names = declared_functions()
+    assert len(names) == 12, names
+    assert set(names) == set(L.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_constants_match_header():
+    text = open(HEADER).read()
+    for name in ["W4_OK", "W4_ERR_NULL", "W4_ERR_SHAPE", "W4_ERR_ALIGN", "W4_ERR_ARG",
+                 "W4_ERR_WORKSPACE", "W4_ERR_HIP", "W4_SYM_PER_CHANNEL", "W4_ASYM_GROUP",
+                 "W4_OUT_F16", "W4_OUT_F32", "W4_OUT_I32", "W4_IN_F16", "W4_IN_F32",
+                 "W4_LAYOUT_W4A8", "W4_LAYOUT_W4A16", "W4_LAYOUT_W2A8", "W4_GROUP_SIZE",
+                 "W4_MAX_K"]:
+        m = re.search(rf"#define\s+{name}\s+(-?\d+)", text)
+        assert m, name
+        assert int(m.group(1)) == getattr(L, name), name
+
+
+def test_status_strings():
+    lib = G.load()
+    for s in range(-6, 1):
+        assert lib.w4_status_string(s)
+    assert lib.w4_status_string(-99) == b"unknown status"
+
+
+def test_sizes():
+    lib = G.load()
+    # 4096x4096 W4A16: codes + fp16 scales + uint8 zeros, in whole tiles
+    assert lib.prepack_bytes(L.W4_LAYOUT_W4A16, 4096, 4096) == 4096 * 2048 + 4096 * 32 * 3
+    assert lib.prepack_bytes(L.W4_LAYOUT_W4A8, 11008, 4096) == 11008 * 2048
+    # ragged shapes round up to 16 rows x 128 k (4-bit) or 256 k (2-bit) tiles
+    assert lib.prepack_bytes(L.W4_LAYOUT_W4A8, 50, 208) == 4 * 2 * 1024
+    assert lib.prepack_bytes(L.W4_LAYOUT_W2A8, 3200, 8640) == 200 * 34 * 1024
+    assert lib.prepack_bytes(L.W4_LAYOUT_W4A16, 16, 100) == 0       # K % 128
+    assert lib.prepack_bytes(7, 16, 128) == 0
+    assert lib.w4_workspace_bytes(L.W4_LAYOUT_W4A16, 1, 4096, 4096) == 0
+    assert lib.w4_workspace_bytes(L.W4_LAYOUT_W2A8, 1, 16, 131072) > 0
+
+
+def test_error_paths_before_launch():
+    lib = G.load()
+    s = None
+    # quantize_pack_w4
+    assert lib.quantize_pack_w4(None, 4, 8, 0, -1, P, P2, None, s) == L.W4_ERR_NULL
+    assert lib.quantize_pack_w4(P, 4, 7, 0, -1, P, P2, None, s) == L.W4_ERR_SHAPE
+    assert lib.quantize_pack_w4(P, 4, 8, 5, -1, P, P2, None, s) == L.W4_ERR_ARG
+    assert lib.quantize_pack_w4(P, 4, 8, 0, 128, P, P2, None, s) == L.W4_ERR_ARG
+    assert lib.quantize_pack_w4(P, 4, 200, 1, 128, P, P2, P2, s) == L.W4_ERR_SHAPE
+    assert lib.quantize_pack_w4(MIS, 4, 8, 0, -1, P, P2, None, s) == L.W4_ERR_ALIGN
+    assert lib.quantize_pack_w4(P, 4, 256, 1, 128, P, P2, None, s) == L.W4_ERR_NULL
+    # quantize_pack_w2 / ternary scale / quantize_a8
+    assert lib.quantize_pack_w2(P, 4, 6, P2, s) == L.W4_ERR_SHAPE
+    assert lib.ternary_scale_f16(P, 0, P2, s) == L.W4_ERR_SHAPE
+    assert lib.quantize_a8(P, 3, 2, 16, P, P2, None, s) == L.W4_ERR_ARG
+    assert lib.quantize_a8(P, 0, 2, 12, P, P2, None, s) == L.W4_ERR_SHAPE
+    # prepack
+    assert lib.prepack_w(0, P, None, None, 16, 24, P2, s) == L.W4_ERR_SHAPE
+    assert lib.prepack_w(1, P, None, None, 16, 128, P2, s) == L.W4_ERR_NULL
+    # matmuls
+    args = (P, P, P, P, None, P2, L.W4_OUT_F16)
+    assert lib.w4a8_gemm(*args, 1, 16, 24, None, 0, s) == L.W4_ERR_SHAPE
+    assert lib.w4a8_gemm(*args, 1, 16, L.W4_MAX_K + 16, None, 0, s) == L.W4_ERR_SHAPE
+    assert lib.w4a8_gemm(*args, 1, 0, 32, None, 0, s) == L.W4_ERR_SHAPE
+    assert lib.w4a8_gemm(P, P, P, P, None, P2, 9, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
+    assert lib.w4a8_gemm(None, P, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_NULL
+    assert lib.w4a8_gemm(MIS, P, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
+    assert lib.w4a8_gemm(None, None, None, None, None, None, 0, 0, 16, 32, None, 0, s) == L.W4_OK
+    assert lib.w2a8_gemm(P, P, P, P, None, P2, 0, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
+    assert lib.w4a16_gemm(P, P, 64, None, P2, 1, 16, 128, None, 0, s) == L.W4_ERR_ARG
+    assert lib.w4a16_gemm(P, P, 128, None, P2, 1, 16, 192, None, 0, s) == L.W4_ERR_SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        G.quantize_pack_w4(torch.zeros(4, 8))

@@ -1,0 +1,275 @@
+"""GPU parity: every kernel through the C ABI against the CPU oracle.
+
+Bit-exact for packed bytes, scales, zeros, INT8 activations and INT32
+accumulators; |gpu - ref| <= 2^-9 |ref| + 1e-3 rms(ref) for fp16/fp32 outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from gemv_nibble_unpack_amd import workloads as WL
+from tests._helpers import say, sample_indices, tol_ok
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemv_nibble_unpack_amd as G
+    G.load()
+    return G
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def f16(x):
+    return dev(np.asarray(x, np.float16))
+
+
+# ---------------------------------------------------------------------------
+# offline weight preparation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K", [(256, 256), (50, 96), (11008, 4096)])
+def test_quantize_pack_w4_sym_bitexact(g, N, K):
+    say(f"case quantize_pack_w4 sym N={N} K={K}")
+    W = WL.weights_f32(N, K, seed=1000 + N + K)
+    W[3 % N, :] = 0.0                                  # a zero row
+    Wq, s, z = g.quantize_pack_w4(dev(W), g.W4_SYM_PER_CHANNEL)
+    q_ref, s_ref = O.quantize_w4_sym(W)
+    assert z is None
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(Wq), O.pack_int4(q_ref))
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008), (37, 256)])
+def test_quantize_pack_w4_group_bitexact(g, N, K):
+    say(f"case quantize_pack_w4 group N={N} K={K}")
+    W = WL.weights_f32(N, K, seed=2000 + N + K)
+    W[0, :128] = 0.25                                  # constant group -> scale 0
+    W[min(1, N - 1), 128:256] = np.linspace(1.0, 2.0, 128, dtype=np.float32)  # clipped zero
+    Wq, s, z = g.quantize_pack_w4(dev(W), g.W4_ASYM_GROUP)
+    q_ref, s_ref, z_ref = O.quantize_w4_group(W, 128)
+    assert np.array_equal(host(s).view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(host(z), z_ref)
+    assert np.array_equal(host(Wq), O.pack_int4(q_ref))
+
+
+@pytest.mark.parametrize("N,K", [(3200, 3200), (8640, 3200), (3200, 8640), (5, 20)])
+def test_quantize_pack_w2_and_scale(g, N, K):
+    say(f"case quantize_pack_w2 N={N} K={K}")
+    codes = WL.ternary_codes(N, K, seed=3000 + N + K)
+    src = WL.weights_f32(N, K, seed=3001 + N + K)
+    Wq = g.quantize_pack_w2(dev(codes))
+    assert np.array_equal(host(Wq), O.pack_int2(codes))
+    s = host(g.ternary_scale_f16(dev(src)))[0]
+    ref = O.ternary_scale(src)
+    # both sides round a float64 mean once to fp16; they may differ only if
+    # the mean sits within float64 summation noise of an fp16 midpoint
+    mean = np.abs(src.astype(np.float64)).sum() / src.size
+    lo, hi = np.float16(mean * (1 - 1e-12)), np.float16(mean * (1 + 1e-12))
+    assert s == ref or (lo != hi and s in (lo, hi))
+
+
+@pytest.mark.parametrize("M,K,dt", [(1, 256, np.float32), (2048, 4096, np.float16),
+                                    (3, 8, np.float16), (17, 1000, np.float32)])
+def test_quantize_a8_bitexact(g, M, K, dt):
+    say(f"case quantize_a8 M={M} K={K} {dt.__name__}")
+    A = WL.activations(M, K, seed=4000 + M + K, dtype=dt)
+    A[M // 2, :] = 0
+    Aq, sa, rs = g.quantize_a8(dev(A))
+    qa_ref, sa_ref, rs_ref = O.quantize_a8(A)
+    assert np.array_equal(host(sa), sa_ref)
+    assert np.array_equal(host(Aq), qa_ref)
+    assert np.array_equal(host(rs), rs_ref)
+
+
+@pytest.mark.parametrize("layout,N,K", [(0, 256, 256), (0, 50, 208), (1, 4096, 4096),
+                                        (1, 37, 384), (2, 3200, 8640), (2, 19, 48)])
+def test_prepack_roundtrip(g, layout, N, K):
+    say(f"case prepack layout={layout} N={N} K={K}")
+    rng = np.random.default_rng(layout * 100 + N)
+    rowbytes = K // 4 if layout == 2 else K // 2
+    Wq = rng.integers(0, 256, size=(N, rowbytes), dtype=np.uint8)
+    s = z = None
+    if layout == 1:
+        s = dev(rng.random((N, K // 128)).astype(np.float16))
+        z = dev(rng.integers(0, 16, size=(N, K // 128), dtype=np.uint8))
+    Wp = g.prepack_w(layout, dev(Wq), N, K, s, z)
+    assert Wp.numel() == g.prepack_bytes(layout, N, K)
+    Wq2, s2, z2 = g.unprepack_w(layout, Wp, N, K)
+    assert np.array_equal(host(Wq2), Wq)
+    if layout == 1:
+        assert np.array_equal(host(s2).view(np.uint16), host(s).view(np.uint16))
+        assert np.array_equal(host(z2), host(z))
+
+
+# ---------------------------------------------------------------------------
+# matmul paths
+# ---------------------------------------------------------------------------
+def prep_w4a8(g, W):
+    N, K = W.shape
+    Wq, s, _ = g.quantize_pack_w4(dev(W), g.W4_SYM_PER_CHANNEL)
+    return g.prepack_w(g.W4_LAYOUT_W4A8, Wq, N, K), s
+
+
+def prep_w4a16(g, W):
+    N, K = W.shape
+    Wq, s, z = g.quantize_pack_w4(dev(W), g.W4_ASYM_GROUP)
+    return g.prepack_w(g.W4_LAYOUT_W4A16, Wq, N, K, s, z)
+
+
+def prep_w2a8(g, codes, src):
+    N, K = codes.shape
+    Wq = g.quantize_pack_w2(dev(codes))
+    return g.prepack_w(g.W4_LAYOUT_W2A8, Wq, N, K), g.ternary_scale_f16(dev(src))
+
+
+def test_w4a8_gemv_tiny_config(g):
+    c = WL.W4A8_TINY
+    say(f"case {c.name}")
+    d = c.inputs()
+    Wp, ws = prep_w4a8(g, d["W"])
+    Aq, sa, _ = g.quantize_a8(dev(d["A"]))
+    q_ref, s_ref = O.quantize_w4_sym(d["W"])
+    qa_ref, sa_ref, _ = O.quantize_a8(d["A"])
+    acc_ref = O.int_accumulate(qa_ref, q_ref)
+    C32 = g.w4a8_gemm(Aq, sa, Wp, ws, c.N, out_dtype=g.W4_OUT_I32)
+    assert np.array_equal(host(C32), acc_ref.astype(np.int32))
+    Cf = g.w4a8_gemm(Aq, sa, Wp, ws, c.N, out_dtype=g.W4_OUT_F32)
+    tol_ok(host(Cf), O.w4a8_gemm(qa_ref, sa_ref, q_ref, s_ref, None, O.OUT_F32), c.name)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (1, 50, 208), (3, 100, 1024), (16, 256, 512),
+                                   (17, 40, 256), (5, 2048, 11008)])
+def test_w4a8_small_shapes_bitexact(g, M, N, K):
+    say(f"case w4a8 M={M} N={N} K={K}")
+    W = WL.weights_f32(N, K, seed=5000 + N)
+    A = WL.activations(M, K, seed=5001 + M)
+    bias = WL.bias_f16(N, seed=5002)
+    Wp, ws = prep_w4a8(g, W)
+    Aq, sa, _ = g.quantize_a8(dev(A))
+    q_ref, s_ref = O.quantize_w4_sym(W)
+    qa_ref, sa_ref, _ = O.quantize_a8(A)
+    acc = O.int_accumulate(qa_ref, q_ref)
+    C32 = g.w4a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I32)
+    assert np.array_equal(host(C32), acc.astype(np.int32))
+    C16 = g.w4a8_gemm(Aq, sa, Wp, ws, N, bias=f16(bias), out_dtype=g.W4_OUT_F16)
+    tol_ok(host(C16).astype(np.float64),
+           O.w4a8_gemm(qa_ref, sa_ref, q_ref, s_ref, bias, O.OUT_F16), "f16")
+
+
+def test_w4a8_prefill_config_sampled(g):
+    c = WL.W4A8_PREFILL
+    say(f"case {c.name}")
+    d = c.inputs()
+    Wp, ws = prep_w4a8(g, d["W"])
+    Aq, sa, _ = g.quantize_a8(dev(d["A"]))
+    bias = d["bias"]
+    C32 = host(g.w4a8_gemm(Aq, sa, Wp, ws, c.N, out_dtype=g.W4_OUT_I32))
+    C16 = host(g.w4a8_gemm(Aq, sa, Wp, ws, c.N, bias=f16(bias), out_dtype=g.W4_OUT_F16))
+    q_ref, s_ref = O.quantize_w4_sym(d["W"])
+    qa_ref, sa_ref, _ = O.quantize_a8(d["A"])
+    assert np.array_equal(host(Aq), qa_ref)
+    rows, cols = sample_indices(c.M, c.N, 4000, seed=7)
+    acc = O.int_accumulate_entries(qa_ref, q_ref, rows, cols)
+    assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
+    ref16 = O.dequant_epilogue(acc, s_ref[cols], sa_ref[rows], bias[cols], O.OUT_F16)
+    tol_ok(C16[rows, cols], ref16, c.name)
+
+
+def _w4a16_case(g, c, full=True):
+    say(f"case {c.name}")
+    d = c.inputs()
+    Wp = prep_w4a16(g, d["W"])
+    C = host(g.w4a16_gemm(dev(d["A"]), Wp, c.N))
+    q, s, z = O.quantize_w4_group(d["W"], 128)
+    if full:
+        ref = O.w4a16_gemm(d["A"], q, s, z, 128)
+        tol_ok(C, ref, c.name)
+    else:
+        rows, cols = sample_indices(c.M, c.N, 2000, seed=8)
+        ref = O.w4a16_entries(d["A"], q, s, z, rows, cols, 128)
+        tol_ok(C[rows, cols], ref, c.name)
+
+
+def test_w4a16_decode_config(g):
+    _w4a16_case(g, WL.W4A16_DECODE)
+
+
+@pytest.mark.parametrize("c", WL.W4A16_SWEEP, ids=lambda c: c.name)
+def test_w4a16_sweep(g, c):
+    _w4a16_case(g, c)
+
+
+def test_w4a16_bitblas_example_shape(g):
+    _w4a16_case(g, WL.BITBLAS_EXAMPLE)
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 37, 256), (16, 130, 384), (33, 64, 128), (1, 16, 128)])
+def test_w4a16_ragged_with_bias(g, M, N, K):
+    say(f"case w4a16 ragged M={M} N={N} K={K}")
+    W = WL.weights_f32(N, K, seed=6000 + N)
+    A = WL.activations(M, K, seed=6001 + M)
+    b = WL.bias_f16(N, seed=6002)
+    Wp = prep_w4a16(g, W)
+    C = host(g.w4a16_gemm(dev(A), Wp, N, bias=f16(b)))
+    q, s, z = O.quantize_w4_group(W, 128)
+    tol_ok(C, O.w4a16_gemm(A, q, s, z, 128, b), "ragged")
+
+
+@pytest.mark.parametrize("c", WL.W2A8_TERNARY, ids=lambda c: c.name)
+def test_w2a8_ternary(g, c):
+    say(f"case {c.name}")
+    d = c.inputs()
+    Wp, s16 = prep_w2a8(g, d["codes"], d["src"])
+    Aq, sa, _ = g.quantize_a8(dev(d["A"]))
+    C32 = host(g.w2a8_gemm(Aq, sa, Wp, s16, c.N, out_dtype=g.W4_OUT_I32))
+    C16 = host(g.w2a8_gemm(Aq, sa, Wp, s16, c.N, out_dtype=g.W4_OUT_F16))
+    qa, sa_ref, _ = O.quantize_a8(d["A"])
+    scale = host(s16)[0]
+    if c.M == 1:
+        acc = O.int_accumulate(qa, d["codes"])
+        assert np.array_equal(C32, acc.astype(np.int32))
+        tol_ok(C16, O.w2a8_gemm(qa, sa_ref, d["codes"], scale, None, O.OUT_F16), c.name)
+    else:
+        rows, cols = sample_indices(c.M, c.N, 3000, seed=9)
+        acc = O.int_accumulate_entries(qa, d["codes"], rows, cols)
+        assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
+        ref = O.dequant_epilogue(acc, np.float64(scale), sa_ref[rows], None, O.OUT_F16)
+        tol_ok(C16[rows, cols], ref, c.name)
+
+
+def test_w2a8_extreme_codes_no_overflow(g):
+    # -2 codes (never produced by quantisation but decodable) times -127 at max K
+    say("case w2a8 extreme K=131072")
+    N, K = 16, 131072
+    codes = np.full((N, K), -2, np.int8)
+    Wp, _ = prep_w2a8(g, codes, np.ones((N, K), np.float32))
+    Aq = dev(np.full((1, K), -127, np.int8))
+    sa = dev(np.ones(1, np.float32))
+    s16 = f16(np.ones(1))
+    C32 = host(g.w2a8_gemm(Aq, sa, Wp, s16, N, out_dtype=g.W4_OUT_I32))
+    assert np.all(C32 == 254 * K)
+
+
+def test_matmul_m0_is_noop_and_errors(g):
+    say("case m0 and error statuses")
+    Aq = dev(np.zeros((0, 256), np.int8))
+    W = WL.weights_f32(16, 256, seed=1)
+    Wp, ws = prep_w4a8(g, W)
+    C = g.w4a8_gemm(Aq, dev(np.zeros(0, np.float32)), Wp, ws, 16)
+    assert C.shape == (0, 16)
+    with pytest.raises(g.W4Error) as e:
+        g.w4a16_gemm(f16(np.zeros((1, 256))), Wp, 16, group_size=64)
+    assert e.value.status == -4
