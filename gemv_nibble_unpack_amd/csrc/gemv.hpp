@@ -226,8 +226,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 #pragma unroll
   for (int t = 0; t < TN; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      red[wave][t][4 * b + e][r] = __builtin_bit_cast(float, acc[t][e]);
+    for (int e = 0; e < 4; ++e) {
+      // copy the element to a scalar first: __builtin_bit_cast applied to an
+      // ext-vector element reads element 0 with this compiler
+      const auto v = acc[t][e];
+      red[wave][t][4 * b + e][r] = __builtin_bit_cast(float, v);
+    }
   __syncthreads();
 
   const int rows = min(16, p.M - mtile * 16);
