@@ -46,12 +46,14 @@ struct MMParams {
 
 // ---- unpack helpers (word layouts are fixed by prepack) --------------------
 // W4A16: one 32-bit word (8 codes) -> 8 fp16 values (q - z), slots in k order.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c);
+
 __device__ __forceinline__ h8 unpack_w4_f16(uint32_t w, h2 zlo, h2 zhi) {
   const uint32_t w8 = w >> 8;
-  const h2 p0 = __builtin_bit_cast(h2, (w & 0x000F000Fu) | 0x64006400u);   // 1024+q
-  const h2 p1 = __builtin_bit_cast(h2, (w & 0x00F000F0u) | 0x64006400u);   // 1024+16q
-  const h2 p2 = __builtin_bit_cast(h2, (w8 & 0x000F000Fu) | 0x64006400u);
-  const h2 p3 = __builtin_bit_cast(h2, (w8 & 0x00F000F0u) | 0x64006400u);
+  const h2 p0 = __builtin_bit_cast(h2, and_or(w, 0x000F000Fu, 0x64006400u));    // 1024+q
+  const h2 p1 = __builtin_bit_cast(h2, and_or(w, 0x00F000F0u, 0x64006400u));    // 1024+16q
+  const h2 p2 = __builtin_bit_cast(h2, and_or(w8, 0x000F000Fu, 0x64006400u));
+  const h2 p3 = __builtin_bit_cast(h2, and_or(w8, 0x00F000F0u, 0x64006400u));
   const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const h2 d0 = p0 + zlo;                                       // q - z
   const h2 d1 = __builtin_elementwise_fma(p1, sixteenth, zhi);  // 64+q-(64+z)
@@ -111,189 +113,227 @@ __device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float
   }
 }
 
-// Grid: x = group of TN n tiles, y = k split, z = 16-row m tile.
-template <int KIND, int WAVES, int TN, int U>
-__global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
-  using Tr = KindTraits<KIND>;
-  constexpr bool A16 = KIND == KIND_W4A16;
-  typedef typename std::conditional<A16, f4, i4>::type Acc;
+// v_and_or_b32: (a & b) | c in one VALU op (the compiler splits the
+// expression into two ops).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;   // A row within the m tile / W row within an n tile
+// Activation staging geometry: the block's rows x k range, row-major in LDS
+// with the row stride padded by 16 bytes so the 16 lanes of a fragment read
+// (one per row) fall on different banks.
+template <int KIND>
+struct AStage {
+  static constexpr int ESZ = KIND == KIND_W4A16 ? 2 : 1;            // bytes per element
+  static constexpr int TILE_ROWB = KindTraits<KIND>::TILE_K * ESZ;  // bytes per row per tile
+};
+
+// Grid: x = n tile, y = k split, z = 16-row m tile. Block = WAVES waves.
+// Phase 1: every thread issues its APER 16-byte activation loads, then each
+// wave issues the weight-tile (and group scale/zero) loads of its whole
+// contiguous k run (at most MAXT tiles per pass). Phase 2: activations go to
+// LDS, one barrier. Phase 3: tiles are unpacked and multiplied in order, each
+// waiting only for its own loads.
+template <int KIND, int WAVES, int MAXT, int APER>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
+  using AS = AStage<KIND>;
+  constexpr bool A16 = KIND == KIND_W4A16;
+  constexpr int NTHR = WAVES * 64;
+  typedef typename std::conditional<A16, f4, i4>::type Acc;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15;   // A row within the m tile / W row within the n tile
   const int b = lane >> 4;   // k quarter of a tile
   const int mtile = blockIdx.z;
-  const int m = mtile * 16 + r;
-  const bool mval = m < p.M;
-  const int t0 = blockIdx.x * TN;
-  const int kt_begin = blockIdx.y * p.kts;
-  const int kt_end = min(p.KT, kt_begin + p.kts);
+  const int rows = min(16, p.M - mtile * 16);
+  const int tile = blockIdx.x;
+  const int kb = blockIdx.y * p.kts;
+  const int ke = min(p.KT, kb + p.kts);
+  const int per = (ke - kb + WAVES - 1) / WAVES;
+  const int wb = kb + wave * per;
+  const int nt = max(0, min(ke, wb + per) - wb);     // tiles of this wave (uniform)
 
-  Acc acc[TN];
+  // ---- phase 1a: activation loads (row-major chunks of 16 bytes) ----------
+  const int rowb = (ke - kb) * AS::TILE_ROWB;        // bytes of one staged row
+  const int cpr = rowb / 16;
+  const int total = rows * cpr;
+  const int sstride = rowb + 16;
+  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A);
+  const size_t arow_bytes = (size_t)p.K * AS::ESZ;
+  const size_t kbyte0 = (size_t)kb * AS::TILE_ROWB;
+  u4 stage[APER];
 #pragma unroll
-  for (int t = 0; t < TN; ++t) acc[t] = Acc{};
+  for (int i = 0; i < APER; ++i) {
+    const int c = min(tid + i * NTHR, total - 1);
+    const int row = c / cpr, col = c - row * cpr;
+    size_t off = kbyte0 + (size_t)col * 16;
+    if constexpr (!A16) off = min(off, arow_bytes - 16);   // k tail: clamp, zeroed below
+    stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)(mtile * 16 + row) * arow_bytes + off);
+  }
 
-  const size_t a_row = (size_t)m * p.K;
-
-  for (int kt0 = kt_begin + wave; kt0 < kt_end; kt0 += WAVES * U) {
-    // ---- issue every load of this step first ------------------------------
-    u4 wv[U][TN];
-    u4 av[U][Tr::A_CHUNKS];
-    uint16_t sv[U][TN];
-    uint32_t zv[U][TN];
+  // ---- phase 1b: this wave's weight tiles --------------------------------
+  Acc acc = Acc{};
+  for (int pass = 0; pass * MAXT < max(nt, 1); ++pass) {
+    const int pb = wb + pass * MAXT;
+    const int pn = min(MAXT, nt - pass * MAXT);      // tiles in this pass (uniform)
+    u4 wv[MAXT];
+    uint16_t sv[MAXT];
+    uint8_t zv[MAXT];
+    // Unconditional loads keep the wait counts exact: slots past the run
+    // read tile 0 (a fixed, cache-resident address) and are skipped below.
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kt = kt0 + u * WAVES;
-      const bool kval = kt < kt_end;
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const int tile = t0 + t;
-        if (kval && tile < p.NT) {
-          wv[u][t] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(
-              p.Wt + ((size_t)tile * p.KT + kt) * TILE_BYTES + lane * 16));
-          if constexpr (A16) {
-            const size_t mi = ((size_t)tile * p.KQ + (kt >> 2)) * TILE_N + r;
-            sv[u][t] = p.St[mi * 4 + (kt & 3)];
-            zv[u][t] = p.Zt[mi * 4 + (kt & 3)];
-          }
-        } else {
-          wv[u][t] = u4{0u, 0u, 0u, 0u};
-          if constexpr (A16) {
-            sv[u][t] = 0;
-            zv[u][t] = 0;
-          }
-        }
-      }
-      const int kbase = kt * Tr::TILE_K + b * (Tr::TILE_K / 4);
-#pragma unroll
-      for (int j = 0; j < Tr::A_CHUNKS; ++j) {
-        if constexpr (A16) {
-          av[u][j] = (kval && mval)
-                         ? *reinterpret_cast<const u4*>(
-                               reinterpret_cast<const uint16_t*>(p.A) + a_row + kbase + 8 * j)
-                         : u4{0u, 0u, 0u, 0u};
-        } else {
-          const int k0 = kbase + 16 * j;
-          av[u][j] = (kval && mval && k0 < p.K)
-                         ? *reinterpret_cast<const u4*>(
-                               reinterpret_cast<const int8_t*>(p.A) + a_row + k0)
-                         : u4{0u, 0u, 0u, 0u};
-        }
+    for (int u = 0; u < MAXT; ++u) {
+      const bool live = u < pn;
+      const int kt = pb + u;
+      const size_t ti = live ? (size_t)tile * p.KT + kt : 0;
+      wv[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u4*>(p.Wt + ti * TILE_BYTES + lane * 16));
+      if constexpr (A16) {
+        const size_t mi =
+            live ? (((size_t)tile * p.KQ + (kt >> 2)) * TILE_N + r) * 4 + (kt & 3) : 0;
+        sv[u] = p.St[mi];
+        zv[u] = p.Zt[mi];
       }
     }
-    // ---- unpack + matrix-core products ------------------------------------
+
+    // ---- phase 2: activations to LDS (first pass only) -------------------
+    if (pass == 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        if constexpr (A16) {
-          const _Float16 z = (_Float16)(float)zv[u][t];
-          const _Float16 zl = -((_Float16)1024.0f + z);
-          const _Float16 zh = -((_Float16)64.0f + z);
-          const h2 zlo = {zl, zl}, zhi = {zh, zh};
-          f4 part = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h8 bf = unpack_w4_f16(wv[u][t][j], zlo, zhi);
-            const h8 af = __builtin_bit_cast(h8, av[u][j]);
-            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, part, 0, 0, 0);
+      for (int i = 0; i < APER; ++i) {
+        const int c = tid + i * NTHR;
+        if (c < total) {
+          const int row = c / cpr, col = c - row * cpr;
+          u4 v = stage[i];
+          if constexpr (!A16) {
+            if (kbyte0 + (size_t)col * 16 >= arow_bytes) v = u4{0u, 0u, 0u, 0u};
           }
-          const float s = h2f(sv[u][t]);
+          *reinterpret_cast<u4*>(smem + row * sstride + col * 16) = v;
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- phase 3: unpack + matrix-core products, tile by tile ------------
+    const uint8_t* arow = smem + min(r, rows - 1) * sstride;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(part[e], s, acc[t][e]);
-        } else if constexpr (KIND == KIND_W4A8) {
+    for (int u = 0; u < MAXT; ++u) {
+      if (u >= pn) continue;                         // uniform: tiles past the wave's run
+      const int kl = pb + u - kb;                    // tile index within the staged range
+      if constexpr (A16) {
+        const _Float16 z = (_Float16)(float)zv[u];
+        const _Float16 zl = -((_Float16)1024.0f + z);
+        const _Float16 zh = -((_Float16)64.0f + z);
+        const h2 zlo = {zl, zl}, zhi = {zh, zh};
+        const u4* af = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB + 64 * b);
+        f4 part = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const i4 bf = unpack_w4_i8(wv[u][t][2 * j], wv[u][t][2 * j + 1]);
-            const i4 af = __builtin_bit_cast(i4, av[u][j]);
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[t], 0, 0, 0);
-          }
-        } else {
+        for (int j = 0; j < 4; ++j) {
+          const h8 bf = unpack_w4_f16(wv[u][j], zlo, zhi);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[j]), bf, part,
+                                                        0, 0, 0);
+        }
+        const float s = h2f(sv[u]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const i4 bf = unpack_w2_i8(wv[u][t][j]);
-            const i4 af = __builtin_bit_cast(i4, av[u][j]);
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[t], 0, 0, 0);
-          }
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(part[e], s, acc[e]);
+      } else if constexpr (KIND == KIND_W4A8) {
+        const u4* af = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB + 32 * b);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const i4 bf = unpack_w4_i8(wv[u][2 * j], wv[u][2 * j + 1]);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[j]), bf, acc, 0,
+                                                      0, 0);
+        }
+      } else {
+        const u4* af = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB + 64 * b);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const i4 bf = unpack_w2_i8(wv[u][j]);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[j]), bf, acc, 0,
+                                                      0, 0);
         }
       }
     }
   }
 
-  // ---- cross-wave reduction through LDS ---------------------------------
+  // ---- cross-wave reduction through LDS (reuses the staging buffer) -----
   // MFMA 16x16 output: lane holds column (lane & 15), rows 4*(lane >> 4) + e.
-  __shared__ float red[WAVES][TN][16][16];
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);       // [WAVES][16 rows][16 cols]
 #pragma unroll
-  for (int t = 0; t < TN; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // copy the element to a scalar first: __builtin_bit_cast applied to an
-      // ext-vector element reads element 0 with this compiler
-      const auto v = acc[t][e];
-      red[wave][t][4 * b + e][r] = __builtin_bit_cast(float, v);
-    }
+  for (int e = 0; e < 4; ++e) {
+    // copy the element to a scalar first: __builtin_bit_cast applied to an
+    // ext-vector element reads element 0 with this compiler
+    const auto v = acc[e];
+    red[(wave * 16 + 4 * b + e) * 16 + r] = __builtin_bit_cast(float, v);
+  }
   __syncthreads();
 
-  const int rows = min(16, p.M - mtile * 16);
-  const int nout = TN * 16 * 16;
   const int ngroups = gridDim.x;
   const size_t slot = (size_t)mtile * ngroups + blockIdx.x;
+  constexpr int NOUT = 256;                          // 16 x 16 outputs of the tile
 
   if (p.ksplit == 1) {
-    for (int idx = threadIdx.x; idx < nout; idx += WAVES * 64) {
-      const int t = idx >> 8, row = (idx >> 4) & 15, col = idx & 15;
-      const int n = (t0 + t) * 16 + col;
+    for (int idx = tid; idx < NOUT; idx += NTHR) {
+      const int row = idx >> 4, col = idx & 15;
+      const int n = tile * 16 + col;
       if (row >= rows || n >= p.N) continue;
       float fs = 0.f;
       int is = 0;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        if constexpr (A16) fs += red[w][t][row][col];
-        else is += __builtin_bit_cast(int, red[w][t][row][col]);
+        const float v = red[(w * 16 + row) * 16 + col];
+        if constexpr (A16) fs += v;
+        else is += __builtin_bit_cast(int, v);
       }
       store_out<KIND>(p, mtile * 16 + row, n, fs, is);
     }
     return;
   }
 
-  // ---- split-K: publish this block's partial, last block finishes -------
+  // ---- split-K: publish this block's partial, the last block finishes ----
   uint32_t* part = reinterpret_cast<uint32_t*>(p.partials) +
-                   ((size_t)mtile * p.ksplit + blockIdx.y) * ngroups * nout +
-                   (size_t)blockIdx.x * nout;
-  for (int idx = threadIdx.x; idx < nout; idx += WAVES * 64) {
-    const int t = idx >> 8, row = (idx >> 4) & 15, col = idx & 15;
+                   ((size_t)mtile * p.ksplit + blockIdx.y) * ngroups * NOUT +
+                   (size_t)blockIdx.x * NOUT;
+  for (int idx = tid; idx < NOUT; idx += NTHR) {
+    const int row = idx >> 4, col = idx & 15;
     float fs = 0.f;
     int is = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      if constexpr (A16) fs += red[w][t][row][col];
-      else is += __builtin_bit_cast(int, red[w][t][row][col]);
+      const float v = red[(w * 16 + row) * 16 + col];
+      if constexpr (A16) fs += v;
+      else is += __builtin_bit_cast(int, v);
     }
     part[idx] = A16 ? __builtin_bit_cast(uint32_t, fs) : (uint32_t)is;
   }
   __threadfence();
   __syncthreads();
   __shared__ int last;
-  if (threadIdx.x == 0) last = atomicAdd(&p.counters[slot], 1u) == (unsigned)(p.ksplit - 1);
+  if (tid == 0) last = atomicAdd(&p.counters[slot], 1u) == (unsigned)(p.ksplit - 1);
   __syncthreads();
   if (!last) return;
   __threadfence();
   const uint32_t* base = reinterpret_cast<const uint32_t*>(p.partials) +
-                         (size_t)mtile * p.ksplit * ngroups * nout + (size_t)blockIdx.x * nout;
-  for (int idx = threadIdx.x; idx < nout; idx += WAVES * 64) {
-    const int t = idx >> 8, row = (idx >> 4) & 15, col = idx & 15;
-    const int n = (t0 + t) * 16 + col;
+                         (size_t)mtile * p.ksplit * ngroups * NOUT + (size_t)blockIdx.x * NOUT;
+  for (int idx = tid; idx < NOUT; idx += NTHR) {
+    const int row = idx >> 4, col = idx & 15;
+    const int n = tile * 16 + col;
     if (row >= rows || n >= p.N) continue;
     float fs = 0.f;
     int is = 0;
-    for (int s = 0; s < p.ksplit; ++s) {
-      const uint32_t v = base[(size_t)s * ngroups * nout + idx];
+    for (int sp = 0; sp < p.ksplit; ++sp) {
+      const uint32_t v = base[(size_t)sp * ngroups * NOUT + idx];
       if constexpr (A16) fs += __builtin_bit_cast(float, v);
       else is += (int)v;
     }
     store_out<KIND>(p, mtile * 16 + row, n, fs, is);
   }
-  if (threadIdx.x == 0) p.counters[slot] = 0u;  // leave the workspace zeroed
+  if (tid == 0) p.counters[slot] = 0u;  // leave the workspace zeroed
 }
 
 }  // namespace w4

@@ -1,23 +1,31 @@
 // C-ABI matmul entry points: argument validation, launch planning, dispatch
 // between the decode kernel (M <= 16) and the prefill GEMM kernel.
 
+#include <algorithm>
+
 #include "gemm.hpp"
 #include "gemv.hpp"
 
 namespace w4 {
 
 constexpr int GEMV_WAVES = 8;
-constexpr int GEMV_U = 4;
-constexpr int TARGET_BLOCKS = 256;  // one block per compute unit
+constexpr int GEMV_THREADS = GEMV_WAVES * 64;
+constexpr int TARGET_BLOCKS = 256;          // one block per compute unit
+constexpr int STAGE_MAX = 8 * 16 * GEMV_THREADS;  // activation bytes one block may stage
 
 struct Plan {
   bool gemm;        // prefill kernel instead of the decode kernel
-  int tn, ksplit, kts, mtiles, ngroups;
+  int ksplit, kts, mtiles, maxt, aper;
+  size_t smem;
   size_t counters_bytes, ws_bytes;
 };
 
 inline int kind_layout(int kind) {
   return kind == KIND_W4A8 ? W4_LAYOUT_W4A8 : kind == KIND_W4A16 ? W4_LAYOUT_W4A16 : W4_LAYOUT_W2A8;
+}
+
+inline int tile_rowb(int kind) {
+  return kind == KIND_W4A16 ? 256 : kind == KIND_W4A8 ? 128 : 256;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -31,21 +39,43 @@ inline Plan make_plan(int kind, int M, int N, int K) {
     P.ws_bytes = gemm_workspace_bytes(kind, M, N, K);
     return P;
   }
-  P.tn = 1;
   P.mtiles = ceil_div(M, 16);
-  P.ngroups = ceil_div(g.NT, P.tn);
-  const int blocks = P.ngroups * P.mtiles;
+  const int rows = M < 16 ? M : 16;
+  const int blocks = g.NT * P.mtiles;
+  const int trb = tile_rowb(kind);
   int ks = 1;
-  // split K across blocks until the chip has a block per CU, keeping at
-  // least GEMV_WAVES k tiles per split so no wave of a block idles
-  while (blocks * ks < TARGET_BLOCKS && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ks *= 2;
+  // split K across blocks while the chip has fewer blocks than CUs (keeping a
+  // tile per wave), and until the block's activation rows fit the staging
+  // buffer
+  while ((blocks * ks < TARGET_BLOCKS && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ||
+         (size_t)rows * ceil_div(g.KT, ks) * trb > (size_t)STAGE_MAX)
+    ks *= 2;
   P.kts = ceil_div(g.KT, ks);
   P.ksplit = ceil_div(g.KT, P.kts);
+  const int per = ceil_div(P.kts, GEMV_WAVES);
+  P.maxt = per <= 4 ? 4 : per <= 8 ? 8 : 16;
+  const int chunks = ceil_div(rows * P.kts * trb, 16);
+  const int aper = ceil_div(chunks, GEMV_THREADS);
+  P.aper = aper <= 1 ? 1 : aper <= 2 ? 2 : aper <= 4 ? 4 : 8;
+  P.smem = std::max((size_t)rows * (P.kts * trb + 16), (size_t)GEMV_WAVES * 1024);
   if (P.ksplit > 1) {
-    P.counters_bytes = align256((size_t)P.mtiles * P.ngroups * sizeof(unsigned));
-    P.ws_bytes = P.counters_bytes + (size_t)P.mtiles * P.ksplit * P.ngroups * P.tn * 256 * 4;
+    P.counters_bytes = align256((size_t)P.mtiles * g.NT * sizeof(unsigned));
+    P.ws_bytes = P.counters_bytes + (size_t)P.mtiles * P.ksplit * g.NT * 256 * 4;
   }
   return P;
+}
+
+template <int KIND, int MAXT>
+int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream) {
+  const dim3 grid(p.NT, P.ksplit, P.mtiles);
+  const dim3 block(GEMV_THREADS);
+  switch (P.aper) {
+    case 1: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 1>), grid, block, P.smem, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 2>), grid, block, P.smem, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 4>), grid, block, P.smem, stream, p); break;
+    default: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 8>), grid, block, P.smem, stream, p); break;
+  }
+  return launch_status();
 }
 
 template <int KIND>
@@ -54,10 +84,9 @@ int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream) {
   p.kts = P.kts;
   p.counters = reinterpret_cast<unsigned*>(ws);
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + P.counters_bytes : nullptr;
-  const dim3 grid(P.ngroups, P.ksplit, P.mtiles);
-  hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, 1, GEMV_U>), grid, dim3(GEMV_WAVES * 64), 0,
-                     stream, p);
-  return launch_status();
+  if (P.maxt == 4) return launch_gemv_m<KIND, 4>(P, p, stream);
+  if (P.maxt == 8) return launch_gemv_m<KIND, 8>(P, p, stream);
+  return launch_gemv_m<KIND, 16>(P, p, stream);
 }
 
 template <int KIND>
