@@ -74,6 +74,12 @@ __host__ __device__ inline Geometry geometry(int layout, int N, int K) {
 // ---------------------------------------------------------------------------
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Kernels that take more than 64 KiB of dynamic LDS must say so once.
+inline void allow_smem(const void* kernel, size_t bytes) {
+  if (bytes > 65536) (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                (int)bytes);
+}
+
 inline int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;

@@ -69,12 +69,16 @@ template <int KIND, int MAXT>
 int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream) {
   const dim3 grid(p.NT, P.ksplit, P.mtiles);
   const dim3 block(GEMV_THREADS);
+#define W4_GEMV_CASE(A)                                                   \
+  allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A>, P.smem);     \
+  hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A>), grid, block, P.smem, stream, p)
   switch (P.aper) {
-    case 1: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 1>), grid, block, P.smem, stream, p); break;
-    case 2: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 2>), grid, block, P.smem, stream, p); break;
-    case 4: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 4>), grid, block, P.smem, stream, p); break;
-    default: hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 8>), grid, block, P.smem, stream, p); break;
+    case 1: W4_GEMV_CASE(1); break;
+    case 2: W4_GEMV_CASE(2); break;
+    case 4: W4_GEMV_CASE(4); break;
+    default: W4_GEMV_CASE(8); break;
   }
+#undef W4_GEMV_CASE
   return launch_status();
 }
 

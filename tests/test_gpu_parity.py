@@ -151,7 +151,8 @@ def test_w4a8_gemv_tiny_config(g):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (1, 50, 208), (3, 100, 1024), (16, 256, 512),
-                                   (17, 40, 256), (5, 2048, 11008)])
+                                   (17, 40, 256), (5, 2048, 11008), (130, 300, 208),
+                                   (256, 4096, 1024), (64, 520, 4096)])
 def test_w4a8_small_shapes_bitexact(g, M, N, K):
     say(f"case w4a8 M={M} N={N} K={K}")
     W = WL.weights_f32(N, K, seed=5000 + N)
@@ -248,6 +249,22 @@ def test_w2a8_ternary(g, c):
         assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
         ref = O.dequant_epilogue(acc, np.float64(scale), sa_ref[rows], None, O.OUT_F16)
         tol_ok(C16[rows, cols], ref, c.name)
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 24, 48), (200, 130, 1040), (33, 4100, 256)])
+def test_w2a8_ragged_bitexact(g, M, N, K):
+    say(f"case w2a8 ragged M={M} N={N} K={K}")
+    codes = WL.ternary_codes(N, K, seed=7000 + N)
+    src = WL.weights_f32(N, K, seed=7001 + N)
+    A = WL.activations(M, K, seed=7002 + M)
+    b = WL.bias_f16(N, seed=7003)
+    Wp, s16 = prep_w2a8(g, codes, src)
+    Aq, sa, _ = g.quantize_a8(dev(A))
+    qa, sa_ref, _ = O.quantize_a8(A)
+    C32 = host(g.w2a8_gemm(Aq, sa, Wp, s16, N, out_dtype=g.W4_OUT_I32))
+    assert np.array_equal(C32, O.int_accumulate(qa, codes).astype(np.int32))
+    C16 = host(g.w2a8_gemm(Aq, sa, Wp, s16, N, bias=f16(b), out_dtype=g.W4_OUT_F16))
+    tol_ok(C16, O.w2a8_gemm(qa, sa_ref, codes, host(s16)[0], b, O.OUT_F16), "w2a8 ragged")
 
 
 def test_w2a8_extreme_codes_no_overflow(g):
