@@ -210,6 +210,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=2048 GEMM")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="time one workload only (for profiler runs); prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -223,8 +225,18 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     stream = torch.cuda.current_stream()
 
+    if args.only == "prefill":
+        cp, pre = bench_prefill(args, stream)
+        ops = 2.0 * cp.M * cp.N * cp.K
+        print(json.dumps({"workload": "w4a8_prefill_gemm", **pre,
+                          "gemm_tops": ops / (pre["gemm_region_ms"] * 1e-3) / 1e12}), flush=True)
+        return
     log("bench: decode W4A16 M=1 N=4096 K=4096")
     c, dec = bench_decode(args, stream)
+    if args.only == "decode":
+        print(json.dumps({"workload": "w4a16_decode_gemv", **dec,
+                          "gbs": dec["bytes"] / (dec["region_ms"] * 1e-3) / 1e9}), flush=True)
+        return
     log("bench: decode", dec)
     gbs = dec["bytes"] / (dec["region_ms"] * 1e-3) / 1e9
     kern_gbs = dec["bytes"] / (dec["per_call_median_ms"] * 1e-3) / 1e9

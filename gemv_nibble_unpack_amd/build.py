@@ -22,7 +22,7 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     # no packed-FP32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-command-line-argument", *os.environ.get("W4_EXTRA_FLAGS", "").split(),
 ]
 
 

@@ -42,6 +42,8 @@ struct GemmShape {
   static constexpr int STAGE = G::A_BYTES + W_BYTES;
   static constexpr int W_CHUNKS = NTILES * 64 / GEMM_THREADS;  // per thread
   static constexpr int NTW = NTILES / 2;                        // n subtiles per wave
+  // register prefetch depth that fits two blocks per CU (256 registers a lane)
+  static constexpr int DEPTH = (KIND == KIND_W4A8 && NTILES == 8) ? 2 : 1;
 };
 
 struct GemmGrid {
@@ -60,8 +62,63 @@ __device__ __forceinline__ void unpack_frag(const u4 w, i4 (&bf)[GemmTraits<KIND
   }
 }
 
-template <int KIND, int NTILES>
-__global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const MMParams p, const GemmGrid gg) {
+// Epilogue of one accumulator fragment: 4 consecutive output columns n..n+3
+// of row m (operands are swapped in the MFMA so a lane owns a column run).
+// ws/bias hold the 4 columns' weight scales and biases, sa the row's scale.
+template <int KIND, int OUT, bool BIAS>
+__device__ __forceinline__ void gemm_store4(const MMParams& p, int m, int n, const i4 v,
+                                            const f4 ws, const f4 bias, float sa, bool vec_ok) {
+  constexpr int SH = KindTraits<KIND>::SHIFT;
+  if (m >= p.M || n >= p.N) return;
+  const bool full = vec_ok && n + 3 < p.N;
+  if constexpr (OUT == W4_OUT_I32) {
+    int32_t* c = reinterpret_cast<int32_t*>(p.C) + (size_t)m * p.N + n;
+    const i4 q = i4{v[0] >> SH, v[1] >> SH, v[2] >> SH, v[3] >> SH};
+    if (full) {
+      *reinterpret_cast<i4*>(c) = q;
+    } else {
+      for (int e = 0; e < 4 && n + e < p.N; ++e) c[e] = q[e];
+    }
+  } else {
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int a = v[e] >> SH;
+      o[e] = (float)a * ws[e] * sa;
+      if constexpr (BIAS && OUT == W4_OUT_F16) o[e] += bias[e];
+    }
+    if constexpr (OUT == W4_OUT_F32) {
+      float* c = reinterpret_cast<float*>(p.C) + (size_t)m * p.N + n;
+      if (full) {
+        *reinterpret_cast<f4*>(c) = f4{o[0], o[1], o[2], o[3]};
+      } else {
+        for (int e = 0; e < 4 && n + e < p.N; ++e) c[e] = o[e];
+      }
+    } else {
+      uint16_t* c = reinterpret_cast<uint16_t*>(p.C) + (size_t)m * p.N + n;
+      if (full) {
+        *reinterpret_cast<u2*>(c) = u2{(uint32_t)f2h(o[0]) | ((uint32_t)f2h(o[1]) << 16),
+                                       (uint32_t)f2h(o[2]) | ((uint32_t)f2h(o[3]) << 16)};
+      } else {
+        for (int e = 0; e < 4 && n + e < p.N; ++e) c[e] = f2h(o[e]);
+      }
+    }
+  }
+}
+
+// Column scales/biases of the 4 columns starting at n (clamped reads).
+template <int KIND, int OUT, bool BIAS>
+__device__ __forceinline__ void gemm_col_params(const MMParams& p, int n, f4& ws, f4& bias) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int ne = min(n + e, p.N - 1);
+    if constexpr (OUT != W4_OUT_I32) ws[e] = KIND == KIND_W4A8 ? p.w_scale[ne] : h2f(p.w_scale16[0]);
+    if constexpr (BIAS && OUT == W4_OUT_F16) bias[e] = h2f(p.bias[ne]);
+  }
+}
+
+template <int KIND, int NTILES, int DEPTH, int OUT, bool BIAS>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, const GemmGrid gg) {
   using G = GemmTraits<KIND>;
   using S = GemmShape<KIND, NTILES>;
   constexpr int TK = G::TILE_K;
@@ -79,6 +136,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const MMParams p, const G
   const int kz = blockIdx.y;
   const int kb = kz * gg.kts;
   const int ke = min(p.KT, kb + gg.kts);
+  const int nk = max(0, ke - kb);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,64 +148,47 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const MMParams p, const G
 
   const int8_t* A = reinterpret_cast<const int8_t*>(p.A);
 
-  // ---- global -> register staging of one k tile ---------------------------
-  u4 ra[G::A_CHUNKS];
-  u4 rw[S::W_CHUNKS];
-  auto gload = [&](int kt) {
+  // ---- global -> register staging of one k tile (two register sets) -------
+  u4 ra[DEPTH][G::A_CHUNKS];
+  u4 rw[DEPTH][S::W_CHUNKS];
+  auto gload = [&](int kt, int set) {
+    kt = min(kt, ke - 1);                            // clamped re-load past the end is unused
 #pragma unroll
     for (int i = 0; i < G::A_CHUNKS; ++i) {
       const int c = tid + i * GEMM_THREADS;          // chunk in the BM x TK tile
       const int row = c / (TK / 16), col = c % (TK / 16);
       const int gm = min(m0 + row, p.M - 1);
       const int gk = min(kt * TK + col * 16, p.K - 16);
-      ra[i] = *reinterpret_cast<const u4*>(A + (size_t)gm * p.K + gk);
+      ra[set][i] = *reinterpret_cast<const u4*>(A + (size_t)gm * p.K + gk);
     }
 #pragma unroll
     for (int i = 0; i < S::W_CHUNKS; ++i) {
       const int c = tid + i * GEMM_THREADS;          // chunk among NTILES x 64
       const int t = min(t0 + (c >> 6), p.NT - 1);
-      rw[i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(
+      rw[set][i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(
           p.Wt + ((size_t)t * p.KT + kt) * TILE_BYTES + (c & 63) * 16));
     }
   };
-  auto sstore = [&](int kt, int buf) {
+  auto sstore = [&](int kt, int set, int buf) {
     uint8_t* sa = smem + buf * S::STAGE;
     uint8_t* sw = sa + G::A_BYTES;
 #pragma unroll
     for (int i = 0; i < G::A_CHUNKS; ++i) {
       const int c = tid + i * GEMM_THREADS;
       const int row = c / (TK / 16), col = c % (TK / 16);
-      u4 v = ra[i];
+      u4 v = ra[set][i];
       if (kt * TK + col * 16 >= p.K) v = u4{0u, 0u, 0u, 0u};   // k tail
       *reinterpret_cast<u4*>(sa + row * G::A_STRIDE + col * 16) = v;
     }
 #pragma unroll
     for (int i = 0; i < S::W_CHUNKS; ++i) {
       const int c = tid + i * GEMM_THREADS;
-      *reinterpret_cast<u4*>(sw + c * 16) = rw[i];
+      *reinterpret_cast<u4*>(sw + c * 16) = rw[set][i];
     }
   };
-
-  i4 acc[4][NTW];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) acc[i][t] = i4{0, 0, 0, 0};
-
-  if (kb < ke) {
-    gload(kb);
-    sstore(kb, 0);
-  }
-  __syncthreads();
-
-  for (int kt = kb; kt < ke; ++kt) {
-    const int buf = (kt - kb) & 1;
-    const bool more = kt + 1 < ke;
-    if (more) gload(kt + 1);
-
+  auto compute = [&](int buf, i4 (&acc)[4][NTW]) {
     const uint8_t* sa = smem + buf * S::STAGE;
     const uint8_t* sw = sa + G::A_BYTES;
-    // activation fragments of this wave: 4 m subtiles x J k steps
     i4 af[4][J];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -163,29 +204,69 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const MMParams p, const G
 #pragma unroll
       for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][j], bf[j], acc[i][t], 0, 0, 0);
+        for (int i = 0; i < 4; ++i)   // weights as the row operand: lane owns 4 columns
+          acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[j], af[i][j], acc[i][t], 0, 0, 0);
     }
+  };
 
-    if (more) sstore(kt + 1, buf ^ 1);
+  i4 acc[4][NTW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[i][t] = i4{0, 0, 0, 0};
+
+  if constexpr (DEPTH == 2) {
+    // prologue: tile kb -> LDS 0, tile kb+1 in flight in register set 1
+    if (nk > 0) {
+      gload(kb, 0);
+      gload(kb + 1, 1);
+      sstore(kb, 0, 0);
+    }
     __syncthreads();
+    // iteration i computes tile kb+i from LDS buffer i&1 while tile kb+i+1
+    // (register set (i+1)&1) lands and tile kb+i+2 is requested
+    for (int i = 0; i < nk; i += 2) {
+      if (i + 2 < nk) gload(kb + i + 2, 0);
+      compute(0, acc);
+      if (i + 1 < nk) sstore(kb + i + 1, 1, 1);
+      __syncthreads();
+      if (i + 1 >= nk) break;
+      if (i + 3 < nk) gload(kb + i + 3, 1);
+      compute(1, acc);
+      if (i + 2 < nk) sstore(kb + i + 2, 0, 0);
+      __syncthreads();
+    }
+  } else {
+    // one register set: tile kb+i+1 is requested before tile kb+i is computed
+    if (nk > 0) {
+      gload(kb, 0);
+      sstore(kb, 0, 0);
+    }
+    __syncthreads();
+    for (int i = 0; i < nk; ++i) {
+      if (i + 1 < nk) gload(kb + i + 1, 0);
+      compute(i & 1, acc);
+      if (i + 1 < nk) sstore(kb + i + 1, 0, (i + 1) & 1);
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  const int ncol0 = (t0 + wn * NTW) * 16 + r;
+  // ---- epilogue: lane owns columns n..n+3 of row m for each fragment -------
+  const bool vec_ok = (p.N % 4) == 0;
+  const int nbase = (t0 + wn * NTW) * 16 + 4 * b;
+  float sav[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    sav[i] = OUT == W4_OUT_I32 ? 0.f : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
   if (gg.ksplit == 1) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      const int n = ncol0 + 16 * t;
-      if (n >= p.N) continue;
+      f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
+      gemm_col_params<KIND, OUT, BIAS>(p, nbase + 16 * t, ws, bias);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = m0 + 64 * wm + 16 * i + 4 * b + e;
-          const int v = acc[i][t][e];
-          if (m < p.M) store_out<KIND>(p, m, n, 0.f, v);
-        }
+        gemm_store4<KIND, OUT, BIAS>(p, m0 + 64 * wm + 16 * i + r, nbase + 16 * t, acc[i][t], ws,
+                                     bias, sav[i], vec_ok);
     }
     return;
   }
@@ -194,17 +275,18 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const MMParams p, const G
   int32_t* part = reinterpret_cast<int32_t*>(p.partials);
   const size_t plane = (size_t)p.M * p.N;
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const int n = ncol0 + 16 * t;
-    if (n >= p.N) continue;
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 64 * wm + 16 * i + r;
+    if (m >= p.M) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < NTW; ++t) {
+      const int n = nbase + 16 * t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * b + e;
         const int v = acc[i][t][e];
-        if (m < p.M) part[(size_t)kz * plane + (size_t)m * p.N + n] = v;
+        if (n + e < p.N) part[(size_t)kz * plane + (size_t)m * p.N + n + e] = v;
       }
+    }
   }
   __threadfence();
   __syncthreads();
@@ -214,19 +296,22 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const MMParams p, const G
   if (!last) return;
   __threadfence();
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const int n = ncol0 + 16 * t;
-    if (n >= p.N) continue;
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 64 * wm + 16 * i + r;
+    if (m >= p.M) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < NTW; ++t) {
+      const int n = nbase + 16 * t;
+      i4 sum = i4{0, 0, 0, 0};
+      for (int z = 0; z < gg.ksplit; ++z) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * b + e;
-        if (m >= p.M) continue;
-        int s = 0;
-        for (int z = 0; z < gg.ksplit; ++z) s += part[(size_t)z * plane + (size_t)m * p.N + n];
-        store_out<KIND>(p, m, n, 0.f, s);
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) sum[e] += part[(size_t)z * plane + (size_t)m * p.N + n + e];
       }
+      f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
+      gemm_col_params<KIND, OUT, BIAS>(p, n, ws, bias);
+      gemm_store4<KIND, OUT, BIAS>(p, m, n, sum, ws, bias, sav[i], vec_ok);
+    }
   }
   if (tid == 0) p.counters[tix] = 0u;
 }
@@ -236,12 +321,15 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const MMParams p, const G
 // ---------------------------------------------------------------------------
 inline bool use_gemm(int kind, int M) { return kind != KIND_W4A16 && M > 16; }
 
-inline int gemm_ntiles(int N) { return N >= 4096 ? 16 : 8; }
+#ifndef W4_GEMM_WIDE_MIN_N
+#define W4_GEMM_WIDE_MIN_N 4096
+#endif
+inline int gemm_ntiles(int kind, int N) { return kind == KIND_W4A8 && N >= W4_GEMM_WIDE_MIN_N ? 16 : 8; }
 
 inline GemmGrid gemm_grid(int kind, int M, int N, int K) {
   const Geometry g = geometry(kind == KIND_W2A8 ? W4_LAYOUT_W2A8 : W4_LAYOUT_W4A8, N, K);
   GemmGrid gg{};
-  const int nt = gemm_ntiles(N);
+  const int nt = gemm_ntiles(kind, N);
   gg.mblocks = ceil_div(M, GEMM_BM);
   gg.nblocks = ceil_div(g.NT, nt);
   gg.tiles = gg.mblocks * gg.nblocks;
@@ -260,17 +348,26 @@ inline size_t gemm_workspace_bytes(int kind, int M, int N, int K) {
   return counters + (size_t)gg.ksplit * M * N * sizeof(int32_t);
 }
 
+template <int KIND, int NTILES, int OUT, bool BIAS>
+int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
+  using S = GemmShape<KIND, NTILES>;
+  constexpr int DEPTH = GemmShape<KIND, NTILES>::DEPTH;
+  const dim3 grid(gg.per_xcd * 8, gg.ksplit);
+  allow_smem((const void*)&k_gemm<KIND, NTILES, DEPTH, OUT, BIAS>, 2 * S::STAGE);
+  hipLaunchKernelGGL((k_gemm<KIND, NTILES, DEPTH, OUT, BIAS>), grid, dim3(GEMM_THREADS),
+                     2 * S::STAGE, stream, p, gg);
+  return launch_status();
+}
+
 template <int KIND, int NTILES>
 int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream) {
-  using S = GemmShape<KIND, NTILES>;
   p.counters = reinterpret_cast<unsigned*>(ws);
   const size_t counters = ((size_t)gg.tiles * sizeof(unsigned) + 255) & ~(size_t)255;
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + counters : nullptr;
-  const dim3 grid(gg.per_xcd * 8, gg.ksplit);
-  allow_smem((const void*)&k_gemm<KIND, NTILES>, 2 * S::STAGE);
-  hipLaunchKernelGGL((k_gemm<KIND, NTILES>), grid, dim3(GEMM_THREADS), 2 * S::STAGE, stream, p,
-                     gg);
-  return launch_status();
+  if (p.out_dtype == W4_OUT_I32) return launch_gemm_o<KIND, NTILES, W4_OUT_I32, false>(p, gg, stream);
+  if (p.out_dtype == W4_OUT_F32) return launch_gemm_o<KIND, NTILES, W4_OUT_F32, false>(p, gg, stream);
+  if (p.bias) return launch_gemm_o<KIND, NTILES, W4_OUT_F16, true>(p, gg, stream);
+  return launch_gemm_o<KIND, NTILES, W4_OUT_F16, false>(p, gg, stream);
 }
 
 template <int KIND>
@@ -279,7 +376,9 @@ int launch_gemm(const MMParams& p, void* ws, hipStream_t stream) {
     return W4_ERR_ARG;
   } else {
     const GemmGrid gg = gemm_grid(KIND, p.M, p.N, p.K);
-    if (gemm_ntiles(p.N) == 16) return launch_gemm_t<KIND, 16>(p, gg, ws, stream);
+    if constexpr (KIND == KIND_W4A8) {
+      if (gemm_ntiles(KIND, p.N) == 16) return launch_gemm_t<KIND, 16>(p, gg, ws, stream);
+    }
     return launch_gemm_t<KIND, 8>(p, gg, ws, stream);
   }
 }
