@@ -29,6 +29,10 @@ METRIC = "W4 GEMV HBM GB/s (% peak) at M=1; W4A8 GEMM TOPS (% MFMA peak) at M=20
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 I8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA
 ROTATE_BYTES = 1 << 30         # weight copies in rotation per workload
+CALIB_BYTES = 256 << 20        # device-to-device copy used to calibrate PMC byte counters
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_TRAFFIC = os.path.join(PROFILES, "k_gemv_w4a16_decode_m1_n4096_k4096_traffic.json")
+PREFILL_TRAFFIC = os.path.join(PROFILES, "k_gemm_w4a8_prefill_m2048_n11008_k4096_traffic.json")
 
 
 def log(*a):
@@ -77,6 +81,39 @@ def time_loop(fn, steps, warmup, stream):
     return region_ms, per_call
 
 
+def time_graph(fn, steps, warmup, stream):
+    """Capture `steps` calls in one HIP graph, replay it once untimed and once
+    timed; returns (ms per call, per-call list from the eager pass)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, []
+
+
+def calibration_copy():
+    """A plain device-to-device copy of CALIB_BYTES, three times (its PMC
+    FETCH_SIZE/WRITE_SIZE readings calibrate the byte counters)."""
+    import torch
+    src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def bench_decode(args, stream):
     import torch
     import gemv_nibble_unpack_amd as G
@@ -98,13 +135,19 @@ def bench_decode(args, stream):
     ws = G.Workspace(dev)
 
     def step(i):
-        G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C, stream=stream)
+        # stream=None: the current stream (the capture stream under --graph)
+        G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C,
+                     stream=None if not args.eager else stream)
 
-    region_ms, per_call = time_loop(step, args.steps, args.warmup, stream)
+    eager_ms, per_call = time_loop(step, args.steps, args.warmup, stream) if args.eager else \
+        time_loop(lambda i: G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C, stream=stream),
+                  args.steps, args.warmup, stream)
+    region_ms = eager_ms if args.eager else time_graph(step, args.steps, args.warmup, stream)[0]
     nbytes = decode_bytes(c.M, c.N, c.K)
     kern_ms = float(np.median(per_call))
     out = {
-        "region_ms": region_ms, "per_call_median_ms": kern_ms,
+        "region_ms": region_ms, "eager_region_ms": eager_ms, "graph": not args.eager,
+        "per_call_median_ms": kern_ms,
         "per_call_mean_ms": float(np.mean(per_call)), "bytes": nbytes, "copies": R,
         "offline_prep_ms": prep_ms,
     }
@@ -151,6 +194,56 @@ def bench_prefill(args, stream):
     return c, {"step_ms": region_ms, "gemm_region_ms": gemm_ms,
                "gemm_per_call_median_ms": float(np.median(per_call)), "steps": steps,
                "bytes": prefill_bytes(c.M, c.N, c.K), "copies": R}
+
+
+def traffic_of(path):
+    """HBM bytes per launch from the committed PMC summary, or None when the
+    summary is missing or the kernel sources changed since it was taken."""
+    from gemv_nibble_unpack_amd.profiling import load_traffic
+    rec = load_traffic(path)
+    return None if rec is None else round(rec["traffic_bytes_per_launch"])
+
+
+def bench_case(case, steps, warmup, stream):
+    """Time one workload case (cold weights); returns a dict for --sweep."""
+    import torch
+    import gemv_nibble_unpack_amd as G
+    dev = torch.device("cuda:0")
+    d = case.inputs()
+    A = torch.from_numpy(d["A"]).to(dev)
+    M, N, K = case.M, case.N, case.K
+    ws = G.Workspace(dev)
+    if case.scheme == "w4a16":
+        Wq, s, z = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_ASYM_GROUP)
+        Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, N, K, s, z)
+        nbytes = decode_bytes(M, N, K)
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
+        fn = lambda i: G.w4a16_gemm(A, copies[i % len(copies)], N, workspace=ws, C=C, stream=stream)
+    else:
+        Aq, sa, _ = G.quantize_a8(A)
+        out = G.W4_OUT_F32 if case.out == "f32" else G.W4_OUT_F16
+        C = torch.empty((M, N), dtype=torch.float32 if out == G.W4_OUT_F32 else torch.float16,
+                        device=dev)
+        if case.scheme == "w4a8":
+            Wq, wsc, _ = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_SYM_PER_CHANNEL)
+            Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, N, K)
+            mm, wbytes = G.w4a8_gemm, N * K // 2 + 4 * N
+        else:
+            Wq = G.quantize_pack_w2(torch.from_numpy(d["codes"]).to(dev))
+            Wp = G.prepack_w(G.W4_LAYOUT_W2A8, Wq, N, K)
+            wsc = G.ternary_scale_f16(torch.from_numpy(d["src"]).to(dev))
+            mm, wbytes = G.w2a8_gemm, N * K // 4 + 2
+        nbytes = wbytes + M * K + 4 * M + M * N * C.element_size()
+        copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
+        fn = lambda i: mm(Aq, sa, copies[i % len(copies)], wsc, N, out_dtype=out, workspace=ws,
+                          C=C, stream=stream)
+    ms, _ = time_loop(fn, steps, warmup, stream)
+    del copies
+    torch.cuda.empty_cache()
+    return {"case": case.name, "M": M, "N": N, "K": K, "us": round(ms * 1e3, 3),
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "TOPS": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
 
 
 def cpu_threads():
@@ -212,6 +305,13 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=2048 GEMM")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="time one workload only (for profiler runs); prints its own JSON line")
+    ap.add_argument("--calib", action="store_true",
+                    help="also run a copy of known size (for PMC byte-counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every configured workload shape; one JSON line per case")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed decode steps one by one from Python instead of "
+                         "replaying them from one captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -225,8 +325,16 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     stream = torch.cuda.current_stream()
 
+    if args.sweep:
+        from gemv_nibble_unpack_amd import workloads as WL
+        for case in WL.ALL_CASES:
+            print(json.dumps(bench_case(case, max(20, args.steps // 4), args.warmup, stream)),
+                  flush=True)
+        return
     if args.only == "prefill":
         cp, pre = bench_prefill(args, stream)
+        if args.calib:
+            calibration_copy()
         ops = 2.0 * cp.M * cp.N * cp.K
         print(json.dumps({"workload": "w4a8_prefill_gemm", **pre,
                           "gemm_tops": ops / (pre["gemm_region_ms"] * 1e-3) / 1e12}), flush=True)
@@ -234,6 +342,8 @@ def main():
     log("bench: decode W4A16 M=1 N=4096 K=4096")
     c, dec = bench_decode(args, stream)
     if args.only == "decode":
+        if args.calib:
+            calibration_copy()
         print(json.dumps({"workload": "w4a16_decode_gemv", **dec,
                           "gbs": dec["bytes"] / (dec["region_ms"] * 1e-3) / 1e9}), flush=True)
         return
@@ -256,9 +366,12 @@ def main():
         "config": {"workload": "w4a16_decode_gemv", "M": c.M, "N": c.N, "K": c.K,
                    "weights": "uint4 group128 fp16 scale + uint8 zero", "act": "fp16",
                    "out": "fp16", "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                   "cold_weight_copies": dec["copies"]},
+                   "cold_weight_copies": dec["copies"],
+                   "timing": "HIP-graph replay of the timed steps" if dec["graph"] else "eager",
+                   "eager_GBps": round(dec["bytes"] / (dec["eager_region_ms"] * 1e-3) / 1e9, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_of(DECODE_TRAFFIC),
                      "bytes_per_launch": dec["bytes"],
                      "per_call_event_gbs": round(kern_gbs, 2)},
         "offline_prep_ms": round(dec["offline_prep_ms"], 3),
@@ -279,7 +392,8 @@ def main():
                        "out": "fp16 + bias", "cold_weight_copies": pre["copies"]},
             "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2),
                          "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
-                         "frac": round(gemm_tops / I8_PEAK_TOPS, 4), "traffic": None,
+                         "frac": round(gemm_tops / I8_PEAK_TOPS, 4),
+                         "traffic": traffic_of(PREFILL_TRAFFIC),
                          "gemm_ms": round(pre["gemm_region_ms"], 5)},
         }
     if not args.no_cpu:

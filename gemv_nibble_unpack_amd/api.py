@@ -133,8 +133,15 @@ def quantize_a8(A, with_rowsum=True, out=None, stream=None):
     return Aq, sa, rs
 
 
+_WS_CACHE = {}
+
+
 def w4_workspace_bytes(layout, M, N, K):
-    return int(L.load().w4_workspace_bytes(layout, M, N, K))
+    key = (layout, M, N, K)
+    v = _WS_CACHE.get(key)
+    if v is None:
+        v = _WS_CACHE[key] = int(L.load().w4_workspace_bytes(layout, M, N, K))
+    return v
 
 
 _OUT_DT = {L.W4_OUT_F16: torch.float16, L.W4_OUT_F32: torch.float32, L.W4_OUT_I32: torch.int32}

@@ -288,13 +288,20 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
       }
     }
   }
-  __threadfence();
-  __syncthreads();
+  // One thread per block does the device-scope fences (each one writes back
+  // and invalidates the XCD's L2, so they must not run once per wave): the
+  // barrier orders every wave's partial stores before thread 0's release
+  // fence, and thread 0's acquire fence (last block only) precedes the reads
+  // of the other blocks' partials.
   __shared__ int last;
-  if (tid == 0) last = atomicAdd(&p.counters[tix], 1u) == (unsigned)(gg.ksplit - 1);
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    last = atomicAdd(&p.counters[tix], 1u) == (unsigned)(gg.ksplit - 1);
+    if (last) __threadfence();
+  }
   __syncthreads();
   if (!last) return;
-  __threadfence();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 64 * wm + 16 * i + r;
@@ -319,7 +326,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
 // ---------------------------------------------------------------------------
 // planning (host)
 // ---------------------------------------------------------------------------
-inline bool use_gemm(int kind, int M) { return kind != KIND_W4A16 && M > 16; }
+inline int gemm_ntiles(int kind, int N);
+
+// The tiled GEMM needs enough 128-row x (16*NTILES)-column tiles to fill the
+// chip without splitting K; smaller products run on the decode kernel, one
+// block per (16-row tile, 16-column tile).
+inline bool use_gemm(int kind, int M, int N) {
+  if (kind == KIND_W4A16 || M <= 16) return false;
+  const int nt = ceil_div(N, TILE_N);
+  const long tiles = (long)ceil_div(M, GEMM_BM) * ceil_div(nt, gemm_ntiles(kind, N));
+  return tiles >= 128;
+}
 
 #ifndef W4_GEMM_WIDE_MIN_N
 #define W4_GEMM_WIDE_MIN_N 4096

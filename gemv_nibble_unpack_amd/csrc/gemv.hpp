@@ -131,12 +131,14 @@ struct AStage {
 };
 
 // Grid: x = n tile, y = k split, z = 16-row m tile. Block = WAVES waves.
-// Phase 1: every thread issues its APER 16-byte activation loads, then each
-// wave issues the weight-tile (and group scale/zero) loads of its whole
-// contiguous k run (at most MAXT tiles per pass). Phase 2: activations go to
-// LDS, one barrier. Phase 3: tiles are unpacked and multiplied in order, each
-// waiting only for its own loads.
-template <int KIND, int WAVES, int MAXT, int APER>
+// Phase 1: (STAGED) every thread issues its APER 16-byte activation loads;
+// then each wave issues the weight-tile (and group scale/zero) loads of its
+// whole contiguous k run (at most MAXT tiles per pass). Phase 2: (STAGED)
+// activations go to LDS, one barrier. Phase 3: tiles are unpacked and
+// multiplied in order, each waiting only for its own loads. Without STAGED
+// (activation rows too large for LDS) each lane loads its own activation
+// fragments from L2 through a ring of RING tiles in flight.
+template <int KIND, int WAVES, int MAXT, int APER, bool STAGED>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   using AS = AStage<KIND>;
   constexpr bool A16 = KIND == KIND_W4A16;
@@ -149,9 +151,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15;   // A row within the m tile / W row within the n tile
   const int b = lane >> 4;   // k quarter of a tile
-  const int mtile = blockIdx.z;
+  // block id -> (n tile, m tile): ids xcd, xcd+8, xcd+16, ... (one XCD) walk
+  // the m tiles of one n tile before moving on, so its weights stay in L2
+  const int mtiles = (p.M + 15) / 16;
+  int tile, mtile;
+  if (mtiles == 1) {
+    tile = blockIdx.x;
+    mtile = 0;
+  } else {
+    const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
+    const int per_xcd = (int)(gridDim.x >> 3);        // grid is a multiple of 8 here
+    const int seq = xcd * per_xcd + local;           // position in the XCD's run
+    tile = seq / mtiles;
+    mtile = seq - tile * mtiles;
+    if (local >= per_xcd || tile >= p.NT) return;
+  }
   const int rows = min(16, p.M - mtile * 16);
-  const int tile = blockIdx.x;
   const int kb = blockIdx.y * p.kts;
   const int ke = min(p.KT, kb + p.kts);
   const int per = (ke - kb + WAVES - 1) / WAVES;
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   const size_t kbyte0 = (size_t)kb * AS::TILE_ROWB;
   u4 stage[APER];
 #pragma unroll
-  for (int i = 0; i < APER; ++i) {
+  for (int i = 0; i < (STAGED ? APER : 0); ++i) {
     const int c = min(tid + i * NTHR, total - 1);
     const int row = c / cpr, col = c - row * cpr;
     size_t off = kbyte0 + (size_t)col * 16;
@@ -201,8 +216,29 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       }
     }
 
+    // ---- activation fragments straight from L2 (not STAGED) --------------
+    constexpr int RING = 4;
+    constexpr int AC = KindTraits<KIND>::A_CHUNKS;
+    u4 ring[STAGED ? 1 : RING][AC];
+    const size_t arow_g = (size_t)min(mtile * 16 + r, p.M - 1) * arow_bytes;
+    auto aload = [&](int u, u4 (&dst)[AC]) {
+      // past the run (or for a wave without tiles) re-read a valid tile
+      const int kt = min(max(pb + min(u, pn - 1), 0), p.KT - 1);
+      const size_t base = (size_t)kt * AS::TILE_ROWB + (AS::TILE_ROWB / 4) * b;
+#pragma unroll
+      for (int j = 0; j < AC; ++j) {
+        size_t off = base + 16 * j;
+        if constexpr (!A16) off = min(off, arow_bytes - 16);
+        dst[j] = *reinterpret_cast<const u4*>(Ab + arow_g + off);
+      }
+    };
+    if constexpr (!STAGED) {
+#pragma unroll
+      for (int u = 0; u < RING; ++u) aload(u, ring[u]);
+    }
+
     // ---- phase 2: activations to LDS (first pass only) -------------------
-    if (pass == 0) {
+    if (STAGED && pass == 0) {
 #pragma unroll
       for (int i = 0; i < APER; ++i) {
         const int c = tid + i * NTHR;
@@ -222,14 +258,33 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     const uint8_t* arow = smem + min(r, rows - 1) * sstride;
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
+      u4 af[AC];
+      if constexpr (STAGED) {
+        if (u >= pn) continue;                       // uniform: tiles past the wave's run
+        const int kl = pb + u - kb;                  // tile index within the staged range
+        const u4* src = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB +
+                                                    (AS::TILE_ROWB / 4) * b);
+#pragma unroll
+        for (int j = 0; j < AC; ++j) af[j] = src[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < AC; ++j) af[j] = ring[u % RING][j];
+        aload(u + RING, ring[u % RING]);             // unconditional: keeps wait counts exact
+      }
       if (u >= pn) continue;                         // uniform: tiles past the wave's run
-      const int kl = pb + u - kb;                    // tile index within the staged range
+      if constexpr (!A16 && !STAGED) {
+        // k tail: fragments past K contribute zero (staged rows are zero-filled)
+        const int kt = pb + u;
+#pragma unroll
+        for (int j = 0; j < AC; ++j)
+          if ((size_t)kt * AS::TILE_ROWB + (AS::TILE_ROWB / 4) * b + 16 * j >= arow_bytes)
+            af[j] = u4{0u, 0u, 0u, 0u};
+      }
       if constexpr (A16) {
         const _Float16 z = (_Float16)(float)zv[u];
         const _Float16 zl = -((_Float16)1024.0f + z);
         const _Float16 zh = -((_Float16)64.0f + z);
         const h2 zlo = {zl, zl}, zhi = {zh, zh};
-        const u4* af = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB + 64 * b);
         f4 part = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -241,7 +296,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = fmaf(part[e], s, acc[e]);
       } else if constexpr (KIND == KIND_W4A8) {
-        const u4* af = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB + 32 * b);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const i4 bf = unpack_w4_i8(wv[u][2 * j], wv[u][2 * j + 1]);
@@ -249,7 +303,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
                                                       0, 0);
         }
       } else {
-        const u4* af = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB + 64 * b);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const i4 bf = unpack_w2_i8(wv[u][j]);
@@ -273,8 +326,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   }
   __syncthreads();
 
-  const int ngroups = gridDim.x;
-  const size_t slot = (size_t)mtile * ngroups + blockIdx.x;
+  const int ngroups = p.NT;
+  const size_t slot = (size_t)mtile * ngroups + tile;
   constexpr int NOUT = 256;                          // 16 x 16 outputs of the tile
 
   if (p.ksplit == 1) {
@@ -298,7 +351,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   // ---- split-K: publish this block's partial, the last block finishes ----
   uint32_t* part = reinterpret_cast<uint32_t*>(p.partials) +
                    ((size_t)mtile * p.ksplit + blockIdx.y) * ngroups * NOUT +
-                   (size_t)blockIdx.x * NOUT;
+                   (size_t)tile * NOUT;
   for (int idx = tid; idx < NOUT; idx += NTHR) {
     const int row = idx >> 4, col = idx & 15;
     float fs = 0.f;
@@ -311,15 +364,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     }
     part[idx] = A16 ? __builtin_bit_cast(uint32_t, fs) : (uint32_t)is;
   }
-  __threadfence();
-  __syncthreads();
+  // One thread per block does the device-scope fences (each one writes back
+  // and invalidates the XCD's L2, so they must not run once per wave): the
+  // barrier orders every wave's partial stores before thread 0's release
+  // fence, and thread 0's acquire fence (last block only) precedes the reads
+  // of the other blocks' partials.
   __shared__ int last;
-  if (tid == 0) last = atomicAdd(&p.counters[slot], 1u) == (unsigned)(p.ksplit - 1);
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    last = atomicAdd(&p.counters[slot], 1u) == (unsigned)(p.ksplit - 1);
+    if (last) __threadfence();
+  }
   __syncthreads();
   if (!last) return;
-  __threadfence();
   const uint32_t* base = reinterpret_cast<const uint32_t*>(p.partials) +
-                         (size_t)mtile * p.ksplit * ngroups * NOUT + (size_t)blockIdx.x * NOUT;
+                         (size_t)mtile * p.ksplit * ngroups * NOUT + (size_t)tile * NOUT;
   for (int idx = tid; idx < NOUT; idx += NTHR) {
     const int row = idx >> 4, col = idx & 15;
     const int n = tile * 16 + col;

@@ -10,11 +10,12 @@ namespace w4 {
 
 constexpr int GEMV_WAVES = 8;
 constexpr int GEMV_THREADS = GEMV_WAVES * 64;
-constexpr int TARGET_BLOCKS = 256;          // one block per compute unit
+constexpr int SPLIT_BELOW = 64;            // blocks below which K is split
 constexpr int STAGE_MAX = 8 * 16 * GEMV_THREADS;  // activation bytes one block may stage
 
 struct Plan {
   bool gemm;        // prefill kernel instead of the decode kernel
+  bool staged;      // activation rows staged in LDS
   int ksplit, kts, mtiles, maxt, aper;
   size_t smem;
   size_t counters_bytes, ws_bytes;
@@ -34,7 +35,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline Plan make_plan(int kind, int M, int N, int K) {
   const Geometry g = geometry(kind_layout(kind), N, K);
   Plan P{};
-  P.gemm = use_gemm(kind, M);
+  P.gemm = use_gemm(kind, M, N);
   if (P.gemm) {
     P.ws_bytes = gemm_workspace_bytes(kind, M, N, K);
     return P;
@@ -44,20 +45,22 @@ inline Plan make_plan(int kind, int M, int N, int K) {
   const int blocks = g.NT * P.mtiles;
   const int trb = tile_rowb(kind);
   int ks = 1;
-  // split K across blocks while the chip has fewer blocks than CUs (keeping a
-  // tile per wave), and until the block's activation rows fit the staging
-  // buffer
-  while ((blocks * ks < TARGET_BLOCKS && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ||
-         (size_t)rows * ceil_div(g.KT, ks) * trb > (size_t)STAGE_MAX)
-    ks *= 2;
+  // split K across blocks only when the grid would leave most CUs idle
+  // (keeping a tile per wave; the cross-block finish costs two device-wide
+  // fences per block), and until the block's activation rows fit the
+  // staging buffer
+  while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ks *= 2;
   P.kts = ceil_div(g.KT, ks);
   P.ksplit = ceil_div(g.KT, P.kts);
   const int per = ceil_div(P.kts, GEMV_WAVES);
   P.maxt = per <= 4 ? 4 : per <= 8 ? 8 : 16;
+  // stage the block's activation rows in LDS when they fit, else each lane
+  // streams its own fragments from L2
+  P.staged = (size_t)rows * P.kts * trb <= (size_t)STAGE_MAX;
   const int chunks = ceil_div(rows * P.kts * trb, 16);
   const int aper = ceil_div(chunks, GEMV_THREADS);
   P.aper = aper <= 1 ? 1 : aper <= 2 ? 2 : aper <= 4 ? 4 : 8;
-  P.smem = std::max((size_t)rows * (P.kts * trb + 16), (size_t)GEMV_WAVES * 1024);
+  P.smem = std::max(P.staged ? (size_t)rows * (P.kts * trb + 16) : 0, (size_t)GEMV_WAVES * 1024);
   if (P.ksplit > 1) {
     P.counters_bytes = align256((size_t)P.mtiles * g.NT * sizeof(unsigned));
     P.ws_bytes = P.counters_bytes + (size_t)P.mtiles * P.ksplit * g.NT * 256 * 4;
@@ -67,16 +70,23 @@ inline Plan make_plan(int kind, int M, int N, int K) {
 
 template <int KIND, int MAXT>
 int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream) {
-  const dim3 grid(p.NT, P.ksplit, P.mtiles);
+  // x enumerates (n tile, m tile) pairs so that the m tiles of one n tile land
+  // on the same XCD (blocks are dealt to the 8 XCDs round-robin by id)
+  const int nblk = P.mtiles == 1 ? p.NT : ceil_div(p.NT * P.mtiles, 8) * 8;
+  const dim3 grid(nblk, P.ksplit, 1);
   const dim3 block(GEMV_THREADS);
-#define W4_GEMV_CASE(A)                                                   \
-  allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A>, P.smem);     \
-  hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A>), grid, block, P.smem, stream, p)
-  switch (P.aper) {
-    case 1: W4_GEMV_CASE(1); break;
-    case 2: W4_GEMV_CASE(2); break;
-    case 4: W4_GEMV_CASE(4); break;
-    default: W4_GEMV_CASE(8); break;
+#define W4_GEMV_CASE(A, ST)                                                   \
+  allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>, P.smem);     \
+  hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>), grid, block, P.smem, stream, p)
+  if (!P.staged) {
+    W4_GEMV_CASE(1, false);
+  } else {
+    switch (P.aper) {
+      case 1: W4_GEMV_CASE(1, true); break;
+      case 2: W4_GEMV_CASE(2, true); break;
+      case 4: W4_GEMV_CASE(4, true); break;
+      default: W4_GEMV_CASE(8, true); break;
+    }
   }
 #undef W4_GEMV_CASE
   return launch_status();

@@ -1,0 +1,157 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+    python -m gemv_nibble_unpack_amd.profiling trace <rocprof_dir> <out.md> --cmd "<command>"
+    python -m gemv_nibble_unpack_amd.profiling traffic <fetch_dir> <write_dir> <out.json> \
+        --kernel <substring> --calib-bytes <bytes> --cmd "<commands>"
+
+``trace`` reads a ``--kernel-trace --output-format csv`` directory and writes
+per-kernel call counts and durations. ``traffic`` reads two ``--pmc
+FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs (KiB per dispatch) of a program that
+also ran a plain device-to-device copy of ``calib-bytes`` bytes; the copy's
+counter readings give the scale factor from counter KiB to real bytes, and the
+kernel's readings times that factor give its HBM bytes per launch. The JSON
+also records a hash of the kernel sources so a later benchmark run reports the
+traffic only while the kernel is unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+
+def kernel_source_hash():
+    """sha256 over every HIP source of the library (any change invalidates)."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def trace_rows(d):
+    """(kernel name, duration ns) per dispatch from a kernel-trace CSV dir."""
+    path = _find(d, "kernel_trace.csv")
+    out = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            out.append((row["Kernel_Name"], int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+    return out
+
+
+def summarize_trace(d, out_path, cmd):
+    rows = trace_rows(d)
+    by = defaultdict(list)
+    for name, ns in rows:
+        by[name].append(ns / 1e3)
+    lines = ["# rocprofv3 kernel trace summary", "", f"Command: `{cmd}`", "",
+             "| kernel | calls | mean us | median us | min us |", "|---|---|---|---|---|"]
+    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {len(v)} | {statistics.mean(v):.2f} | "
+                     f"{statistics.median(v):.2f} | {min(v):.2f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
+
+
+def pmc_values(d, counter):
+    path = _find(d, "counter_collection.csv")
+    out = defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_traffic(fetch_dir, write_dir, out_path, kernel, calib_bytes, cmd):
+    fetch = pmc_values(fetch_dir, "FETCH_SIZE")
+    write = pmc_values(write_dir, "WRITE_SIZE")
+
+    def pick(table, key):
+        vals = [v for name, vs in table.items() if key in name for v in vs]
+        if not vals:
+            raise KeyError(f"no dispatch matching {key!r}")
+        return statistics.median(vals)
+
+    def copy_kernel(table):
+        names = [n for n in table if "copy" in n.lower() or "elementwise" in n.lower()]
+        # the calibration copy is the largest copy in the run
+        return max(names, key=lambda n: statistics.median(table[n]))
+
+    cf, cw = copy_kernel(fetch), copy_kernel(write)
+    f_scale = calib_bytes / statistics.median(fetch[cf])
+    w_scale = calib_bytes / statistics.median(write[cw])
+    kf, kw = pick(fetch, kernel), pick(write, kernel)
+    rec = {
+        "kernel": kernel,
+        "fetch_kib_per_launch": kf, "write_kib_per_launch": kw,
+        "calibration": {"copy_kernel": cf, "bytes": calib_bytes,
+                        "fetch_kib": statistics.median(fetch[cf]),
+                        "write_kib": statistics.median(write[cw]),
+                        "fetch_bytes_per_kib": f_scale, "write_bytes_per_kib": w_scale},
+        "read_bytes_per_launch": kf * f_scale,
+        "write_bytes_per_launch": kw * w_scale,
+        "traffic_bytes_per_launch": kf * f_scale + kw * w_scale,
+        "source_hash": kernel_source_hash(),
+        "command": cmd,
+    }
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def load_traffic(path):
+    """The recorded traffic, or None if absent or the kernels changed since."""
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("out")
+    t.add_argument("--cmd", required=True)
+    q = sub.add_parser("traffic")
+    q.add_argument("fetch_dir")
+    q.add_argument("write_dir")
+    q.add_argument("out")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--calib-bytes", type=int, required=True)
+    q.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    if a.what == "trace":
+        print(summarize_trace(a.dir, a.out, a.cmd))
+    else:
+        print(json.dumps(summarize_traffic(a.fetch_dir, a.write_dir, a.out, a.kernel,
+                                           a.calib_bytes, a.cmd), indent=1))
+
+
+if __name__ == "__main__":
+    main()
