@@ -104,13 +104,15 @@ def time_graph(fn, steps, warmup, stream):
 
 
 def calibration_copy():
-    """A plain device-to-device copy of CALIB_BYTES, three times (its PMC
-    FETCH_SIZE/WRITE_SIZE readings calibrate the byte counters)."""
+    """A plain copy kernel of CALIB_BYTES (read once, written once), three
+    times: torch's elementwise bitwise_not on uint8 (a device kernel, unlike
+    copy_, which the runtime may hand to a DMA engine). Its PMC
+    FETCH_SIZE/WRITE_SIZE readings calibrate the byte counters."""
     import torch
     src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)
     torch.cuda.synchronize()
 
 

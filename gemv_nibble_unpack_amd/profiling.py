@@ -2,7 +2,7 @@
 
     python -m gemv_nibble_unpack_amd.profiling trace <rocprof_dir> <out.md> --cmd "<command>"
     python -m gemv_nibble_unpack_amd.profiling traffic <fetch_dir> <write_dir> <out.json> \
-        --kernel <substring> --calib-bytes <bytes> --cmd "<commands>"
+        --kernel <substring> --calib-bytes <bytes> [--calib-kernel <substring>] --cmd "<commands>"
 
 ``trace`` reads a ``--kernel-trace --output-format csv`` directory and writes
 per-kernel call counts and durations. ``traffic`` reads two ``--pmc
@@ -81,7 +81,8 @@ def pmc_values(d, counter):
     return out
 
 
-def summarize_traffic(fetch_dir, write_dir, out_path, kernel, calib_bytes, cmd):
+def summarize_traffic(fetch_dir, write_dir, out_path, kernel, calib_bytes, cmd,
+                      calib_kernel="bitwise_not"):
     fetch = pmc_values(fetch_dir, "FETCH_SIZE")
     write = pmc_values(write_dir, "WRITE_SIZE")
 
@@ -92,9 +93,10 @@ def summarize_traffic(fetch_dir, write_dir, out_path, kernel, calib_bytes, cmd):
         return statistics.median(vals)
 
     def copy_kernel(table):
-        names = [n for n in table if "copy" in n.lower() or "elementwise" in n.lower()]
-        # the calibration copy is the largest copy in the run
-        return max(names, key=lambda n: statistics.median(table[n]))
+        names = [n for n in table if calib_kernel in n]
+        if not names:
+            raise KeyError(f"no calibration kernel matching {calib_kernel!r}")
+        return names[0]
 
     cf, cw = copy_kernel(fetch), copy_kernel(write)
     f_scale = calib_bytes / statistics.median(fetch[cf])
@@ -144,13 +146,15 @@ def main():
     q.add_argument("out")
     q.add_argument("--kernel", required=True)
     q.add_argument("--calib-bytes", type=int, required=True)
+    q.add_argument("--calib-kernel", default="bitwise_not",
+                   help="name substring of the calibration copy kernel")
     q.add_argument("--cmd", required=True)
     a = ap.parse_args()
     if a.what == "trace":
         print(summarize_trace(a.dir, a.out, a.cmd))
     else:
         print(json.dumps(summarize_traffic(a.fetch_dir, a.write_dir, a.out, a.kernel,
-                                           a.calib_bytes, a.cmd), indent=1))
+                                           a.calib_bytes, a.cmd, a.calib_kernel), indent=1))
 
 
 if __name__ == "__main__":
