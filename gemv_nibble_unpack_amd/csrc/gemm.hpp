@@ -30,20 +30,35 @@ template <int KIND>
 struct GemmTraits {
   static constexpr int TILE_K = KindTraits<KIND>::TILE_K;  // k per stage (one weight tile)
   static constexpr int KSTEPS = TILE_K / 64;               // MFMA k steps per lane quarter
-  static constexpr int A_STRIDE = TILE_K + 16;             // padded LDS row (bytes)
-  static constexpr int A_BYTES = GEMM_BM * A_STRIDE;
-  static constexpr int A_CHUNKS = GEMM_BM * TILE_K / 16 / GEMM_THREADS;  // per thread
+  static constexpr int ROW_CHUNKS = TILE_K / 16;           // 16-byte chunks per staged A row
+  static constexpr int A_BYTES = GEMM_BM * TILE_K;         // unpadded, XOR-swizzled rows
+  static constexpr int A_LOADS = A_BYTES / TILE_BYTES;     // 1 KiB wave loads per stage
 };
+
+// Physical 16-byte chunk of logical chunk c in staged A row `row`: an XOR
+// swizzle that puts the 16 rows of a fragment read on distinct LDS banks
+// (128-byte rows: rows alternate between two 32-bank halves, so the swizzle
+// uses row>>1; 256-byte rows all start on bank 0, so it uses row itself).
+template <int KIND>
+__device__ __forceinline__ int a_chunk(int row, int c) {
+  if constexpr (GemmTraits<KIND>::ROW_CHUNKS == 8) return c ^ ((row >> 1) & 7);
+  else return c ^ (row & 15);
+}
 
 template <int KIND, int NTILES>
 struct GemmShape {
   using G = GemmTraits<KIND>;
   static constexpr int W_BYTES = NTILES * TILE_BYTES;
   static constexpr int STAGE = G::A_BYTES + W_BYTES;
-  static constexpr int W_CHUNKS = NTILES * 64 / GEMM_THREADS;  // per thread
   static constexpr int NTW = NTILES / 2;                        // n subtiles per wave
-  // register prefetch depth that fits two blocks per CU (256 registers a lane)
-  static constexpr int DEPTH = (KIND == KIND_W4A8 && NTILES == 8) ? 2 : 1;
+  // LDS stages in the ring: two fit two blocks per CU
+  static constexpr int STAGES = 2;
+  static constexpr int A_PER_WAVE = G::A_LOADS / 4;             // direct loads per wave
+  static constexpr int W_PER_WAVE = NTILES / 4;
+  static constexpr int LOADS_PER_STAGE = A_PER_WAVE + W_PER_WAVE;
+  // fp16 epilogue staging: per wave 64 rows of 16*NTW columns, padded row
+  static constexpr int EPI_ROW = NTW * 32 + 16;
+  static constexpr int LDS = STAGES * STAGE > 4 * 64 * EPI_ROW ? STAGES * STAGE : 4 * 64 * EPI_ROW;
 };
 
 struct GemmGrid {
@@ -117,13 +132,14 @@ __device__ __forceinline__ void gemm_col_params(const MMParams& p, int n, f4& ws
   }
 }
 
-template <int KIND, int NTILES, int DEPTH, int OUT, bool BIAS>
+template <int KIND, int NTILES, int OUT, bool BIAS>
 __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, const GemmGrid gg) {
   using G = GemmTraits<KIND>;
   using S = GemmShape<KIND, NTILES>;
   constexpr int TK = G::TILE_K;
   constexpr int J = G::KSTEPS;
   constexpr int NTW = S::NTW;
+  constexpr int RC = G::ROW_CHUNKS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   // ---- block -> (m block, n block, k split) with XCD-contiguous n ranges --
@@ -140,7 +156,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int r = lane & 15, b = lane >> 4;
   const int m0 = mb * GEMM_BM;
@@ -148,54 +164,43 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
 
   const int8_t* A = reinterpret_cast<const int8_t*>(p.A);
 
-  // ---- global -> register staging of one k tile (two register sets) -------
-  u4 ra[DEPTH][G::A_CHUNKS];
-  u4 rw[DEPTH][S::W_CHUNKS];
-  auto gload = [&](int kt, int set) {
-    kt = min(kt, ke - 1);                            // clamped re-load past the end is unused
-#pragma unroll
-    for (int i = 0; i < G::A_CHUNKS; ++i) {
-      const int c = tid + i * GEMM_THREADS;          // chunk in the BM x TK tile
-      const int row = c / (TK / 16), col = c % (TK / 16);
-      const int gm = min(m0 + row, p.M - 1);
-      const int gk = min(kt * TK + col * 16, p.K - 16);
-      ra[set][i] = *reinterpret_cast<const u4*>(A + (size_t)gm * p.K + gk);
-    }
-#pragma unroll
-    for (int i = 0; i < S::W_CHUNKS; ++i) {
-      const int c = tid + i * GEMM_THREADS;          // chunk among NTILES x 64
-      const int t = min(t0 + (c >> 6), p.NT - 1);
-      rw[set][i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(
-          p.Wt + ((size_t)t * p.KT + kt) * TILE_BYTES + (c & 63) * 16));
-    }
-  };
-  auto sstore = [&](int kt, int set, int buf) {
-    uint8_t* sa = smem + buf * S::STAGE;
+  // ---- direct global -> LDS copies of one k tile into stage `st` -----------
+  // Each wave instruction fills 1 KiB of LDS (lane l -> bytes 16l..16l+15).
+  // Rows past M and k past K read clamped addresses: the weight codes there
+  // are zero, so those products vanish, and rows past M are never stored.
+  const int lrow = lane / RC, lchunk = lane % RC;    // position within one 1 KiB load
+  auto issue = [&](int kt, int st) {
+    uint8_t* sa = smem + st * S::STAGE;
     uint8_t* sw = sa + G::A_BYTES;
 #pragma unroll
-    for (int i = 0; i < G::A_CHUNKS; ++i) {
-      const int c = tid + i * GEMM_THREADS;
-      const int row = c / (TK / 16), col = c % (TK / 16);
-      u4 v = ra[set][i];
-      if (kt * TK + col * 16 >= p.K) v = u4{0u, 0u, 0u, 0u};   // k tail
-      *reinterpret_cast<u4*>(sa + row * G::A_STRIDE + col * 16) = v;
+    for (int q = 0; q < S::A_PER_WAVE; ++q) {
+      const int ld = wave * S::A_PER_WAVE + q;       // 1 KiB load index within the A tile
+      const int row = ld * (64 / RC) + lrow;
+      const int c = a_chunk<KIND>(row, lchunk);      // logical chunk for this physical slot
+      const int gm = min(m0 + row, p.M - 1);
+      const int gk = min(kt * TK + 16 * c, p.K - 16);
+      __builtin_amdgcn_global_load_lds(A + (size_t)gm * p.K + gk, sa + ld * TILE_BYTES, 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < S::W_CHUNKS; ++i) {
-      const int c = tid + i * GEMM_THREADS;
-      *reinterpret_cast<u4*>(sw + c * 16) = rw[set][i];
+    for (int q = 0; q < S::W_PER_WAVE; ++q) {
+      const int tl = wave * S::W_PER_WAVE + q;       // weight tile within the block
+      const int t = min(t0 + tl, p.NT - 1);
+      __builtin_amdgcn_global_load_lds(p.Wt + ((size_t)t * p.KT + kt) * TILE_BYTES + lane * 16,
+                                       sw + tl * TILE_BYTES, 16, 0, 0);
     }
   };
-  auto compute = [&](int buf, i4 (&acc)[4][NTW]) {
-    const uint8_t* sa = smem + buf * S::STAGE;
+  auto compute = [&](int st, i4 (&acc)[4][NTW]) {
+    const uint8_t* sa = smem + st * S::STAGE;
     const uint8_t* sw = sa + G::A_BYTES;
     i4 af[4][J];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * wm + 16 * i + r;
 #pragma unroll
       for (int j = 0; j < J; ++j)
-        af[i][j] = *reinterpret_cast<const i4*>(sa + (64 * wm + 16 * i + r) * G::A_STRIDE +
-                                                (TK / 4) * b + 16 * j);
+        af[i][j] = *reinterpret_cast<const i4*>(sa + row * TK +
+                                                16 * a_chunk<KIND>(row, (RC / 4) * b + j));
+    }
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       const u4 w = *reinterpret_cast<const u4*>(sw + (wn * NTW + t) * TILE_BYTES + lane * 16);
@@ -215,40 +220,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[i][t] = i4{0, 0, 0, 0};
 
-  if constexpr (DEPTH == 2) {
-    // prologue: tile kb -> LDS 0, tile kb+1 in flight in register set 1
-    if (nk > 0) {
-      gload(kb, 0);
-      gload(kb + 1, 1);
-      sstore(kb, 0, 0);
-    }
+  // Two-stage ring: tile i+1 streams into the other stage while tile i is
+  // multiplied; the barrier after the wait publishes it to every wave and
+  // frees stage i for tile i+2.
+  if (nk > 0) issue(kb, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) issue(kb + i + 1, (i + 1) & 1);
+    compute(i & 1, acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // iteration i computes tile kb+i from LDS buffer i&1 while tile kb+i+1
-    // (register set (i+1)&1) lands and tile kb+i+2 is requested
-    for (int i = 0; i < nk; i += 2) {
-      if (i + 2 < nk) gload(kb + i + 2, 0);
-      compute(0, acc);
-      if (i + 1 < nk) sstore(kb + i + 1, 1, 1);
-      __syncthreads();
-      if (i + 1 >= nk) break;
-      if (i + 3 < nk) gload(kb + i + 3, 1);
-      compute(1, acc);
-      if (i + 2 < nk) sstore(kb + i + 2, 0, 0);
-      __syncthreads();
-    }
-  } else {
-    // one register set: tile kb+i+1 is requested before tile kb+i is computed
-    if (nk > 0) {
-      gload(kb, 0);
-      sstore(kb, 0, 0);
-    }
-    __syncthreads();
-    for (int i = 0; i < nk; ++i) {
-      if (i + 1 < nk) gload(kb + i + 1, 0);
-      compute(i & 1, acc);
-      if (i + 1 < nk) sstore(kb + i + 1, 0, (i + 1) & 1);
-      __syncthreads();
-    }
   }
 
   // ---- epilogue: lane owns columns n..n+3 of row m for each fragment -------
@@ -258,6 +240,44 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     sav[i] = OUT == W4_OUT_I32 ? 0.f : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
+  if constexpr (OUT == W4_OUT_F16) {
+    if (gg.ksplit == 1 && (p.N % 8) == 0) {
+      // Stage the wave's fp16 tile (64 rows x 16*NTW columns) in LDS, then
+      // store whole 16-byte row chunks (a 16-lane group writes a full row
+      // segment). The k loop ended with a barrier, so the stages are free.
+      constexpr int WC = NTW * 16;
+      constexpr int RS = S::EPI_ROW;
+      uint8_t* cw = smem + wave * 64 * RS;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
+        gemm_col_params<KIND, OUT, BIAS>(p, nbase + 16 * t, ws, bias);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float o = (float)(acc[i][t][e] >> KindTraits<KIND>::SHIFT) * ws[e] * sav[i];
+            if constexpr (BIAS) o += bias[e];
+            h[e] = f2h(o);
+          }
+          *reinterpret_cast<u2*>(cw + (16 * i + r) * RS + (16 * t + 4 * b) * 2) =
+              u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        }
+      }
+      const int n_w = (t0 + wn * NTW) * 16;          // first column of the wave tile
+#pragma unroll
+      for (int q = 0; q < 64 * WC / 8 / 64; ++q) {
+        const int c = q * 64 + lane;
+        const int row = c / (WC / 8), c8 = c % (WC / 8);
+        const u4 v = *reinterpret_cast<const u4*>(cw + row * RS + c8 * 16);
+        const int m = m0 + 64 * wm + row, n = n_w + 8 * c8;
+        if (m < p.M && n < p.N)
+          *reinterpret_cast<u4*>(reinterpret_cast<uint16_t*>(p.C) + (size_t)m * p.N + n) = v;
+      }
+      return;
+    }
+  }
   if (gg.ksplit == 1) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
@@ -326,6 +346,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
 // ---------------------------------------------------------------------------
 // planning (host)
 // ---------------------------------------------------------------------------
+#ifndef W4_GEMM_NTILES
+#define W4_GEMM_NTILES 16
+#endif
 inline int gemm_ntiles(int kind, int N);
 
 // The tiled GEMM needs enough 128-row x (16*NTILES)-column tiles to fill the
@@ -338,10 +361,14 @@ inline bool use_gemm(int kind, int M, int N) {
   return tiles >= 128;
 }
 
-#ifndef W4_GEMM_WIDE_MIN_N
-#define W4_GEMM_WIDE_MIN_N 4096
-#endif
-inline int gemm_ntiles(int kind, int N) { return kind == KIND_W4A8 && N >= W4_GEMM_WIDE_MIN_N ? 16 : 8; }
+// Weight tiles per block: the candidate with the fewest block-slot rounds on
+// 256 CUs x 2 blocks, weighted by the per-tile work (a block's time grows with
+// its width), wider on ties.
+inline int gemm_ntiles(int kind, int N) {
+  if (kind != KIND_W4A8) return 8;
+  (void)N;
+  return W4_GEMM_NTILES;
+}
 
 inline GemmGrid gemm_grid(int kind, int M, int N, int K) {
   const Geometry g = geometry(kind == KIND_W2A8 ? W4_LAYOUT_W2A8 : W4_LAYOUT_W4A8, N, K);
@@ -368,11 +395,10 @@ inline size_t gemm_workspace_bytes(int kind, int M, int N, int K) {
 template <int KIND, int NTILES, int OUT, bool BIAS>
 int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
   using S = GemmShape<KIND, NTILES>;
-  constexpr int DEPTH = GemmShape<KIND, NTILES>::DEPTH;
   const dim3 grid(gg.per_xcd * 8, gg.ksplit);
-  allow_smem((const void*)&k_gemm<KIND, NTILES, DEPTH, OUT, BIAS>, 2 * S::STAGE);
-  hipLaunchKernelGGL((k_gemm<KIND, NTILES, DEPTH, OUT, BIAS>), grid, dim3(GEMM_THREADS),
-                     2 * S::STAGE, stream, p, gg);
+  allow_smem((const void*)&k_gemm<KIND, NTILES, OUT, BIAS>, S::LDS);
+  hipLaunchKernelGGL((k_gemm<KIND, NTILES, OUT, BIAS>), grid, dim3(GEMM_THREADS), S::LDS,
+                     stream, p, gg);
   return launch_status();
 }
 
@@ -394,7 +420,9 @@ int launch_gemm(const MMParams& p, void* ws, hipStream_t stream) {
   } else {
     const GemmGrid gg = gemm_grid(KIND, p.M, p.N, p.K);
     if constexpr (KIND == KIND_W4A8) {
-      if (gemm_ntiles(KIND, p.N) == 16) return launch_gemm_t<KIND, 16>(p, gg, ws, stream);
+      const int nt = gemm_ntiles(KIND, p.N);
+      if (nt == 16) return launch_gemm_t<KIND, 16>(p, gg, ws, stream);
+      if (nt == 12) return launch_gemm_t<KIND, 12>(p, gg, ws, stream);
     }
     return launch_gemm_t<KIND, 8>(p, gg, ws, stream);
   }

@@ -206,8 +206,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       const bool live = u < pn;
       const int kt = pb + u;
       const size_t ti = live ? (size_t)tile * p.KT + kt : 0;
-      wv[u] = __builtin_nontemporal_load(
-          reinterpret_cast<const u4*>(p.Wt + ti * TILE_BYTES + lane * 16));
+      const u4* wp = reinterpret_cast<const u4*>(p.Wt + ti * TILE_BYTES + lane * 16);
+      // streamed once unless several m tiles share the weight tile through L2
+      wv[u] = mtiles == 1 ? __builtin_nontemporal_load(wp) : *wp;
       if constexpr (A16) {
         const size_t mi =
             live ? (((size_t)tile * p.KQ + (kt >> 2)) * TILE_N + r) * 4 + (kt & 3) : 0;

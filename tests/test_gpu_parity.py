@@ -189,6 +189,47 @@ def test_w4a8_prefill_config_sampled(g):
     tol_ok(C16[rows, cols], ref16, c.name)
 
 
+@pytest.mark.parametrize("scheme,M,N,K", [("w4a8", 2000, 3000, 1040), ("w4a8", 1100, 4004, 512),
+                                          ("w2a8", 2000, 3000, 1040), ("w2a8", 1030, 4100, 528)])
+def test_gemm_path_ragged_sampled(g, scheme, M, N, K):
+    # shapes large enough for the tiled prefill GEMM (>= 128 tiles), with
+    # ragged M, N (N % 8 != 0 takes the direct epilogue) and K tails
+    say(f"case gemm path {scheme} M={M} N={N} K={K}")
+    A = WL.activations(M, K, seed=8000 + M)
+    bias = WL.bias_f16(N, seed=8001)
+    Aq, sa, _ = g.quantize_a8(dev(A))
+    qa, sa_ref, _ = O.quantize_a8(A)
+    if scheme == "w4a8":
+        W = WL.weights_f32(N, K, seed=8002 + N)
+        Wp, ws = prep_w4a8(g, W)
+        qw, s_ref = O.quantize_w4_sym(W)
+        mm = g.w4a8_gemm
+        ws_ref = lambda cols: s_ref[cols]
+    else:
+        codes = WL.ternary_codes(N, K, seed=8003 + N)
+        Wp, ws = prep_w2a8(g, codes, WL.weights_f32(N, K, seed=8004 + N))
+        qw = codes
+        mm = g.w2a8_gemm
+        scale = np.float64(host(ws)[0])
+        ws_ref = lambda cols: np.full(len(cols), scale)
+    C32 = host(mm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I32))
+    C16 = host(mm(Aq, sa, Wp, ws, N, bias=f16(bias), out_dtype=g.W4_OUT_F16))
+    C32f = host(mm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_F32))
+    rows, cols = sample_indices(M, N, 3000, seed=11)
+    acc = O.int_accumulate_entries(qa, qw, rows, cols)
+    assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
+    tol_ok(C16[rows, cols], O.dequant_epilogue(acc, ws_ref(cols), sa_ref[rows], bias[cols],
+                                               O.OUT_F16), "f16")
+    tol_ok(C32f[rows, cols], O.dequant_epilogue(acc, ws_ref(cols), sa_ref[rows], None,
+                                                O.OUT_F32), "f32")
+    # the last rows and columns (tails) in full
+    tail_r = np.arange(max(0, M - 3), M)
+    tail_c = np.arange(max(0, N - 40), N)
+    rr, cc = np.meshgrid(tail_r, tail_c, indexing="ij")
+    acc_t = O.int_accumulate_entries(qa, qw, rr.ravel(), cc.ravel())
+    assert np.array_equal(C32[rr, cc].ravel(), acc_t.astype(np.int32))
+
+
 def _w4a16_case(g, c, full=True):
     say(f"case {c.name}")
     d = c.inputs()
