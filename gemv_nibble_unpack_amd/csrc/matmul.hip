@@ -56,7 +56,10 @@ inline Plan make_plan(int kind, int M, int N, int K) {
   P.maxt = per <= 4 ? 4 : per <= 8 ? 8 : 16;
   // stage the block's activation rows in LDS when they fit, else each lane
   // streams its own fragments from L2
-  P.staged = (size_t)rows * P.kts * trb <= (size_t)STAGE_MAX;
+#ifndef W4_GEMV_STAGE_MIN_ROWS
+#define W4_GEMV_STAGE_MIN_ROWS 1
+#endif
+  P.staged = rows >= W4_GEMV_STAGE_MIN_ROWS && (size_t)rows * P.kts * trb <= (size_t)STAGE_MAX;
   const int chunks = ceil_div(rows * P.kts * trb, 16);
   const int aper = ceil_div(chunks, GEMV_THREADS);
   P.aper = aper <= 1 ? 1 : aper <= 2 ? 2 : aper <= 4 ? 4 : 8;

@@ -161,7 +161,10 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
   }
 }
 
-template <typename T>
+// One block per row m. CPT > 0: the row is read once into registers
+// (CPT chunks of 8 elements per thread, K <= 8 * QB * CPT); CPT == 0: two
+// passes over the row (the second read hits L2).
+template <typename T, int CPT>
 __global__ __launch_bounds__(QB) void k_quant_a8(const T* __restrict__ A, int K,
                                                    int8_t* __restrict__ Aq,
                                                    float* __restrict__ a_scale,
@@ -172,29 +175,56 @@ __global__ __launch_bounds__(QB) void k_quant_a8(const T* __restrict__ A, int K,
   const T* row = A + (size_t)m * K;
   const int nch = K / 8;
   float mx = 0.f;
-  for (int c = threadIdx.x; c < nch; c += QB) {
-    float x[8];
-    load8<T>(row + 8 * c, x);
+  float x[CPT > 0 ? CPT : 1][8];
+  if constexpr (CPT > 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(x[i]));
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * QB;
+      if (c < nch) {
+        load8<T>(row + 8 * c, x[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[i][e]));
+    }
+  } else {
+    for (int c = threadIdx.x; c < nch; c += QB) {
+      float y[8];
+      load8<T>(row + 8 * c, y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(y[e]));
+    }
   }
   mx = block_max(mx, shf);
   const float s = mx / 127.0f;
   int sum = 0;
   int8_t* out = Aq + (size_t)m * K;
-  for (int c = threadIdx.x; c < nch; c += QB) {
-    float x[8];
-    load8<T>(row + 8 * c, x);
+  auto emit = [&](int c, const float (&y)[8]) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int q = sym_code(x[i], s, 127.f);
+      const int q = sym_code(y[i], s, 127.f);
       sum += q;
-      const uint32_t b = (uint32_t)(q & 0xFF);
-      if (i < 4) lo |= b << (8 * i);
-      else hi |= b << (8 * (i - 4));
+      const uint32_t bq = (uint32_t)(q & 0xFF);
+      if (i < 4) lo |= bq << (8 * i);
+      else hi |= bq << (8 * (i - 4));
     }
     *reinterpret_cast<u2*>(out + 8 * c) = u2{lo, hi};
+  };
+  if constexpr (CPT > 0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * QB;
+      if (c < nch) emit(c, x[i]);
+    }
+  } else {
+    for (int c = threadIdx.x; c < nch; c += QB) {
+      float y[8];
+      load8<T>(row + 8 * c, y);
+      emit(c, y);
+    }
   }
   sum = block_sum_i(sum, shi);
   if (threadIdx.x == 0) {
@@ -272,11 +302,20 @@ extern "C" int quantize_a8(const void* A, int in_dtype, int M, int K, int8_t* Aq
   if (!aligned(A, 16) || !aligned(Aq, 16) || !aligned(a_scale, 4) ||
       (rowsum && !aligned(rowsum, 4)))
     return W4_ERR_ALIGN;
-  if (in_dtype == W4_IN_F16)
-    hipLaunchKernelGGL(k_quant_a8<uint16_t>, dim3(M), dim3(QB), 0, stream,
-                       (const uint16_t*)A, K, Aq, a_scale, rowsum);
-  else
-    hipLaunchKernelGGL(k_quant_a8<float>, dim3(M), dim3(QB), 0, stream, (const float*)A, K, Aq,
-                       a_scale, rowsum);
+  const int cpt = (K / 8 + QB - 1) / QB;            // 8-element chunks per thread
+#define W4_QA8(T, C) \
+  hipLaunchKernelGGL((k_quant_a8<T, C>), dim3(M), dim3(QB), 0, stream, (const T*)A, K, Aq, a_scale, rowsum)
+  if (in_dtype == W4_IN_F16) {
+    if (cpt <= 1) W4_QA8(uint16_t, 1);
+    else if (cpt <= 2) W4_QA8(uint16_t, 2);
+    else if (cpt <= 4) W4_QA8(uint16_t, 4);
+    else W4_QA8(uint16_t, 0);
+  } else {
+    if (cpt <= 1) W4_QA8(float, 1);
+    else if (cpt <= 2) W4_QA8(float, 2);
+    else if (cpt <= 4) W4_QA8(float, 4);
+    else W4_QA8(float, 0);
+  }
+#undef W4_QA8
   return launch_status();
 }
