@@ -12,8 +12,12 @@
 // epilogue shifts out the 2^4 (2^6) factor and applies
 // w_scale * a_scale (+ bias) (INT4 page, Part 1 step 4) before the store.
 //
-// Block: 256 threads = 4 waves in a 2 (m) x 2 (n) grid, block tile
-// BM = 128 rows x BN = 16 * NTILES columns, wave tile 64 x 8*NTILES.
+// Block: 2*WM waves in a WM (m) x 2 (n) grid, block tile BM = 64*WM rows x
+// BN = 16 * NTILES columns, wave tile 64 x 8*NTILES. WM = 2 runs two blocks
+// per CU; WM = 4 runs one 512-thread block per CU, whose two waves per SIMD
+// meet at the same barrier every k tile (two independent blocks drift apart:
+// the hardware favours the older one, and the younger then finishes alone
+// with one wave per SIMD, too few to keep the matrix core busy).
 // Blocks are mapped so that each of the 8 XCDs works on a contiguous range of
 // weight columns (its slice of W stays in that XCD's L2 while all m blocks
 // pass over it).
@@ -23,16 +27,11 @@
 
 namespace w4 {
 
-constexpr int GEMM_THREADS = 256;
-constexpr int GEMM_BM = 128;
-
 template <int KIND>
 struct GemmTraits {
   static constexpr int TILE_K = KindTraits<KIND>::TILE_K;  // k per stage (one weight tile)
   static constexpr int KSTEPS = TILE_K / 64;               // MFMA k steps per lane quarter
   static constexpr int ROW_CHUNKS = TILE_K / 16;           // 16-byte chunks per staged A row
-  static constexpr int A_BYTES = GEMM_BM * TILE_K;         // unpadded, XOR-swizzled rows
-  static constexpr int A_LOADS = A_BYTES / TILE_BYTES;     // 1 KiB wave loads per stage
 };
 
 // Physical 16-byte chunk of logical chunk c in staged A row `row`: an XOR
@@ -45,20 +44,39 @@ __device__ __forceinline__ int a_chunk(int row, int c) {
   else return c ^ (row & 15);
 }
 
-template <int KIND, int NTILES>
+template <int KIND, int NTILES, int WM>
 struct GemmShape {
   using G = GemmTraits<KIND>;
+  static_assert(WM == 2 || WM == 4, "128- or 256-row blocks");
+  static constexpr int WAVES = 2 * WM;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 64 * WM;
+  static constexpr int BLOCKS_PER_CU = 4 / WM;                  // two waves per SIMD
+  static constexpr int A_BYTES = BM * G::TILE_K;                // unpadded, XOR-swizzled rows
+  static constexpr int A_LOADS = A_BYTES / TILE_BYTES;          // 1 KiB wave loads per stage
   static constexpr int W_BYTES = NTILES * TILE_BYTES;
-  static constexpr int STAGE = G::A_BYTES + W_BYTES;
+  static constexpr int STAGE = A_BYTES + W_BYTES;
+  static_assert(NTILES % 2 == 0, "two waves split the block's columns");
   static constexpr int NTW = NTILES / 2;                        // n subtiles per wave
-  // LDS stages in the ring: two fit two blocks per CU
+  // LDS stages in the ring (two fit the CU's 160 KiB in every configuration)
   static constexpr int STAGES = 2;
-  static constexpr int A_PER_WAVE = G::A_LOADS / 4;             // direct loads per wave
-  static constexpr int W_PER_WAVE = NTILES / 4;
-  static constexpr int LOADS_PER_STAGE = A_PER_WAVE + W_PER_WAVE;
-  // fp16 epilogue staging: per wave 64 rows of 16*NTW columns, padded row
-  static constexpr int EPI_ROW = NTW * 32 + 16;
-  static constexpr int LDS = STAGES * STAGE > 4 * 64 * EPI_ROW ? STAGES * STAGE : 4 * 64 * EPI_ROW;
+  static constexpr int A_PER_WAVE = A_LOADS / WAVES;            // direct loads per wave
+  static constexpr int W_PER_WAVE = (NTILES + WAVES - 1) / WAVES;  // last round may be partial
+  // fp16 epilogue staging: per wave and pass, 32 rows of 16*NTW columns
+  static constexpr int EPI_ROWS = 32;
+  static constexpr int EPI_ROW = NTW * 32 + 16;                 // padded row bytes
+  static constexpr int EPI = WAVES * EPI_ROWS * EPI_ROW;
+  // the block's column scales (f32) and biases (f16) sit in LDS behind the
+  // stages when two blocks still fit a CU's 160 KiB, so that the epilogue
+  // does not hold them in registers next to every accumulator
+  static constexpr int PARAM_OFF = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
+  static constexpr int PARAM_BYTES = NTILES * 16 * 6;
+  static constexpr bool LDS_PARAMS = BLOCKS_PER_CU * (PARAM_OFF + PARAM_BYTES) <= 160 * 1024;
+  static constexpr int LDS = PARAM_OFF + (LDS_PARAMS ? PARAM_BYTES : 0);
+  static_assert(BLOCKS_PER_CU * LDS <= 160 * 1024, "LDS exceeds the CU");
+  // the split-K finish holds every accumulator next to its partial sums;
+  // wider blocks would spill, so they are only planned with ksplit == 1
+  static constexpr bool SPLIT_OK = NTILES <= 16;
 };
 
 struct GemmGrid {
@@ -132,10 +150,11 @@ __device__ __forceinline__ void gemm_col_params(const MMParams& p, int n, f4& ws
   }
 }
 
-template <int KIND, int NTILES, int OUT, bool BIAS>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, const GemmGrid gg) {
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
+__global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const GemmGrid gg) {
   using G = GemmTraits<KIND>;
-  using S = GemmShape<KIND, NTILES>;
+  using S = GemmShape<KIND, NTILES, WM>;
+  static_assert(S::THREADS == 128 * WM, "launch bounds");
   constexpr int TK = G::TILE_K;
   constexpr int J = G::KSTEPS;
   constexpr int NTW = S::NTW;
@@ -157,9 +176,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int r = lane & 15, b = lane >> 4;
-  const int m0 = mb * GEMM_BM;
+  const int m0 = mb * S::BM;
   const int t0 = nb * NTILES;                        // first n tile of the block
 
   const int8_t* A = reinterpret_cast<const int8_t*>(p.A);
@@ -171,7 +190,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
   const int lrow = lane / RC, lchunk = lane % RC;    // position within one 1 KiB load
   auto issue = [&](int kt, int st) {
     uint8_t* sa = smem + st * S::STAGE;
-    uint8_t* sw = sa + G::A_BYTES;
+    uint8_t* sw = sa + S::A_BYTES;
 #pragma unroll
     for (int q = 0; q < S::A_PER_WAVE; ++q) {
       const int ld = wave * S::A_PER_WAVE + q;       // 1 KiB load index within the A tile
@@ -183,7 +202,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
     }
 #pragma unroll
     for (int q = 0; q < S::W_PER_WAVE; ++q) {
-      const int tl = wave * S::W_PER_WAVE + q;       // weight tile within the block
+      const int tl = q * S::WAVES + wave;            // weight tile within the block
+      if (NTILES % S::WAVES != 0 && tl >= NTILES) break;  // wave-uniform
       const int t = min(t0 + tl, p.NT - 1);
       __builtin_amdgcn_global_load_lds(p.Wt + ((size_t)t * p.KT + kt) * TILE_BYTES + lane * 16,
                                        sw + tl * TILE_BYTES, 16, 0, 0);
@@ -191,7 +211,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
   };
   auto compute = [&](int st, i4 (&acc)[4][NTW]) {
     const uint8_t* sa = smem + st * S::STAGE;
-    const uint8_t* sw = sa + G::A_BYTES;
+    const uint8_t* sw = sa + S::A_BYTES;
     i4 af[4][J];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -201,16 +221,42 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
         af[i][j] = *reinterpret_cast<const i4*>(sa + row * TK +
                                                 16 * a_chunk<KIND>(row, (RC / 4) * b + j));
     }
+    // Software pipeline over the wave's weight fragments: fragment t+2 is in
+    // flight from LDS and fragment t+1 is unpacked while the MFMAs of
+    // fragment t run.
+    const uint8_t* swl = sw + wn * NTW * TILE_BYTES + lane * 16;
+    u4 w2 = *reinterpret_cast<const u4*>(swl + (NTW > 1 ? TILE_BYTES : 0));
+    i4 bc[J];
+    unpack_frag<KIND>(*reinterpret_cast<const u4*>(swl), bc);
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      const u4 w = *reinterpret_cast<const u4*>(sw + (wn * NTW + t) * TILE_BYTES + lane * 16);
-      i4 bf[J];
-      unpack_frag<KIND>(w, bf);
+      // Least progress first: the two waves of a SIMD run the same fragment
+      // sequence, and a wave lowers its priority as it gets through its
+      // fragments, so the one that is behind is issued first and both reach
+      // the k-tile barrier together (with equal priority the older wave wins
+      // every arbitration, and the younger one finishes the tile alone).
+      if (t == 0 || (4 * t) / NTW != (4 * (t - 1)) / NTW) {
+        switch ((4 * t) / NTW) {
+          case 0: __builtin_amdgcn_s_setprio(3); break;
+          case 1: __builtin_amdgcn_s_setprio(2); break;
+          case 2: __builtin_amdgcn_s_setprio(1); break;
+          default: __builtin_amdgcn_s_setprio(0); break;
+        }
+      }
+      u4 w3 = w2;
+      if (t + 2 < NTW) w3 = *reinterpret_cast<const u4*>(swl + (t + 2) * TILE_BYTES);
+      i4 bn[J];
+      if (t + 1 < NTW) unpack_frag<KIND>(w2, bn);
 #pragma unroll
       for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)   // weights as the row operand: lane owns 4 columns
-          acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[j], af[i][j], acc[i][t], 0, 0, 0);
+          acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bc[j], af[i][j], acc[i][t], 0, 0, 0);
+      if (t + 1 < NTW) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) bc[j] = bn[j];
+        w2 = w3;
+      }
     }
   };
 
@@ -224,6 +270,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
   // multiplied; the barrier after the wait publishes it to every wave and
   // frees stage i for tile i+2.
   if (nk > 0) issue(kb, 0);
+  constexpr bool LP = S::LDS_PARAMS && OUT == W4_OUT_F16;
+  float* lws = reinterpret_cast<float*>(smem + S::PARAM_OFF);
+  uint16_t* lbias = reinterpret_cast<uint16_t*>(smem + S::PARAM_OFF + NTILES * 16 * 4);
+  if constexpr (LP) {
+#pragma unroll
+    for (int c = tid; c < NTILES * 16; c += S::THREADS) {
+      const int n = min(t0 * 16 + c, p.N - 1);
+      lws[c] = KIND == KIND_W4A8 ? p.w_scale[n] : h2f(p.w_scale16[0]);
+      if constexpr (BIAS) lbias[c] = p.bias[n];
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
@@ -241,44 +298,62 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
   for (int i = 0; i < 4; ++i)
     sav[i] = OUT == W4_OUT_I32 ? 0.f : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
   if constexpr (OUT == W4_OUT_F16) {
-    if (gg.ksplit == 1 && (p.N % 8) == 0) {
-      // Stage the wave's fp16 tile (64 rows x 16*NTW columns) in LDS, then
-      // store whole 16-byte row chunks (a 16-lane group writes a full row
-      // segment). The k loop ended with a barrier, so the stages are free.
+    if ((!S::SPLIT_OK || gg.ksplit == 1) && (p.N % 8) == 0) {
+      // Stage the wave's fp16 tile in LDS, 32 rows x 16*NTW columns per pass,
+      // then store whole 16-byte row chunks (a lane group writes a contiguous
+      // row segment). The k loop ended with a barrier, so the stages are
+      // free; each wave only touches its own region, and its LDS accesses
+      // complete in order, so the passes need no barrier.
       constexpr int WC = NTW * 16;
       constexpr int RS = S::EPI_ROW;
-      uint8_t* cw = smem + wave * 64 * RS;
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
-        gemm_col_params<KIND, OUT, BIAS>(p, nbase + 16 * t, ws, bias);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float o = (float)(acc[i][t][e] >> KindTraits<KIND>::SHIFT) * ws[e] * sav[i];
-            if constexpr (BIAS) o += bias[e];
-            h[e] = f2h(o);
-          }
-          *reinterpret_cast<u2*>(cw + (16 * i + r) * RS + (16 * t + 4 * b) * 2) =
-              u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        }
-      }
+      constexpr int ER = S::EPI_ROWS;
+      constexpr int IP = ER / 16;                    // fragments rows per pass
+      uint8_t* cw = smem + wave * ER * RS;
       const int n_w = (t0 + wn * NTW) * 16;          // first column of the wave tile
 #pragma unroll
-      for (int q = 0; q < 64 * WC / 8 / 64; ++q) {
-        const int c = q * 64 + lane;
-        const int row = c / (WC / 8), c8 = c % (WC / 8);
-        const u4 v = *reinterpret_cast<const u4*>(cw + row * RS + c8 * 16);
-        const int m = m0 + 64 * wm + row, n = n_w + 8 * c8;
-        if (m < p.M && n < p.N)
-          *reinterpret_cast<u4*>(reinterpret_cast<uint16_t*>(p.C) + (size_t)m * p.N + n) = v;
+      for (int h = 0; h < 4 / IP; ++h) {
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (LP) {
+            const int c = (wn * NTW + t) * 16 + 4 * b;
+            ws = *reinterpret_cast<const f4*>(lws + c);
+            if constexpr (BIAS) {
+              const u2 bb = *reinterpret_cast<const u2*>(lbias + c);
+              bias = f4{h2f((uint16_t)bb[0]), h2f((uint16_t)(bb[0] >> 16)), h2f((uint16_t)bb[1]),
+                        h2f((uint16_t)(bb[1] >> 16))};
+            }
+          } else {
+            gemm_col_params<KIND, OUT, BIAS>(p, nbase + 16 * t, ws, bias);
+          }
+#pragma unroll
+          for (int ii = 0; ii < IP; ++ii) {
+            const int i = h * IP + ii;
+            uint32_t hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float o = (float)(acc[i][t][e] >> KindTraits<KIND>::SHIFT) * ws[e] * sav[i];
+              if constexpr (BIAS) o += bias[e];
+              hv[e] = f2h(o);
+            }
+            *reinterpret_cast<u2*>(cw + (16 * ii + r) * RS + (16 * t + 4 * b) * 2) =
+                u2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < ER * WC / 8 / 64; ++q) {
+          const int c = q * 64 + lane;
+          const int row = c / (WC / 8), c8 = c % (WC / 8);
+          const u4 v = *reinterpret_cast<const u4*>(cw + row * RS + c8 * 16);
+          const int m = m0 + 64 * wm + ER * h + row, n = n_w + 8 * c8;
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<u4*>(reinterpret_cast<uint16_t*>(p.C) + (size_t)m * p.N + n) = v;
+        }
       }
       return;
     }
   }
-  if (gg.ksplit == 1) {
+  if (!S::SPLIT_OK || gg.ksplit == 1) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
@@ -346,39 +421,61 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void k_gemm(const MMParams p, cons
 // ---------------------------------------------------------------------------
 // planning (host)
 // ---------------------------------------------------------------------------
-#ifndef W4_GEMM_NTILES
-#define W4_GEMM_NTILES 16
+#ifndef W4_GEMM_CFG
+#define W4_GEMM_CFG 0  // 0: chosen per shape; else 100 * ntiles + wm to force one
 #endif
-inline int gemm_ntiles(int kind, int N);
+constexpr int GEMM_CUS = 256;
 
-// The tiled GEMM needs enough 128-row x (16*NTILES)-column tiles to fill the
-// chip without splitting K; smaller products run on the decode kernel, one
-// block per (16-row tile, 16-column tile).
-inline bool use_gemm(int kind, int M, int N) {
-  if (kind == KIND_W4A16 || M <= 16) return false;
-  const int nt = ceil_div(N, TILE_N);
-  const long tiles = (long)ceil_div(M, GEMM_BM) * ceil_div(nt, gemm_ntiles(kind, N));
-  return tiles >= 128;
+struct GemmCfg {
+  int ntiles, wm;
+};
+
+inline int gemm_tiles(int M, int N, GemmCfg c) {
+  return ceil_div(M, 64 * c.wm) * ceil_div(ceil_div(N, TILE_N), c.ntiles);
 }
 
-// Weight tiles per block: the candidate with the fewest block-slot rounds on
-// 256 CUs x 2 blocks, weighted by the per-tile work (a block's time grows with
-// its width), wider on ties.
-inline int gemm_ntiles(int kind, int N) {
-  if (kind != KIND_W4A8) return 8;
-  (void)N;
-  return W4_GEMM_NTILES;
+// Block shape per product. 2-bit weights unpack into twice the registers and
+// stay at 128 x 128. For W4A8 each candidate is costed by the rounds of
+// resident blocks it needs times the work of one round on a CU (256 rows x
+// 16*ntiles columns in every candidate); the 352-column shapes never split K,
+// so they are only candidates where their grid fills most of the chip.
+inline GemmCfg gemm_cfg(int kind, int M, int N) {
+  if (kind != KIND_W4A8) return GemmCfg{8, 2};
+  const GemmCfg narrow{16, 2};
+  if (W4_GEMM_CFG) {
+    const GemmCfg f{W4_GEMM_CFG / 100, W4_GEMM_CFG % 100};
+    return gemm_tiles(M, N, f) * f.wm >= GEMM_CUS * 3 / 2 ? f : narrow;
+  }
+  GemmCfg best = narrow;
+  int best_cost = ceil_div(gemm_tiles(M, N, narrow), GEMM_CUS * 2) * 16;
+  for (const GemmCfg c : {GemmCfg{22, 2}, GemmCfg{22, 4}}) {
+    const int tiles = gemm_tiles(M, N, c);
+    const int slots = GEMM_CUS * 4 / c.wm;
+    if (tiles * 4 < slots * 3) continue;           // under 3/4 of the chip
+    const int cost = ceil_div(tiles, slots) * c.ntiles;
+    if (cost <= best_cost) best = c, best_cost = cost;
+  }
+  return best;
+}
+
+// The tiled GEMM needs enough block tiles to fill the chip without splitting
+// K much; smaller products run on the decode kernel, one block per (16-row
+// tile, 16-column tile).
+inline bool use_gemm(int kind, int M, int N) {
+  if (kind == KIND_W4A16 || M <= 16) return false;
+  return gemm_tiles(M, N, gemm_cfg(kind, M, N)) >= 128;
 }
 
 inline GemmGrid gemm_grid(int kind, int M, int N, int K) {
   const Geometry g = geometry(kind == KIND_W2A8 ? W4_LAYOUT_W2A8 : W4_LAYOUT_W4A8, N, K);
+  const GemmCfg c = gemm_cfg(kind, M, N);
   GemmGrid gg{};
-  const int nt = gemm_ntiles(kind, N);
-  gg.mblocks = ceil_div(M, GEMM_BM);
-  gg.nblocks = ceil_div(g.NT, nt);
+  gg.mblocks = ceil_div(M, 64 * c.wm);
+  gg.nblocks = ceil_div(g.NT, c.ntiles);
   gg.tiles = gg.mblocks * gg.nblocks;
   int ks = 1;
-  while (gg.tiles * ks < 256 && ceil_div(g.KT, ks * 2) >= 2) ks *= 2;
+  if (c.ntiles <= 16)
+    while (gg.tiles * ks < 256 && ceil_div(g.KT, ks * 2) >= 2) ks *= 2;
   gg.kts = ceil_div(g.KT, ks);
   gg.ksplit = ceil_div(g.KT, gg.kts);
   gg.per_xcd = ceil_div(gg.tiles, 8);
@@ -392,25 +489,25 @@ inline size_t gemm_workspace_bytes(int kind, int M, int N, int K) {
   return counters + (size_t)gg.ksplit * M * N * sizeof(int32_t);
 }
 
-template <int KIND, int NTILES, int OUT, bool BIAS>
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
 int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
-  using S = GemmShape<KIND, NTILES>;
+  using S = GemmShape<KIND, NTILES, WM>;
   const dim3 grid(gg.per_xcd * 8, gg.ksplit);
-  allow_smem((const void*)&k_gemm<KIND, NTILES, OUT, BIAS>, S::LDS);
-  hipLaunchKernelGGL((k_gemm<KIND, NTILES, OUT, BIAS>), grid, dim3(GEMM_THREADS), S::LDS,
+  allow_smem((const void*)&k_gemm<KIND, NTILES, WM, OUT, BIAS>, S::LDS);
+  hipLaunchKernelGGL((k_gemm<KIND, NTILES, WM, OUT, BIAS>), grid, dim3(S::THREADS), S::LDS,
                      stream, p, gg);
   return launch_status();
 }
 
-template <int KIND, int NTILES>
+template <int KIND, int NTILES, int WM>
 int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream) {
   p.counters = reinterpret_cast<unsigned*>(ws);
   const size_t counters = ((size_t)gg.tiles * sizeof(unsigned) + 255) & ~(size_t)255;
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + counters : nullptr;
-  if (p.out_dtype == W4_OUT_I32) return launch_gemm_o<KIND, NTILES, W4_OUT_I32, false>(p, gg, stream);
-  if (p.out_dtype == W4_OUT_F32) return launch_gemm_o<KIND, NTILES, W4_OUT_F32, false>(p, gg, stream);
-  if (p.bias) return launch_gemm_o<KIND, NTILES, W4_OUT_F16, true>(p, gg, stream);
-  return launch_gemm_o<KIND, NTILES, W4_OUT_F16, false>(p, gg, stream);
+  if (p.out_dtype == W4_OUT_I32) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I32, false>(p, gg, stream);
+  if (p.out_dtype == W4_OUT_F32) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F32, false>(p, gg, stream);
+  if (p.bias) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, true>(p, gg, stream);
+  return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, false>(p, gg, stream);
 }
 
 template <int KIND>
@@ -420,11 +517,13 @@ int launch_gemm(const MMParams& p, void* ws, hipStream_t stream) {
   } else {
     const GemmGrid gg = gemm_grid(KIND, p.M, p.N, p.K);
     if constexpr (KIND == KIND_W4A8) {
-      const int nt = gemm_ntiles(KIND, p.N);
-      if (nt == 16) return launch_gemm_t<KIND, 16>(p, gg, ws, stream);
-      if (nt == 12) return launch_gemm_t<KIND, 12>(p, gg, ws, stream);
+      const GemmCfg c = gemm_cfg(KIND, p.M, p.N);
+      if (c.ntiles == 22 && c.wm == 4) return launch_gemm_t<KIND, 22, 4>(p, gg, ws, stream);
+      if (c.ntiles == 22) return launch_gemm_t<KIND, 22, 2>(p, gg, ws, stream);
+      return launch_gemm_t<KIND, 16, 2>(p, gg, ws, stream);
+    } else {
+      return launch_gemm_t<KIND, 8, 2>(p, gg, ws, stream);
     }
-    return launch_gemm_t<KIND, 8>(p, gg, ws, stream);
   }
 }
 

@@ -190,10 +190,12 @@ def test_w4a8_prefill_config_sampled(g):
 
 
 @pytest.mark.parametrize("scheme,M,N,K", [("w4a8", 2000, 3000, 1040), ("w4a8", 1100, 4004, 512),
+                                          ("w4a8", 2000, 11000, 1040), ("w4a8", 1900, 11004, 512),
                                           ("w2a8", 2000, 3000, 1040), ("w2a8", 1030, 4100, 528)])
 def test_gemm_path_ragged_sampled(g, scheme, M, N, K):
     # shapes large enough for the tiled prefill GEMM (>= 128 tiles), with
-    # ragged M, N (N % 8 != 0 takes the direct epilogue) and K tails
+    # ragged M, N (N % 8 != 0 takes the direct epilogue) and K tails; the
+    # N ~ 11000 shapes run 22-tile (352-column) blocks, the others 16 or 8
     say(f"case gemm path {scheme} M={M} N={N} K={K}")
     A = WL.activations(M, K, seed=8000 + M)
     bias = WL.bias_f16(N, seed=8001)
