@@ -94,6 +94,44 @@ def test_quantize_a8_bitexact(g, M, K, dt):
     assert np.array_equal(host(rs), rs_ref)
 
 
+def _near_tie_rows(K=2048):
+    """Rows whose quotients a / s sit on and next to every half integer: for
+    several row maxima, a = fl((k + 1/2) * s) and its float32 neighbours up to
+    4 ulp away, so the code decision is taken right at its rounding edges."""
+    rows = []
+    for amax in (127.0, 100.0, 3.7, 0.013, 6.1e4):
+        s = np.float32(np.float32(amax) / np.float32(127.0))
+        vals = [np.float32(amax)]
+        for k in range(-127, 127):
+            x = np.float32((k + 0.5) * np.float64(s))
+            for d in range(-4, 5):
+                y = x
+                step = np.float32(np.inf if d > 0 else -np.inf)
+                for _ in range(abs(d)):
+                    y = np.nextafter(y, step)
+                if abs(y) <= amax:
+                    vals.append(y)
+        for i in range(0, len(vals), K - 1):
+            row = np.zeros(K, np.float32)
+            chunk = vals[i:i + K - 1]
+            row[0] = np.float32(amax)
+            row[1:1 + len(chunk)] = chunk
+            rows.append(row)
+    return np.stack(rows)
+
+
+def test_quantize_a8_near_ties(g):
+    # the kernel decides codes by a reciprocal multiply and falls back to the
+    # division only near half integers; this pins that edge bit-exactly
+    A = _near_tie_rows()
+    say(f"case quantize_a8 near ties M={A.shape[0]} K={A.shape[1]}")
+    Aq, sa, rs = g.quantize_a8(dev(A))
+    qa_ref, sa_ref, rs_ref = O.quantize_a8(A)
+    assert np.array_equal(host(sa), sa_ref)
+    assert np.array_equal(host(Aq), qa_ref)
+    assert np.array_equal(host(rs), rs_ref)
+
+
 @pytest.mark.parametrize("layout,N,K", [(0, 256, 256), (0, 50, 208), (1, 4096, 4096),
                                         (1, 37, 384), (2, 3200, 8640), (2, 19, 48)])
 def test_prepack_roundtrip(g, layout, N, K):
