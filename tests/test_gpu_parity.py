@@ -82,7 +82,9 @@ def test_quantize_pack_w2_and_scale(g, N, K):
 
 
 @pytest.mark.parametrize("M,K,dt", [(1, 256, np.float32), (2048, 4096, np.float16),
-                                    (3, 8, np.float16), (17, 1000, np.float32)])
+                                    (3, 8, np.float16), (17, 1000, np.float32),
+                                    (5, 8192, np.float16), (3, 11008, np.float16),
+                                    (6, 8200, np.float32)])
 def test_quantize_a8_bitexact(g, M, K, dt):
     say(f"case quantize_a8 M={M} K={K} {dt.__name__}")
     A = WL.activations(M, K, seed=4000 + M + K, dtype=dt)
