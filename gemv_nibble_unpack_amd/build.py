@@ -47,8 +47,22 @@ def build(verbose=True):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+    undefined_kernels(tmp)
     os.replace(tmp, OUT)
     return OUT
+
+
+def undefined_kernels(path):
+    """Fail if the library references a kernel it does not define: clang drops
+    a kernel's host stub without an error when the host pass cannot
+    instantiate it, which would only surface when the library is loaded."""
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    if not os.path.exists(nm):
+        return
+    res = subprocess.run([nm, "-C", "--undefined-only", path], capture_output=True, text=True)
+    bad = [l.strip() for l in res.stdout.splitlines() if "w4::" in l]
+    if bad:
+        raise RuntimeError("kernels referenced but not defined:\n" + "\n".join(bad))
 
 
 if __name__ == "__main__":
