@@ -193,3 +193,51 @@ def w4a16_gemm(A, Wp, N, bias=None, workspace=None, C=None, group_size=L.W4_GROU
     L.check("w4a16_gemm", L.load().w4a16_gemm(_ptr(A), _ptr(Wp), group_size, _ptr(bias), _ptr(C),
                                               M, N, K, _ptr(buf), nb, _stream(stream)))
     return C
+
+
+_FWS_CACHE = {}
+
+
+def w4_fused_act_workspace_bytes(layout, M, N, K):
+    key = (layout, M, N, K)
+    v = _FWS_CACHE.get(key)
+    if v is None:
+        v = _FWS_CACHE[key] = int(L.load().w4_fused_act_workspace_bytes(layout, M, N, K))
+    return v
+
+
+def _fused(name, layout, A, Wp, scale, N, bias, out_dtype, workspace, C, stream):
+    dev = _dev(A)
+    M, K = A.shape
+    if A.dtype == torch.float16:
+        dt = L.W4_IN_F16
+    elif A.dtype == torch.float32:
+        dt = L.W4_IN_F32
+    else:
+        raise ValueError("A must be float16 or float32")
+    if C is None:
+        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
+    need = w4_fused_act_workspace_bytes(layout, M, N, K)
+    buf, nb = None, 0
+    if need:
+        if workspace is None:
+            workspace = Workspace(dev)
+        buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+        nb = buf.numel()
+    L.check(name, getattr(L.load(), name)(_ptr(A), dt, _ptr(Wp), _ptr(scale), _ptr(bias), _ptr(C),
+                                          out_dtype, M, N, K, _ptr(buf), nb, _stream(stream)))
+    return C
+
+
+def w4a8_gemm_fused_act(A, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, workspace=None,
+                        C=None, stream=None):
+    """fp16/float32 A [M,K] -> quantize_a8 + w4a8_gemm in one C call."""
+    return _fused("w4a8_gemm_fused_act", L.W4_LAYOUT_W4A8, A, Wp, w_scale, N, bias, out_dtype,
+                  workspace, C, stream)
+
+
+def w2a8_gemm_fused_act(A, Wp, w_scale16, N, bias=None, out_dtype=L.W4_OUT_F16, workspace=None,
+                        C=None, stream=None):
+    """fp16/float32 A [M,K] -> quantize_a8 + w2a8_gemm in one C call."""
+    return _fused("w2a8_gemm_fused_act", L.W4_LAYOUT_W2A8, A, Wp, w_scale16, N, bias, out_dtype,
+                  workspace, C, stream)

@@ -91,7 +91,8 @@ struct KindTraits<KIND_W2A8> {
 
 // Epilogue for one output element.
 template <int KIND>
-__device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float facc, int iacc) {
+__device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float facc, int iacc,
+                                          float sa) {
   if constexpr (KIND == KIND_W4A16) {
     float v = facc;
     if (p.bias) v += h2f(p.bias[n]);
@@ -103,7 +104,7 @@ __device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float
       return;
     }
     const float ws = KIND == KIND_W4A8 ? p.w_scale[n] : h2f(p.w_scale16[0]);
-    float v = (float)acc * ws * p.a_scale[m];
+    float v = (float)acc * ws * sa;
     if (p.out_dtype == W4_OUT_F32) {
       reinterpret_cast<float*>(p.C)[(size_t)m * p.N + n] = v;
     } else {
@@ -138,8 +139,18 @@ struct AStage {
 // multiplied in order, each waiting only for its own loads. Without STAGED
 // (activation rows too large for LDS) each lane loads its own activation
 // fragments from L2 through a ring of RING tiles in flight.
-template <int KIND, int WAVES, int MAXT, int APER, bool STAGED>
+//
+// FQ (fused activation quantization, A8 kinds, STAGED only): A holds fp16
+// (FQ = 1) or fp32 (FQ = 2) rows instead of int8 codes. Each block computes
+// the per-token scale of its rows from the whole row (the same max, the same
+// float32 division and the same code decision as quantize_a8, so the codes are
+// identical), quantizes its staged k range straight into LDS, and keeps the
+// scales for the epilogue. Rows <= 8: the waves split into groups of G waves
+// per row; rows > 8: wave w owns rows w and w + 8. Each lane holds up to FQC
+// 8-element chunks of its rows, loaded before the weight tiles.
+template <int KIND, int WAVES, int MAXT, int APER, bool STAGED, int FQ = 0, int FQC = 1>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
+  static_assert(FQ == 0 || (STAGED && KIND != KIND_W4A16 && WAVES == 8), "fused quantization");
   using AS = AStage<KIND>;
   constexpr bool A16 = KIND == KIND_W4A16;
   constexpr int NTHR = WAVES * 64;
@@ -173,6 +184,36 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   const int wb = kb + wave * per;
   const int nt = max(0, min(ke, wb + per) - wb);     // tiles of this wave (uniform)
 
+  // ---- phase 0 (FQ): whole activation rows, 8 elements per chunk ----------
+  constexpr int FESZ = FQ == 2 ? 4 : 2;              // input element bytes
+  constexpr int FU4 = FESZ / 2;                      // u4 loads per chunk
+  __shared__ float fq_part[WAVES * 2];               // per wave, per owned row: partial max
+  __shared__ float fq_s[16];                         // per row: the activation scale
+  u4 fqr[FQ ? FQC * FU4 : 1];
+  const int rpw = rows > 8 ? 2 : 1;                  // rows per wave
+  const int fq_g = rows > 8 ? 1 : rows > 4 ? 1 : rows > 2 ? 2 : rows > 1 ? 4 : 8;  // waves per row
+  const int cpk = p.K / 8;                           // chunks per row
+  const int fq_per = (cpk + 64 * fq_g - 1) / (64 * fq_g);  // chunk slots per lane per row
+  auto fq_slot = [&](int sl, int& row, int& col) {   // slot -> (row, chunk) or row = -1
+    const int rr = sl / fq_per, j = sl - rr * fq_per;
+    row = rows > 8 ? wave + 8 * rr : wave / fq_g;
+    col = (wave % fq_g) * 64 + lane + 64 * fq_g * j;
+    if (rr >= rpw || row >= rows || col >= cpk) row = -1;
+  };
+  if constexpr (FQ != 0) {
+    const uint8_t* Ab0 = reinterpret_cast<const uint8_t*>(p.A);
+#pragma unroll
+    for (int sl = 0; sl < FQC; ++sl) {
+      int row, col;
+      fq_slot(sl, row, col);
+      // dead slots re-read chunk 0 of row 0 (unconditional loads, exact waits)
+      const size_t off = row < 0 ? (size_t)mtile * 16 * p.K * FESZ
+                                 : ((size_t)(mtile * 16 + row) * p.K + (size_t)col * 8) * FESZ;
+#pragma unroll
+      for (int h = 0; h < FU4; ++h) fqr[sl * FU4 + h] = *reinterpret_cast<const u4*>(Ab0 + off + 16 * h);
+    }
+  }
+
   // ---- phase 1a: activation loads (row-major chunks of 16 bytes) ----------
   const int rowb = (ke - kb) * AS::TILE_ROWB;        // bytes of one staged row
   const int cpr = rowb / 16;
@@ -183,7 +224,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   const size_t kbyte0 = (size_t)kb * AS::TILE_ROWB;
   u4 stage[APER];
 #pragma unroll
-  for (int i = 0; i < (STAGED ? APER : 0); ++i) {
+  for (int i = 0; i < (STAGED && FQ == 0 ? APER : 0); ++i) {
     const int c = min(tid + i * NTHR, total - 1);
     const int row = c / cpr, col = c - row * cpr;
     size_t off = kbyte0 + (size_t)col * 16;
@@ -239,7 +280,85 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     }
 
     // ---- phase 2: activations to LDS (first pass only) -------------------
-    if (STAGED && pass == 0) {
+    if (FQ != 0 && pass == 0) {
+      auto chunk = [&](int sl, float (&x)[8]) {
+        if constexpr (FQ == 1) {
+          const h8 hv = __builtin_bit_cast(h8, fqr[sl]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (float)hv[e];
+        } else {
+          // whole-vector casts (a bit cast of one ext-vector element reads
+          // element 0 with this compiler)
+          const f4 a0 = __builtin_bit_cast(f4, fqr[sl * 2]);
+          const f4 a1 = __builtin_bit_cast(f4, fqr[sl * 2 + 1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = a0[e];
+            x[4 + e] = a1[e];
+          }
+        }
+      };
+      // per-wave maxima of the owned rows, then the row maxima across the group
+      float mx[2] = {0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < FQC; ++sl) {
+        int row, col;
+        fq_slot(sl, row, col);
+        if (row < 0) continue;
+        float x[8];
+        chunk(sl, x);
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+        const int rr = sl / fq_per;
+        mx[rr] = fmaxf(mx[rr], m);
+      }
+      mx[0] = wave_max(mx[0]);
+      mx[1] = wave_max(mx[1]);
+      if (lane == 0) {
+        fq_part[wave * 2] = mx[0];
+        fq_part[wave * 2 + 1] = mx[1];
+      }
+      __syncthreads();
+      auto row_scale = [&](int row) {
+        float m = 0.f;
+        if (rows > 8) {
+          m = fq_part[(row & 7) * 2 + (row >> 3)];
+        } else {
+          for (int g = 0; g < fq_g; ++g) m = fmaxf(m, fq_part[(row * fq_g + g) * 2]);
+        }
+        return m / 127.0f;
+      };
+      if (tid < rows) fq_s[tid] = row_scale(tid);
+      // quantize this block's staged k range into LDS
+      const int k0 = kb * AS::TILE_ROWB;                 // int8: one byte per element
+      const int k1 = min(ke * AS::TILE_ROWB, p.K);
+#pragma unroll
+      for (int sl = 0; sl < FQC; ++sl) {
+        int row, col;
+        fq_slot(sl, row, col);
+        if (row < 0 || 8 * col < k0 || 8 * col >= k1) continue;
+        const float sa = row_scale(row);
+        const float rs = sa > 0.f ? 1.0f / sa : 0.f;
+        float x[8];
+        chunk(sl, x);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bq = (uint32_t)(sym_code_rcp(x[e], sa, rs, 127.f) & 0xFF);
+          if (e < 4) lo |= bq << (8 * e);
+          else hi |= bq << (8 * (e - 4));
+        }
+        *reinterpret_cast<u2*>(smem + row * sstride + (8 * col - k0)) = u2{lo, hi};
+      }
+      // k tail past K inside the last staged tile contributes zero
+      const int tail = kb * AS::TILE_ROWB + rowb - k1;   // bytes, a multiple of 16
+      for (int c = tid; c < rows * (tail / 16); c += NTHR) {
+        const int row = c / (tail / 16), col = c - row * (tail / 16);
+        *reinterpret_cast<u4*>(smem + row * sstride + (k1 - k0) + 16 * col) = u4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    } else if (STAGED && pass == 0) {
 #pragma unroll
       for (int i = 0; i < APER; ++i) {
         const int c = tid + i * NTHR;
@@ -329,6 +448,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 
   const int ngroups = p.NT;
   const size_t slot = (size_t)mtile * ngroups + tile;
+  auto row_sa = [&](int row) {                       // the row's activation scale (A8 kinds)
+    if constexpr (A16) return 0.f;
+    else if constexpr (FQ != 0) return fq_s[row];
+    else return p.a_scale[mtile * 16 + row];
+  };
   constexpr int NOUT = 256;                          // 16 x 16 outputs of the tile
 
   if (p.ksplit == 1) {
@@ -344,7 +468,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
         if constexpr (A16) fs += v;
         else is += __builtin_bit_cast(int, v);
       }
-      store_out<KIND>(p, mtile * 16 + row, n, fs, is);
+      store_out<KIND>(p, mtile * 16 + row, n, fs, is, row_sa(row));
     }
     return;
   }
@@ -392,7 +516,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       if constexpr (A16) fs += __builtin_bit_cast(float, v);
       else is += (int)v;
     }
-    store_out<KIND>(p, mtile * 16 + row, n, fs, is);
+    store_out<KIND>(p, mtile * 16 + row, n, fs, is, row_sa(row));
   }
   if (tid == 0) p.counters[slot] = 0u;  // leave the workspace zeroed
 }

@@ -71,13 +71,38 @@ inline Plan make_plan(int kind, int M, int N, int K) {
   return P;
 }
 
+// Chunk slots per lane the fused-quantization prologue needs for a block of
+// `rows` activation rows (see k_gemv), or 0 when more than 8 would be needed.
+inline int fq_slots(int rows, int K) {
+  const int rpw = rows > 8 ? 2 : 1;
+  const int g = rows > 4 ? 1 : rows > 2 ? 2 : rows > 1 ? 4 : 8;
+  const int need = rpw * ceil_div(K / 8, 64 * g);
+  return need <= 2 ? 2 : need <= 8 ? 8 : 0;
+}
+
 template <int KIND, int MAXT>
-int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream) {
+int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq = 0, int fqc = 0) {
   // x enumerates (n tile, m tile) pairs so that the m tiles of one n tile land
   // on the same XCD (blocks are dealt to the 8 XCDs round-robin by id)
   const int nblk = P.mtiles == 1 ? p.NT : ceil_div(p.NT * P.mtiles, 8) * 8;
   const dim3 grid(nblk, P.ksplit, 1);
   const dim3 block(GEMV_THREADS);
+#define W4_GEMV_FQ(F, C)                                                                  \
+  do {                                                                                    \
+    allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, 1, true, F, C>, P.smem);      \
+    hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 1, true, F, C>), grid, block,      \
+                       P.smem, stream, p);                                                \
+  } while (0)
+  if constexpr (KIND != KIND_W4A16) {
+    if (fq) {
+      if (fq == 1 && fqc == 2) W4_GEMV_FQ(1, 2);
+      else if (fq == 1) W4_GEMV_FQ(1, 8);
+      else if (fqc == 2) W4_GEMV_FQ(2, 2);
+      else W4_GEMV_FQ(2, 8);
+      return launch_status();
+    }
+  }
+#undef W4_GEMV_FQ
 #define W4_GEMV_CASE(A, ST)                                                   \
   allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>, P.smem);     \
   hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>), grid, block, P.smem, stream, p)
@@ -96,14 +121,14 @@ int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream) {
 }
 
 template <int KIND>
-int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream) {
+int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream, int fq = 0, int fqc = 0) {
   p.ksplit = P.ksplit;
   p.kts = P.kts;
   p.counters = reinterpret_cast<unsigned*>(ws);
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + P.counters_bytes : nullptr;
-  if (P.maxt == 4) return launch_gemv_m<KIND, 4>(P, p, stream);
-  if (P.maxt == 8) return launch_gemv_m<KIND, 8>(P, p, stream);
-  return launch_gemv_m<KIND, 16>(P, p, stream);
+  if (P.maxt == 4) return launch_gemv_m<KIND, 4>(P, p, stream, fq, fqc);
+  if (P.maxt == 8) return launch_gemv_m<KIND, 8>(P, p, stream, fq, fqc);
+  return launch_gemv_m<KIND, 16>(P, p, stream, fq, fqc);
 }
 
 template <int KIND>
@@ -211,4 +236,102 @@ extern "C" int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size,
   p.N = N;
   p.K = K;
   return run<KIND_W4A16>(p, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// fused activation quantization: quantize_a8 + w4a8_gemm / w2a8_gemm in one
+// call. Decode shapes whose activation rows fit the block's LDS staging run
+// one kernel that quantizes in its prologue; everything else quantizes into
+// the workspace first.
+// ---------------------------------------------------------------------------
+namespace w4 {
+
+struct FusedPlan {
+  Plan P;
+  int fqc;            // prologue slots per lane (0: two launches)
+  size_t q_bytes;     // workspace for the quantized rows and their scales (two launches)
+  size_t ws_bytes;    // total workspace
+};
+
+inline FusedPlan fused_plan(int kind, int M, int N, int K) {
+  FusedPlan F{};
+  F.P = make_plan(kind, M, N, K);
+  F.fqc = (!F.P.gemm && F.P.staged) ? fq_slots(M < 16 ? M : 16, K) : 0;
+  F.q_bytes = F.fqc ? 0 : align256((size_t)M * K) + align256((size_t)M * sizeof(float));
+  F.ws_bytes = F.q_bytes + F.P.ws_bytes;
+  return F;
+}
+
+}  // namespace w4
+
+extern "C" size_t w4_fused_act_workspace_bytes(int layout, int M, int N, int K) {
+  if (layout != W4_LAYOUT_W4A8 && layout != W4_LAYOUT_W2A8) return 0;
+  if (check_common(M, N, K, 16) != W4_OK || M == 0) return 0;
+  return fused_plan(layout == W4_LAYOUT_W4A8 ? KIND_W4A8 : KIND_W2A8, M, N, K).ws_bytes;
+}
+
+extern "C" int quantize_a8(const void* A, int in_dtype, int M, int K, int8_t* Aq, float* a_scale,
+                           int32_t* rowsum, hipStream_t stream);
+
+static int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp,
+                        const void* scale, const uint16_t* bias, void* C, int out_dtype, int M,
+                        int N, int K, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (in_dtype != W4_IN_F16 && in_dtype != W4_IN_F32) return W4_ERR_ARG;
+  if (out_dtype != W4_OUT_F16 && out_dtype != W4_OUT_F32 && out_dtype != W4_OUT_I32)
+    return W4_ERR_ARG;
+  const int st = check_common(M, N, K, 16);
+  if (st != W4_OK) return st;
+  if (M == 0) return W4_OK;
+  if (!A || !Wp || !scale || !C) return W4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(Wp, 16) || !out_aligned(C, out_dtype) ||
+      (bias && !aligned(bias, 2)) || !aligned(scale, kind == KIND_W4A8 ? 4 : 2))
+    return W4_ERR_ALIGN;
+  const FusedPlan F = fused_plan(kind, M, N, K);
+  if (F.ws_bytes) {
+    if (!ws || ws_bytes < F.ws_bytes) return W4_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return W4_ERR_ALIGN;
+  }
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  if (!F.fqc) {
+    int8_t* Aq = reinterpret_cast<int8_t*>(wsb);
+    float* sa = reinterpret_cast<float*>(wsb + align256((size_t)M * K));
+    const int q = quantize_a8(A, in_dtype, M, K, Aq, sa, nullptr, stream);
+    if (q != W4_OK) return q;
+    return a8_common(kind, Aq, sa, Wp, scale, bias, C, out_dtype, M, N, K,
+                     F.P.ws_bytes ? wsb + F.q_bytes : nullptr, ws_bytes - F.q_bytes, stream);
+  }
+  const Geometry g = geometry(kind_layout(kind), N, K);
+  MMParams p{};
+  p.A = A;
+  p.Wt = Wp;
+  p.w_scale = kind == KIND_W4A8 ? (const float*)scale : nullptr;
+  p.w_scale16 = kind == KIND_W2A8 ? (const uint16_t*)scale : nullptr;
+  p.bias = out_dtype == W4_OUT_I32 ? nullptr : bias;
+  p.C = C;
+  p.out_dtype = out_dtype;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.NT = g.NT;
+  p.KT = g.KT;
+  p.KQ = g.KQ;
+  const int fq = in_dtype == W4_IN_F16 ? 1 : 2;
+  return kind == KIND_W4A8 ? launch_gemv<KIND_W4A8>(F.P, p, ws, stream, fq, F.fqc)
+                           : launch_gemv<KIND_W2A8>(F.P, p, ws, stream, fq, F.fqc);
+}
+
+extern "C" int w4a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
+                                   const float* w_scale, const uint16_t* bias, void* C,
+                                   int out_dtype, int M, int N, int K, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return fused_common(KIND_W4A8, A, in_dtype, Wp, w_scale, bias, C, out_dtype, M, N, K, workspace,
+                      workspace_bytes, stream);
+}
+
+extern "C" int w2a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
+                                   const uint16_t* w_scale16, const uint16_t* bias, void* C,
+                                   int out_dtype, int M, int N, int K, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return fused_common(KIND_W2A8, A, in_dtype, Wp, w_scale16, bias, C, out_dtype, M, N, K,
+                      workspace, workspace_bytes, stream);
 }

@@ -47,20 +47,6 @@ __device__ __forceinline__ int sym_code(float w, float s, float lim) {
   return s > 0.f ? (int)fminf(fmaxf(rintf(w / s), -lim), lim) : 0;
 }
 
-// The same code decision rint(fl(w / s)) for |w / s| <= 128, with a multiply
-// by rs = fl(1 / s) (correctly rounded) instead of a division per element.
-// y = fl(w * rs) differs from w / s by at most 128 * (2^-24 + 2^-24) = 2^-16,
-// and fl(w / s) differs from w / s by at most 2^-17, so rint(y) and
-// rint(fl(w / s)) can differ only if y lies within 2^-15 of a half integer.
-// Lanes within 2^-14 of one take the correctly rounded division.
-__device__ __forceinline__ int sym_code_rcp(float w, float s, float rs, float lim) {
-  if (!(s > 0.f)) return 0;
-  const float y = w * rs;
-  float q = rintf(y);
-  if (__builtin_expect(fabsf(y - floorf(y) - 0.5f) < 0x1p-14f, 0)) q = rintf(w / s);
-  return (int)fminf(fmaxf(q, -lim), lim);
-}
-
 // --- symmetric per-channel INT4: one block per row n -----------------------
 __global__ __launch_bounds__(QB) void k_quant_w4_sym(const float* __restrict__ W, int K,
                                                        uint8_t* __restrict__ Wq,

@@ -205,6 +205,39 @@ int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size, const uint1
                uint16_t* C, int M, int N, int K, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
 
+/*
+ * w4_fused_act_workspace_bytes -- device workspace w4a8_gemm_fused_act
+ * (layout W4_LAYOUT_W4A8) or w2a8_gemm_fused_act (W4_LAYOUT_W2A8) needs, 0 if
+ * none. Same zero-fill and sharing rules as w4_workspace_bytes; the buffer
+ * must be 256-byte aligned.
+ */
+size_t w4_fused_act_workspace_bytes(int layout, int M, int N, int K);
+
+/*
+ * w4a8_gemm_fused_act -- quantize_a8 followed by w4a8_gemm in one call
+ * (INT4 page, Part 1 steps 2-4: dynamic per-token INT8 activations, INT8 x
+ * INT4 products summed in INT32, dequantization): the outputs are identical,
+ * bit for bit, to those two calls. A holds fp16 (in_dtype W4_IN_F16) or
+ * float32 (W4_IN_F32) rows [M,K], 16-byte aligned; the other arguments are
+ * those of w4a8_gemm. Decode shapes whose rows fit the kernel's LDS staging
+ * quantize in the matmul kernel's prologue (one launch, no int8 copy of A in
+ * memory); other shapes quantize into the workspace first (two launches).
+ * Errors as w4a8_gemm, plus W4_ERR_ARG for an unknown in_dtype.
+ */
+int w4a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp, const float* w_scale,
+                        const uint16_t* bias, void* C, int out_dtype, int M, int N, int K,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * w2a8_gemm_fused_act -- quantize_a8 followed by w2a8_gemm in one call, as
+ * w4a8_gemm_fused_act with the ternary weights and per-tensor fp16 scale of
+ * w2a8_gemm.
+ */
+int w2a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
+                        const uint16_t* w_scale16, const uint16_t* bias, void* C, int out_dtype,
+                        int M, int N, int K, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -63,6 +63,11 @@ def test_sizes():
     assert lib.prepack_bytes(7, 16, 128) == 0
     assert lib.w4_workspace_bytes(L.W4_LAYOUT_W4A16, 1, 4096, 4096) == 0
     assert lib.w4_workspace_bytes(L.W4_LAYOUT_W2A8, 1, 16, 131072) > 0
+    # fused activation quantization: decode rows that fit LDS need nothing;
+    # 16 rows of 4096 quantize into the workspace first (int8 rows + scales)
+    assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A8, 1, 4096, 4096) == 0
+    assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A8, 16, 4096, 4096) == 16 * 4096 + 256
+    assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A16, 1, 4096, 4096) == 0
 
 
 def test_error_paths_before_launch():
@@ -96,6 +101,15 @@ def test_error_paths_before_launch():
     assert lib.w2a8_gemm(P, P, P, P, None, P2, 0, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
     assert lib.w4a16_gemm(P, P, 64, None, P2, 1, 16, 128, None, 0, s) == L.W4_ERR_ARG
     assert lib.w4a16_gemm(P, P, 128, None, P2, 1, 16, 192, None, 0, s) == L.W4_ERR_SHAPE
+    # fused activation quantization
+    for fn in (lib.w4a8_gemm_fused_act, lib.w2a8_gemm_fused_act):
+        assert fn(P, 2, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
+        assert fn(P, 0, P, P, None, P2, 9, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
+        assert fn(P, 0, P, P, None, P2, 0, 1, 16, 24, None, 0, s) == L.W4_ERR_SHAPE
+        assert fn(None, 0, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_NULL
+        assert fn(MIS, 0, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
+        assert fn(None, 0, None, None, None, None, 0, 0, 16, 32, None, 0, s) == L.W4_OK
+        assert fn(P, 1, P, P, None, P2, 0, 16, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
 
 
 def test_binding_refuses_host_tensors():

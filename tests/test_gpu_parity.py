@@ -373,3 +373,51 @@ def test_matmul_m0_is_noop_and_errors(g):
     with pytest.raises(g.W4Error) as e:
         g.w4a16_gemm(f16(np.zeros((1, 256))), Wp, 16, group_size=64)
     assert e.value.status == -4
+
+
+# ---------------------------------------------------------------------------
+# fused activation quantization (quantize_a8 + matmul in one call)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scheme,M,N,K,dt", [
+    ("w4a8", 1, 256, 256, np.float32),      # the tiny GEMV configuration
+    ("w4a8", 1, 4096, 4096, np.float16),
+    ("w4a8", 4, 4096, 4096, np.float16),
+    ("w4a8", 3, 130, 208, np.float16),      # ragged rows and columns, k tail in the last tile
+    ("w4a8", 9, 512, 1024, np.float32),     # more than 8 rows: two rows per wave
+    ("w4a8", 1, 256, 4096, np.float16),     # split K: every block reads the whole row
+    ("w4a8", 40, 300, 512, np.float16),     # three 16-row tiles through the prologue
+    ("w4a8", 1, 4096, 11008, np.float16),   # long rows: several chunks per lane
+    ("w4a8", 16, 4096, 4096, np.float16),   # too wide for the prologue: two launches
+    ("w4a8", 300, 2000, 1040, np.float16),  # prefill GEMM: two launches
+    ("w2a8", 1, 3200, 3200, np.float16),
+    ("w2a8", 1, 8640, 3200, np.float16),
+    ("w2a8", 5, 100, 528, np.float32),
+])
+def test_fused_act_matches_two_calls_and_oracle(g, scheme, M, N, K, dt):
+    say(f"case fused act {scheme} M={M} N={N} K={K} {dt.__name__}")
+    A = WL.activations(M, K, seed=9000 + M + K, dtype=dt)
+    if M > 2:
+        A[1, :] = 0                             # a zero row: scale 0, codes 0, output = bias
+    bias = WL.bias_f16(N, seed=9001)
+    if scheme == "w4a8":
+        W = WL.weights_f32(N, K, seed=9002 + N)
+        Wp, ws = prep_w4a8(g, W)
+        qw, _ = O.quantize_w4_sym(W)
+        mm, fused = g.w4a8_gemm, g.w4a8_gemm_fused_act
+    else:
+        codes = WL.ternary_codes(N, K, seed=9003 + N)
+        Wp, ws = prep_w2a8(g, codes, WL.weights_f32(N, K, seed=9004 + N))
+        qw = codes
+        mm, fused = g.w2a8_gemm, g.w2a8_gemm_fused_act
+    Ad = dev(A)
+    Aq, sa, _ = g.quantize_a8(Ad)
+    for out in (g.W4_OUT_I32, g.W4_OUT_F32, g.W4_OUT_F16):
+        b = f16(bias) if out == g.W4_OUT_F16 else None
+        ref = host(mm(Aq, sa, Wp, ws, N, bias=b, out_dtype=out))
+        got = host(fused(Ad, Wp, ws, N, bias=b, out_dtype=out))
+        assert np.array_equal(ref, got), out
+        if out == g.W4_OUT_I32:
+            qa, _, _ = O.quantize_a8(A)
+            rows, cols = sample_indices(M, N, 2000, seed=13)
+            acc = O.int_accumulate_entries(qa, qw, rows, cols)
+            assert np.array_equal(got[rows, cols], acc.astype(np.int32))
