@@ -198,6 +198,67 @@ def bench_prefill(args, stream):
                "bytes": prefill_bytes(c.M, c.N, c.K), "copies": R}
 
 
+def bench_decode_extra(stream, steps):
+    """Context lines at M=1 (graph replay, cold weight copies): the W4A16
+    GEMV at the two 11008-sized projection shapes, and the W4A8 GEMV with
+    activations quantized by a separate kernel versus in the GEMV prologue
+    (w4a8_gemm_fused_act)."""
+    import torch
+    import gemv_nibble_unpack_amd as G
+    from gemv_nibble_unpack_amd import workloads as WL
+    dev = torch.device("cuda:0")
+    out = {"w4a16_m1": []}
+    for c in WL.W4A16_SWEEP:
+        if c.M != 1 or c.N * c.K == 4096 * 4096:
+            continue
+        d = c.inputs()
+        Wq, s, z = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_ASYM_GROUP)
+        Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, c.N, c.K, s, z)
+        del Wq
+        A = torch.from_numpy(d["A"]).to(dev)
+        R = max(1, math.ceil(ROTATE_BYTES / Wp.numel()))
+        copies = [Wp] + [Wp.clone() for _ in range(R - 1)]
+        C = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
+        ws = G.Workspace(dev)
+        ms, _ = time_graph(lambda i: G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C),
+                           steps, 10, stream)
+        nb = decode_bytes(c.M, c.N, c.K)
+        out["w4a16_m1"].append({"N": c.N, "K": c.K, "us": round(ms * 1e3, 3),
+                                "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                "pct_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+        del copies
+    # W4A8 M=1 N=K=4096: two launches vs the fused prologue
+    N = K = 4096
+    rng = np.random.default_rng(700)
+    W = torch.from_numpy(rng.normal(0, 0.02, (N, K)).astype(np.float32)).to(dev)
+    A = torch.from_numpy(rng.normal(0, 1, (1, K)).astype(np.float16)).to(dev)
+    Wq, wsc, _ = G.quantize_pack_w4(W, G.W4_SYM_PER_CHANNEL)
+    Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, N, K)
+    del W, Wq
+    R = max(1, math.ceil(ROTATE_BYTES / Wp.numel()))
+    copies = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    C = torch.empty((1, N), dtype=torch.float16, device=dev)
+    q = (torch.empty((1, K), dtype=torch.int8, device=dev), torch.empty(1, device=dev), None)
+    ws = G.Workspace(dev)
+
+    def two(i):
+        G.quantize_a8(A, out=q)
+        G.w4a8_gemm(q[0], q[1], copies[i % R], wsc, N, workspace=ws, C=C)
+
+    def fused(i):
+        G.w4a8_gemm_fused_act(A, copies[i % R], wsc, N, workspace=ws, C=C)
+
+    nb = N * K // 2 + 4 * N + 2 * K + 2 * N
+    row = {"N": N, "K": K, "bytes": nb}
+    for name, fn in (("two_launch", two), ("fused", fused)):
+        ms, _ = time_graph(fn, steps, 10, stream)
+        row[name] = {"us": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    out["w4a8_m1"] = row
+    del copies
+    torch.cuda.empty_cache()
+    return out
+
+
 def traffic_of(path):
     """HBM bytes per launch from the committed PMC summary, or None when the
     summary is missing or the kernel sources changed since it was taken."""
@@ -305,6 +366,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=2048 GEMM")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the M=1 context shapes (11008-sized W4A16, fused W4A8)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="time one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--calib", action="store_true",
@@ -398,6 +461,9 @@ def main():
                          "traffic": traffic_of(PREFILL_TRAFFIC),
                          "gemm_ms": round(pre["gemm_region_ms"], 5)},
         }
+    if not args.no_extra:
+        log("bench: decode context shapes")
+        line["decode_context"] = bench_decode_extra(stream, min(args.steps, 100))
     if not args.no_cpu:
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline_decode(c)
