@@ -421,3 +421,67 @@ def test_fused_act_matches_two_calls_and_oracle(g, scheme, M, N, K, dt):
             rows, cols = sample_indices(M, N, 2000, seed=13)
             acc = O.int_accumulate_entries(qa, qw, rows, cols)
             assert np.array_equal(got[rows, cols], acc.astype(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# graph capture of a decode chain (INT4 page, Part 2)
+# ---------------------------------------------------------------------------
+def test_decode_chain_graph_replays_match_eager(g):
+    # A decode step's chain of GEMVs captured once and replayed: fp16 output
+    # of one layer feeds the next (4096 -> 11008 -> 4096 -> 4096 -> 3200
+    # columns), mixing W4A16, fused W4A8 and fused W2A8 calls, one of them
+    # split over K (workspace in use). Each replay, with eager work and a
+    # synchronization in between, must equal the eager chain bit for bit.
+    say("case decode chain graph capture")
+    dims = [4096, 11008, 4096, 256, 3200]
+    kinds = ["w4a16", "w4a8", "w4a16", "w2a8"]
+    layers = []
+    for i, kind in enumerate(kinds):
+        K, N = dims[i], dims[i + 1]
+        W = WL.weights_f32(N, K, seed=9100 + i)
+        if kind == "w4a16":
+            layers.append((kind, prep_w4a16(g, W), None, N))
+        elif kind == "w4a8":
+            Wp, ws = prep_w4a8(g, W)
+            layers.append((kind, Wp, ws, N))
+        else:
+            codes = WL.ternary_codes(N, K, seed=9200 + i)
+            Wp, ws = prep_w2a8(g, codes, W)
+            layers.append((kind, Wp, ws, N))
+    bufs = [torch.empty((1, d), dtype=torch.float16, device="cuda") for d in dims]
+    wss = [g.Workspace("cuda") for _ in layers]
+    x0 = dev(WL.activations(1, dims[0], seed=9300, dtype=np.float16))
+
+    def chain():
+        for i, (kind, Wp, ws, N) in enumerate(layers):
+            if kind == "w4a16":
+                g.w4a16_gemm(bufs[i], Wp, N, workspace=wss[i], C=bufs[i + 1])
+            elif kind == "w4a8":
+                g.w4a8_gemm_fused_act(bufs[i], Wp, ws, N, workspace=wss[i], C=bufs[i + 1])
+            else:
+                g.w2a8_gemm_fused_act(bufs[i], Wp, ws, N, workspace=wss[i], C=bufs[i + 1])
+
+    bufs[0].copy_(x0)
+    chain()
+    torch.cuda.synchronize()
+    eager = [host(b) for b in bufs[1:]]
+    assert all(np.isfinite(e.astype(np.float32)).all() for e in eager)
+    # warm the workspaces, then capture on a side stream
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    for rep in range(3):
+        for b in bufs[1:]:
+            b.fill_(0)                          # eager work between replays
+        bufs[0].copy_(x0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, b in enumerate(bufs[1:]):
+            assert np.array_equal(host(b).view(np.uint16), eager[i].view(np.uint16)), (rep, i)
