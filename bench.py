@@ -276,7 +276,16 @@ def bench_case(case, steps, warmup, stream):
     A = torch.from_numpy(d["A"]).to(dev)
     M, N, K = case.M, case.N, case.K
     ws = G.Workspace(dev)
-    if case.scheme == "w4a16":
+    if case.scheme == "w2a16":
+        Wq = G.quantize_pack_w2(torch.from_numpy(d["codes"]).to(dev))
+        Wp = G.prepack_w(G.W4_LAYOUT_W2A8, Wq, N, K)
+        wsc = G.ternary_scale_f16(torch.from_numpy(d["src"]).to(dev))
+        nbytes = N * K // 4 + 2 + 2 * M * K + 2 * M * N
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
+        fn = lambda i: G.w2a16_gemm(A, copies[i % len(copies)], wsc, N, workspace=ws, C=C,
+                                    stream=stream)
+    elif case.scheme == "w4a16":
         Wq, s, z = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_ASYM_GROUP)
         Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, N, K, s, z)
         nbytes = decode_bytes(M, N, K)

@@ -37,6 +37,7 @@ SIGNATURES = {
     "w4a8_gemm": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w2a8_gemm": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w4a16_gemm": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _p, _sz, _p]),
+    "w2a16_gemm": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _p, _sz, _p]),
     "w4_fused_act_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "w4a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w2a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),

@@ -195,6 +195,17 @@ def w4a16_gemm(A, Wp, N, bias=None, workspace=None, C=None, group_size=L.W4_GROU
     return C
 
 
+def w2a16_gemm(A, Wp, w_scale16, N, bias=None, workspace=None, C=None, stream=None):
+    """fp16 A [M,K] x ternary weights (the W2A8 prepacked buffer) -> fp16 C [M,N]."""
+    dev = _dev(A)
+    M, K = A.shape
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+    buf, nb = _workspace(workspace, L.W4_LAYOUT_W2A8, M, N, K, dev)
+    L.check("w2a16_gemm", L.load().w2a16_gemm(_ptr(A), _ptr(Wp), _ptr(w_scale16), _ptr(bias),
+                                              _ptr(C), M, N, K, _ptr(buf), nb, _stream(stream)))
+    return C
+
 _FWS_CACHE = {}
 
 

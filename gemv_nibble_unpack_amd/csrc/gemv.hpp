@@ -25,7 +25,7 @@
 
 namespace w4 {
 
-enum Kind { KIND_W4A8 = 0, KIND_W4A16 = 1, KIND_W2A8 = 2 };
+enum Kind { KIND_W4A8 = 0, KIND_W4A16 = 1, KIND_W2A8 = 2, KIND_W2A16 = 3 };
 
 struct MMParams {
   const void* A;               // int8 [M,K] (A8) or fp16 [M,K] (A16)
@@ -74,6 +74,25 @@ __device__ __forceinline__ i4 unpack_w2_i8(uint32_t w) {
             (int)((w << 2) & 0xC0C0C0C0u), (int)(w & 0xC0C0C0C0u)};
 }
 
+// W2A16: the same word (byte j holds k_j, k_{j+4}, k_{j+8}, k_{j+12} as
+// two's-complement crumbs) -> two fp16 MFMA operands, k 0..7 and 8..15.
+// Bytes are reordered to (b0, b2, b1, b3) so that one mask takes the crumbs
+// of k and k+1 into the two halves; flipping each crumb's high bit turns the
+// code c into c + 2 in [0, 3]; the 0x6400 exponent makes the half 1024 + c + 2,
+// and one packed subtract of 1026 leaves c exactly.
+__device__ __forceinline__ void unpack_w2_f16(uint32_t w, h8& lo, h8& hi) {
+  const uint32_t v = __builtin_amdgcn_perm(w, w, 0x03010200u) ^ 0xAAAAAAAAu;
+  const h2 off = {(_Float16)-1026.0f, (_Float16)-1026.0f};
+  h2 pr[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pr[2 * i] = __builtin_bit_cast(h2, and_or(v >> (2 * i), 0x00030003u, 0x64006400u)) + off;
+    pr[2 * i + 1] = __builtin_bit_cast(h2, and_or(v >> (2 * i + 8), 0x00030003u, 0x64006400u)) + off;
+  }
+  lo = h8{pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+  hi = h8{pr[4][0], pr[4][1], pr[5][0], pr[5][1], pr[6][0], pr[6][1], pr[7][0], pr[7][1]};
+}
+
 template <int KIND>
 struct KindTraits;
 template <>
@@ -88,13 +107,17 @@ template <>
 struct KindTraits<KIND_W2A8> {
   static constexpr int TILE_K = 256, A_CHUNKS = 4, SHIFT = 6;
 };
+template <>
+struct KindTraits<KIND_W2A16> {
+  static constexpr int TILE_K = 256, A_CHUNKS = 8, SHIFT = 0;
+};
 
 // Epilogue for one output element.
 template <int KIND>
 __device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float facc, int iacc,
                                           float sa) {
-  if constexpr (KIND == KIND_W4A16) {
-    float v = facc;
+  if constexpr (KIND == KIND_W4A16 || KIND == KIND_W2A16) {
+    float v = KIND == KIND_W2A16 ? facc * h2f(p.w_scale16[0]) : facc;
     if (p.bias) v += h2f(p.bias[n]);
     reinterpret_cast<uint16_t*>(p.C)[(size_t)m * p.N + n] = f2h(v);
   } else {
@@ -127,7 +150,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
 // (one per row) fall on different banks.
 template <int KIND>
 struct AStage {
-  static constexpr int ESZ = KIND == KIND_W4A16 ? 2 : 1;            // bytes per element
+  static constexpr int ESZ = KIND == KIND_W4A16 || KIND == KIND_W2A16 ? 2 : 1;  // element bytes
   static constexpr int TILE_ROWB = KindTraits<KIND>::TILE_K * ESZ;  // bytes per row per tile
 };
 
@@ -150,9 +173,15 @@ struct AStage {
 // 8-element chunks of its rows, loaded before the weight tiles.
 template <int KIND, int WAVES, int MAXT, int APER, bool STAGED, int FQ = 0, int FQC = 1>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
-  static_assert(FQ == 0 || (STAGED && KIND != KIND_W4A16 && WAVES == 8), "fused quantization");
+  static_assert(FQ == 0 || (STAGED && (KIND == KIND_W4A8 || KIND == KIND_W2A8) && WAVES == 8),
+                "fused quantization");
   using AS = AStage<KIND>;
-  constexpr bool A16 = KIND == KIND_W4A16;
+  constexpr bool A16 = KIND == KIND_W4A16 || KIND == KIND_W2A16;  // fp16 activations
+  constexpr bool GRP = KIND == KIND_W4A16;                         // group scales and zeros
+  // K need not be a multiple of the tile's k extent (every kind but W4A16,
+  // whose K is a multiple of its 128 group): activation reads past K are
+  // clamped into the row and their fragments zeroed
+  constexpr bool KTAIL = KIND != KIND_W4A16;
   constexpr int NTHR = WAVES * 64;
   typedef typename std::conditional<A16, f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -228,7 +257,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     const int c = min(tid + i * NTHR, total - 1);
     const int row = c / cpr, col = c - row * cpr;
     size_t off = kbyte0 + (size_t)col * 16;
-    if constexpr (!A16) off = min(off, arow_bytes - 16);   // k tail: clamp, zeroed below
+    if constexpr (KTAIL) off = min(off, arow_bytes - 16);  // k tail: clamp, zeroed below
     stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)(mtile * 16 + row) * arow_bytes + off);
   }
 
@@ -250,7 +279,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       const u4* wp = reinterpret_cast<const u4*>(p.Wt + ti * TILE_BYTES + lane * 16);
       // streamed once unless several m tiles share the weight tile through L2
       wv[u] = mtiles == 1 ? __builtin_nontemporal_load(wp) : *wp;
-      if constexpr (A16) {
+      if constexpr (GRP) {
         const size_t mi =
             live ? (((size_t)tile * p.KQ + (kt >> 2)) * TILE_N + r) * 4 + (kt & 3) : 0;
         sv[u] = p.St[mi];
@@ -270,7 +299,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 #pragma unroll
       for (int j = 0; j < AC; ++j) {
         size_t off = base + 16 * j;
-        if constexpr (!A16) off = min(off, arow_bytes - 16);
+        if constexpr (KTAIL) off = min(off, arow_bytes - 16);
         dst[j] = *reinterpret_cast<const u4*>(Ab + arow_g + off);
       }
     };
@@ -365,7 +394,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
         if (c < total) {
           const int row = c / cpr, col = c - row * cpr;
           u4 v = stage[i];
-          if constexpr (!A16) {
+          if constexpr (KTAIL) {
             if (kbyte0 + (size_t)col * 16 >= arow_bytes) v = u4{0u, 0u, 0u, 0u};
           }
           *reinterpret_cast<u4*>(smem + row * sstride + col * 16) = v;
@@ -392,7 +421,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
         aload(u + RING, ring[u % RING]);             // unconditional: keeps wait counts exact
       }
       if (u >= pn) continue;                         // uniform: tiles past the wave's run
-      if constexpr (!A16 && !STAGED) {
+      if constexpr (KTAIL && !STAGED) {
         // k tail: fragments past K contribute zero (staged rows are zero-filled)
         const int kt = pb + u;
 #pragma unroll
@@ -400,7 +429,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
           if ((size_t)kt * AS::TILE_ROWB + (AS::TILE_ROWB / 4) * b + 16 * j >= arow_bytes)
             af[j] = u4{0u, 0u, 0u, 0u};
       }
-      if constexpr (A16) {
+      if constexpr (GRP) {
         const _Float16 z = (_Float16)(float)zv[u];
         const _Float16 zl = -((_Float16)1024.0f + z);
         const _Float16 zh = -((_Float16)64.0f + z);
@@ -415,6 +444,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
         const float s = h2f(sv[u]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = fmaf(part[e], s, acc[e]);
+      } else if constexpr (KIND == KIND_W2A16) {
+        // fp32 sums of exact fp16 products; the tensor scale is applied once
+        // in the epilogue
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h8 b0, b1;
+          unpack_w2_f16(wv[u][j], b0, b1);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[2 * j]), b0, acc,
+                                                       0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[2 * j + 1]), b1,
+                                                       acc, 0, 0, 0);
+        }
       } else if constexpr (KIND == KIND_W4A8) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {

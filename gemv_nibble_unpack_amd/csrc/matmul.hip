@@ -22,11 +22,12 @@ struct Plan {
 };
 
 inline int kind_layout(int kind) {
+  // the 2-bit weights serve INT8 and fp16 activations from one prepacked layout
   return kind == KIND_W4A8 ? W4_LAYOUT_W4A8 : kind == KIND_W4A16 ? W4_LAYOUT_W4A16 : W4_LAYOUT_W2A8;
 }
 
 inline int tile_rowb(int kind) {
-  return kind == KIND_W4A16 ? 256 : kind == KIND_W4A8 ? 128 : 256;
+  return kind == KIND_W4A16 ? 256 : kind == KIND_W4A8 ? 128 : kind == KIND_W2A16 ? 512 : 256;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -93,7 +94,7 @@ int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq =
     hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 1, true, F, C>), grid, block,      \
                        P.smem, stream, p);                                                \
   } while (0)
-  if constexpr (KIND != KIND_W4A16) {
+  if constexpr (KIND == KIND_W4A8 || KIND == KIND_W2A8) {
     if (fq) {
       if (fq == 1 && fqc == 2) W4_GEMV_FQ(1, 2);
       else if (fq == 1) W4_GEMV_FQ(1, 8);
@@ -334,4 +335,27 @@ extern "C" int w2a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* W
                                    size_t workspace_bytes, hipStream_t stream) {
   return fused_common(KIND_W2A8, A, in_dtype, Wp, w_scale16, bias, C, out_dtype, M, N, K,
                       workspace, workspace_bytes, stream);
+}
+
+extern "C" int w2a16_gemm(const uint16_t* A, const uint8_t* Wp, const uint16_t* w_scale16,
+                          const uint16_t* bias, uint16_t* C, int M, int N, int K, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_common(M, N, K, 16);
+  if (st != W4_OK) return st;
+  if (M == 0) return W4_OK;
+  if (!A || !Wp || !w_scale16 || !C) return W4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(Wp, 16) || !aligned(C, 2) || !aligned(w_scale16, 2) ||
+      (bias && !aligned(bias, 2)))
+    return W4_ERR_ALIGN;
+  MMParams p{};
+  p.A = A;
+  p.Wt = Wp;
+  p.w_scale16 = w_scale16;
+  p.bias = bias;
+  p.C = C;
+  p.out_dtype = W4_OUT_F16;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return run<KIND_W2A16>(p, workspace, workspace_bytes, stream);
 }

@@ -67,7 +67,7 @@ class Case:
         s = self.seed
         d = {"A": activations(self.M, self.K, s + 1,
                               np.float32 if self.act_dtype == "f32" else np.float16)}
-        if self.scheme == "w2a8":
+        if self.scheme in ("w2a8", "w2a16"):
             d["codes"] = ternary_codes(self.N, self.K, s + 2)
             d["src"] = weights_f32(self.N, self.K, s + 3)
         else:
@@ -103,9 +103,22 @@ W4A8_PREFILL = Case("w4a8_prefill_2048x11008x4096", "w4a8", 2048, 11008, 4096,
                     bias=True, seed=400)
 W2A8_TERNARY = _ternary()
 
+# The data-type table's FP16 x INT2 row on the same ternary weights (fp16
+# activations instead of INT8), a "next" row beyond the five families.
+def _ternary_a16():
+    out = []
+    for M in (1, 128):
+        for (N, K) in ((3200, 3200), (8640, 3200), (3200, 8640)):
+            out.append(Case(f"w2a16_M{M}_N{N}_K{K}", "w2a16", M, N, K,
+                            seed=800 + M + (N // 100) + 3 * (K // 100)))
+    return out
+
+
+W2A16_TERNARY = _ternary_a16()
+
 # The example configuration printed on the BitBLAS page (M=1, N=2048,
 # K=1024, fp16 x int4, layout nt, no bias), as an extra small shape.
 BITBLAS_EXAMPLE = Case("w4a16_bitblas_example", "w4a16", 1, 2048, 1024, seed=600)
 
 ALL_CASES = [W4A8_TINY, W4A16_DECODE, *W4A16_SWEEP, W4A8_PREFILL, *W2A8_TERNARY,
-             BITBLAS_EXAMPLE]
+             BITBLAS_EXAMPLE, *W2A16_TERNARY]

@@ -206,6 +206,21 @@ int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size, const uint1
                hipStream_t stream);
 
 /*
+ * w2a16_gemm -- fp16 activations x ternary 2-bit weights (BitBLAS page,
+ * data-type table row FP16 x INT2, on the ternary weights of the BitNet-b1.58
+ * case):
+ *   C[m,n] = fp16( s * sum_k A[m,k] * c[n,k] + bias[n] ), float32 sums,
+ *   A fp16[M,K]; Wp from prepack_w(W4_LAYOUT_W2A8) -- the same prepacked
+ *   buffer w2a8_gemm reads; w_scale16 the per-tensor fp16 scale s (device
+ *   pointer); bias fp16[N] or NULL; C fp16[M,N]. K multiple of 16. Every M
+ *   runs the decode kernel over 16-row tiles. The workspace it needs is at
+ *   most w4_workspace_bytes(W4_LAYOUT_W2A8, M, N, K).
+ */
+int w2a16_gemm(const uint16_t* A, const uint8_t* Wp, const uint16_t* w_scale16,
+               const uint16_t* bias, uint16_t* C, int M, int N, int K, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * w4_fused_act_workspace_bytes -- device workspace w4a8_gemm_fused_act
  * (layout W4_LAYOUT_W4A8) or w2a8_gemm_fused_act (W4_LAYOUT_W2A8) needs, 0 if
  * none. Same zero-fill and sharing rules as w4_workspace_bytes; the buffer

@@ -16,7 +16,7 @@ Sources (cited by page title and section):
 * [BitBLAS page] "BitBLAS practical guide: mixed-precision matmul in vLLM"
   (BitBLAS实战指南：在vLLM中集成混合精度计算，降低70%内存使用): section
   "What is BitBLAS" (the problem statement C[M,N] = A[M,K] x W[N,K], layout
-  "nt"), the data-type table (FP16 x INT4, INT8 x INT2), the memory-saving
+  "nt"), the data-type table (FP16 x INT4, FP16 x INT2, INT8 x INT2), the memory-saving
   list (INT4 saves 75 %, INT2 87.5 % against FP16), "Advanced features 2:
   weight group quantization" (group_size 128, with scaling, with zeros,
   zeros_mode "original"), and the BitNet-b1.58 case (ternary weights).
@@ -39,12 +39,15 @@ listed again in the design notes):
    step uses the fp16-rounded scale, z = clip(rint(-min / s), 0, 15),
    q = clip(rint(w / s) + z, 0, 15), and w is reconstructed as (q - z) * s.
    A group with s == 0 gets q = z = 0.
-6. Accumulation for FP16 x INT4 is float32 in the kernels (the BitBLAS
-   example names fp16; fp16 accumulation over K = 11008 would not meet the
-   output tolerance); the oracle accumulates in float64.
+6. Accumulation for FP16 x INT4 (and FP16 x INT2) is float32 in the kernels
+   (the BitBLAS example names fp16; fp16 accumulation over K = 11008 would
+   not meet the output tolerance); the oracle accumulates in float64.
 7. Activations are quantized per token (row m), dynamically, to [-127, 127].
 8. Ternary codes are inputs; their per-tensor scale is fp16(mean |src|) of
    the float32 source, summed in float64.
+9. FP16 x INT2 (a table row with no scheme on the pages) uses the ternary
+   codes and tensor scale of reading 8, the only INT2 weights the pages
+   describe: C = fp16(s * sum a * c + bias).
 """
 from __future__ import annotations
 
@@ -63,6 +66,8 @@ __all__ = [
     "int_accumulate_entries",
     "dequant_epilogue",
     "w4a8_gemm",
+    "w2a16_gemm",
+    "w2a16_entries",
     "w2a8_gemm",
     "w4a16_gemm",
     "w4a16_entries",
@@ -281,6 +286,32 @@ def w2a8_gemm(qa, sa, codes, scale16, bias=None, out=OUT_F16):
     ws = np.float64(np.float16(scale16))
     return dequant_epilogue(acc, ws, np.asarray(sa, np.float32)[:, None],
                             None if bias is None else np.asarray(bias)[None, :], out)
+
+
+def w2a16_gemm(A16, codes, scale16, bias=None):
+    """W2A16: fp16 activations x ternary codes with one fp16 tensor scale.
+
+    BitBLAS page data-type table row FP16 x INT2, on the ternary weights of
+    the BitNet-b1.58 case (reading 8). C[m,n] = fp16(s * sum_k a[m,k] *
+    c[n,k] + bias[n]); the sum is taken in float64 (reading 6).
+    """
+    C = np.asarray(A16).astype(np.float64) @ np.asarray(codes).astype(np.float64).T
+    C = C * np.float64(np.float16(scale16))
+    if bias is not None:
+        C = C + np.asarray(bias).astype(np.float64)[None, :]
+    return C.astype(np.float16)
+
+
+def w2a16_entries(A16, codes, scale16, rows, cols, bias=None):
+    """The W2A16 result for selected (rows[i], cols[i]) entries only."""
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    a = np.asarray(A16)[rows].astype(np.float64)
+    c = np.asarray(codes)[cols].astype(np.float64)
+    v = np.einsum("ik,ik->i", a, c) * np.float64(np.float16(scale16))
+    if bias is not None:
+        v = v + np.asarray(bias).astype(np.float64)[cols]
+    return v.astype(np.float16)
 
 
 def _dequant_group(q, s16, z, group_size):

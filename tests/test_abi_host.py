@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -101,6 +101,11 @@ def test_error_paths_before_launch():
     assert lib.w2a8_gemm(P, P, P, P, None, P2, 0, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
     assert lib.w4a16_gemm(P, P, 64, None, P2, 1, 16, 128, None, 0, s) == L.W4_ERR_ARG
     assert lib.w4a16_gemm(P, P, 128, None, P2, 1, 16, 192, None, 0, s) == L.W4_ERR_SHAPE
+    assert lib.w2a16_gemm(P, P, P, None, P2, 1, 16, 24, None, 0, s) == L.W4_ERR_SHAPE
+    assert lib.w2a16_gemm(P, P, None, None, P2, 1, 16, 32, None, 0, s) == L.W4_ERR_NULL
+    assert lib.w2a16_gemm(MIS, P, P, None, P2, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
+    assert lib.w2a16_gemm(None, None, None, None, None, 0, 16, 32, None, 0, s) == L.W4_OK
+    assert lib.w2a16_gemm(P, P, P, None, P2, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
     # fused activation quantization
     for fn in (lib.w4a8_gemm_fused_act, lib.w2a8_gemm_fused_act):
         assert fn(P, 2, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG

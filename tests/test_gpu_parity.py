@@ -485,3 +485,34 @@ def test_decode_chain_graph_replays_match_eager(g):
         torch.cuda.synchronize()
         for i, b in enumerate(bufs[1:]):
             assert np.array_equal(host(b).view(np.uint16), eager[i].view(np.uint16)), (rep, i)
+
+
+# ---------------------------------------------------------------------------
+# FP16 x INT2 (ternary weights, fp16 activations)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("c", WL.W2A16_TERNARY, ids=lambda c: c.name)
+def test_w2a16_ternary(g, c):
+    say(f"case {c.name}")
+    d = c.inputs()
+    Wp, ws = prep_w2a8(g, d["codes"], d["src"])
+    scale = host(ws)[0]
+    C = host(g.w2a16_gemm(dev(d["A"]), Wp, ws, c.N))
+    if c.M == 1:
+        tol_ok(C, O.w2a16_gemm(d["A"], d["codes"], scale), c.name)
+    else:
+        rows, cols = sample_indices(c.M, c.N, 3000, seed=17)
+        tol_ok(C[rows, cols], O.w2a16_entries(d["A"], d["codes"], scale, rows, cols), c.name)
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 100, 528), (3, 37, 48), (17, 260, 1040), (1, 256, 8640),
+                                   (40, 300, 512)])
+def test_w2a16_ragged_and_split(g, M, N, K):
+    # ragged rows/columns/k tails, 16-row tiles, and a split over K (N=256)
+    say(f"case w2a16 M={M} N={N} K={K}")
+    A = WL.activations(M, K, seed=9500 + M, dtype=np.float16)
+    codes = WL.ternary_codes(N, K, seed=9501 + N)
+    bias = WL.bias_f16(N, seed=9502)
+    Wp, ws = prep_w2a8(g, codes, WL.weights_f32(N, K, seed=9503))
+    scale = host(ws)[0]
+    C = host(g.w2a16_gemm(dev(A), Wp, ws, N, bias=f16(bias)))
+    tol_ok(C, O.w2a16_gemm(A, codes, scale, bias), f"w2a16 {M}x{N}x{K}")

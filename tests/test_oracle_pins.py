@@ -381,3 +381,46 @@ def test_group_codes_use_fp16_rounded_scale():
     assert round(7.5 * s16 / s32) == 7          # the rejected reading
     assert q[0, 3] == 8 + 5
     assert q[0, 2] == 2 + 5                     # 2.5 -> 2 (half-even)
+
+
+# ---------------------------------------------------------------------------
+# FP16 x INT2 (BitBLAS data-type table), on ternary codes (reading 9)
+# ---------------------------------------------------------------------------
+def test_w2a16_one_hot_rows_pick_scaled_codes():
+    rng = np.random.default_rng(31)
+    N, K = 7, 48
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    s16 = np.float16(0.015625)                     # 2^-6: products exact
+    bias = (rng.normal(0, 0.5, N)).astype(np.float16)
+    A = np.zeros((K, K), np.float16)
+    A[np.arange(K), np.arange(K)] = 1.0            # row k = e_k
+    C = O.w2a16_gemm(A, codes, s16, bias)
+    want = (codes.T.astype(np.float64) * 2.0 ** -6 + bias.astype(np.float64)[None, :])
+    assert np.array_equal(C, want.astype(np.float16))
+
+
+def test_w2a16_zero_codes_give_bias_and_negative_codes_subtract():
+    A = np.full((2, 32), 2.0, np.float16)
+    bias = np.array([0.5, -1.25, 3.0], np.float16)
+    C = O.w2a16_gemm(A, np.zeros((3, 32), np.int8), np.float16(0.1), bias)
+    assert np.array_equal(C, np.broadcast_to(bias, (2, 3)))
+    codes = np.full((3, 32), -1, np.int8)
+    C = O.w2a16_gemm(A, codes, np.float16(0.25), None)
+    assert np.all(C == np.float16(-16.0))           # 32 * 2 * -1 * 0.25
+
+
+def test_w2a16_bruteforce_tiny():
+    rng = np.random.default_rng(32)
+    M, N, K = 3, 5, 64
+    A = rng.normal(0, 1, (M, K)).astype(np.float16)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    s16 = np.float16(0.0173)
+    bias = rng.normal(0, 0.1, N).astype(np.float16)
+    C = O.w2a16_gemm(A, codes, s16, bias)
+    for m in range(M):
+        for n in range(N):
+            acc = math.fsum(float(A[m, k]) * int(codes[n, k]) for k in range(K))
+            v = acc * float(s16) + float(bias[n])
+            assert C[m, n] == np.float16(v), (m, n)
+    rows, cols = np.array([0, 2, 1]), np.array([4, 0, 3])
+    assert np.array_equal(O.w2a16_entries(A, codes, s16, rows, cols, bias), C[rows, cols])
