@@ -268,7 +268,8 @@ def traffic_of(path):
 
 
 def bench_case(case, steps, warmup, stream):
-    """Time one workload case (cold weights); returns a dict for --sweep."""
+    """Time one workload case (cold weights, steps replayed from one captured
+    HIP graph); returns a dict for --sweep."""
     import torch
     import gemv_nibble_unpack_amd as G
     dev = torch.device("cuda:0")
@@ -283,15 +284,14 @@ def bench_case(case, steps, warmup, stream):
         nbytes = N * K // 4 + 2 + 2 * M * K + 2 * M * N
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
         copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
-        fn = lambda i: G.w2a16_gemm(A, copies[i % len(copies)], wsc, N, workspace=ws, C=C,
-                                    stream=stream)
+        fn = lambda i: G.w2a16_gemm(A, copies[i % len(copies)], wsc, N, workspace=ws, C=C)
     elif case.scheme == "w4a16":
         Wq, s, z = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_ASYM_GROUP)
         Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, N, K, s, z)
         nbytes = decode_bytes(M, N, K)
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
         copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
-        fn = lambda i: G.w4a16_gemm(A, copies[i % len(copies)], N, workspace=ws, C=C, stream=stream)
+        fn = lambda i: G.w4a16_gemm(A, copies[i % len(copies)], N, workspace=ws, C=C)
     else:
         Aq, sa, _ = G.quantize_a8(A)
         out = G.W4_OUT_F32 if case.out == "f32" else G.W4_OUT_F16
@@ -309,8 +309,9 @@ def bench_case(case, steps, warmup, stream):
         nbytes = wbytes + M * K + 4 * M + M * N * C.element_size()
         copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
         fn = lambda i: mm(Aq, sa, copies[i % len(copies)], wsc, N, out_dtype=out, workspace=ws,
-                          C=C, stream=stream)
-    ms, _ = time_loop(fn, steps, warmup, stream)
+                          C=C)
+    # the calls use the current stream: the capture stream while capturing
+    ms, _ = time_graph(fn, steps, warmup, stream)
     del copies
     torch.cuda.empty_cache()
     return {"case": case.name, "M": M, "N": N, "K": K, "us": round(ms * 1e3, 3),
@@ -382,7 +383,8 @@ def main():
     ap.add_argument("--calib", action="store_true",
                     help="also run a copy of known size (for PMC byte-counter calibration)")
     ap.add_argument("--sweep", action="store_true",
-                    help="time every configured workload shape; one JSON line per case")
+                    help="time every configured workload shape (graph replay); one JSON line "
+                         "per case")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed decode steps one by one from Python instead of "
                          "replaying them from one captured HIP graph")

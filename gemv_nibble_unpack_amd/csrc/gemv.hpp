@@ -145,6 +145,55 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
   return d;
 }
 
+// One weight tile times its activation fragments into the accumulator:
+// unpack in registers, then the tile's MFMAs (lane quarter b covers a
+// contiguous quarter of the tile's k range in both operands). W4A16 scales
+// each 128-k partial by its fp16 group scale; the A8 kinds and W2A16 leave
+// their scales to the epilogue.
+template <int KIND, typename Acc, int AC>
+__device__ __forceinline__ void tile_mma(const u4& w, const u4 (&af)[AC], uint16_t sv, uint8_t zv,
+                                         Acc& acc) {
+  if constexpr (KIND == KIND_W4A16) {
+    const _Float16 z = (_Float16)(float)zv;
+    const _Float16 zl = -((_Float16)1024.0f + z);
+    const _Float16 zh = -((_Float16)64.0f + z);
+    const h2 zlo = {zl, zl}, zhi = {zh, zh};
+    f4 part = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const h8 bf = unpack_w4_f16(w[j], zlo, zhi);
+      part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[j]), bf, part, 0, 0,
+                                                    0);
+    }
+    const float s = h2f(sv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(part[e], s, acc[e]);
+  } else if constexpr (KIND == KIND_W2A16) {
+    // fp32 sums of exact fp16 products
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h8 b0, b1;
+      unpack_w2_f16(w[j], b0, b1);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[2 * j]), b0, acc, 0,
+                                                   0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[2 * j + 1]), b1, acc,
+                                                   0, 0, 0);
+    }
+  } else if constexpr (KIND == KIND_W4A8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const i4 bf = unpack_w4_i8(w[2 * j], w[2 * j + 1]);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[j]), bf, acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i4 bf = unpack_w2_i8(w[j]);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[j]), bf, acc, 0, 0, 0);
+    }
+  }
+}
+
 // Activation staging geometry: the block's rows x k range, row-major in LDS
 // with the row stride padded by 16 bytes so the 16 lanes of a fragment read
 // (one per row) fall on different banks.
@@ -429,48 +478,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
           if ((size_t)kt * AS::TILE_ROWB + (AS::TILE_ROWB / 4) * b + 16 * j >= arow_bytes)
             af[j] = u4{0u, 0u, 0u, 0u};
       }
-      if constexpr (GRP) {
-        const _Float16 z = (_Float16)(float)zv[u];
-        const _Float16 zl = -((_Float16)1024.0f + z);
-        const _Float16 zh = -((_Float16)64.0f + z);
-        const h2 zlo = {zl, zl}, zhi = {zh, zh};
-        f4 part = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const h8 bf = unpack_w4_f16(wv[u][j], zlo, zhi);
-          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[j]), bf, part,
-                                                        0, 0, 0);
-        }
-        const float s = h2f(sv[u]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(part[e], s, acc[e]);
-      } else if constexpr (KIND == KIND_W2A16) {
-        // fp32 sums of exact fp16 products; the tensor scale is applied once
-        // in the epilogue
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          h8 b0, b1;
-          unpack_w2_f16(wv[u][j], b0, b1);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[2 * j]), b0, acc,
-                                                       0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[2 * j + 1]), b1,
-                                                       acc, 0, 0, 0);
-        }
-      } else if constexpr (KIND == KIND_W4A8) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const i4 bf = unpack_w4_i8(wv[u][2 * j], wv[u][2 * j + 1]);
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[j]), bf, acc, 0,
-                                                      0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const i4 bf = unpack_w2_i8(wv[u][j]);
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[j]), bf, acc, 0,
-                                                      0, 0);
-        }
-      }
+      tile_mma<KIND>(wv[u], af, sv[u], zv[u], acc);
     }
   }
 

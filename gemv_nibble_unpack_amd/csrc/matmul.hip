@@ -5,6 +5,7 @@
 
 #include "gemm.hpp"
 #include "gemv.hpp"
+#include "skinny.hpp"
 
 namespace w4 {
 
@@ -15,6 +16,8 @@ constexpr int STAGE_MAX = 8 * 16 * GEMV_THREADS;  // activation bytes one block 
 
 struct Plan {
   bool gemm;        // prefill kernel instead of the decode kernel
+  bool skinny;      // > 16 rows without enough GEMM tiles: 16 rows x 128 columns per block
+  int ngroups;      // skinny: groups of 8 weight n-tiles
   bool staged;      // activation rows staged in LDS
   int ksplit, kts, mtiles, maxt, aper;
   size_t smem;
@@ -42,6 +45,11 @@ inline Plan make_plan(int kind, int M, int N, int K) {
     return P;
   }
   P.mtiles = ceil_div(M, 16);
+  // several activation tiles: share each staged tile across 8 weight
+  // n-tiles when that still gives enough blocks
+  P.ngroups = ceil_div(g.NT, SKINNY_WAVES);
+  P.skinny = P.mtiles > 1 && P.ngroups * P.mtiles >= SPLIT_BELOW;
+  if (P.skinny) return P;
   const int rows = M < 16 ? M : 16;
   const int blocks = g.NT * P.mtiles;
   const int trb = tile_rowb(kind);
@@ -133,6 +141,15 @@ int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream, int fq 
 }
 
 template <int KIND>
+int launch_skinny(const Plan& P, const MMParams& p, hipStream_t stream) {
+  const dim3 grid(ceil_div(P.ngroups * P.mtiles, 8) * 8);
+  const size_t smem = skinny_smem<KIND>();
+  allow_smem((const void*)&k_skinny<KIND, 8>, smem);
+  hipLaunchKernelGGL((k_skinny<KIND, 8>), grid, dim3(SKINNY_THREADS), smem, stream, p, P.ngroups);
+  return launch_status();
+}
+
+template <int KIND>
 int run(MMParams p, void* ws, size_t ws_bytes, hipStream_t stream) {
   const Plan P = make_plan(KIND, p.M, p.N, p.K);
   if (P.ws_bytes) {
@@ -144,6 +161,7 @@ int run(MMParams p, void* ws, size_t ws_bytes, hipStream_t stream) {
   p.KT = g.KT;
   p.KQ = g.KQ;
   if (P.gemm) return launch_gemm<KIND>(p, ws, stream);
+  if (P.skinny) return launch_skinny<KIND>(P, p, stream);
   return launch_gemv<KIND>(P, p, ws, stream);
 }
 
