@@ -301,6 +301,10 @@ def bench_case(case, steps, warmup, stream):
             Wq, wsc, _ = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_SYM_PER_CHANNEL)
             Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, N, K)
             mm, wbytes = G.w4a8_gemm, N * K // 2 + 4 * N
+        elif case.scheme == "w8a8":
+            Wq, wsc = G.quantize_pack_w8(torch.from_numpy(d["W"]).to(dev))
+            Wp = G.prepack_w(G.W4_LAYOUT_W8A8, Wq, N, K)
+            mm, wbytes = G.w8a8_gemm, N * K + 4 * N
         else:
             Wq = G.quantize_pack_w2(torch.from_numpy(d["codes"]).to(dev))
             Wp = G.prepack_w(G.W4_LAYOUT_W2A8, Wq, N, K)

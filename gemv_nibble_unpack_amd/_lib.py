@@ -12,9 +12,9 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_ARG, W4_ERR_WORKSPACE, W4_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 W4_SYM_PER_CHANNEL, W4_ASYM_GROUP = 0, 1
-W4_OUT_F16, W4_OUT_F32, W4_OUT_I32 = 0, 1, 2
+W4_OUT_F16, W4_OUT_F32, W4_OUT_I32, W4_OUT_I8 = 0, 1, 2, 3
 W4_IN_F16, W4_IN_F32 = 0, 1
-W4_LAYOUT_W4A8, W4_LAYOUT_W4A16, W4_LAYOUT_W2A8 = 0, 1, 2
+W4_LAYOUT_W4A8, W4_LAYOUT_W4A16, W4_LAYOUT_W2A8, W4_LAYOUT_W8A8 = 0, 1, 2, 3
 W4_GROUP_SIZE = 128
 W4_MAX_K = 131072
 
@@ -38,6 +38,8 @@ SIGNATURES = {
     "w2a8_gemm": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w4a16_gemm": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _p, _sz, _p]),
     "w2a16_gemm": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _p, _sz, _p]),
+    "quantize_pack_w8": (_i, [_p, _i, _i, _p, _p, _p]),
+    "w8a8_gemm": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w4_fused_act_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "w4a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w2a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),

@@ -100,7 +100,7 @@ def prepack_w(layout, Wq, N, K, scales=None, zeros=None, stream=None):
 def unprepack_w(layout, Wp, N, K, stream=None):
     """Inverse of prepack_w -> (Wq, scales-or-None, zeros-or-None)."""
     dev = _dev(Wp)
-    rowbytes = K // 4 if layout == L.W4_LAYOUT_W2A8 else K // 2
+    rowbytes = {L.W4_LAYOUT_W2A8: K // 4, L.W4_LAYOUT_W8A8: K}.get(layout, K // 2)
     Wq = torch.empty((N, rowbytes), dtype=torch.uint8, device=dev)
     scales = zeros = None
     if layout == L.W4_LAYOUT_W4A16:
@@ -144,7 +144,8 @@ def w4_workspace_bytes(layout, M, N, K):
     return v
 
 
-_OUT_DT = {L.W4_OUT_F16: torch.float16, L.W4_OUT_F32: torch.float32, L.W4_OUT_I32: torch.int32}
+_OUT_DT = {L.W4_OUT_F16: torch.float16, L.W4_OUT_F32: torch.float32, L.W4_OUT_I32: torch.int32,
+           L.W4_OUT_I8: torch.int8}
 
 
 def _workspace(ws, layout, M, N, K, dev):
@@ -205,6 +206,31 @@ def w2a16_gemm(A, Wp, w_scale16, N, bias=None, workspace=None, C=None, stream=No
     L.check("w2a16_gemm", L.load().w2a16_gemm(_ptr(A), _ptr(Wp), _ptr(w_scale16), _ptr(bias),
                                               _ptr(C), M, N, K, _ptr(buf), nb, _stream(stream)))
     return C
+
+def quantize_pack_w8(W, stream=None):
+    """float32 [N,K] -> (Wq int8 [N,K], scales float32 [N]): symmetric INT8 per row."""
+    dev = _dev(W)
+    N, K = W.shape
+    Wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    scales = torch.empty(N, dtype=torch.float32, device=dev)
+    L.check("quantize_pack_w8", L.load().quantize_pack_w8(_ptr(W), N, K, _ptr(Wq), _ptr(scales),
+                                                          _stream(stream)))
+    return Wq, scales
+
+
+def w8a8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, out_scale=None,
+              workspace=None, C=None, stream=None):
+    """INT8 x INT8; out_dtype W4_OUT_I8 re-quantizes by out_scale (device float32 [1])."""
+    dev = _dev(Aq)
+    M, K = Aq.shape
+    if C is None:
+        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
+    buf, nb = _workspace(workspace, L.W4_LAYOUT_W8A8, M, N, K, dev)
+    L.check("w8a8_gemm", L.load().w8a8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale),
+                                            _ptr(bias), _ptr(out_scale), _ptr(C), out_dtype, M, N,
+                                            K, _ptr(buf), nb, _stream(stream)))
+    return C
+
 
 _FWS_CACHE = {}
 

@@ -54,7 +54,7 @@ __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; 
 
 __host__ __device__ inline Geometry geometry(int layout, int N, int K) {
   Geometry g{};
-  g.tile_k = layout == W4_LAYOUT_W2A8 ? 256 : 128;
+  g.tile_k = layout == W4_LAYOUT_W2A8 ? 256 : layout == W4_LAYOUT_W8A8 ? 64 : 128;
   g.NT = ceil_div(N, TILE_N);
   g.KT = ceil_div(K, g.tile_k);
   g.KQ = ceil_div(g.KT, 4);
@@ -108,6 +108,12 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// The code decision rint(fl(w / s)), clipped to [-lim, lim] (0 for s == 0),
+// with the correctly rounded float32 division.
+__device__ __forceinline__ int sym_code_div(float w, float s, float lim) {
+  return s > 0.f ? (int)fminf(fmaxf(rintf(w / s), -lim), lim) : 0;
 }
 
 // The code decision rint(fl(w / s)) of a division by a scale, for

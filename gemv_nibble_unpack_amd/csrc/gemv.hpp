@@ -25,7 +25,7 @@
 
 namespace w4 {
 
-enum Kind { KIND_W4A8 = 0, KIND_W4A16 = 1, KIND_W2A8 = 2, KIND_W2A16 = 3 };
+enum Kind { KIND_W4A8 = 0, KIND_W4A16 = 1, KIND_W2A8 = 2, KIND_W2A16 = 3, KIND_W8A8 = 4 };
 
 struct MMParams {
   const void* A;               // int8 [M,K] (A8) or fp16 [M,K] (A16)
@@ -36,6 +36,7 @@ struct MMParams {
   const float* w_scale;        // W4A8 per-row scales [N]
   const uint16_t* w_scale16;   // W2A8 per-tensor scale [1]
   const uint16_t* bias;        // [N] or NULL
+  const float* out_scale;      // [1], W4_OUT_I8 only
   void* C;
   int out_dtype;
   int M, N, K, NT, KT, KQ;
@@ -111,6 +112,10 @@ template <>
 struct KindTraits<KIND_W2A16> {
   static constexpr int TILE_K = 256, A_CHUNKS = 8, SHIFT = 0;
 };
+template <>
+struct KindTraits<KIND_W8A8> {
+  static constexpr int TILE_K = 64, A_CHUNKS = 1, SHIFT = 0;
+};
 
 // Epilogue for one output element.
 template <int KIND>
@@ -126,9 +131,13 @@ __device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float
       reinterpret_cast<int32_t*>(p.C)[(size_t)m * p.N + n] = acc;
       return;
     }
-    const float ws = KIND == KIND_W4A8 ? p.w_scale[n] : h2f(p.w_scale16[0]);
+    const float ws = KIND == KIND_W2A8 ? h2f(p.w_scale16[0]) : p.w_scale[n];
     float v = (float)acc * ws * sa;
-    if (p.out_dtype == W4_OUT_F32) {
+    if (p.out_dtype == W4_OUT_I8) {
+      // re-quantized for a following INT8 layer, the code decided in float32
+      reinterpret_cast<int8_t*>(p.C)[(size_t)m * p.N + n] =
+          (int8_t)sym_code_div(v, p.out_scale[0], 127.f);
+    } else if (p.out_dtype == W4_OUT_F32) {
       reinterpret_cast<float*>(p.C)[(size_t)m * p.N + n] = v;
     } else {
       if (p.bias) v += h2f(p.bias[n]);
@@ -185,6 +194,10 @@ __device__ __forceinline__ void tile_mma(const u4& w, const u4 (&af)[AC], uint16
       const i4 bf = unpack_w4_i8(w[2 * j], w[2 * j + 1]);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[j]), bf, acc, 0, 0, 0);
     }
+  } else if constexpr (KIND == KIND_W8A8) {
+    // INT8 weights are the operand as they are
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[0]),
+                                                __builtin_bit_cast(i4, w), acc, 0, 0, 0);
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

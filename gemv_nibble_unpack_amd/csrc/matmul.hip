@@ -26,11 +26,15 @@ struct Plan {
 
 inline int kind_layout(int kind) {
   // the 2-bit weights serve INT8 and fp16 activations from one prepacked layout
-  return kind == KIND_W4A8 ? W4_LAYOUT_W4A8 : kind == KIND_W4A16 ? W4_LAYOUT_W4A16 : W4_LAYOUT_W2A8;
+  return kind == KIND_W4A8    ? W4_LAYOUT_W4A8
+         : kind == KIND_W4A16 ? W4_LAYOUT_W4A16
+         : kind == KIND_W8A8  ? W4_LAYOUT_W8A8
+                              : W4_LAYOUT_W2A8;
 }
 
 inline int tile_rowb(int kind) {
-  return kind == KIND_W4A16 ? 256 : kind == KIND_W4A8 ? 128 : kind == KIND_W2A16 ? 512 : 256;
+  return kind == KIND_W4A16 ? 256 : kind == KIND_W4A8 ? 128 : kind == KIND_W2A16 ? 512
+                                                       : kind == KIND_W8A8  ? 64 : 256;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -183,6 +187,7 @@ extern "C" size_t w4_workspace_bytes(int layout, int M, int N, int K) {
   if (layout == W4_LAYOUT_W4A8) kind = KIND_W4A8;
   else if (layout == W4_LAYOUT_W4A16) kind = KIND_W4A16;
   else if (layout == W4_LAYOUT_W2A8) kind = KIND_W2A8;
+  else if (layout == W4_LAYOUT_W8A8) kind = KIND_W8A8;
   else return 0;
   if (check_common(M, N, K, kind == KIND_W4A16 ? W4_GROUP_SIZE : 16) != W4_OK || M == 0) return 0;
   return make_plan(kind, M, N, K).ws_bytes;
@@ -376,4 +381,36 @@ extern "C" int w2a16_gemm(const uint16_t* A, const uint8_t* Wp, const uint16_t* 
   p.N = N;
   p.K = K;
   return run<KIND_W2A16>(p, workspace, workspace_bytes, stream);
+}
+
+extern "C" int w8a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp,
+                         const float* w_scale, const uint16_t* bias, const float* out_scale,
+                         void* C, int out_dtype, int M, int N, int K, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (out_dtype != W4_OUT_F16 && out_dtype != W4_OUT_F32 && out_dtype != W4_OUT_I32 &&
+      out_dtype != W4_OUT_I8)
+    return W4_ERR_ARG;
+  if (out_dtype == W4_OUT_I8 && bias) return W4_ERR_ARG;
+  const int st = check_common(M, N, K, 16);
+  if (st != W4_OK) return st;
+  if (M == 0) return W4_OK;
+  if (!Aq || !a_scale || !Wp || !w_scale || !C || (out_dtype == W4_OUT_I8 && !out_scale))
+    return W4_ERR_NULL;
+  if (!aligned(Aq, 16) || !aligned(Wp, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
+      (out_dtype != W4_OUT_I8 && !out_aligned(C, out_dtype)) || (bias && !aligned(bias, 2)) ||
+      (out_scale && !aligned(out_scale, 4)))
+    return W4_ERR_ALIGN;
+  MMParams p{};
+  p.A = Aq;
+  p.a_scale = a_scale;
+  p.Wt = Wp;
+  p.w_scale = w_scale;
+  p.bias = (out_dtype == W4_OUT_I32 || out_dtype == W4_OUT_I8) ? nullptr : bias;
+  p.out_scale = out_scale;
+  p.C = C;
+  p.out_dtype = out_dtype;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return run<KIND_W8A8>(p, workspace, workspace_bytes, stream);
 }

@@ -16,6 +16,7 @@
 //   W2A8 : byte j holds (k_j, k_{j+4}, k_{j+8}, k_{j+12}) in bit pairs 0,2,4,6.
 //          Then (w << 6), (w << 4), (w << 2), w masked with 0xC0C0C0C0 give
 //          k0..3, k4..7, k8..11, k12..15 as int8 values 64*c.
+//   W8A8 : bytes stay in k order (they are the MFMA operand as they are).
 
 #include "common.hpp"
 
@@ -34,12 +35,14 @@ __device__ __forceinline__ uint32_t shuffle_word(int layout, uint32_t w) {
     constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 #pragma unroll
     for (int p = 0; p < 8; ++p) o |= nib(w, perm[p]) << (4 * p);
-  } else {
+  } else if (layout == W4_LAYOUT_W2A8) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       o |= (crumb(w, j) | (crumb(w, j + 4) << 2) | (crumb(w, j + 8) << 4) |
             (crumb(w, j + 12) << 6))
            << (8 * j);
+  } else {
+    o = w;
   }
   return o;
 }
@@ -58,13 +61,15 @@ __device__ __forceinline__ uint32_t unshuffle_word(int layout, uint32_t o) {
     constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 #pragma unroll
     for (int p = 0; p < 8; ++p) w |= nib(o, p) << (4 * perm[p]);
-  } else {
+  } else if (layout == W4_LAYOUT_W2A8) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t b = (o >> (8 * j)) & 0xFFu;
 #pragma unroll
       for (int i = 0; i < 4; ++i) w |= ((b >> (2 * i)) & 3u) << (2 * (j + 4 * i));
     }
+  } else {
+    w = o;
   }
   return w;
 }
@@ -171,8 +176,14 @@ __global__ __launch_bounds__(256) void k_unprepack_meta(const uint16_t* __restri
   }
 }
 
+// canonical bytes per weight row
+inline int code_row_bytes(int layout, int K) {
+  return layout == W4_LAYOUT_W2A8 ? K / 4 : layout == W4_LAYOUT_W8A8 ? K : K / 2;
+}
+
 inline int check_layout_shape(int layout, int N, int K) {
-  if (layout != W4_LAYOUT_W4A8 && layout != W4_LAYOUT_W4A16 && layout != W4_LAYOUT_W2A8)
+  if (layout != W4_LAYOUT_W4A8 && layout != W4_LAYOUT_W4A16 && layout != W4_LAYOUT_W2A8 &&
+      layout != W4_LAYOUT_W8A8)
     return W4_ERR_ARG;
   if (N < 1 || K < 16 || K > W4_MAX_K || K % 16) return W4_ERR_SHAPE;
   if (layout == W4_LAYOUT_W4A16 && K % W4_GROUP_SIZE) return W4_ERR_SHAPE;
@@ -197,7 +208,7 @@ extern "C" int prepack_w(int layout, const uint8_t* Wq, const void* scales, cons
   if (!aligned(Wq, 16) || !aligned(Wp, 16) || (scales && !aligned(scales, 2)))
     return W4_ERR_ALIGN;
   const Geometry g = geometry(layout, N, K);
-  const int rowbytes = layout == W4_LAYOUT_W2A8 ? K / 4 : K / 2;
+  const int rowbytes = code_row_bytes(layout, K);
   const size_t nchunks = (size_t)g.NT * g.KT * 64;
   hipLaunchKernelGGL(k_prepack_codes, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0,
                      stream, layout, Wq, N, rowbytes, g.KT, nchunks, Wp);
@@ -219,7 +230,7 @@ extern "C" int unprepack_w(int layout, const uint8_t* Wp, int N, int K, uint8_t*
   if (!aligned(Wq, 16) || !aligned(Wp, 16) || (scales && !aligned(scales, 2)))
     return W4_ERR_ALIGN;
   const Geometry g = geometry(layout, N, K);
-  const int rowbytes = layout == W4_LAYOUT_W2A8 ? K / 4 : K / 2;
+  const int rowbytes = code_row_bytes(layout, K);
   const size_t nchunks = (size_t)g.NT * g.KT * 64;
   hipLaunchKernelGGL(k_unprepack_codes, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0,
                      stream, layout, Wp, N, rowbytes, g.KT, nchunks, Wq);

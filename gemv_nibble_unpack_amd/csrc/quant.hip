@@ -43,9 +43,6 @@ __device__ __forceinline__ int block_sum_i(int v, int* sh) {
   return r;
 }
 
-__device__ __forceinline__ int sym_code(float w, float s, float lim) {
-  return s > 0.f ? (int)fminf(fmaxf(rintf(w / s), -lim), lim) : 0;
-}
 
 // --- symmetric per-channel INT4: one block per row n -----------------------
 __global__ __launch_bounds__(QB) void k_quant_w4_sym(const float* __restrict__ W, int K,
@@ -61,10 +58,26 @@ __global__ __launch_bounds__(QB) void k_quant_w4_sym(const float* __restrict__ W
   if (threadIdx.x == 0) scales[n] = s;
   uint8_t* out = Wq + (size_t)n * (K / 2);
   for (int j = threadIdx.x; j < K / 2; j += QB) {
-    const int q0 = sym_code(row[2 * j], s, 7.f);
-    const int q1 = sym_code(row[2 * j + 1], s, 7.f);
+    const int q0 = sym_code_div(row[2 * j], s, 7.f);
+    const int q1 = sym_code_div(row[2 * j + 1], s, 7.f);
     out[j] = (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
   }
+}
+
+// --- symmetric per-channel INT8 (the page's /127 formula): one block per row
+__global__ __launch_bounds__(QB) void k_quant_w8_sym(const float* __restrict__ W, int K,
+                                                       int8_t* __restrict__ Wq,
+                                                       float* __restrict__ scales) {
+  __shared__ float sh[QB / 64];
+  const int n = blockIdx.x;
+  const float* row = W + (size_t)n * K;
+  float m = 0.f;
+  for (int k = threadIdx.x; k < K; k += QB) m = fmaxf(m, fabsf(row[k]));
+  m = block_max(m, sh);
+  const float s = m / 127.0f;
+  if (threadIdx.x == 0) scales[n] = s;
+  int8_t* out = Wq + (size_t)n * K;
+  for (int k = threadIdx.x; k < K; k += QB) out[k] = (int8_t)sym_code_div(row[k], s, 127.f);
 }
 
 // --- asymmetric group-128 uINT4: one wave per (row, group) -----------------
@@ -272,6 +285,15 @@ extern "C" int quantize_pack_w4(const float* W, int N, int K, int scheme, int gr
   const size_t blocks = (groups + QB / 64 - 1) / (QB / 64);
   hipLaunchKernelGGL(k_quant_w4_group, dim3((unsigned)blocks), dim3(QB), 0, stream, W, N, K, Wq,
                      (uint16_t*)scales, zeros);
+  return launch_status();
+}
+
+extern "C" int quantize_pack_w8(const float* W, int N, int K, int8_t* Wq, float* scales,
+                                hipStream_t stream) {
+  if (!W || !Wq || !scales) return W4_ERR_NULL;
+  if (N < 1 || K < 16 || K % 16 || K > W4_MAX_K) return W4_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(scales, 4)) return W4_ERR_ALIGN;
+  hipLaunchKernelGGL(k_quant_w8_sym, dim3(N), dim3(QB), 0, stream, W, K, Wq, scales);
   return launch_status();
 }
 

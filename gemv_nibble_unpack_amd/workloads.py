@@ -116,9 +116,14 @@ def _ternary_a16():
 
 W2A16_TERNARY = _ternary_a16()
 
+# The table's INT8 x INT8 row (INT8 weights with the page's /127 formula,
+# INT8 per-token activations) on the 4096 x 4096 projection, M in {1, 16, 128}.
+W8A8_CASES = [Case(f"w8a8_M{M}_N4096_K4096", "w8a8", M, 4096, 4096, seed=900 + M)
+              for M in (1, 16, 128)]
+
 # The example configuration printed on the BitBLAS page (M=1, N=2048,
 # K=1024, fp16 x int4, layout nt, no bias), as an extra small shape.
 BITBLAS_EXAMPLE = Case("w4a16_bitblas_example", "w4a16", 1, 2048, 1024, seed=600)
 
 ALL_CASES = [W4A8_TINY, W4A16_DECODE, *W4A16_SWEEP, W4A8_PREFILL, *W2A8_TERNARY,
-             BITBLAS_EXAMPLE, *W2A16_TERNARY]
+             BITBLAS_EXAMPLE, *W2A16_TERNARY, *W8A8_CASES]

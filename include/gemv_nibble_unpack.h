@@ -62,6 +62,7 @@ extern "C" {
 #define W4_OUT_F16 0
 #define W4_OUT_F32 1
 #define W4_OUT_I32 2          /* the raw INT32 accumulators (A8 paths only)  */
+#define W4_OUT_I8  3          /* INT8 re-quantized by an output scale (w8a8) */
 /* activation input types for quantize_a8 */
 #define W4_IN_F16 0
 #define W4_IN_F32 1
@@ -69,6 +70,7 @@ extern "C" {
 #define W4_LAYOUT_W4A8  0     /* INT4 codes for the INT8-activation kernels   */
 #define W4_LAYOUT_W4A16 1     /* uINT4 codes + group scales/zeros, fp16 acts  */
 #define W4_LAYOUT_W2A8  2     /* ternary 2-bit codes, INT8 activations        */
+#define W4_LAYOUT_W8A8  3     /* INT8 codes, INT8 activations                 */
 
 #define W4_GROUP_SIZE 128
 #define W4_MAX_K 131072
@@ -133,6 +135,8 @@ size_t prepack_bytes(int layout, int N, int K);
  *   W4_LAYOUT_W4A16: Wq uint8[N,K/2] (uINT4), scales fp16[N,K/128], zeros
  *                    uint8[N,K/128]; K multiple of 128.
  *   W4_LAYOUT_W2A8 : Wq uint8[N,K/4]; scales, zeros unused; K multiple of 16.
+ *   W4_LAYOUT_W8A8 : Wq int8[N,K] (from quantize_pack_w8), tiles of 16 rows x
+ *                    64 k, bytes in k order; scales, zeros unused.
  * Wp must hold prepack_bytes(layout, N, K) bytes.
  */
 int prepack_w(int layout, const uint8_t* Wq, const void* scales, const uint8_t* zeros,
@@ -219,6 +223,34 @@ int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size, const uint1
 int w2a16_gemm(const uint16_t* A, const uint8_t* Wp, const uint16_t* w_scale16,
                const uint16_t* bias, uint16_t* C, int M, int N, int K, void* workspace,
                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * quantize_pack_w8 -- symmetric per-output-channel INT8 weights (INT4 page,
+ * Part 1 step 1 as printed there, with the INT8 range: scale = max|w| / 127,
+ * code = round(w / scale) clipped to [-127, 127]; float32 division, round
+ * half to even):
+ *   W float32[N,K] -> Wq int8[N,K], scales float32[N]. K multiple of 16.
+ *   Wq goes through prepack_w(W4_LAYOUT_W8A8).
+ */
+int quantize_pack_w8(const float* W, int N, int K, int8_t* Wq, float* scales,
+                     hipStream_t stream);
+
+/*
+ * w8a8_gemm -- INT8 activations x INT8 weights (BitBLAS page, data-type table
+ * row INT8 x INT8, INT32 accumulation, INT8 output; INT4 page, Part 1 step 3:
+ * the INT32 result either dequantized or handed to a following quantized
+ * layer):
+ *   acc[m,n] = sum_k Aq[m,k] * q[n,k] (exact INT32; K <= 131072 keeps it in
+ *   range), then as w4a8_gemm for W4_OUT_I32 / W4_OUT_F32 / W4_OUT_F16, and
+ *   W4_OUT_I8: v = float32(float32(float32(acc) * w_scale[n]) * a_scale[m]),
+ *   C = clip(rint(v / out_scale[0]), -127, 127) (int8[M,N]; float32 division,
+ *   half to even; an out_scale of 0 gives 0), bias must be NULL.
+ *   Wp from prepack_w(W4_LAYOUT_W8A8); out_scale a device float32[1] (may be
+ *   NULL unless W4_OUT_I8). Every M runs the decode or skinny kernels.
+ */
+int w8a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp, const float* w_scale,
+              const uint16_t* bias, const float* out_scale, void* C, int out_dtype, int M, int N,
+              int K, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * w4_fused_act_workspace_bytes -- device workspace w4a8_gemm_fused_act

@@ -48,6 +48,13 @@ listed again in the design notes):
 9. FP16 x INT2 (a table row with no scheme on the pages) uses the ternary
    codes and tensor scale of reading 8, the only INT2 weights the pages
    describe: C = fp16(s * sum a * c + bias).
+10. INT8 x INT8 with INT8 output: weights use the INT4 page's printed
+    formula as it stands (scale = max|w| / 127 per row, codes in [-127,
+    127]); the INT8 output is the INT32 result re-quantized for a following
+    INT8 layer by a given per-tensor output scale: v = acc * w_scale *
+    a_scale in float32, left to right, code = clip(rint(v / out_scale), -127,
+    127) with a float32 division (the precision the kernel decides it in); an
+    output scale of 0 gives 0. The INT8 output takes no bias.
 """
 from __future__ import annotations
 
@@ -67,6 +74,10 @@ __all__ = [
     "dequant_epilogue",
     "w4a8_gemm",
     "w2a16_gemm",
+    "quantize_w8_sym",
+    "requantize_i8",
+    "w8a8_gemm",
+    "OUT_I8",
     "w2a16_entries",
     "w2a8_gemm",
     "w4a16_gemm",
@@ -76,7 +87,7 @@ __all__ = [
     "OUT_I32",
 ]
 
-OUT_F16, OUT_F32, OUT_I32 = "f16", "f32", "i32"
+OUT_F16, OUT_F32, OUT_I32, OUT_I8 = "f16", "f32", "i32", "i8"
 
 _F32 = np.float32
 
@@ -312,6 +323,53 @@ def w2a16_entries(A16, codes, scale16, rows, cols, bias=None):
     if bias is not None:
         v = v + np.asarray(bias).astype(np.float64)[cols]
     return v.astype(np.float16)
+
+
+def quantize_w8_sym(W):
+    """Symmetric per-output-channel INT8 codes and float32 scales.
+
+    INT4 page, Part 1 step 1 exactly as printed: scale = largest magnitude /
+    127, code = round(w / scale) clipped to [-127, 127] (reading 10), one
+    scale per row n (reading 2), float32 division and half-even rounding
+    (reading 3). Returns (q int8 [N,K], s float32 [N]).
+    """
+    W = np.ascontiguousarray(W, dtype=_F32)
+    amax = np.max(np.abs(W), axis=1)
+    s = (amax / _F32(127.0)).astype(_F32)
+    q = np.zeros(W.shape, dtype=np.int8)
+    live = s > 0
+    if np.any(live):
+        r = np.rint(W[live] / s[live, None])
+        q[live] = np.clip(r, -127, 127).astype(np.int8)
+    return q, s
+
+
+def requantize_i8(acc, ws, sa, out_scale):
+    """INT8 output codes from INT32 accumulators (reading 10).
+
+    BitBLAS page data-type table row INT8 x INT8 -> INT8; INT4 page, Part 1
+    step 3 (the INT32 result handed to a following quantized layer). ``acc``
+    [M,N] (or flat entries with matching ``ws``/``sa``); the product and the
+    division are taken in float32, in that order.
+    """
+    v = (np.asarray(acc, np.int64).astype(_F32) * np.asarray(ws, _F32)).astype(_F32)
+    v = (v * np.asarray(sa, _F32)).astype(_F32)
+    so = _F32(out_scale)
+    if not so > 0:
+        return np.zeros(v.shape, np.int8)
+    return np.clip(np.rint(v / so), -127, 127).astype(np.int8)
+
+
+def w8a8_gemm(qa, sa, qw, ws, bias=None, out=OUT_F16, out_scale=None):
+    """W8A8: INT8 activations x INT8 weights, exact INT32 sums, then the
+    dequantized (f16/f32), raw (i32) or re-quantized (i8) output."""
+    acc = int_accumulate(qa, qw)
+    if out == OUT_I8:
+        return requantize_i8(acc, np.asarray(ws, _F32)[None, :], np.asarray(sa, _F32)[:, None],
+                             out_scale)
+    return dequant_epilogue(acc, np.asarray(ws, np.float64)[None, :],
+                            np.asarray(sa, np.float32)[:, None],
+                            None if bias is None else np.asarray(bias)[None, :], out)
 
 
 def _dequant_group(q, s16, z, group_size):

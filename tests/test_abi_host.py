@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -36,8 +36,9 @@ def test_constants_match_header():
     text = open(HEADER).read()
     for name in ["W4_OK", "W4_ERR_NULL", "W4_ERR_SHAPE", "W4_ERR_ALIGN", "W4_ERR_ARG",
                  "W4_ERR_WORKSPACE", "W4_ERR_HIP", "W4_SYM_PER_CHANNEL", "W4_ASYM_GROUP",
-                 "W4_OUT_F16", "W4_OUT_F32", "W4_OUT_I32", "W4_IN_F16", "W4_IN_F32",
-                 "W4_LAYOUT_W4A8", "W4_LAYOUT_W4A16", "W4_LAYOUT_W2A8", "W4_GROUP_SIZE",
+                 "W4_OUT_F16", "W4_OUT_F32", "W4_OUT_I32", "W4_OUT_I8", "W4_IN_F16", "W4_IN_F32",
+                 "W4_LAYOUT_W4A8", "W4_LAYOUT_W4A16", "W4_LAYOUT_W2A8", "W4_LAYOUT_W8A8",
+                 "W4_GROUP_SIZE",
                  "W4_MAX_K"]:
         m = re.search(rf"#define\s+{name}\s+(-?\d+)", text)
         assert m, name
@@ -61,6 +62,9 @@ def test_sizes():
     assert lib.prepack_bytes(L.W4_LAYOUT_W2A8, 3200, 8640) == 200 * 34 * 1024
     assert lib.prepack_bytes(L.W4_LAYOUT_W4A16, 16, 100) == 0       # K % 128
     assert lib.prepack_bytes(7, 16, 128) == 0
+    # INT8 weights: 16 rows x 64 k per 1 KiB tile
+    assert lib.prepack_bytes(L.W4_LAYOUT_W8A8, 4096, 4096) == 4096 * 4096
+    assert lib.prepack_bytes(L.W4_LAYOUT_W8A8, 50, 208) == 4 * 4 * 1024
     assert lib.w4_workspace_bytes(L.W4_LAYOUT_W4A16, 1, 4096, 4096) == 0
     assert lib.w4_workspace_bytes(L.W4_LAYOUT_W2A8, 1, 16, 131072) > 0
     # fused activation quantization: decode rows that fit LDS need nothing;
@@ -106,6 +110,19 @@ def test_error_paths_before_launch():
     assert lib.w2a16_gemm(MIS, P, P, None, P2, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
     assert lib.w2a16_gemm(None, None, None, None, None, 0, 16, 32, None, 0, s) == L.W4_OK
     assert lib.w2a16_gemm(P, P, P, None, P2, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
+    # INT8 weights and the INT8-output matmul
+    assert lib.quantize_pack_w8(P, 4, 24, P, P2, s) == L.W4_ERR_SHAPE
+    assert lib.quantize_pack_w8(None, 4, 32, P, P2, s) == L.W4_ERR_NULL
+    assert lib.quantize_pack_w8(P, 4, 32, MIS, P2, s) == L.W4_ERR_ALIGN
+    a8 = (P, P, P, P)
+    assert lib.w8a8_gemm(*a8, P2, P, P2, L.W4_OUT_I8, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
+    assert lib.w8a8_gemm(*a8, None, None, P2, L.W4_OUT_I8, 1, 16, 32, None, 0, s) == L.W4_ERR_NULL
+    assert lib.w8a8_gemm(*a8, None, P, P2, 7, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
+    assert lib.w8a8_gemm(*a8, None, P, P2, L.W4_OUT_I8, 1, 16, 24, None, 0, s) == L.W4_ERR_SHAPE
+    assert lib.w8a8_gemm(None, None, None, None, None, None, None, 0, 0, 16, 32, None, 0,
+                         s) == L.W4_OK
+    # the other A8 matmuls have no INT8 output
+    assert lib.w4a8_gemm(P, P, P, P, None, P2, L.W4_OUT_I8, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
     # fused activation quantization
     for fn in (lib.w4a8_gemm_fused_act, lib.w2a8_gemm_fused_act):
         assert fn(P, 2, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG

@@ -516,3 +516,59 @@ def test_w2a16_ragged_and_split(g, M, N, K):
     scale = host(ws)[0]
     C = host(g.w2a16_gemm(dev(A), Wp, ws, N, bias=f16(bias)))
     tol_ok(C, O.w2a16_gemm(A, codes, scale, bias), f"w2a16 {M}x{N}x{K}")
+
+
+# ---------------------------------------------------------------------------
+# INT8 x INT8 (BitBLAS data-type table), INT8 output re-quantized
+# ---------------------------------------------------------------------------
+def prep_w8a8(g, W):
+    N, K = W.shape
+    Wq, s = g.quantize_pack_w8(dev(W))
+    return g.prepack_w(g.W4_LAYOUT_W8A8, Wq, N, K), s, Wq
+
+
+def test_quantize_w8_bitexact_and_prepack_roundtrip(g):
+    say("case quantize_pack_w8 300x528")
+    W = WL.weights_f32(300, 528, seed=9600)
+    W[3, :8] = [127.0, 63.5, -0.5, 2.5, 126.5, -127.0, 0.49, 1.5]    # ties, scale 1
+    W[3, 8:] = 0
+    W[7, :] = 0
+    Wp, s, Wq = prep_w8a8(g, W)
+    q_ref, s_ref = O.quantize_w8_sym(W)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(Wq), q_ref)
+    back, _, _ = g.unprepack_w(g.W4_LAYOUT_W8A8, Wp, 300, 528)
+    assert np.array_equal(host(back).view(np.int8), q_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (4, 4096, 4096), (16, 4096, 4096),
+                                   (128, 3200, 3200), (3, 130, 208), (1, 256, 8640),
+                                   (40, 300, 512), (300, 2000, 1040)])
+def test_w8a8_outputs(g, M, N, K):
+    # decode (M <= 16), skinny (M = 128, 300) and 16-row-tile (M = 40) kernels,
+    # ragged tails and a split over K; INT32 and INT8 bit-exact, f16/f32 to
+    # the tolerance
+    say(f"case w8a8 M={M} N={N} K={K}")
+    A = WL.activations(M, K, seed=9700 + M, dtype=np.float16)
+    W = WL.weights_f32(N, K, seed=9701 + N)
+    bias = WL.bias_f16(N, seed=9702)
+    Wp, ws, _ = prep_w8a8(g, W)
+    Aq, sa, _ = g.quantize_a8(dev(A))
+    qa, sa_ref, _ = O.quantize_a8(A)
+    qw, ws_ref = O.quantize_w8_sym(W)
+    rows, cols = sample_indices(M, N, 3000, seed=19)
+    acc = O.int_accumulate_entries(qa, qw, rows, cols)
+    C32 = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I32))
+    assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
+    # output scale that saturates the largest few codes
+    vmax = float(np.max(np.abs((acc.astype(np.float32) * ws_ref[cols]) * sa_ref[rows])))
+    so = np.float32(vmax / 100.0)
+    C8 = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I8,
+                          out_scale=dev(np.array([so], np.float32))))
+    assert np.array_equal(C8[rows, cols], O.requantize_i8(acc, ws_ref[cols], sa_ref[rows], so))
+    C16 = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, bias=f16(bias), out_dtype=g.W4_OUT_F16))
+    tol_ok(C16[rows, cols], O.dequant_epilogue(acc, ws_ref[cols], sa_ref[rows], bias[cols],
+                                               O.OUT_F16), "f16")
+    C32f = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_F32))
+    tol_ok(C32f[rows, cols], O.dequant_epilogue(acc, ws_ref[cols], sa_ref[rows], None,
+                                                O.OUT_F32), "f32")

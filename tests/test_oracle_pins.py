@@ -424,3 +424,58 @@ def test_w2a16_bruteforce_tiny():
             assert C[m, n] == np.float16(v), (m, n)
     rows, cols = np.array([0, 2, 1]), np.array([4, 0, 3])
     assert np.array_equal(O.w2a16_entries(A, codes, s16, rows, cols, bias), C[rows, cols])
+
+
+# ---------------------------------------------------------------------------
+# INT8 x INT8 with INT8 output (BitBLAS data-type table; reading 10)
+# ---------------------------------------------------------------------------
+def test_w8_page_formula_ties_and_range():
+    # the INT4 page's printed formula, /127: max 127 -> scale exactly 1
+    W = np.array([[127.0, 63.5, -0.5, 2.5, 126.5, -127.0, 0.49]], np.float32)
+    q, s = O.quantize_w8_sym(W)
+    assert s.tolist() == [1.0]
+    assert q.tolist() == [[127, 64, 0, 2, 126, -127, 0]]
+    rng = np.random.default_rng(41)
+    W = rng.normal(0, 0.02, (6, 256)).astype(np.float32)
+    q, s = O.quantize_w8_sym(W)
+    i = np.argmax(np.abs(W), axis=1)
+    assert np.all(np.abs(q[np.arange(6), i]) == 127)
+    err = np.abs(W.astype(np.float64) - q.astype(np.float64) * s[:, None])
+    assert np.all(err <= s[:, None].astype(np.float64) * 0.5 * (1 + 2.0 ** -20))
+    q0, s0 = O.quantize_w8_sym(np.zeros((1, 16), np.float32))
+    assert s0[0] == 0 and not q0.any()
+
+
+def test_requantize_i8_exact_cases():
+    acc = np.array([[254, -254, 1000, -1000, 5, 0]], np.int64)
+    ws = np.array([0.5, 0.5, 0.5, 0.5, 0.5, 0.5], np.float32)
+    sa = np.array([1.0], np.float32)
+    q = O.requantize_i8(acc, ws[None, :], sa[:, None], 1.0)
+    assert q.tolist() == [[127, -127, 127, -127, 2, 0]]         # 2.5 -> 2 (half-even)
+    assert not O.requantize_i8(acc, ws[None, :], sa[:, None], 0.0).any()
+    # float32 conversion of a large accumulator rounds to nearest even
+    big = np.array([[2 ** 24 + 1, 2 ** 24 + 3]], np.int64)
+    q = O.requantize_i8(big, np.ones((1, 2), np.float32), np.ones((1, 1), np.float32),
+                        2.0 ** 18)
+    assert q.tolist() == [[64, 64]]                              # 2^24/2^18, (2^24+4)/2^18
+
+
+def test_w8a8_one_hot_and_bruteforce():
+    rng = np.random.default_rng(42)
+    N, K = 5, 32
+    qw = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    qa = np.zeros((K, K), np.int8)
+    qa[np.arange(K), np.arange(K)] = 1
+    acc = O.int_accumulate(qa, qw)
+    assert np.array_equal(acc, qw.T.astype(np.int64))           # "nt": row k picks column k
+    qa = rng.integers(-127, 128, (3, K)).astype(np.int8)
+    ws = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    sa = rng.uniform(0.01, 0.1, 3).astype(np.float32)
+    so = np.float32(0.02)
+    q = O.w8a8_gemm(qa, sa, qw, ws, out=O.OUT_I8, out_scale=so)
+    for m in range(3):
+        for n in range(N):
+            a = sum(int(qa[m, k]) * int(qw[n, k]) for k in range(K))
+            v = np.float32(np.float32(np.float32(a) * ws[n]) * sa[m])
+            want = int(np.clip(np.rint(np.float32(v / so)), -127, 127))
+            assert q[m, n] == want, (m, n)
