@@ -15,6 +15,7 @@ W4_SYM_PER_CHANNEL, W4_ASYM_GROUP = 0, 1
 W4_OUT_F16, W4_OUT_F32, W4_OUT_I32, W4_OUT_I8 = 0, 1, 2, 3
 W4_IN_F16, W4_IN_F32 = 0, 1
 W4_LAYOUT_W4A8, W4_LAYOUT_W4A16, W4_LAYOUT_W2A8, W4_LAYOUT_W8A8 = 0, 1, 2, 3
+W4_OP_W4A8, W4_OP_W4A16, W4_OP_W2A8, W4_OP_W2A16, W4_OP_W8A8 = 0, 1, 2, 3, 4
 W4_GROUP_SIZE = 128
 W4_MAX_K = 131072
 
@@ -43,6 +44,12 @@ SIGNATURES = {
     "w4_fused_act_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "w4a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w2a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
+    "w4_plan_count": (_i, [_i, _i, _i, _i]),
+    "w4_plan_name": (_i, [_i, _i, _i, _i, _i, ctypes.c_char_p, _sz]),
+    "w4_plan_pin": (_i, [_i, _i, _i, _i, _i]),
+    "w4_plan_current": (_i, [_i, _i, _i, _i]),
+    "w4_plan_reset": (_i, []),
+    "w4_plan_workspace_bytes": (_sz, [_i, _i, _i, _i]),
 }
 
 _LIB = None

@@ -1,6 +1,8 @@
 """torch-tensor wrappers with the C entry points' names (marshalling only)."""
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib as L
@@ -144,12 +146,21 @@ def w4_workspace_bytes(layout, M, N, K):
     return v
 
 
+def w4_plan_workspace_bytes(op, M, N, K):
+    """Workspace bytes of a call of ``op`` (W4_OP_*) under the plan in force."""
+    key = ("op", op, M, N, K)
+    v = _WS_CACHE.get(key)
+    if v is None:
+        v = _WS_CACHE[key] = int(L.load().w4_plan_workspace_bytes(op, M, N, K))
+    return v
+
+
 _OUT_DT = {L.W4_OUT_F16: torch.float16, L.W4_OUT_F32: torch.float32, L.W4_OUT_I32: torch.int32,
            L.W4_OUT_I8: torch.int8}
 
 
-def _workspace(ws, layout, M, N, K, dev):
-    need = w4_workspace_bytes(layout, M, N, K)
+def _workspace(ws, op, M, N, K, dev):
+    need = w4_plan_workspace_bytes(op, M, N, K)
     if need == 0:
         return None, 0
     if ws is None:
@@ -164,7 +175,7 @@ def w4a8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, wo
     M, K = Aq.shape
     if C is None:
         C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
-    buf, nb = _workspace(workspace, L.W4_LAYOUT_W4A8, M, N, K, dev)
+    buf, nb = _workspace(workspace, L.W4_OP_W4A8, M, N, K, dev)
     L.check("w4a8_gemm", L.load().w4a8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale),
                                             _ptr(bias), _ptr(C), out_dtype, M, N, K, _ptr(buf), nb,
                                             _stream(stream)))
@@ -177,7 +188,7 @@ def w2a8_gemm(Aq, a_scale, Wp, w_scale16, N, bias=None, out_dtype=L.W4_OUT_F16, 
     M, K = Aq.shape
     if C is None:
         C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
-    buf, nb = _workspace(workspace, L.W4_LAYOUT_W2A8, M, N, K, dev)
+    buf, nb = _workspace(workspace, L.W4_OP_W2A8, M, N, K, dev)
     L.check("w2a8_gemm", L.load().w2a8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale16),
                                             _ptr(bias), _ptr(C), out_dtype, M, N, K, _ptr(buf), nb,
                                             _stream(stream)))
@@ -190,7 +201,7 @@ def w4a16_gemm(A, Wp, N, bias=None, workspace=None, C=None, group_size=L.W4_GROU
     M, K = A.shape
     if C is None:
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
-    buf, nb = _workspace(workspace, L.W4_LAYOUT_W4A16, M, N, K, dev)
+    buf, nb = _workspace(workspace, L.W4_OP_W4A16, M, N, K, dev)
     L.check("w4a16_gemm", L.load().w4a16_gemm(_ptr(A), _ptr(Wp), group_size, _ptr(bias), _ptr(C),
                                               M, N, K, _ptr(buf), nb, _stream(stream)))
     return C
@@ -202,7 +213,7 @@ def w2a16_gemm(A, Wp, w_scale16, N, bias=None, workspace=None, C=None, stream=No
     M, K = A.shape
     if C is None:
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
-    buf, nb = _workspace(workspace, L.W4_LAYOUT_W2A8, M, N, K, dev)
+    buf, nb = _workspace(workspace, L.W4_OP_W2A16, M, N, K, dev)
     L.check("w2a16_gemm", L.load().w2a16_gemm(_ptr(A), _ptr(Wp), _ptr(w_scale16), _ptr(bias),
                                               _ptr(C), M, N, K, _ptr(buf), nb, _stream(stream)))
     return C
@@ -225,7 +236,7 @@ def w8a8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, ou
     M, K = Aq.shape
     if C is None:
         C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
-    buf, nb = _workspace(workspace, L.W4_LAYOUT_W8A8, M, N, K, dev)
+    buf, nb = _workspace(workspace, L.W4_OP_W8A8, M, N, K, dev)
     L.check("w8a8_gemm", L.load().w8a8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale),
                                             _ptr(bias), _ptr(out_scale), _ptr(C), out_dtype, M, N,
                                             K, _ptr(buf), nb, _stream(stream)))
@@ -233,6 +244,47 @@ def w8a8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, ou
 
 
 _FWS_CACHE = {}
+
+
+def w4_plan_count(op, M, N, K):
+    """Number of candidate plans for (op, M, N, K); op is one of W4_OP_*."""
+    n = int(L.load().w4_plan_count(op, M, N, K))
+    if n < 0:
+        L.check("w4_plan_count", n)
+    return n
+
+
+def w4_plan_name(op, M, N, K, index):
+    """Name of candidate ``index`` ("decode:ksplit=S", "skinny", "gemm:RxC")."""
+    buf = ctypes.create_string_buffer(64)
+    L.check("w4_plan_name", L.load().w4_plan_name(op, M, N, K, index, buf, len(buf)))
+    return buf.value.decode()
+
+
+def _plans_changed():
+    # pins change the workspace sizes of their shapes
+    _WS_CACHE.clear()
+    _FWS_CACHE.clear()
+
+
+def w4_plan_pin(op, M, N, K, index):
+    """Pin candidate ``index`` for the shape (-1 removes the pin)."""
+    L.check("w4_plan_pin", L.load().w4_plan_pin(op, M, N, K, index))
+    _plans_changed()
+
+
+def w4_plan_current(op, M, N, K):
+    """Index of the candidate a call of this shape runs now."""
+    i = int(L.load().w4_plan_current(op, M, N, K))
+    if i < 0:
+        L.check("w4_plan_current", i)
+    return i
+
+
+def w4_plan_reset():
+    """Remove every pinned plan."""
+    L.check("w4_plan_reset", L.load().w4_plan_reset())
+    _plans_changed()
 
 
 def w4_fused_act_workspace_bytes(layout, M, N, K):

@@ -39,6 +39,15 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 constexpr int TILE_N = 16;
 constexpr int TILE_BYTES = 1024;
 
+// Workspace layout shared by every plan that splits K across blocks: the
+// first WS_COUNTERS bytes hold only the per-output-tile arrival counters,
+// which each call leaves zero again; the partial sums start right after and
+// are written before they are read. Any mix of shapes and plans can therefore
+// reuse one workspace (zero-filled once) on one stream: a call's counters never
+// land on bytes an earlier call used as scratch.
+constexpr size_t WS_COUNTERS = 16 * 1024;
+constexpr int WS_COUNTER_SLOTS = (int)(WS_COUNTERS / sizeof(unsigned));
+
 struct Geometry {
   int NT;          // n tiles
   int KT;          // k tiles

@@ -421,9 +421,6 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
 // ---------------------------------------------------------------------------
 // planning (host)
 // ---------------------------------------------------------------------------
-#ifndef W4_GEMM_CFG
-#define W4_GEMM_CFG 0  // 0: chosen per shape; else 100 * ntiles + wm to force one
-#endif
 constexpr int GEMM_CUS = 256;
 
 struct GemmCfg {
@@ -442,10 +439,6 @@ inline int gemm_tiles(int M, int N, GemmCfg c) {
 inline GemmCfg gemm_cfg(int kind, int M, int N) {
   if (kind != KIND_W4A8) return GemmCfg{8, 2};
   const GemmCfg narrow{16, 2};
-  if (W4_GEMM_CFG) {
-    const GemmCfg f{W4_GEMM_CFG / 100, W4_GEMM_CFG % 100};
-    return gemm_tiles(M, N, f) * f.wm >= GEMM_CUS * 3 / 2 ? f : narrow;
-  }
   GemmCfg best = narrow;
   int best_cost = ceil_div(gemm_tiles(M, N, narrow), GEMM_CUS * 2) * 16;
   for (const GemmCfg c : {GemmCfg{22, 2}, GemmCfg{22, 4}}) {
@@ -466,15 +459,14 @@ inline bool use_gemm(int kind, int M, int N) {
   return gemm_tiles(M, N, gemm_cfg(kind, M, N)) >= 128;
 }
 
-inline GemmGrid gemm_grid(int kind, int M, int N, int K) {
+inline GemmGrid gemm_grid(int kind, int M, int N, int K, GemmCfg c) {
   const Geometry g = geometry(kind == KIND_W2A8 ? W4_LAYOUT_W2A8 : W4_LAYOUT_W4A8, N, K);
-  const GemmCfg c = gemm_cfg(kind, M, N);
   GemmGrid gg{};
   gg.mblocks = ceil_div(M, 64 * c.wm);
   gg.nblocks = ceil_div(g.NT, c.ntiles);
   gg.tiles = gg.mblocks * gg.nblocks;
   int ks = 1;
-  if (c.ntiles <= 16)
+  if (c.ntiles <= 16 && gg.tiles <= WS_COUNTER_SLOTS)
     while (gg.tiles * ks < 256 && ceil_div(g.KT, ks * 2) >= 2) ks *= 2;
   gg.kts = ceil_div(g.KT, ks);
   gg.ksplit = ceil_div(g.KT, gg.kts);
@@ -482,11 +474,10 @@ inline GemmGrid gemm_grid(int kind, int M, int N, int K) {
   return gg;
 }
 
-inline size_t gemm_workspace_bytes(int kind, int M, int N, int K) {
-  const GemmGrid gg = gemm_grid(kind, M, N, K);
+inline size_t gemm_workspace_bytes(int kind, int M, int N, int K, GemmCfg c) {
+  const GemmGrid gg = gemm_grid(kind, M, N, K, c);
   if (gg.ksplit == 1) return 0;
-  const size_t counters = ((size_t)gg.tiles * sizeof(unsigned) + 255) & ~(size_t)255;
-  return counters + (size_t)gg.ksplit * M * N * sizeof(int32_t);
+  return WS_COUNTERS + (size_t)gg.ksplit * M * N * sizeof(int32_t);
 }
 
 template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
@@ -502,8 +493,7 @@ int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
 template <int KIND, int NTILES, int WM>
 int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream) {
   p.counters = reinterpret_cast<unsigned*>(ws);
-  const size_t counters = ((size_t)gg.tiles * sizeof(unsigned) + 255) & ~(size_t)255;
-  p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + counters : nullptr;
+  p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + WS_COUNTERS : nullptr;
   if (p.out_dtype == W4_OUT_I32) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I32, false>(p, gg, stream);
   if (p.out_dtype == W4_OUT_F32) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F32, false>(p, gg, stream);
   if (p.bias) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, true>(p, gg, stream);
@@ -511,13 +501,12 @@ int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream) 
 }
 
 template <int KIND>
-int launch_gemm(const MMParams& p, void* ws, hipStream_t stream) {
+int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream) {
   if constexpr (KIND == KIND_W4A16 || KIND == KIND_W2A16 || KIND == KIND_W8A8) {
     return W4_ERR_ARG;
   } else {
-    const GemmGrid gg = gemm_grid(KIND, p.M, p.N, p.K);
+    const GemmGrid gg = gemm_grid(KIND, p.M, p.N, p.K, c);
     if constexpr (KIND == KIND_W4A8) {
-      const GemmCfg c = gemm_cfg(KIND, p.M, p.N);
       if (c.ntiles == 22 && c.wm == 4) return launch_gemm_t<KIND, 22, 4>(p, gg, ws, stream);
       if (c.ntiles == 22) return launch_gemm_t<KIND, 22, 2>(p, gg, ws, stream);
       return launch_gemm_t<KIND, 16, 2>(p, gg, ws, stream);

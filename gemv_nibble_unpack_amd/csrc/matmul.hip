@@ -2,6 +2,12 @@
 // between the decode kernel (M <= 16) and the prefill GEMM kernel.
 
 #include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "gemm.hpp"
 #include "gemv.hpp"
@@ -14,9 +20,20 @@ constexpr int GEMV_THREADS = GEMV_WAVES * 64;
 constexpr int SPLIT_BELOW = 64;            // blocks below which K is split
 constexpr int STAGE_MAX = 8 * 16 * GEMV_THREADS;  // activation bytes one block may stage
 
+// The three ways a product can run. Every candidate computes the same
+// result; they differ in how the work is cut into blocks.
+enum PlanPath { PATH_DECODE = 0, PATH_SKINNY = 1, PATH_GEMM = 2 };
+
+struct Candidate {
+  int path;
+  int ks;           // decode: requested k split (0: chosen from the grid size)
+  GemmCfg cfg;      // gemm: block shape
+};
+
 struct Plan {
   bool gemm;        // prefill kernel instead of the decode kernel
   bool skinny;      // > 16 rows without enough GEMM tiles: 16 rows x 128 columns per block
+  GemmCfg cfg;      // gemm: block shape
   int ngroups;      // skinny: groups of 8 weight n-tiles
   bool staged;      // activation rows staged in LDS
   int ksplit, kts, mtiles, maxt, aper;
@@ -39,49 +56,126 @@ inline int tile_rowb(int kind) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Deterministic in (kind, M, N, K): w4_workspace_bytes and the launch agree.
-inline Plan make_plan(int kind, int M, int N, int K) {
+// The plan a candidate gives for one shape.
+inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   const Geometry g = geometry(kind_layout(kind), N, K);
   Plan P{};
-  P.gemm = use_gemm(kind, M, N);
-  if (P.gemm) {
-    P.ws_bytes = gemm_workspace_bytes(kind, M, N, K);
+  if (c.path == PATH_GEMM) {
+    P.gemm = true;
+    P.cfg = c.cfg;
+    P.ws_bytes = gemm_workspace_bytes(kind, M, N, K, c.cfg);
     return P;
   }
   P.mtiles = ceil_div(M, 16);
-  // several activation tiles: share each staged tile across 8 weight
-  // n-tiles when that still gives enough blocks
   P.ngroups = ceil_div(g.NT, SKINNY_WAVES);
-  P.skinny = P.mtiles > 1 && P.ngroups * P.mtiles >= SPLIT_BELOW;
-  if (P.skinny) return P;
+  if (c.path == PATH_SKINNY) {
+    P.skinny = true;
+    return P;
+  }
   const int rows = M < 16 ? M : 16;
   const int blocks = g.NT * P.mtiles;
   const int trb = tile_rowb(kind);
-  int ks = 1;
-  // split K across blocks only when the grid would leave most CUs idle
-  // (keeping a tile per wave; the cross-block finish costs two device-wide
-  // fences per block), and until the block's activation rows fit the
-  // staging buffer
-  while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ks *= 2;
+  int ks = g.NT * P.mtiles <= WS_COUNTER_SLOTS ? c.ks : 1;  // one counter per block slot
+  if (ks <= 0) {
+    // split K across blocks only when the grid would leave most CUs idle
+    // (keeping a tile per wave; the cross-block finish costs two device-wide
+    // fences per block)
+    ks = 1;
+    while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ks *= 2;
+  }
   P.kts = ceil_div(g.KT, ks);
   P.ksplit = ceil_div(g.KT, P.kts);
   const int per = ceil_div(P.kts, GEMV_WAVES);
   P.maxt = per <= 4 ? 4 : per <= 8 ? 8 : 16;
   // stage the block's activation rows in LDS when they fit, else each lane
   // streams its own fragments from L2
-#ifndef W4_GEMV_STAGE_MIN_ROWS
-#define W4_GEMV_STAGE_MIN_ROWS 1
-#endif
-  P.staged = rows >= W4_GEMV_STAGE_MIN_ROWS && (size_t)rows * P.kts * trb <= (size_t)STAGE_MAX;
+  P.staged = (size_t)rows * P.kts * trb <= (size_t)STAGE_MAX;
   const int chunks = ceil_div(rows * P.kts * trb, 16);
   const int aper = ceil_div(chunks, GEMV_THREADS);
   P.aper = aper <= 1 ? 1 : aper <= 2 ? 2 : aper <= 4 ? 4 : 8;
   P.smem = std::max(P.staged ? (size_t)rows * (P.kts * trb + 16) : 0, (size_t)GEMV_WAVES * 1024);
   if (P.ksplit > 1) {
-    P.counters_bytes = align256((size_t)P.mtiles * g.NT * sizeof(unsigned));
-    P.ws_bytes = P.counters_bytes + (size_t)P.mtiles * P.ksplit * g.NT * 256 * 4;
+    P.counters_bytes = WS_COUNTERS;
+    P.ws_bytes = WS_COUNTERS + (size_t)P.mtiles * P.ksplit * g.NT * 256 * 4;
   }
   return P;
+}
+
+// The built-in choice: the prefill GEMM when it has enough tiles, the skinny
+// kernel when several activation tiles can share staged rows across enough
+// blocks, else the decode kernel with its own k split.
+inline Candidate heuristic(int kind, int M, int N, int K) {
+  if (use_gemm(kind, M, N)) return Candidate{PATH_GEMM, 0, gemm_cfg(kind, M, N)};
+  const Geometry g = geometry(kind_layout(kind), N, K);
+  const int mtiles = ceil_div(M, 16);
+  if (mtiles > 1 && ceil_div(g.NT, SKINNY_WAVES) * mtiles >= SPLIT_BELOW)
+    return Candidate{PATH_SKINNY, 0, {}};
+  return Candidate{PATH_DECODE, 0, {}};
+}
+
+constexpr int MAX_CANDIDATES = 16;
+constexpr int CAND_MAX_BLOCKS = 1024;      // decode k splits tried up to this many blocks
+
+// Every plan that may run the shape, in a fixed order: the decode kernel at
+// each distinct k split that keeps a tile per wave, the skinny kernel, then
+// (INT8 activations, more than 16 rows) each GEMM block shape.
+inline int candidates(int kind, int M, int N, int K, Candidate* out) {
+  const Geometry g = geometry(kind_layout(kind), N, K);
+  const int blocks = g.NT * ceil_div(M, 16);
+  int n = 0, last = 0;
+  for (int ks = 1; ks <= 64; ks *= 2) {
+    if (ks > 1 && (ceil_div(g.KT, ks) < GEMV_WAVES || blocks * ks > CAND_MAX_BLOCKS)) break;
+    const int eff = ceil_div(g.KT, ceil_div(g.KT, ks));
+    if (eff == last) continue;
+    last = eff;
+    out[n++] = Candidate{PATH_DECODE, ks, {}};
+  }
+  out[n++] = Candidate{PATH_SKINNY, 0, {}};
+  if (M > 16 && kind == KIND_W4A8) {
+    out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{16, 2}};
+    out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 2}};
+    out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 4}};
+  } else if (M > 16 && kind == KIND_W2A8) {
+    out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{8, 2}};
+  }
+  return n;
+}
+
+inline bool same_plan(const Plan& a, const Plan& b) {
+  if (a.gemm != b.gemm || a.skinny != b.skinny) return false;
+  if (a.gemm) return a.cfg.ntiles == b.cfg.ntiles && a.cfg.wm == b.cfg.wm;
+  return a.skinny || a.ksplit == b.ksplit;
+}
+
+// Plans pinned per shape (w4_plan_pin); a shape without one takes the
+// built-in choice. One table per process, shared by all devices.
+typedef std::tuple<int, int, int, int> ShapeKey;
+inline std::mutex& pin_mutex() {
+  static std::mutex m;
+  return m;
+}
+inline std::map<ShapeKey, Candidate>& pin_table() {
+  static std::map<ShapeKey, Candidate> t;
+  return t;
+}
+inline std::atomic<int>& pin_count() {
+  static std::atomic<int> c{0};
+  return c;
+}
+
+inline Candidate chosen(int kind, int M, int N, int K) {
+  if (pin_count().load(std::memory_order_acquire) > 0) {
+    std::lock_guard<std::mutex> lock(pin_mutex());
+    const auto it = pin_table().find(ShapeKey{kind, M, N, K});
+    if (it != pin_table().end()) return it->second;
+  }
+  return heuristic(kind, M, N, K);
+}
+
+// Deterministic in (kind, M, N, K) and the pin table: w4_workspace_bytes and
+// the launch agree as long as no pin changes in between.
+inline Plan make_plan(int kind, int M, int N, int K) {
+  return plan_from(kind, M, N, K, chosen(kind, M, N, K));
 }
 
 // Chunk slots per lane the fused-quantization prologue needs for a block of
@@ -164,7 +258,7 @@ int run(MMParams p, void* ws, size_t ws_bytes, hipStream_t stream) {
   p.NT = g.NT;
   p.KT = g.KT;
   p.KQ = g.KQ;
-  if (P.gemm) return launch_gemm<KIND>(p, ws, stream);
+  if (P.gemm) return launch_gemm<KIND>(p, P.cfg, ws, stream);
   if (P.skinny) return launch_skinny<KIND>(P, p, stream);
   return launch_gemv<KIND>(P, p, ws, stream);
 }
@@ -273,16 +367,24 @@ namespace w4 {
 struct FusedPlan {
   Plan P;
   int fqc;            // prologue slots per lane (0: two launches)
-  size_t q_bytes;     // workspace for the quantized rows and their scales (two launches)
+  size_t q_off;       // two launches: offset of the quantized rows and their scales
   size_t ws_bytes;    // total workspace
 };
 
+// Two launches: the matmul's own workspace (counters, partial sums) keeps
+// offset 0 and the quantized rows follow it, past the counter area even when
+// the matmul does not split, so the counters of every call stay where they
+// are in every other call.
 inline FusedPlan fused_plan(int kind, int M, int N, int K) {
   FusedPlan F{};
   F.P = make_plan(kind, M, N, K);
-  F.fqc = (!F.P.gemm && F.P.staged) ? fq_slots(M < 16 ? M : 16, K) : 0;
-  F.q_bytes = F.fqc ? 0 : align256((size_t)M * K) + align256((size_t)M * sizeof(float));
-  F.ws_bytes = F.q_bytes + F.P.ws_bytes;
+  F.fqc = (!F.P.gemm && !F.P.skinny && F.P.staged) ? fq_slots(M < 16 ? M : 16, K) : 0;
+  if (F.fqc) {
+    F.ws_bytes = F.P.ws_bytes;
+  } else {
+    F.q_off = align256(std::max(F.P.ws_bytes, WS_COUNTERS));
+    F.ws_bytes = F.q_off + align256((size_t)M * K) + align256((size_t)M * sizeof(float));
+  }
   return F;
 }
 
@@ -317,12 +419,11 @@ static int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp
   }
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
   if (!F.fqc) {
-    int8_t* Aq = reinterpret_cast<int8_t*>(wsb);
-    float* sa = reinterpret_cast<float*>(wsb + align256((size_t)M * K));
+    int8_t* Aq = reinterpret_cast<int8_t*>(wsb + F.q_off);
+    float* sa = reinterpret_cast<float*>(wsb + F.q_off + align256((size_t)M * K));
     const int q = quantize_a8(A, in_dtype, M, K, Aq, sa, nullptr, stream);
     if (q != W4_OK) return q;
-    return a8_common(kind, Aq, sa, Wp, scale, bias, C, out_dtype, M, N, K,
-                     F.P.ws_bytes ? wsb + F.q_bytes : nullptr, ws_bytes - F.q_bytes, stream);
+    return a8_common(kind, Aq, sa, Wp, scale, bias, C, out_dtype, M, N, K, wsb, F.q_off, stream);
   }
   const Geometry g = geometry(kind_layout(kind), N, K);
   MMParams p{};
@@ -413,4 +514,88 @@ extern "C" int w8a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* 
   p.N = N;
   p.K = K;
   return run<KIND_W8A8>(p, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// plan table: list, name, pin and query the plans a shape may run with
+// ---------------------------------------------------------------------------
+namespace w4 {
+
+// op code -> kind (the op codes equal the kind codes) and the K multiple
+inline int op_check(int op, int M, int N, int K) {
+  if (op < KIND_W4A8 || op > KIND_W8A8) return W4_ERR_ARG;
+  const int st = check_common(M, N, K, op == KIND_W4A16 ? W4_GROUP_SIZE : 16);
+  if (st != W4_OK) return st;
+  return M < 1 ? W4_ERR_SHAPE : W4_OK;
+}
+
+inline int candidate_name(int kind, const Candidate& c, int M, int N, int K, char* buf,
+                          size_t len) {
+  int n;
+  if (c.path == PATH_GEMM) {
+    // block tile: 64 rows per m wave group, 16 columns per n tile
+    n = snprintf(buf, len, "gemm:%dx%d", 64 * c.cfg.wm, 16 * c.cfg.ntiles);
+  } else if (c.path == PATH_SKINNY) {
+    n = snprintf(buf, len, "skinny");
+  } else {
+    n = snprintf(buf, len, "decode:ksplit=%d", plan_from(kind, M, N, K, c).ksplit);
+  }
+  return n < 0 || (size_t)n >= len ? W4_ERR_ARG : W4_OK;
+}
+
+}  // namespace w4
+
+extern "C" int w4_plan_count(int op, int M, int N, int K) {
+  const int st = op_check(op, M, N, K);
+  if (st != W4_OK) return st;
+  Candidate c[MAX_CANDIDATES];
+  return candidates(op, M, N, K, c);
+}
+
+extern "C" int w4_plan_name(int op, int M, int N, int K, int index, char* buf, size_t len) {
+  const int st = op_check(op, M, N, K);
+  if (st != W4_OK) return st;
+  if (!buf) return W4_ERR_NULL;
+  Candidate c[MAX_CANDIDATES];
+  const int n = candidates(op, M, N, K, c);
+  if (index < 0 || index >= n || len == 0) return W4_ERR_ARG;
+  return candidate_name(op, c[index], M, N, K, buf, len);
+}
+
+extern "C" int w4_plan_pin(int op, int M, int N, int K, int index) {
+  const int st = op_check(op, M, N, K);
+  if (st != W4_OK) return st;
+  Candidate c[MAX_CANDIDATES];
+  const int n = candidates(op, M, N, K, c);
+  if (index < -1 || index >= n) return W4_ERR_ARG;
+  std::lock_guard<std::mutex> lock(pin_mutex());
+  auto& t = pin_table();
+  const ShapeKey key{op, M, N, K};
+  if (index < 0) t.erase(key);
+  else t[key] = c[index];
+  pin_count().store((int)t.size(), std::memory_order_release);
+  return W4_OK;
+}
+
+extern "C" int w4_plan_current(int op, int M, int N, int K) {
+  const int st = op_check(op, M, N, K);
+  if (st != W4_OK) return st;
+  Candidate c[MAX_CANDIDATES];
+  const int n = candidates(op, M, N, K, c);
+  const Plan cur = make_plan(op, M, N, K);
+  for (int i = 0; i < n; ++i)
+    if (same_plan(plan_from(op, M, N, K, c[i]), cur)) return i;
+  return W4_ERR_ARG;   // not reached: the built-in choice is always a candidate
+}
+
+extern "C" size_t w4_plan_workspace_bytes(int op, int M, int N, int K) {
+  if (op_check(op, M, N, K) != W4_OK) return 0;
+  return make_plan(op, M, N, K).ws_bytes;
+}
+
+extern "C" int w4_plan_reset(void) {
+  std::lock_guard<std::mutex> lock(pin_mutex());
+  pin_table().clear();
+  pin_count().store(0, std::memory_order_release);
+  return W4_OK;
 }

@@ -22,7 +22,8 @@
  *   IEEE binary16 bit patterns.
  * - Every call is asynchronous on `stream` (NULL = the default stream). The
  *   library never allocates device memory, never synchronises, and holds no
- *   state besides its code objects.
+ *   state besides its code objects and the process-wide table of pinned plans
+ *   (w4_plan_pin; empty until a caller pins one).
  * - Every call validates its arguments before touching the GPU and returns
  *   W4_OK (0) or a negative status; nothing is launched when it fails.
  *   W4_ERR_HIP means the launch itself failed (hipGetLastError).
@@ -71,6 +72,12 @@ extern "C" {
 #define W4_LAYOUT_W4A16 1     /* uINT4 codes + group scales/zeros, fp16 acts  */
 #define W4_LAYOUT_W2A8  2     /* ternary 2-bit codes, INT8 activations        */
 #define W4_LAYOUT_W8A8  3     /* INT8 codes, INT8 activations                 */
+
+#define W4_OP_W4A8  0         /* w4a8_gemm and w4a8_gemm_fused_act            */
+#define W4_OP_W4A16 1         /* w4a16_gemm                                   */
+#define W4_OP_W2A8  2         /* w2a8_gemm and w2a8_gemm_fused_act            */
+#define W4_OP_W2A16 3         /* w2a16_gemm                                   */
+#define W4_OP_W8A8  4         /* w8a8_gemm                                    */
 
 #define W4_GROUP_SIZE 128
 #define W4_MAX_K 131072
@@ -164,8 +171,10 @@ int quantize_a8(const void* A, int in_dtype, int M, int K, int8_t* Aq, float* a_
  * w4_workspace_bytes -- device workspace a matmul call needs (0 if none).
  * The workspace must be zero-filled once before its first use; every call
  * leaves the part it relies on zero again, so the same buffer can be reused
- * by later calls on the same stream. Calls that overlap in time must not
- * share a workspace.
+ * by later calls on the same stream, whatever their shapes and plans: its
+ * first 16 KiB only ever hold split-K arrival counters (zero between calls),
+ * and every byte past them is scratch that a call writes before it reads.
+ * Calls that overlap in time must not share a workspace.
  */
 size_t w4_workspace_bytes(int layout, int M, int N, int K);
 
@@ -216,9 +225,11 @@ int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size, const uint1
  *   C[m,n] = fp16( s * sum_k A[m,k] * c[n,k] + bias[n] ), float32 sums,
  *   A fp16[M,K]; Wp from prepack_w(W4_LAYOUT_W2A8) -- the same prepacked
  *   buffer w2a8_gemm reads; w_scale16 the per-tensor fp16 scale s (device
- *   pointer); bias fp16[N] or NULL; C fp16[M,N]. K multiple of 16. Every M
- *   runs the decode kernel over 16-row tiles. The workspace it needs is at
- *   most w4_workspace_bytes(W4_LAYOUT_W2A8, M, N, K).
+ *   pointer); bias fp16[N] or NULL; C fp16[M,N]. K multiple of 16. Runs
+ *   the decode kernel over 16-row tiles, or the skinny kernel when many
+ *   16-row tiles share few columns. Its workspace size is
+ *   w4_plan_workspace_bytes(W4_OP_W2A16, M, N, K); while neither op has a
+ *   pinned plan that equals w4_workspace_bytes(W4_LAYOUT_W2A8, M, N, K).
  */
 int w2a16_gemm(const uint16_t* A, const uint8_t* Wp, const uint16_t* w_scale16,
                const uint16_t* bias, uint16_t* C, int M, int N, int K, void* workspace,
@@ -284,6 +295,58 @@ int w2a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
                         const uint16_t* w_scale16, const uint16_t* bias, void* C, int out_dtype,
                         int M, int N, int K, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/* ---- plan table ---------------------------------------------------------
+ * A shape-keyed table of launch plans, after the KoGPT FasterTransformer
+ * page, section 2.3 (GEMM tuning per matrix shape, with its table of the best
+ * algorithm and tile per (M, N, K), and the advice to re-tune per GPU).
+ *
+ * Every matmul call runs one of several plans that compute the same result:
+ * the decode kernel at one of its k splits, the skinny kernel, or (INT8
+ * activations, M > 16) the tiled GEMM at one of its block shapes. Without a
+ * pin the library picks one from the shape (built-in choice). A caller that
+ * has timed the candidates (the Python package's tune module does) pins the
+ * fastest per (op, M, N, K); every later call of that op and shape, on any
+ * device and stream of the process, then uses it. Results do not depend on
+ * the plan: INT32 accumulators and INT8 outputs are identical across plans;
+ * floating-point outputs differ only by the order of the k-split reduction.
+ *
+ * The table is guarded by a mutex and may be changed from any thread. A pin
+ * changes what w4_workspace_bytes and w4_fused_act_workspace_bytes return for
+ * its shape: query them after pinning. A call whose workspace is too small for
+ * the plan in force fails with W4_ERR_WORKSPACE, as usual.
+ *
+ * `op` is one of W4_OP_*; M >= 1, N and K as the op's matmul entry point
+ * (K a multiple of 16, or of 128 for W4_OP_W4A16). Each of these calls returns
+ * W4_ERR_ARG for an unknown op and W4_ERR_SHAPE for a size out of range.
+ */
+
+/* Number of candidate plans for the shape (>= 1), or a negative status. The
+ * list and its order are fixed for a given (op, M, N, K) and library build. */
+int w4_plan_count(int op, int M, int N, int K);
+
+/* Writes the name of candidate `index` (NUL-terminated, at most len bytes,
+ * host memory) to buf: "decode:ksplit=S", "skinny" or "gemm:RxC" (R rows x C
+ * columns per block). W4_ERR_NULL for buf NULL; W4_ERR_ARG for an index out
+ * of range or a buffer too small. */
+int w4_plan_name(int op, int M, int N, int K, int index, char* buf, size_t len);
+
+/* Pins candidate `index` for the shape; index -1 removes the shape's pin. */
+int w4_plan_pin(int op, int M, int N, int K, int index);
+
+/* Index of the candidate a call with this shape would run now (pinned or
+ * built-in), or a negative status. */
+int w4_plan_current(int op, int M, int N, int K);
+
+/* Removes every pin. Always returns W4_OK. */
+int w4_plan_reset(void);
+
+/* Workspace bytes a call of `op` with this shape needs under the plan in
+ * force now (0 if none, or if an argument is invalid). For the ops with a
+ * layout of their own this equals w4_workspace_bytes of that layout;
+ * W4_OP_W2A16 needs this query, since it shares the W2A8 layout but not the
+ * W2A8 op's pin. */
+size_t w4_plan_workspace_bytes(int op, int M, int N, int K);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 24, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -38,6 +38,7 @@ def test_constants_match_header():
                  "W4_ERR_WORKSPACE", "W4_ERR_HIP", "W4_SYM_PER_CHANNEL", "W4_ASYM_GROUP",
                  "W4_OUT_F16", "W4_OUT_F32", "W4_OUT_I32", "W4_OUT_I8", "W4_IN_F16", "W4_IN_F32",
                  "W4_LAYOUT_W4A8", "W4_LAYOUT_W4A16", "W4_LAYOUT_W2A8", "W4_LAYOUT_W8A8",
+                 "W4_OP_W4A8", "W4_OP_W4A16", "W4_OP_W2A8", "W4_OP_W2A16", "W4_OP_W8A8",
                  "W4_GROUP_SIZE",
                  "W4_MAX_K"]:
         m = re.search(rf"#define\s+{name}\s+(-?\d+)", text)
@@ -70,7 +71,9 @@ def test_sizes():
     # fused activation quantization: decode rows that fit LDS need nothing;
     # 16 rows of 4096 quantize into the workspace first (int8 rows + scales)
     assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A8, 1, 4096, 4096) == 0
-    assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A8, 16, 4096, 4096) == 16 * 4096 + 256
+    # two launches: the 16 KiB counter area, then the int8 rows and their scales
+    assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A8, 16, 4096, 4096) == (
+        16384 + 16 * 4096 + 256)
     assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A16, 1, 4096, 4096) == 0
 
 
@@ -132,6 +135,80 @@ def test_error_paths_before_launch():
         assert fn(MIS, 0, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
         assert fn(None, 0, None, None, None, None, 0, 0, 16, 32, None, 0, s) == L.W4_OK
         assert fn(P, 1, P, P, None, P2, 0, 16, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
+
+
+def _names(lib, op, M, N, K):
+    out = []
+    buf = ctypes.create_string_buffer(64)
+    for i in range(lib.w4_plan_count(op, M, N, K)):
+        assert lib.w4_plan_name(op, M, N, K, i, buf, 64) == L.W4_OK
+        out.append(buf.value.decode())
+    return out
+
+
+def test_plan_table_candidates():
+    lib = G.load()
+    # decode shape: the decode kernel at each k split up to 1024 blocks, then skinny
+    assert _names(lib, L.W4_OP_W4A8, 1, 4096, 4096) == [
+        "decode:ksplit=1", "decode:ksplit=2", "decode:ksplit=4", "skinny"]
+    # prefill shape: plus the three GEMM block shapes of the INT4 x INT8 kernel
+    assert _names(lib, L.W4_OP_W4A8, 2048, 4096, 4096) == [
+        "decode:ksplit=1", "skinny", "gemm:128x256", "gemm:128x352", "gemm:256x352"]
+    assert _names(lib, L.W4_OP_W2A8, 128, 3200, 8640)[-1] == "gemm:128x128"
+    # fp16 activations and INT8 weights have no GEMM candidate
+    for op in (L.W4_OP_W4A16, L.W4_OP_W2A16, L.W4_OP_W8A8):
+        assert not any(n.startswith("gemm") for n in _names(lib, op, 2048, 4096, 4096))
+    # a tiny-N, huge-K decode splits K 64 ways on its own (one output tile)
+    names = _names(lib, L.W4_OP_W2A8, 1, 16, 131072)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 1, 16, 131072)] == "decode:ksplit=64"
+
+
+def test_plan_table_pin_and_workspace():
+    lib = G.load()
+    op, lay, M, N, K = L.W4_OP_W2A8, L.W4_LAYOUT_W2A8, 1, 16, 131072
+    assert lib.w4_plan_reset() == L.W4_OK
+    # built-in: 64-way split, 16 KiB counter area + 64 partial tiles of 1 KiB
+    assert lib.w4_workspace_bytes(lay, M, N, K) == 16384 + 64 * 1024
+    assert lib.w4_plan_pin(op, M, N, K, 0) == L.W4_OK          # decode, no split
+    assert lib.w4_plan_current(op, M, N, K) == 0
+    assert lib.w4_workspace_bytes(lay, M, N, K) == 0
+    assert lib.w4_plan_workspace_bytes(op, M, N, K) == 0
+    # the fp16-activation op on the same layout keeps its own (built-in) plan
+    assert lib.w4_plan_workspace_bytes(L.W4_OP_W2A16, M, N, K) == 16384 + 64 * 1024
+    # the pin is per (op, shape): another op or size keeps its built-in plan
+    assert lib.w4_plan_current(op, M, N, K - 256) == 6
+    assert lib.w4_workspace_bytes(lay, M, N, K - 256) > 0
+    # the fused entry points share the W2A8 op's plan: unsplit, the 128 KiB
+    # row does not fit the LDS staging, so it is quantized into the workspace
+    assert lib.w4_fused_act_workspace_bytes(lay, M, N, K) == 16384 + K + 256
+    assert lib.w4_plan_pin(op, M, N, K, -1) == L.W4_OK
+    assert lib.w4_plan_current(op, M, N, K) == 6
+    assert lib.w4_plan_pin(op, M, N, K, 2) == L.W4_OK
+    assert lib.w4_plan_pin(L.W4_OP_W4A8, 2048, 4096, 4096, 1) == L.W4_OK
+    assert lib.w4_plan_current(L.W4_OP_W4A8, 2048, 4096, 4096) == 1
+    assert lib.w4_plan_reset() == L.W4_OK
+    assert lib.w4_plan_current(op, M, N, K) == 6
+    assert lib.w4_plan_current(L.W4_OP_W4A8, 2048, 4096, 4096) != 1
+
+
+def test_plan_table_errors():
+    lib = G.load()
+    buf = ctypes.create_string_buffer(64)
+    assert lib.w4_plan_count(5, 1, 16, 128) == L.W4_ERR_ARG
+    assert lib.w4_plan_count(-1, 1, 16, 128) == L.W4_ERR_ARG
+    assert lib.w4_plan_count(L.W4_OP_W4A8, 0, 16, 128) == L.W4_ERR_SHAPE
+    assert lib.w4_plan_count(L.W4_OP_W4A8, 1, 16, 24) == L.W4_ERR_SHAPE
+    assert lib.w4_plan_count(L.W4_OP_W4A16, 1, 16, 192) == L.W4_ERR_SHAPE
+    n = lib.w4_plan_count(L.W4_OP_W4A8, 1, 16, 128)
+    assert n >= 2
+    assert lib.w4_plan_name(L.W4_OP_W4A8, 1, 16, 128, n, buf, 64) == L.W4_ERR_ARG
+    assert lib.w4_plan_name(L.W4_OP_W4A8, 1, 16, 128, 0, None, 64) == L.W4_ERR_NULL
+    assert lib.w4_plan_name(L.W4_OP_W4A8, 1, 16, 128, 0, buf, 4) == L.W4_ERR_ARG
+    assert lib.w4_plan_pin(L.W4_OP_W4A8, 1, 16, 128, n) == L.W4_ERR_ARG
+    assert lib.w4_plan_pin(L.W4_OP_W4A8, 1, 16, 128, -2) == L.W4_ERR_ARG
+    assert lib.w4_plan_pin(L.W4_OP_W4A8, 1, 16, 24, 0) == L.W4_ERR_SHAPE
+    assert lib.w4_plan_workspace_bytes(9, 1, 16, 131072) == 0
+    assert lib.w4_plan_workspace_bytes(L.W4_OP_W2A8, 0, 16, 131072) == 0
 
 
 def test_binding_refuses_host_tensors():

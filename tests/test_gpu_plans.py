@@ -1,0 +1,203 @@
+"""GPU parity of the plan table: every candidate plan of a shape against the
+oracle, one workspace shared by any mix of shapes and plans, and the tuner.
+
+INT32 accumulators and INT8 outputs must be bit-exact for every plan (the
+products are exact integers whatever the k split); fp16 outputs meet the
+same tolerance as the other parity tests, |gpu - ref| <= 2^-9 |ref| +
+1e-3 rms(ref).
+"""
+import json
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gemv_nibble_unpack_amd import workloads as WL
+from tests._helpers import say, sample_indices, tol_ok
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemv_nibble_unpack_amd as G
+    G.load()
+    G.w4_plan_reset()
+    yield G
+    G.w4_plan_reset()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def f16(x):
+    return dev(np.asarray(x, np.float16))
+
+
+class Shape:
+    """Operands of one (op, M, N, K) on the device plus the oracle's view."""
+
+    def __init__(self, g, op, M, N, K, seed):
+        self.g, self.op, self.M, self.N, self.K = g, op, M, N, K
+        self.A = WL.activations(M, K, seed=seed, dtype=np.float16)
+        self.bias = WL.bias_f16(N, seed=seed + 1)
+        self.rows, self.cols = sample_indices(M, N, 3000, seed=seed + 2)
+        a8 = op in (g.W4_OP_W4A8, g.W4_OP_W2A8, g.W4_OP_W8A8)
+        if a8:
+            self.Aq, self.sa, _ = g.quantize_a8(dev(self.A))
+            self.qa, self.sa_ref, _ = O.quantize_a8(self.A)
+        if op in (g.W4_OP_W2A8, g.W4_OP_W2A16):
+            self.codes = WL.ternary_codes(N, K, seed=seed + 3)
+            Wq = g.quantize_pack_w2(dev(self.codes))
+            self.Wp = g.prepack_w(g.W4_LAYOUT_W2A8, Wq, N, K)
+            self.scale = g.ternary_scale_f16(dev(WL.weights_f32(N, K, seed=seed + 4)))
+            s = np.float64(host(self.scale)[0])
+            self.qw, self.ws_ref = self.codes, np.full(len(self.cols), s)
+        elif op == g.W4_OP_W4A16:
+            W = WL.weights_f32(N, K, seed=seed + 3)
+            Wq, s, z = g.quantize_pack_w4(dev(W), g.W4_ASYM_GROUP)
+            self.Wp = g.prepack_w(g.W4_LAYOUT_W4A16, Wq, N, K, s, z)
+            self.q, self.s16, self.z = O.quantize_w4_group(W, 128)
+        elif op == g.W4_OP_W8A8:
+            W = WL.weights_f32(N, K, seed=seed + 3)
+            Wq, self.scale = g.quantize_pack_w8(dev(W))
+            self.Wp = g.prepack_w(g.W4_LAYOUT_W8A8, Wq, N, K)
+            self.qw, ws = O.quantize_w8_sym(W)
+            self.ws_ref = ws[self.cols]
+        else:
+            W = WL.weights_f32(N, K, seed=seed + 3)
+            Wq, self.scale, _ = g.quantize_pack_w4(dev(W), g.W4_SYM_PER_CHANNEL)
+            self.Wp = g.prepack_w(g.W4_LAYOUT_W4A8, Wq, N, K)
+            self.qw, ws = O.quantize_w4_sym(W)
+            self.ws_ref = ws[self.cols]
+        if a8:
+            self.acc = O.int_accumulate_entries(self.qa, self.qw, self.rows, self.cols)
+
+    def run(self, out_dtype, bias=False, workspace=None, out_scale=None):
+        g, N = self.g, self.N
+        b = f16(self.bias) if bias else None
+        if self.op == g.W4_OP_W4A16:
+            return host(g.w4a16_gemm(dev(self.A), self.Wp, N, bias=b, workspace=workspace))
+        if self.op == g.W4_OP_W2A16:
+            return host(g.w2a16_gemm(dev(self.A), self.Wp, self.scale, N, bias=b,
+                                     workspace=workspace))
+        mm = {g.W4_OP_W4A8: g.w4a8_gemm, g.W4_OP_W2A8: g.w2a8_gemm}.get(self.op)
+        if mm is None:
+            return host(g.w8a8_gemm(self.Aq, self.sa, self.Wp, self.scale, N, bias=b,
+                                    out_dtype=out_dtype, out_scale=out_scale, workspace=workspace))
+        return host(mm(self.Aq, self.sa, self.Wp, self.scale, N, bias=b, out_dtype=out_dtype,
+                       workspace=workspace))
+
+    def check(self, what):
+        """Every output type of the op against the oracle on the sampled entries."""
+        g, r, c = self.g, self.rows, self.cols
+        if self.op == g.W4_OP_W4A16:
+            ref = O.w4a16_entries(self.A, self.q, self.s16, self.z, r, c, 128, self.bias)
+            tol_ok(self.run(g.W4_OUT_F16, bias=True)[r, c], ref, what)
+            return
+        if self.op == g.W4_OP_W2A16:
+            s = np.float64(host(self.scale)[0])
+            ref = O.w2a16_entries(self.A, self.codes, s, r, c, self.bias)
+            tol_ok(self.run(g.W4_OUT_F16, bias=True)[r, c], ref, what)
+            return
+        C32 = self.run(g.W4_OUT_I32)
+        assert np.array_equal(C32[r, c], self.acc.astype(np.int32)), what
+        ref = O.dequant_epilogue(self.acc, self.ws_ref, self.sa_ref[r], self.bias[c], O.OUT_F16)
+        tol_ok(self.run(g.W4_OUT_F16, bias=True)[r, c], ref, what)
+        if self.op == g.W4_OP_W8A8:
+            vmax = float(np.max(np.abs((self.acc.astype(np.float32) * self.ws_ref) *
+                                       self.sa_ref[r])))
+            so = np.float32(vmax / 100.0)
+            C8 = self.run(g.W4_OUT_I8, out_scale=dev(np.array([so], np.float32)))
+            assert np.array_equal(C8[r, c], O.requantize_i8(self.acc, self.ws_ref,
+                                                            self.sa_ref[r], so)), what
+
+
+PLAN_SHAPES = [
+    ("w4a8", 1, 4096, 4096), ("w4a8", 37, 1000, 1040), ("w4a8", 130, 4100, 528),
+    ("w2a8", 1, 16, 131072), ("w2a8", 70, 3000, 2000),
+    ("w4a16", 16, 4096, 4096), ("w4a16", 33, 1000, 1024),
+    ("w2a16", 3, 3200, 8640), ("w2a16", 40, 3000, 2000),
+    ("w8a8", 16, 4096, 4096), ("w8a8", 20, 1000, 528),
+]
+
+
+@pytest.mark.parametrize("name,M,N,K", PLAN_SHAPES)
+def test_every_plan_matches_oracle(g, name, M, N, K):
+    # every candidate: decode at each k split, skinny, and (INT8 activations,
+    # M > 16) every GEMM block shape, with ragged M, N and k tails
+    op = getattr(g, "W4_OP_" + name.upper())
+    s = Shape(g, op, M, N, K, seed=12000 + M + N)
+    n = g.w4_plan_count(op, M, N, K)
+    assert n >= 2
+    try:
+        for i in range(n):
+            plan = g.w4_plan_name(op, M, N, K, i)
+            say(f"case plan {name} M={M} N={N} K={K} {plan}")
+            g.w4_plan_pin(op, M, N, K, i)
+            assert g.w4_plan_current(op, M, N, K) == i
+            s.check(f"{name} {M}x{N}x{K} {plan}")
+    finally:
+        g.w4_plan_pin(op, M, N, K, -1)
+
+
+def test_one_workspace_for_any_mix_of_shapes_and_plans(g):
+    # A decode call split 64 ways leaves partial sums past the counter area; a
+    # split GEMM (144 output tiles) and a 4-way split decode (256 output
+    # tiles) then count arrivals in the same buffer. Each must equal its
+    # result on a fresh workspace, bit for bit.
+    say("case shared workspace: decode split 64, gemm split, decode split 4")
+    cases = [Shape(g, g.W4_OP_W2A8, 1, 16, 131072, seed=13000),
+             Shape(g, g.W4_OP_W4A8, 1100, 4004, 512, seed=13100),
+             Shape(g, g.W4_OP_W4A8, 1, 4096, 4096, seed=13200)]
+    names = [g.w4_plan_name(c.op, c.M, c.N, c.K, g.w4_plan_current(c.op, c.M, c.N, c.K))
+             for c in cases[:2]]
+    assert names == ["decode:ksplit=64", "gemm:128x256"]
+    try:
+        g.w4_plan_pin(g.W4_OP_W4A8, 1, 4096, 4096, 2)
+        assert g.w4_plan_name(g.W4_OP_W4A8, 1, 4096, 4096, 2) == "decode:ksplit=4"
+        need = max(g.w4_plan_workspace_bytes(c.op, c.M, c.N, c.K) for c in cases)
+        assert need > 16384
+        shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        for rep in range(2):
+            for c in cases:
+                got = c.run(g.W4_OUT_I32, workspace=shared)
+                fresh = c.run(g.W4_OUT_I32)
+                assert np.array_equal(got, fresh), (rep, c.op, c.M, c.N, c.K)
+                assert np.array_equal(got[c.rows, c.cols], c.acc.astype(np.int32))
+        # the counter area is zero again after the calls
+        assert not host(shared[:16384]).any()
+    finally:
+        g.w4_plan_pin(g.W4_OP_W4A8, 1, 4096, 4096, -1)
+
+
+def test_tuner_pins_a_candidate_and_results_hold(g, tmp_path):
+    from gemv_nibble_unpack_amd import tune
+    op, M, N, K = g.W4_OP_W4A8, 130, 4100, 528
+    say(f"case tune w4a8 M={M} N={N} K={K}")
+    try:
+        rec = tune.tune_shape(op, M, N, K, reps=5, warmup=1)
+        names = tune.candidates(op, M, N, K)
+        assert set(rec["candidates"]) == set(names)
+        assert rec["plan"] in names and rec["us"] == min(rec["candidates"].values())
+        assert names[g.w4_plan_current(op, M, N, K)] == rec["plan"]
+        Shape(g, op, M, N, K, seed=14000).check(f"tuned {rec['plan']}")
+        # the saved table pins the same plan by name in a clean table
+        path = tmp_path / "plans.json"
+        tune.save(str(path), [rec])
+        assert json.loads(path.read_text())["plans"][0]["plan"] == rec["plan"]
+        g.w4_plan_reset()
+        assert tune.load(str(path)) == []
+        assert names[g.w4_plan_current(op, M, N, K)] == rec["plan"]
+    finally:
+        g.w4_plan_reset()
