@@ -141,6 +141,26 @@ __device__ __forceinline__ int sym_code_rcp(float w, float s, float rs, float li
 }
 
 // fp16 bit pattern <-> float
+// Cross-block exchange of split-K partial sums through the workspace, at
+// device scope. A device-scope fence writes back and invalidates the whole
+// L2 of the XCD (costly once per block); instead the partial sums themselves
+// are stored and loaded at device scope (written through to, and read from,
+// the level all XCDs share), so the only ordering a block needs is that its
+// stores have completed before it counts itself in (stores_done, then a
+// barrier, then the device-scope arrival count).
+__device__ __forceinline__ void dev_store(uint32_t* a, uint32_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t dev_load(const uint32_t* a) {
+  return __hip_atomic_load(const_cast<uint32_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned dev_arrive(unsigned* c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this wave's stores are acknowledged; the clobber keeps the
+// compiler from moving memory accesses across the wait
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
   }
 
   // split K: exact INT32 partial sums, the last block of the tile finishes
-  int32_t* part = reinterpret_cast<int32_t*>(p.partials);
+  uint32_t* part = reinterpret_cast<uint32_t*>(p.partials);
   const size_t plane = (size_t)p.M * p.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -379,22 +379,16 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = acc[i][t][e];
-        if (n + e < p.N) part[(size_t)kz * plane + (size_t)m * p.N + n + e] = v;
+        if (n + e < p.N) dev_store(&part[(size_t)kz * plane + (size_t)m * p.N + n + e], (uint32_t)v);
       }
     }
   }
-  // One thread per block does the device-scope fences (each one writes back
-  // and invalidates the XCD's L2, so they must not run once per wave): the
-  // barrier orders every wave's partial stores before thread 0's release
-  // fence, and thread 0's acquire fence (last block only) precedes the reads
-  // of the other blocks' partials.
+  // every wave's partial stores are complete before thread 0 counts the
+  // block in; the last block reads the partials at device scope
   __shared__ int last;
+  stores_done();
   __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    last = atomicAdd(&p.counters[tix], 1u) == (unsigned)(gg.ksplit - 1);
-    if (last) __threadfence();
-  }
+  if (tid == 0) last = dev_arrive(&p.counters[tix]) == (unsigned)(gg.ksplit - 1);
   __syncthreads();
   if (!last) return;
 #pragma unroll
@@ -408,14 +402,14 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
       for (int z = 0; z < gg.ksplit; ++z) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) sum[e] += part[(size_t)z * plane + (size_t)m * p.N + n + e];
+          if (n + e < p.N) sum[e] += (int)dev_load(&part[(size_t)z * plane + (size_t)m * p.N + n + e]);
       }
       f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
       gemm_col_params<KIND, OUT, BIAS>(p, n, ws, bias);
       gemm_store4<KIND, OUT, BIAS>(p, m, n, sum, ws, bias, sav[i], vec_ok);
     }
   }
-  if (tid == 0) p.counters[tix] = 0u;
+  if (tid == 0) dev_store(&p.counters[tix], 0u);
 }
 
 // ---------------------------------------------------------------------------

@@ -549,20 +549,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       if constexpr (A16) fs += v;
       else is += __builtin_bit_cast(int, v);
     }
-    part[idx] = A16 ? __builtin_bit_cast(uint32_t, fs) : (uint32_t)is;
+    dev_store(&part[idx], A16 ? __builtin_bit_cast(uint32_t, fs) : (uint32_t)is);
   }
-  // One thread per block does the device-scope fences (each one writes back
-  // and invalidates the XCD's L2, so they must not run once per wave): the
-  // barrier orders every wave's partial stores before thread 0's release
-  // fence, and thread 0's acquire fence (last block only) precedes the reads
-  // of the other blocks' partials.
+  // every wave's partial stores are complete before thread 0 counts the
+  // block in; the last block reads the partials at device scope
   __shared__ int last;
+  stores_done();
   __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    last = atomicAdd(&p.counters[slot], 1u) == (unsigned)(p.ksplit - 1);
-    if (last) __threadfence();
-  }
+  if (tid == 0) last = dev_arrive(&p.counters[slot]) == (unsigned)(p.ksplit - 1);
   __syncthreads();
   if (!last) return;
   const uint32_t* base = reinterpret_cast<const uint32_t*>(p.partials) +
@@ -574,13 +568,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     float fs = 0.f;
     int is = 0;
     for (int sp = 0; sp < p.ksplit; ++sp) {
-      const uint32_t v = base[(size_t)sp * ngroups * NOUT + idx];
+      const uint32_t v = dev_load(&base[(size_t)sp * ngroups * NOUT + idx]);
       if constexpr (A16) fs += __builtin_bit_cast(float, v);
       else is += (int)v;
     }
     store_out<KIND>(p, mtile * 16 + row, n, fs, is, row_sa(row));
   }
-  if (tid == 0) p.counters[slot] = 0u;  // leave the workspace zeroed
+  if (tid == 0) dev_store(&p.counters[slot], 0u);  // leave the workspace zeroed
 }
 
 }  // namespace w4

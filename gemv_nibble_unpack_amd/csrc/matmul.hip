@@ -77,9 +77,9 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   const int trb = tile_rowb(kind);
   int ks = g.NT * P.mtiles <= WS_COUNTER_SLOTS ? c.ks : 1;  // one counter per block slot
   if (ks <= 0) {
-    // split K across blocks only when the grid would leave most CUs idle
-    // (keeping a tile per wave; the cross-block finish costs two device-wide
-    // fences per block)
+    // split K across blocks only when the grid would leave most CUs idle,
+    // keeping a tile per wave (larger grids gain little or lose from the
+    // partial-sum round trip; the plan table can pin a split per shape)
     ks = 1;
     while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ks *= 2;
   }

@@ -149,3 +149,39 @@ def load(path):
         else:
             skipped.append(r)
     return skipped
+
+
+def workload_shapes():
+    """The distinct (op, M, N, K) of the configured workload cases."""
+    seen = []
+    for c in WL.ALL_CASES:
+        s = (OPS[c.scheme], c.M, c.N, c.K)
+        if s not in seen:
+            seen.append(s)
+    return seen
+
+
+def main(argv=None):
+    """Tune the configured workload shapes; print one JSON line per shape
+    (tuned plan, built-in plan, every candidate's time) and save the table."""
+    import argparse
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--out", default=None, help="write the tuned table here (JSON)")
+    ap.add_argument("--reps", type=int, default=50)
+    args = ap.parse_args(argv)
+    table = []
+    for op, M, N, K in workload_shapes():
+        G.w4_plan_pin(op, M, N, K, -1)
+        builtin = candidates(op, M, N, K)[G.w4_plan_current(op, M, N, K)]
+        rec = tune_shape(op, M, N, K, reps=args.reps)
+        rec["builtin"] = builtin
+        rec["builtin_us"] = rec["candidates"][builtin]
+        print(json.dumps(rec), flush=True)
+        table.append(rec)
+    if args.out:
+        save(args.out, table)
+    return table
+
+
+if __name__ == "__main__":
+    main()
