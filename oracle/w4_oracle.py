@@ -55,6 +55,18 @@ listed again in the design notes):
     a_scale in float32, left to right, code = clip(rint(v / out_scale), -127,
     127) with a float32 division (the precision the kernel decides it in); an
     output scale of 0 gives 0. The INT8 output takes no bias.
+11. FP8_E4M3 x FP8_E4M3 (the table's last row: FP32 accumulate, FP16
+    output). The pages name the format only; E4M3 is taken as the OCP 8-bit
+    floating-point format: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits, subnormals m * 2^-9 at exponent 0, no infinities, S.1111.111 the
+    only NaN, largest magnitude 448. Conversion to E4M3 rounds to nearest,
+    ties to the even code, keeps the sign of zero, and saturates at +-448.
+    Both operands are quantized per row (activations per token, weights per
+    output channel) the way the INT8 rows are: scale = max|x| / 448 in
+    float32, code = E4M3(x / scale) with a float32 division; a zero row gets
+    scale 0 and code 0. C = out(sum_k a_k * w_k * w_scale[n] * a_scale[m]
+    + bias[n]), the sum of exact products taken in float64 here (float32 in
+    the kernels).
 """
 from __future__ import annotations
 
@@ -77,6 +89,12 @@ __all__ = [
     "quantize_w8_sym",
     "requantize_i8",
     "w8a8_gemm",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_f8",
+    "f8f8_gemm",
+    "f8f8_entries",
+    "E4M3_MAX",
     "OUT_I8",
     "w2a16_entries",
     "w2a8_gemm",
@@ -406,3 +424,88 @@ def w4a16_entries(A16, q, s16, z, rows, cols, group_size=128, bias=None):
     if bias is not None:
         v = v + np.asarray(bias).astype(np.float64)[cols]
     return v.astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 x FP8 E4M3 (reading 11)
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """Values of E4M3 codes in float64, from the bit fields (reading 11):
+    exponent 0 -> m * 2^-9; else (1 + m / 8) * 2^(e - 7); 0x7F / 0xFF NaN."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+# the 127 non-negative finite values, in code order (increasing)
+_E4M3_POS = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_encode(x):
+    """E4M3 codes (uint8) of float32 values: the nearest of the 127 finite
+    magnitudes, ties to the even code, sign kept (also for zero), magnitudes
+    above 448 saturated to 448 (reading 11). A plain nearest-neighbour search
+    over the value table, not a bit-level conversion."""
+    x = np.asarray(x, _F32)
+    a = np.minimum(np.abs(x).astype(np.float64), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")      # first value >= a
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    code = np.where(d_lo < d_hi, lo, hi)
+    tie = d_lo == d_hi
+    code = np.where(tie, np.where(lo % 2 == 0, lo, hi), code)
+    code = np.where(_E4M3_POS[hi] == a, hi, code)          # exact values
+    neg = np.signbit(x)
+    return (code.astype(np.uint8) | np.where(neg, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def quantize_f8(X):
+    """Per-row E4M3 quantization (reading 11): s = max|x| / 448 in float32,
+    code = E4M3(fl32(x / s)); zero rows give s = 0 and code 0. X is float32
+    (weights) or fp16 (activations, widened exactly). Returns (codes uint8
+    [R,K], s float32 [R])."""
+    X = np.asarray(X)
+    X = X.astype(_F32) if X.dtype != _F32 else np.ascontiguousarray(X)
+    amax = np.max(np.abs(X), axis=1)
+    s = (amax / _F32(E4M3_MAX)).astype(_F32)
+    q = np.zeros(X.shape, dtype=np.uint8)
+    live = s > 0
+    if np.any(live):
+        q[live] = e4m3_encode((X[live] / s[live, None]).astype(_F32))
+    return q, s
+
+
+def _f8_out(v, bias, out):
+    if bias is not None:
+        v = v + bias
+    return v.astype(np.float16) if out == OUT_F16 else v.astype(np.float32)
+
+
+def f8f8_gemm(qa, sa, qw, sw, bias=None, out=OUT_F16):
+    """FP8 x FP8: C[m,n] = out(sum_k dec(qa[m,k]) dec(qw[n,k]) * sw[n] * sa[m]
+    + bias[n]); the products are exact and summed in float64."""
+    acc = e4m3_decode(qa) @ e4m3_decode(qw).T
+    v = acc * np.asarray(sw, np.float64)[None, :] * np.asarray(sa, np.float64)[:, None]
+    b = None if bias is None else np.asarray(bias).astype(np.float64)[None, :]
+    return _f8_out(v, b, out)
+
+
+def f8f8_entries(qa, sa, qw, sw, rows, cols, bias=None, out=OUT_F16):
+    """The FP8 x FP8 result for selected (rows[i], cols[i]) entries only."""
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    a = e4m3_decode(np.asarray(qa)[rows])
+    w = e4m3_decode(np.asarray(qw)[cols])
+    v = np.einsum("ik,ik->i", a, w) * np.asarray(sw, np.float64)[cols] * \
+        np.asarray(sa, np.float64)[rows]
+    b = None if bias is None else np.asarray(bias).astype(np.float64)[cols]
+    return _f8_out(v, b, out)

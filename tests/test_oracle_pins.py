@@ -479,3 +479,108 @@ def test_w8a8_one_hot_and_bruteforce():
             v = np.float32(np.float32(np.float32(a) * ws[n]) * sa[m])
             want = int(np.clip(np.rint(np.float32(v / so)), -127, 127))
             assert q[m, n] == want, (m, n)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 x FP8 E4M3 (reading 11: the OCP E4M3 format)
+# ---------------------------------------------------------------------------
+def _e4m3_by_hand(c):
+    """One code's value written out from the bit fields with math.ldexp."""
+    s = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 0xF, c & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return s * math.ldexp(m, -9)
+    return s * math.ldexp(8 + m, e - 10)
+
+
+def test_e4m3_decode_closed_forms_and_table():
+    vals = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    for c, v in [(0x7E, 448.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+                 (0x38, 1.0), (0x39, 1.125), (0x40, 2.0), (0x77, 240.0), (0xB8, -1.0),
+                 (0xFE, -448.0), (0x00, 0.0)]:
+        assert vals[c] == v, hex(c)
+    assert np.signbit(vals[0x80]) and vals[0x80] == 0.0
+    nan = np.isnan(vals)
+    assert np.flatnonzero(nan).tolist() == [0x7F, 0xFF]       # the only NaNs
+    for c in range(256):
+        h = _e4m3_by_hand(c)
+        assert (np.isnan(h) and np.isnan(vals[c])) or h == vals[c], hex(c)
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)                           # strictly increasing codes
+    # each binade [2^e, 2^(e+1)) holds 8 values 2^(e-3) apart; the top one
+    # holds 7, its last slot being the NaN
+    for e in range(-6, 9):
+        b = pos[(pos >= 2.0 ** e) & (pos < 2.0 ** (e + 1))]
+        assert len(b) == (7 if e == 8 else 8) and np.all(np.diff(b) == 2.0 ** (e - 3)), e
+
+
+def test_e4m3_encode_ties_saturation_and_library():
+    c = np.arange(256, dtype=np.uint8)
+    fin = ~np.isnan(O.e4m3_decode(c))
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(c[fin]).astype(np.float32)), c[fin])
+    f32 = np.float32
+    cases = [(1.0625, 0x38), (1.1875, 0x3A),                  # midpoints go to the even code
+             (np.nextafter(f32(1.0625), f32(2)), 0x39), (np.nextafter(f32(1.0625), f32(0)), 0x38),
+             (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02),     # subnormal ties
+             (460.0, 0x7E), (470.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE),   # saturation, no NaN
+             (-0.0, 0x80), (-(2.0 ** -12), 0x80), (0.0, 0x00)]
+    for x, want in cases:
+        assert O.e4m3_encode(np.array([x], f32))[0] == want, (x, hex(want))
+    # against the library conversion (round to nearest even, in range)
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(51)
+    x = np.concatenate([rng.normal(0, 30, 20000), rng.normal(0, 0.01, 5000),
+                        (O.e4m3_decode(c[:0x7E]) + O.e4m3_decode(c[1:0x7F])) / 2]).astype(f32)
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), ref)
+
+
+def test_quantize_f8_rows():
+    rng = np.random.default_rng(52)
+    W = rng.normal(0, 0.02, (6, 256)).astype(np.float32)
+    W[2] = 0
+    q, s = O.quantize_f8(W)
+    assert s[2] == 0 and not q[2].any()
+    live = [0, 1, 3, 4, 5]
+    assert np.array_equal(s[live], (np.max(np.abs(W[live]), axis=1) / np.float32(448)).astype(np.float32))
+    i = np.argmax(np.abs(W[live]), axis=1)
+    assert np.all(np.abs(O.e4m3_decode(q[live, i])) == 448.0)   # the row max is the top code
+    rec = O.e4m3_decode(q[live]) * s[live, None]
+    err = np.abs(W[live] - rec)
+    # half a unit in the last of 3 mantissa bits, or half the subnormal step
+    bound = np.maximum(np.abs(W[live]) * 2.0 ** -4, s[live, None] * 2.0 ** -10) * (1 + 2.0 ** -20)
+    assert np.all(err <= bound)
+    # fp16 activations widen exactly
+    A = rng.normal(0, 1, (3, 64)).astype(np.float16)
+    qa, sa = O.quantize_f8(A)
+    qb, sb = O.quantize_f8(A.astype(np.float32))
+    assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
+
+
+def test_f8f8_one_hot_and_bruteforce():
+    rng = np.random.default_rng(53)
+    N, K = 4, 32
+    qw = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    qw[(qw & 0x7F) == 0x7F] = 0x38                            # no NaN codes
+    one = np.zeros((K, K), np.uint8)
+    one[np.arange(K), np.arange(K)] = 0x38                    # 1.0 on the diagonal
+    C = O.f8f8_gemm(one, np.ones(K, np.float32), qw, np.ones(N, np.float32), out=O.OUT_F32)
+    assert np.array_equal(C, O.e4m3_decode(qw).T.astype(np.float32))   # "nt": row k picks column k
+    qa = rng.integers(0, 256, (3, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0xB8
+    sw = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    sa = rng.uniform(0.01, 0.1, 3).astype(np.float32)
+    bias = rng.normal(0, 0.01, N).astype(np.float16)
+    C = O.f8f8_gemm(qa, sa, qw, sw, bias=bias, out=O.OUT_F16)
+    for m in range(3):
+        for n in range(N):
+            acc = math.fsum(_e4m3_by_hand(int(qa[m, k])) * _e4m3_by_hand(int(qw[n, k]))
+                            for k in range(K))
+            want = np.float16(acc * float(sw[n]) * float(sa[m]) + float(bias[n]))
+            assert C[m, n] == want, (m, n)
+    rows, cols = np.array([0, 2, 1]), np.array([3, 0, 1])
+    e = O.f8f8_entries(qa, sa, qw, sw, rows, cols, bias=bias)
+    assert np.array_equal(e, C[rows, cols])
