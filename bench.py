@@ -297,7 +297,12 @@ def bench_case(case, steps, warmup, stream):
         out = G.W4_OUT_F32 if case.out == "f32" else G.W4_OUT_F16
         C = torch.empty((M, N), dtype=torch.float32 if out == G.W4_OUT_F32 else torch.float16,
                         device=dev)
-        if case.scheme == "w4a8":
+        if case.scheme == "f8f8":
+            Aq, sa = G.quantize_f8(A)
+            Wq, wsc = G.quantize_f8(torch.from_numpy(d["W"]).to(dev))
+            Wp = G.prepack_w(G.W4_LAYOUT_W8A8, Wq, N, K)
+            mm, wbytes = G.f8f8_gemm, N * K + 4 * N
+        elif case.scheme == "w4a8":
             Wq, wsc, _ = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_SYM_PER_CHANNEL)
             Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, N, K)
             mm, wbytes = G.w4a8_gemm, N * K // 2 + 4 * N

@@ -15,7 +15,7 @@ W4_SYM_PER_CHANNEL, W4_ASYM_GROUP = 0, 1
 W4_OUT_F16, W4_OUT_F32, W4_OUT_I32, W4_OUT_I8 = 0, 1, 2, 3
 W4_IN_F16, W4_IN_F32 = 0, 1
 W4_LAYOUT_W4A8, W4_LAYOUT_W4A16, W4_LAYOUT_W2A8, W4_LAYOUT_W8A8 = 0, 1, 2, 3
-W4_OP_W4A8, W4_OP_W4A16, W4_OP_W2A8, W4_OP_W2A16, W4_OP_W8A8 = 0, 1, 2, 3, 4
+W4_OP_W4A8, W4_OP_W4A16, W4_OP_W2A8, W4_OP_W2A16, W4_OP_W8A8, W4_OP_F8F8 = 0, 1, 2, 3, 4, 5
 W4_GROUP_SIZE = 128
 W4_MAX_K = 131072
 
@@ -41,6 +41,8 @@ SIGNATURES = {
     "w2a16_gemm": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _p, _sz, _p]),
     "quantize_pack_w8": (_i, [_p, _i, _i, _p, _p, _p]),
     "w8a8_gemm": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
+    "quantize_f8": (_i, [_p, _i, _i, _i, _p, _p, _p]),
+    "f8f8_gemm": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w4_fused_act_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "w4a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w2a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),

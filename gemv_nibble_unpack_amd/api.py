@@ -243,6 +243,37 @@ def w8a8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, ou
     return C
 
 
+def quantize_f8(X, stream=None):
+    """fp16/float32 [R,K] -> (codes uint8 [R,K] E4M3, scales float32 [R]), per row."""
+    dev = _dev(X)
+    R, K = X.shape
+    if X.dtype == torch.float16:
+        dt = L.W4_IN_F16
+    elif X.dtype == torch.float32:
+        dt = L.W4_IN_F32
+    else:
+        raise ValueError("X must be float16 or float32")
+    Xq = torch.empty((R, K), dtype=torch.uint8, device=dev)
+    scales = torch.empty(R, dtype=torch.float32, device=dev)
+    L.check("quantize_f8", L.load().quantize_f8(_ptr(X), dt, R, K, _ptr(Xq), _ptr(scales),
+                                                _stream(stream)))
+    return Xq, scales
+
+
+def f8f8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, workspace=None,
+              C=None, stream=None):
+    """FP8 E4M3 x FP8 E4M3 (Wp: prepack_w(W4_LAYOUT_W8A8) of E4M3 codes)."""
+    dev = _dev(Aq)
+    M, K = Aq.shape
+    if C is None:
+        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
+    buf, nb = _workspace(workspace, L.W4_OP_F8F8, M, N, K, dev)
+    L.check("f8f8_gemm", L.load().f8f8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale),
+                                            _ptr(bias), _ptr(C), out_dtype, M, N, K, _ptr(buf),
+                                            nb, _stream(stream)))
+    return C
+
+
 _FWS_CACHE = {}
 
 

@@ -449,7 +449,8 @@ inline GemmCfg gemm_cfg(int kind, int M, int N) {
 // K much; smaller products run on the decode kernel, one block per (16-row
 // tile, 16-column tile).
 inline bool use_gemm(int kind, int M, int N) {
-  if (kind == KIND_W4A16 || kind == KIND_W2A16 || kind == KIND_W8A8 || M <= 16) return false;
+  if (kind != KIND_W4A8 && kind != KIND_W2A8) return false;
+  if (M <= 16) return false;
   return gemm_tiles(M, N, gemm_cfg(kind, M, N)) >= 128;
 }
 
@@ -496,7 +497,7 @@ int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream) 
 
 template <int KIND>
 int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream) {
-  if constexpr (KIND == KIND_W4A16 || KIND == KIND_W2A16 || KIND == KIND_W8A8) {
+  if constexpr (KIND != KIND_W4A8 && KIND != KIND_W2A8) {
     return W4_ERR_ARG;
   } else {
     const GemmGrid gg = gemm_grid(KIND, p.M, p.N, p.K, c);

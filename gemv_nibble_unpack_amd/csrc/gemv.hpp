@@ -25,15 +25,24 @@
 
 namespace w4 {
 
-enum Kind { KIND_W4A8 = 0, KIND_W4A16 = 1, KIND_W2A8 = 2, KIND_W2A16 = 3, KIND_W8A8 = 4 };
+enum Kind {
+  KIND_W4A8 = 0, KIND_W4A16 = 1, KIND_W2A8 = 2, KIND_W2A16 = 3, KIND_W8A8 = 4, KIND_F8F8 = 5
+};
+
+// Kinds whose matrix-core sums are float32 (fp16 or FP8 operands); the others
+// sum exactly in int32.
+template <int KIND>
+__host__ __device__ constexpr bool float_acc() {
+  return KIND == KIND_W4A16 || KIND == KIND_W2A16 || KIND == KIND_F8F8;
+}
 
 struct MMParams {
-  const void* A;               // int8 [M,K] (A8) or fp16 [M,K] (A16)
-  const float* a_scale;        // [M] (A8)
+  const void* A;               // int8 or FP8 [M,K] (A8, F8) or fp16 [M,K] (A16)
+  const float* a_scale;        // [M] (A8, F8)
   const uint8_t* Wt;           // prepacked code section
   const uint16_t* St;          // W4A16 scale section
   const uint8_t* Zt;           // W4A16 zero section
-  const float* w_scale;        // W4A8 per-row scales [N]
+  const float* w_scale;        // W4A8, W8A8, F8F8 per-row scales [N]
   const uint16_t* w_scale16;   // W2A8 per-tensor scale [1]
   const uint16_t* bias;        // [N] or NULL
   const float* out_scale;      // [1], W4_OUT_I8 only
@@ -116,6 +125,10 @@ template <>
 struct KindTraits<KIND_W8A8> {
   static constexpr int TILE_K = 64, A_CHUNKS = 1, SHIFT = 0;
 };
+template <>
+struct KindTraits<KIND_F8F8> {  // FP8 bytes in the INT8-weight tile layout
+  static constexpr int TILE_K = 64, A_CHUNKS = 1, SHIFT = 0;
+};
 
 // Epilogue for one output element.
 template <int KIND>
@@ -125,6 +138,14 @@ __device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float
     float v = KIND == KIND_W2A16 ? facc * h2f(p.w_scale16[0]) : facc;
     if (p.bias) v += h2f(p.bias[n]);
     reinterpret_cast<uint16_t*>(p.C)[(size_t)m * p.N + n] = f2h(v);
+  } else if constexpr (KIND == KIND_F8F8) {
+    float v = facc * p.w_scale[n] * sa;
+    if (p.out_dtype == W4_OUT_F32) {
+      reinterpret_cast<float*>(p.C)[(size_t)m * p.N + n] = v;
+    } else {
+      if (p.bias) v += h2f(p.bias[n]);
+      reinterpret_cast<uint16_t*>(p.C)[(size_t)m * p.N + n] = f2h(v);
+    }
   } else {
     const int acc = iacc >> KindTraits<KIND>::SHIFT;  // exact: the sum is a multiple of 2^SHIFT
     if (p.out_dtype == W4_OUT_I32) {
@@ -198,6 +219,17 @@ __device__ __forceinline__ void tile_mma(const u4& w, const u4 (&af)[AC], uint16
     // INT8 weights are the operand as they are
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4, af[0]),
                                                 __builtin_bit_cast(i4, w), acc, 0, 0, 0);
+  } else if constexpr (KIND == KIND_F8F8) {
+    // FP8 bytes as stored: each lane's 16 bytes (the same k positions in both
+    // operands) feed two 32-k products, low and high 8 bytes; the products
+    // are exact and the matrix core sums them in float32
+    const u4 a = af[0];
+    const long a0 = __builtin_bit_cast(long, u2{a[0], a[1]});
+    const long a1 = __builtin_bit_cast(long, u2{a[2], a[3]});
+    const long w0 = __builtin_bit_cast(long, u2{w[0], w[1]});
+    const long w1 = __builtin_bit_cast(long, u2{w[2], w[3]});
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, w0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, w1, acc, 0, 0, 0);
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -245,7 +277,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   // clamped into the row and their fragments zeroed
   constexpr bool KTAIL = KIND != KIND_W4A16;
   constexpr int NTHR = WAVES * 64;
-  typedef typename std::conditional<A16, f4, i4>::type Acc;
+  constexpr bool FACC = float_acc<KIND>();                        // float32 sums
+  typedef typename std::conditional<FACC, f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -527,7 +560,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
         const float v = red[(w * 16 + row) * 16 + col];
-        if constexpr (A16) fs += v;
+        if constexpr (FACC) fs += v;
         else is += __builtin_bit_cast(int, v);
       }
       store_out<KIND>(p, mtile * 16 + row, n, fs, is, row_sa(row));
@@ -546,10 +579,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
       const float v = red[(w * 16 + row) * 16 + col];
-      if constexpr (A16) fs += v;
+      if constexpr (FACC) fs += v;
       else is += __builtin_bit_cast(int, v);
     }
-    dev_store(&part[idx], A16 ? __builtin_bit_cast(uint32_t, fs) : (uint32_t)is);
+    dev_store(&part[idx], FACC ? __builtin_bit_cast(uint32_t, fs) : (uint32_t)is);
   }
   // every wave's partial stores are complete before thread 0 counts the
   // block in; the last block reads the partials at device scope
@@ -569,7 +602,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     int is = 0;
     for (int sp = 0; sp < p.ksplit; ++sp) {
       const uint32_t v = dev_load(&base[(size_t)sp * ngroups * NOUT + idx]);
-      if constexpr (A16) fs += __builtin_bit_cast(float, v);
+      if constexpr (FACC) fs += __builtin_bit_cast(float, v);
       else is += (int)v;
     }
     store_out<KIND>(p, mtile * 16 + row, n, fs, is, row_sa(row));

@@ -42,16 +42,27 @@ struct Plan {
 };
 
 inline int kind_layout(int kind) {
-  // the 2-bit weights serve INT8 and fp16 activations from one prepacked layout
-  return kind == KIND_W4A8    ? W4_LAYOUT_W4A8
-         : kind == KIND_W4A16 ? W4_LAYOUT_W4A16
-         : kind == KIND_W8A8  ? W4_LAYOUT_W8A8
-                              : W4_LAYOUT_W2A8;
+  // the 2-bit weights serve INT8 and fp16 activations from one prepacked
+  // layout; INT8 and FP8 weights share the byte-tile layout
+  switch (kind) {
+    case KIND_W4A8: return W4_LAYOUT_W4A8;
+    case KIND_W4A16: return W4_LAYOUT_W4A16;
+    case KIND_W8A8:
+    case KIND_F8F8: return W4_LAYOUT_W8A8;
+    default: return W4_LAYOUT_W2A8;
+  }
 }
 
+// activation bytes per row per weight tile (the tile's k extent x element size)
 inline int tile_rowb(int kind) {
-  return kind == KIND_W4A16 ? 256 : kind == KIND_W4A8 ? 128 : kind == KIND_W2A16 ? 512
-                                                       : kind == KIND_W8A8  ? 64 : 256;
+  switch (kind) {
+    case KIND_W4A16: return 256;
+    case KIND_W4A8: return 128;
+    case KIND_W2A16: return 512;
+    case KIND_W8A8:
+    case KIND_F8F8: return 64;
+    default: return 256;
+  }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -516,6 +527,32 @@ extern "C" int w8a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* 
   return run<KIND_W8A8>(p, workspace, workspace_bytes, stream);
 }
 
+extern "C" int f8f8_gemm(const uint8_t* Aq, const float* a_scale, const uint8_t* Wp,
+                         const float* w_scale, const uint16_t* bias, void* C, int out_dtype, int M,
+                         int N, int K, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (out_dtype != W4_OUT_F16 && out_dtype != W4_OUT_F32) return W4_ERR_ARG;
+  const int st = check_common(M, N, K, 16);
+  if (st != W4_OK) return st;
+  if (M == 0) return W4_OK;
+  if (!Aq || !a_scale || !Wp || !w_scale || !C) return W4_ERR_NULL;
+  if (!aligned(Aq, 16) || !aligned(Wp, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
+      !out_aligned(C, out_dtype) || (bias && !aligned(bias, 2)))
+    return W4_ERR_ALIGN;
+  MMParams p{};
+  p.A = Aq;
+  p.a_scale = a_scale;
+  p.Wt = Wp;
+  p.w_scale = w_scale;
+  p.bias = out_dtype == W4_OUT_F32 ? nullptr : bias;
+  p.C = C;
+  p.out_dtype = out_dtype;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return run<KIND_F8F8>(p, workspace, workspace_bytes, stream);
+}
+
 // ---------------------------------------------------------------------------
 // plan table: list, name, pin and query the plans a shape may run with
 // ---------------------------------------------------------------------------
@@ -523,7 +560,7 @@ namespace w4 {
 
 // op code -> kind (the op codes equal the kind codes) and the K multiple
 inline int op_check(int op, int M, int N, int K) {
-  if (op < KIND_W4A8 || op > KIND_W8A8) return W4_ERR_ARG;
+  if (op < KIND_W4A8 || op > KIND_F8F8) return W4_ERR_ARG;
   const int st = check_common(M, N, K, op == KIND_W4A16 ? W4_GROUP_SIZE : 16);
   if (st != W4_OK) return st;
   return M < 1 ? W4_ERR_SHAPE : W4_OK;

@@ -251,6 +251,63 @@ __global__ __launch_bounds__(QB) void k_quant_a8(const T* __restrict__ A, int K,
 
 using namespace w4;
 
+// --- per-row FP8 E4M3 (weights per output channel, activations per token) --
+// BitBLAS data-type table, row FP8_E4M3 x FP8_E4M3, in the OCP E4M3 format:
+// bias 7, 3 mantissa bits, subnormals below 2^-6 in steps of 2^-9, largest
+// finite magnitude 448, no infinities. Scale = max|x| / 448 per row, like the
+// INT8 rows' max / 127.
+//
+// Code of a float32 value: round to nearest, ties to even, sign kept (also for
+// zero), magnitude saturated at 448. Normal range: scale the value to [8, 16)
+// by a power of two (exact), round to an integer (8 + mantissa; 16 carries
+// into the next exponent, which the code arithmetic does by itself).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  uint32_t mag;
+  if (a < 0.015625f) {
+    mag = (uint32_t)__builtin_rintf(a * 512.0f);           // 0..8 (8 is 2^-6, code 0x08)
+  } else {
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -6 <= e <= 8
+    const uint32_t m = (uint32_t)__builtin_rintf(ldexpf(a, 3 - e));  // 8..16
+    mag = (uint32_t)(e + 7) * 8u + m - 8u;
+  }
+  return sign | mag;
+}
+
+// One block per row: the row max, then the codes, 8 elements per chunk.
+template <typename T>
+__global__ __launch_bounds__(QB) void k_quant_f8(const T* __restrict__ X, int K,
+                                                  uint8_t* __restrict__ Xq,
+                                                  float* __restrict__ scales) {
+  __shared__ float sh[QB / 64];
+  const int rr = blockIdx.x;
+  const T* row = X + (size_t)rr * K;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < K / 8; c += QB) {
+    float x[8];
+    load8<T>(row + 8 * c, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  }
+  m = block_max(m, sh);
+  const float s = m / 448.0f;
+  if (threadIdx.x == 0) scales[rr] = s;
+  uint8_t* out = Xq + (size_t)rr * K;
+  for (int c = threadIdx.x; c < K / 8; c += QB) {
+    float x[8];
+    load8<T>(row + 8 * c, x);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t q = s > 0.f ? e4m3_code(x[e] / s) : 0u;   // zero row: code 0
+      if (e < 4) lo |= q << (8 * e);
+      else hi |= q << (8 * (e - 4));
+    }
+    *reinterpret_cast<u2*>(out + 8 * c) = u2{lo, hi};
+  }
+}
+
 extern "C" const char* w4_status_string(int status) {
   switch (status) {
     case W4_OK: return "ok";
@@ -294,6 +351,21 @@ extern "C" int quantize_pack_w8(const float* W, int N, int K, int8_t* Wq, float*
   if (N < 1 || K < 16 || K % 16 || K > W4_MAX_K) return W4_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(scales, 4)) return W4_ERR_ALIGN;
   hipLaunchKernelGGL(k_quant_w8_sym, dim3(N), dim3(QB), 0, stream, W, K, Wq, scales);
+  return launch_status();
+}
+
+extern "C" int quantize_f8(const void* X, int in_dtype, int rows, int K, uint8_t* Xq,
+                           float* scales, hipStream_t stream) {
+  if (!X || !Xq || !scales) return W4_ERR_NULL;
+  if (in_dtype != W4_IN_F16 && in_dtype != W4_IN_F32) return W4_ERR_ARG;
+  if (rows < 1 || K < 16 || K % 16 || K > W4_MAX_K) return W4_ERR_SHAPE;
+  if (!aligned(X, 16) || !aligned(Xq, 16) || !aligned(scales, 4)) return W4_ERR_ALIGN;
+  if (in_dtype == W4_IN_F16)
+    hipLaunchKernelGGL(k_quant_f8<uint16_t>, dim3(rows), dim3(QB), 0, stream,
+                       (const uint16_t*)X, K, Xq, scales);
+  else
+    hipLaunchKernelGGL(k_quant_f8<float>, dim3(rows), dim3(QB), 0, stream, (const float*)X, K,
+                       Xq, scales);
   return launch_status();
 }
 

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   constexpr int SSTRIDE = ROWB + 16;                 // padded: conflict-free fragment reads
   constexpr int APER = 16 * ROWB / 16 / SKINNY_THREADS;  // 16-byte staging loads per thread
   static_assert(16 * ROWB % (16 * SKINNY_THREADS) == 0, "staging chunk");
-  typedef typename std::conditional<A16, f4, i4>::type Acc;
+  typedef typename std::conditional<float_acc<KIND>(), f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -142,6 +142,8 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
     const auto v = acc[e];                           // scalar copy before any bit cast
     if constexpr (A16) {
       store_out<KIND>(p, m, n, v, 0, 0.f);
+    } else if constexpr (float_acc<KIND>()) {
+      store_out<KIND>(p, m, n, v, 0, p.a_scale[m]);
     } else {
       store_out<KIND>(p, m, n, 0.f, v, p.a_scale[m]);
     }

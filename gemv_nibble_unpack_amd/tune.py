@@ -28,7 +28,7 @@ from . import api as G
 from . import workloads as WL
 
 OPS = {"w4a8": L.W4_OP_W4A8, "w4a16": L.W4_OP_W4A16, "w2a8": L.W4_OP_W2A8,
-       "w2a16": L.W4_OP_W2A16, "w8a8": L.W4_OP_W8A8}
+       "w2a16": L.W4_OP_W2A16, "w8a8": L.W4_OP_W8A8, "f8f8": L.W4_OP_F8F8}
 OP_NAMES = {v: k for k, v in OPS.items()}
 ROTATE_BYTES = 1 << 30
 
@@ -54,12 +54,19 @@ def _operands(op, M, N, K, device, seed):
         W = torch.from_numpy(WL.weights_f32(N, K, seed=seed + 1)).to(device)
         Wq, scale = G.quantize_pack_w8(W)
         Wp = G.prepack_w(L.W4_LAYOUT_W8A8, Wq, N, K)
+    elif op == L.W4_OP_F8F8:
+        W = torch.from_numpy(WL.weights_f32(N, K, seed=seed + 1)).to(device)
+        Wq, scale = G.quantize_f8(W)
+        Wp = G.prepack_w(L.W4_LAYOUT_W8A8, Wq, N, K)
     else:
         W = torch.from_numpy(WL.weights_f32(N, K, seed=seed + 1)).to(device)
         Wq, scale, _ = G.quantize_pack_w4(W, L.W4_SYM_PER_CHANNEL)
         Wp = G.prepack_w(L.W4_LAYOUT_W4A8, Wq, N, K)
     C = torch.empty((M, N), dtype=torch.float16, device=device)
-    if op in (L.W4_OP_W4A8, L.W4_OP_W2A8, L.W4_OP_W8A8):
+    if op == L.W4_OP_F8F8:
+        Aq, sa = G.quantize_f8(A)
+        call = lambda w, ws: G.f8f8_gemm(Aq, sa, w, scale, N, workspace=ws, C=C)
+    elif op in (L.W4_OP_W4A8, L.W4_OP_W2A8, L.W4_OP_W8A8):
         Aq, sa, _ = G.quantize_a8(A)
         mm = {L.W4_OP_W4A8: G.w4a8_gemm, L.W4_OP_W2A8: G.w2a8_gemm, L.W4_OP_W8A8: G.w8a8_gemm}[op]
         call = lambda w, ws: mm(Aq, sa, w, scale, N, workspace=ws, C=C)

@@ -52,7 +52,7 @@ def ternary_codes(N, K, seed):
 class Case:
     """One (scheme, M, N, K) workload with its seeds."""
     name: str
-    scheme: str          # "w4a8", "w4a16", "w2a8"
+    scheme: str          # "w4a8", "w4a16", "w2a8", "w2a16", "w8a8", "f8f8"
     M: int
     N: int
     K: int
@@ -121,9 +121,14 @@ W2A16_TERNARY = _ternary_a16()
 W8A8_CASES = [Case(f"w8a8_M{M}_N4096_K4096", "w8a8", M, 4096, 4096, seed=900 + M)
               for M in (1, 16, 128)]
 
+# The table's FP8_E4M3 x FP8_E4M3 row (per-row E4M3 quantization of the same
+# float32 weights and fp16 activations) on the 4096 x 4096 projection.
+F8F8_CASES = [Case(f"f8f8_M{M}_N4096_K4096", "f8f8", M, 4096, 4096, seed=950 + M)
+              for M in (1, 16, 128)]
+
 # The example configuration printed on the BitBLAS page (M=1, N=2048,
 # K=1024, fp16 x int4, layout nt, no bias), as an extra small shape.
 BITBLAS_EXAMPLE = Case("w4a16_bitblas_example", "w4a16", 1, 2048, 1024, seed=600)
 
 ALL_CASES = [W4A8_TINY, W4A16_DECODE, *W4A16_SWEEP, W4A8_PREFILL, *W2A8_TERNARY,
-             BITBLAS_EXAMPLE, *W2A16_TERNARY, *W8A8_CASES]
+             BITBLAS_EXAMPLE, *W2A16_TERNARY, *W8A8_CASES, *F8F8_CASES]

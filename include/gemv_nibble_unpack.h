@@ -78,6 +78,7 @@ extern "C" {
 #define W4_OP_W2A8  2         /* w2a8_gemm and w2a8_gemm_fused_act            */
 #define W4_OP_W2A16 3         /* w2a16_gemm                                   */
 #define W4_OP_W8A8  4         /* w8a8_gemm                                    */
+#define W4_OP_F8F8  5         /* f8f8_gemm                                    */
 
 #define W4_GROUP_SIZE 128
 #define W4_MAX_K 131072
@@ -262,6 +263,38 @@ int quantize_pack_w8(const float* W, int N, int K, int8_t* Wq, float* scales,
 int w8a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp, const float* w_scale,
               const uint16_t* bias, const float* out_scale, void* C, int out_dtype, int M, int N,
               int K, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * quantize_f8 -- per-row FP8 E4M3 quantization (BitBLAS page, data-type
+ * table row FP8_E4M3 x FP8_E4M3; the format is the OCP E4M3: bias 7, 3
+ * mantissa bits, subnormals, largest magnitude 448, no infinities). For each
+ * of `rows` rows of X [rows,K] (fp16 with in_dtype W4_IN_F16, float32 with
+ * W4_IN_F32; device, 16-byte aligned): scale = max|x| / 448 (float32),
+ * code = E4M3(x / scale) with a float32 division, rounded to nearest with
+ * ties to the even code, sign kept, saturated at 448; a zero row gets scale
+ * 0 and codes 0. Serves both operands: weights per output channel (then
+ * prepack_w(W4_LAYOUT_W8A8, ...), the INT8 byte-tile layout) and activations
+ * per token. Xq uint8 [rows,K] (16-byte aligned), scales float32 [rows].
+ * K multiple of 16. W4_ERR_ARG for an unknown in_dtype.
+ */
+int quantize_f8(const void* X, int in_dtype, int rows, int K, uint8_t* Xq, float* scales,
+                hipStream_t stream);
+
+/*
+ * f8f8_gemm -- FP8 x FP8 (BitBLAS page, data-type table row FP8_E4M3 x
+ * FP8_E4M3: float32 accumulation, fp16 output):
+ *   C[m,n] = out( a_scale[m] * w_scale[n] * sum_k a[m,k] * w[n,k] + bias[n] )
+ * Aq uint8 [M,K] E4M3 codes and a_scale float32 [M] from quantize_f8; Wp
+ * from prepack_w(W4_LAYOUT_W8A8) of E4M3 weight codes, w_scale float32 [N].
+ * out_dtype W4_OUT_F16 (bias applied) or W4_OUT_F32 (bias ignored). K
+ * multiple of 16. M <= 16 (and small grids) run the decode kernel, more rows
+ * the skinny or 16-row-tile kernels; there is no tiled GEMM for this row.
+ * Workspace: w4_plan_workspace_bytes(W4_OP_F8F8, M, N, K). Errors as
+ * w8a8_gemm.
+ */
+int f8f8_gemm(const uint8_t* Aq, const float* a_scale, const uint8_t* Wp, const float* w_scale,
+              const uint16_t* bias, void* C, int out_dtype, int M, int N, int K, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * w4_fused_act_workspace_bytes -- device workspace w4a8_gemm_fused_act

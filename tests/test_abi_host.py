@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -39,6 +39,7 @@ def test_constants_match_header():
                  "W4_OUT_F16", "W4_OUT_F32", "W4_OUT_I32", "W4_OUT_I8", "W4_IN_F16", "W4_IN_F32",
                  "W4_LAYOUT_W4A8", "W4_LAYOUT_W4A16", "W4_LAYOUT_W2A8", "W4_LAYOUT_W8A8",
                  "W4_OP_W4A8", "W4_OP_W4A16", "W4_OP_W2A8", "W4_OP_W2A16", "W4_OP_W8A8",
+                 "W4_OP_F8F8",
                  "W4_GROUP_SIZE",
                  "W4_MAX_K"]:
         m = re.search(rf"#define\s+{name}\s+(-?\d+)", text)
@@ -124,6 +125,22 @@ def test_error_paths_before_launch():
     assert lib.w8a8_gemm(*a8, None, P, P2, L.W4_OUT_I8, 1, 16, 24, None, 0, s) == L.W4_ERR_SHAPE
     assert lib.w8a8_gemm(None, None, None, None, None, None, None, 0, 0, 16, 32, None, 0,
                          s) == L.W4_OK
+    # FP8: per-row quantizer and the FP8 x FP8 matmul
+    assert lib.quantize_f8(P, 2, 4, 32, P, P2, s) == L.W4_ERR_ARG
+    assert lib.quantize_f8(P, 0, 4, 24, P, P2, s) == L.W4_ERR_SHAPE
+    assert lib.quantize_f8(P, 0, 0, 32, P, P2, s) == L.W4_ERR_SHAPE
+    assert lib.quantize_f8(None, 0, 4, 32, P, P2, s) == L.W4_ERR_NULL
+    assert lib.quantize_f8(MIS, 0, 4, 32, P, P2, s) == L.W4_ERR_ALIGN
+    f8 = (P, P, P, P, None, P2)
+    assert lib.f8f8_gemm(*f8, L.W4_OUT_I32, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
+    assert lib.f8f8_gemm(*f8, L.W4_OUT_F16, 1, 16, 24, None, 0, s) == L.W4_ERR_SHAPE
+    assert lib.f8f8_gemm(None, P, P, P, None, P2, L.W4_OUT_F16, 1, 16, 32, None, 0,
+                         s) == L.W4_ERR_NULL
+    assert lib.f8f8_gemm(MIS, P, P, P, None, P2, L.W4_OUT_F16, 1, 16, 32, None, 0,
+                         s) == L.W4_ERR_ALIGN
+    assert lib.f8f8_gemm(None, None, None, None, None, None, 0, 0, 16, 32, None, 0, s) == L.W4_OK
+    assert lib.f8f8_gemm(*f8, L.W4_OUT_F16, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
+    assert lib.w4_plan_workspace_bytes(L.W4_OP_F8F8, 1, 16, 131072) > 16384
     # the other A8 matmuls have no INT8 output
     assert lib.w4a8_gemm(P, P, P, P, None, P2, L.W4_OUT_I8, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
     # fused activation quantization
@@ -194,7 +211,8 @@ def test_plan_table_pin_and_workspace():
 def test_plan_table_errors():
     lib = G.load()
     buf = ctypes.create_string_buffer(64)
-    assert lib.w4_plan_count(5, 1, 16, 128) == L.W4_ERR_ARG
+    assert lib.w4_plan_count(6, 1, 16, 128) == L.W4_ERR_ARG
+    assert lib.w4_plan_count(L.W4_OP_F8F8, 1, 16, 128) >= 2
     assert lib.w4_plan_count(-1, 1, 16, 128) == L.W4_ERR_ARG
     assert lib.w4_plan_count(L.W4_OP_W4A8, 0, 16, 128) == L.W4_ERR_SHAPE
     assert lib.w4_plan_count(L.W4_OP_W4A8, 1, 16, 24) == L.W4_ERR_SHAPE

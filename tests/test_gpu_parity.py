@@ -572,3 +572,85 @@ def test_w8a8_outputs(g, M, N, K):
     C32f = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_F32))
     tol_ok(C32f[rows, cols], O.dequant_epilogue(acc, ws_ref[cols], sa_ref[rows], None,
                                                 O.OUT_F32), "f32")
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 x FP8 E4M3 (BitBLAS data-type table, last row)
+# ---------------------------------------------------------------------------
+def _e4m3_tie_row(K=2048):
+    """A row whose max is 448 (scale exactly 1, so x / s = x): every midpoint
+    between neighbouring E4M3 magnitudes, its float32 neighbours, the exact
+    grid values, subnormal ties, both signs, and -0.0."""
+    pos = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    vals = [np.float32(448.0), np.float32(-0.0)]
+    for m in mids:
+        vals += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9))]
+    vals += list(pos.astype(np.float32))
+    vals += [-v for v in vals[2:]]
+    row = np.zeros(K, np.float32)
+    row[:len(vals)] = vals[:K]
+    return row
+
+
+@pytest.mark.parametrize("R,K,dt", [(5, 2048, np.float32), (3, 4096, np.float16),
+                                    (300, 528, np.float32), (1, 16, np.float16)])
+def test_quantize_f8_bitexact(g, R, K, dt):
+    say(f"case quantize_f8 R={R} K={K} {dt.__name__}")
+    X = WL.activations(R, K, seed=9800 + R + K, dtype=np.float32)
+    if dt == np.float32:
+        X = X * np.float32(0.02)
+        if K >= 2048:
+            X[0] = _e4m3_tie_row(K)
+    X = X.astype(dt)
+    X[R // 2] = 0
+    Xq, s = g.quantize_f8(dev(X))
+    q_ref, s_ref = O.quantize_f8(X)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(Xq), q_ref)
+
+
+def test_f8_every_code_through_the_matrix_core(g):
+    # one-hot 1.0 rows against every finite code, on either operand: a single
+    # exact product per output, so the float32 result is the code's value
+    say("case f8f8 code table")
+    codes = np.arange(256, dtype=np.uint8)
+    codes[np.isnan(O.e4m3_decode(codes))] = 0
+    ones = np.ones(256, np.float32)
+    eye = np.zeros((256, 256), np.uint8)
+    eye[np.arange(256), np.arange(256)] = 0x38                 # 1.0
+    W = np.tile(codes, (16, 1))                                # every row holds codes 0..255
+    Wp = g.prepack_w(g.W4_LAYOUT_W8A8, dev(W), 16, 256)
+    C = host(g.f8f8_gemm(dev(eye), dev(ones), Wp, dev(ones[:16]), 16, out_dtype=g.W4_OUT_F32))
+    want = O.e4m3_decode(codes).astype(np.float32)
+    assert np.array_equal(C, np.tile(want[:, None], (1, 16)))
+    # codes on the activation side, identity weights
+    A = np.tile(codes, (16, 1))
+    Wp = g.prepack_w(g.W4_LAYOUT_W8A8, dev(eye), 256, 256)
+    C = host(g.f8f8_gemm(dev(A), dev(ones[:16]), Wp, dev(ones), 256, out_dtype=g.W4_OUT_F32))
+    assert np.array_equal(C, np.tile(want[None, :], (16, 1)))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (1, 4096, 4096), (16, 4096, 4096),
+                                   (128, 3200, 3200), (3, 130, 208), (1, 256, 8640),
+                                   (40, 300, 512), (300, 2000, 1040)])
+def test_f8f8_outputs(g, M, N, K):
+    # decode (M <= 16), skinny (M = 128, 300) and 16-row-tile (M = 40)
+    # kernels, ragged tails and a split over K (N = 256, K = 8640)
+    say(f"case f8f8 M={M} N={N} K={K}")
+    A = WL.activations(M, K, seed=9900 + M, dtype=np.float16)
+    W = WL.weights_f32(N, K, seed=9901 + N)
+    bias = WL.bias_f16(N, seed=9902)
+    Wq, ws = g.quantize_f8(dev(W))
+    Wp = g.prepack_w(g.W4_LAYOUT_W8A8, Wq, N, K)
+    Aq, sa = g.quantize_f8(dev(A))
+    qa, sa_ref = O.quantize_f8(A)
+    qw, ws_ref = O.quantize_f8(W)
+    assert np.array_equal(host(Aq), qa) and np.array_equal(host(Wq), qw)
+    rows, cols = sample_indices(M, N, 3000, seed=23)
+    C16 = host(g.f8f8_gemm(Aq, sa, Wp, ws, N, bias=f16(bias), out_dtype=g.W4_OUT_F16))
+    tol_ok(C16[rows, cols], O.f8f8_entries(qa, sa_ref, qw, ws_ref, rows, cols, bias, O.OUT_F16),
+           "f16")
+    C32 = host(g.f8f8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_F32))
+    tol_ok(C32[rows, cols], O.f8f8_entries(qa, sa_ref, qw, ws_ref, rows, cols, None, O.OUT_F32),
+           "f32")

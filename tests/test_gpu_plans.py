@@ -56,7 +56,14 @@ class Shape:
         if a8:
             self.Aq, self.sa, _ = g.quantize_a8(dev(self.A))
             self.qa, self.sa_ref, _ = O.quantize_a8(self.A)
-        if op in (g.W4_OP_W2A8, g.W4_OP_W2A16):
+        if op == g.W4_OP_F8F8:
+            self.Aq, self.sa = g.quantize_f8(dev(self.A))
+            self.qa, self.sa_ref = O.quantize_f8(self.A)
+            W = WL.weights_f32(N, K, seed=seed + 3)
+            Wq, self.scale = g.quantize_f8(dev(W))
+            self.Wp = g.prepack_w(g.W4_LAYOUT_W8A8, Wq, N, K)
+            self.qw, self.sw = O.quantize_f8(W)
+        elif op in (g.W4_OP_W2A8, g.W4_OP_W2A16):
             self.codes = WL.ternary_codes(N, K, seed=seed + 3)
             Wq = g.quantize_pack_w2(dev(self.codes))
             self.Wp = g.prepack_w(g.W4_LAYOUT_W2A8, Wq, N, K)
@@ -91,6 +98,9 @@ class Shape:
         if self.op == g.W4_OP_W2A16:
             return host(g.w2a16_gemm(dev(self.A), self.Wp, self.scale, N, bias=b,
                                      workspace=workspace))
+        if self.op == g.W4_OP_F8F8:
+            return host(g.f8f8_gemm(self.Aq, self.sa, self.Wp, self.scale, N, bias=b,
+                                    out_dtype=out_dtype, workspace=workspace))
         mm = {g.W4_OP_W4A8: g.w4a8_gemm, g.W4_OP_W2A8: g.w2a8_gemm}.get(self.op)
         if mm is None:
             return host(g.w8a8_gemm(self.Aq, self.sa, self.Wp, self.scale, N, bias=b,
@@ -109,6 +119,13 @@ class Shape:
             s = np.float64(host(self.scale)[0])
             ref = O.w2a16_entries(self.A, self.codes, s, r, c, self.bias)
             tol_ok(self.run(g.W4_OUT_F16, bias=True)[r, c], ref, what)
+            return
+        if self.op == g.W4_OP_F8F8:
+            for out, bias in ((O.OUT_F16, self.bias), (O.OUT_F32, None)):
+                ref = O.f8f8_entries(self.qa, self.sa_ref, self.qw, self.sw, r, c, bias, out)
+                got = self.run(g.W4_OUT_F16 if out == O.OUT_F16 else g.W4_OUT_F32,
+                               bias=bias is not None)
+                tol_ok(got[r, c], ref, f"{what} {out}")
             return
         C32 = self.run(g.W4_OUT_I32)
         assert np.array_equal(C32[r, c], self.acc.astype(np.int32)), what
@@ -129,6 +146,7 @@ PLAN_SHAPES = [
     ("w4a16", 16, 4096, 4096), ("w4a16", 33, 1000, 1024),
     ("w2a16", 3, 3200, 8640), ("w2a16", 40, 3000, 2000),
     ("w8a8", 16, 4096, 4096), ("w8a8", 20, 1000, 528),
+    ("f8f8", 16, 4096, 4096), ("f8f8", 20, 1000, 528),
 ]
 
 
