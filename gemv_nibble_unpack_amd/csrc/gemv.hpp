@@ -167,6 +167,21 @@ __device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float
   }
 }
 
+// Fetch the kernel arguments in one batch at kernel entry. Left to itself the
+// compiler loads the pointers only after the shape fields have arrived and
+// been branched on, which puts two dependent kernel-argument fetches (each a
+// scalar-cache miss of several hundred ns) in front of the first weight load
+// of a kernel that lasts a few microseconds. Naming every field as an SGPR
+// operand of one empty asm statement makes all the loads issue together,
+// followed by a single wait.
+__device__ __forceinline__ void fetch_args(const MMParams& p) {
+  asm volatile("" ::"s"(p.A), "s"(p.a_scale), "s"(p.Wt), "s"(p.St), "s"(p.Zt), "s"(p.w_scale),
+               "s"(p.w_scale16), "s"(p.bias), "s"(p.out_scale), "s"(p.C));
+  asm volatile("" ::"s"(p.out_dtype), "s"(p.M), "s"(p.N), "s"(p.K), "s"(p.NT), "s"(p.KT),
+               "s"(p.KQ), "s"(p.ksplit), "s"(p.kts), "s"(p.counters), "s"(p.partials),
+               "s"(gridDim.x));
+}
+
 // v_and_or_b32: (a & b) | c in one VALU op (the compiler splits the
 // expression into two ops).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
@@ -265,10 +280,12 @@ struct AStage {
 // scales for the epilogue. Rows <= 8: the waves split into groups of G waves
 // per row; rows > 8: wave w owns rows w and w + 8. Each lane holds up to FQC
 // 8-element chunks of its rows, loaded before the weight tiles.
-template <int KIND, int WAVES, int MAXT, int APER, bool STAGED, int FQ = 0, int FQC = 1>
+template <int KIND, int WAVES, int MAXT, int APER, bool STAGED, int FQ = 0, int FQC = 1,
+          bool WST = false>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   static_assert(FQ == 0 || (STAGED && (KIND == KIND_W4A8 || KIND == KIND_W2A8) && WAVES == 8),
                 "fused quantization");
+  static_assert(!WST || (STAGED && FQ == 0), "wave staging");
   using AS = AStage<KIND>;
   constexpr bool A16 = KIND == KIND_W4A16 || KIND == KIND_W2A16;  // fp16 activations
   constexpr bool GRP = KIND == KIND_W4A16;                         // group scales and zeros
@@ -281,6 +298,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   typedef typename std::conditional<FACC, f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
+  fetch_args(p);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -346,14 +364,35 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A);
   const size_t arow_bytes = (size_t)p.K * AS::ESZ;
   const size_t kbyte0 = (size_t)kb * AS::TILE_ROWB;
+  // WST: each wave stages only its own k range [wb, wb + per) of the block's
+  // rows, in a region of its own, and is the only reader of it, so no block
+  // barrier stands between a wave's loads and its first products. APER then
+  // counts 16-byte loads per lane of the wave.
+  const int wrowb = per * AS::TILE_ROWB;             // bytes of one row of the wave's range
+  const int wcpr = wrowb / 16;
+  const int wtotal = rows * wcpr;
+  const int wstride = wrowb + 16;
+  const int wreg = WST ? wave * rows * wstride : 0;  // LDS offset of the wave's region
+  const size_t wbyte0 = (size_t)wb * AS::TILE_ROWB;
   u4 stage[APER];
+  if constexpr (WST) {
 #pragma unroll
-  for (int i = 0; i < (STAGED && FQ == 0 ? APER : 0); ++i) {
-    const int c = min(tid + i * NTHR, total - 1);
-    const int row = c / cpr, col = c - row * cpr;
-    size_t off = kbyte0 + (size_t)col * 16;
-    if constexpr (KTAIL) off = min(off, arow_bytes - 16);  // k tail: clamp, zeroed below
-    stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)(mtile * 16 + row) * arow_bytes + off);
+    for (int i = 0; i < APER; ++i) {
+      const int c = min(lane + i * 64, wtotal - 1);
+      const int row = c / wcpr, col = c - row * wcpr;
+      // past the wave's run or past K: clamp into the row, zeroed below
+      const size_t off = min(wbyte0 + (size_t)col * 16, arow_bytes - 16);
+      stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)(mtile * 16 + row) * arow_bytes + off);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < (STAGED && FQ == 0 ? APER : 0); ++i) {
+      const int c = min(tid + i * NTHR, total - 1);
+      const int row = c / cpr, col = c - row * cpr;
+      size_t off = kbyte0 + (size_t)col * 16;
+      if constexpr (KTAIL) off = min(off, arow_bytes - 16);  // k tail: clamp, zeroed below
+      stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)(mtile * 16 + row) * arow_bytes + off);
+    }
   }
 
   // ---- phase 1b: this wave's weight tiles --------------------------------
@@ -482,6 +521,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
         *reinterpret_cast<u4*>(smem + row * sstride + (k1 - k0) + 16 * col) = u4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
+    } else if (WST && pass == 0) {
+      // a wave's LDS accesses complete in issue order: its reads below see
+      // these writes without a barrier
+#pragma unroll
+      for (int i = 0; i < APER; ++i) {
+        const int c = lane + i * 64;
+        if (c < wtotal) {
+          const int row = c / wcpr, col = c - row * wcpr;
+          u4 v = stage[i];
+          if (col * 16 >= nt * AS::TILE_ROWB || wbyte0 + (size_t)col * 16 >= arow_bytes)
+            v = u4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u4*>(smem + wreg + row * wstride + col * 16) = v;
+        }
+      }
     } else if (STAGED && pass == 0) {
 #pragma unroll
       for (int i = 0; i < APER; ++i) {
@@ -499,13 +552,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     }
 
     // ---- phase 3: unpack + matrix-core products, tile by tile ------------
-    const uint8_t* arow = smem + min(r, rows - 1) * sstride;
+    const int aoff = WST ? wreg + min(r, rows - 1) * wstride : min(r, rows - 1) * sstride;
+    const uint8_t* arow = smem + aoff;
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
       u4 af[AC];
       if constexpr (STAGED) {
         if (u >= pn) continue;                       // uniform: tiles past the wave's run
-        const int kl = pb + u - kb;                  // tile index within the staged range
+        const int kl = pb + u - (WST ? wb : kb);     // tile index within the staged range
         const u4* src = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB +
                                                     (AS::TILE_ROWB / 4) * b);
 #pragma unroll

@@ -36,6 +36,8 @@ struct Plan {
   GemmCfg cfg;      // gemm: block shape
   int ngroups;      // skinny: groups of 8 weight n-tiles
   bool staged;      // activation rows staged in LDS
+  bool wst;         // staged per wave (each wave its own k range, no block barrier)
+  int apw;          // wave staging: 16-byte loads per lane
   int ksplit, kts, mtiles, maxt, aper;
   size_t smem;
   size_t counters_bytes, ws_bytes;
@@ -104,7 +106,15 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   const int chunks = ceil_div(rows * P.kts * trb, 16);
   const int aper = ceil_div(chunks, GEMV_THREADS);
   P.aper = aper <= 1 ? 1 : aper <= 2 ? 2 : aper <= 4 ? 4 : 8;
-  P.smem = std::max(P.staged ? (size_t)rows * (P.kts * trb + 16) : 0, (size_t)GEMV_WAVES * 1024);
+  // small per-wave ranges (up to 4 loads per lane) are staged by each wave
+  // for itself: a wave then starts on its first tile without waiting for the
+  // slowest wave of the block
+  const int wchunks = rows * per * trb / 16;
+  P.wst = P.staged && wchunks <= 4 * 64;
+  P.apw = wchunks <= 64 ? 1 : wchunks <= 128 ? 2 : 4;
+  const size_t block_stage = P.staged ? (size_t)rows * (P.kts * trb + 16) : 0;
+  const size_t wave_stage = P.wst ? (size_t)GEMV_WAVES * rows * (per * trb + 16) : 0;
+  P.smem = std::max({block_stage, wave_stage, (size_t)GEMV_WAVES * 1024});
   if (P.ksplit > 1) {
     P.counters_bytes = WS_COUNTERS;
     P.ws_bytes = WS_COUNTERS + (size_t)P.mtiles * P.ksplit * g.NT * 256 * 4;
@@ -224,8 +234,18 @@ int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq =
 #define W4_GEMV_CASE(A, ST)                                                   \
   allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>, P.smem);     \
   hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>), grid, block, P.smem, stream, p)
+#define W4_GEMV_WCASE(A)                                                                  \
+  do {                                                                                    \
+    allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A, true, 0, 1, true>, P.smem); \
+    hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A, true, 0, 1, true>), grid, block, \
+                       P.smem, stream, p);                                                \
+  } while (0)
   if (!P.staged) {
     W4_GEMV_CASE(1, false);
+  } else if (P.wst) {
+    if (P.apw == 1) W4_GEMV_WCASE(1);
+    else if (P.apw == 2) W4_GEMV_WCASE(2);
+    else W4_GEMV_WCASE(4);
   } else {
     switch (P.aper) {
       case 1: W4_GEMV_CASE(1, true); break;
@@ -235,6 +255,7 @@ int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq =
     }
   }
 #undef W4_GEMV_CASE
+#undef W4_GEMV_WCASE
   return launch_status();
 }
 

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   typedef typename std::conditional<float_acc<KIND>(), f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
+  fetch_args(p);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
