@@ -395,6 +395,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     }
   }
 
+  // Loads complete in issue order, so the activation loads (needed before any
+  // product) must be issued before the weight tiles. The empty asm statement
+  // with a memory clobber keeps the compiler from moving them after (left
+  // alone it may, and the wait before their LDS write then waits for every
+  // weight tile too).
+  asm volatile("" ::: "memory");
+
   // ---- phase 1b: this wave's weight tiles --------------------------------
   Acc acc = Acc{};
   for (int pass = 0; pass * MAXT < max(nt, 1); ++pass) {
