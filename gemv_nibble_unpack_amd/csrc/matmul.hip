@@ -83,6 +83,14 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   P.ngroups = ceil_div(g.NT, SKINNY_WAVES);
   if (c.path == PATH_SKINNY) {
     P.skinny = true;
+    // k split: one counter per (row tile, column group)
+    const int ks = c.ks > 1 && P.mtiles * P.ngroups <= WS_COUNTER_SLOTS ? c.ks : 1;
+    P.kts = ceil_div(g.KT, ks);
+    P.ksplit = ceil_div(g.KT, P.kts);
+    if (P.ksplit > 1) {
+      P.counters_bytes = WS_COUNTERS;
+      P.ws_bytes = WS_COUNTERS + (size_t)P.mtiles * P.ksplit * P.ngroups * SKINNY_WAVES * 256 * 4;
+    }
     return P;
   }
   const int rows = M < 16 ? M : 16;
@@ -134,7 +142,7 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   return Candidate{PATH_DECODE, 0, {}};
 }
 
-constexpr int MAX_CANDIDATES = 16;
+constexpr int MAX_CANDIDATES = 32;
 constexpr int CAND_MAX_BLOCKS = 1024;      // decode k splits tried up to this many blocks
 
 // Every plan that may run the shape, in a fixed order: the decode kernel at
@@ -151,7 +159,17 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     last = eff;
     out[n++] = Candidate{PATH_DECODE, ks, {}};
   }
-  out[n++] = Candidate{PATH_SKINNY, 0, {}};
+  // the skinny kernel, whole K and at each distinct k split up to the same
+  // block count
+  const int sblocks = ceil_div(g.NT, SKINNY_WAVES) * ceil_div(M, 16);
+  last = 0;
+  for (int ks = 1; ks <= 64; ks *= 2) {
+    if (ks > 1 && (ceil_div(g.KT, ks) < 2 || sblocks * ks > CAND_MAX_BLOCKS)) break;
+    const int eff = ceil_div(g.KT, ceil_div(g.KT, ks));
+    if (eff == last) continue;
+    last = eff;
+    out[n++] = Candidate{PATH_SKINNY, ks, {}};
+  }
   if (M > 16 && kind == KIND_W4A8) {
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{16, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 2}};
@@ -165,7 +183,7 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
 inline bool same_plan(const Plan& a, const Plan& b) {
   if (a.gemm != b.gemm || a.skinny != b.skinny) return false;
   if (a.gemm) return a.cfg.ntiles == b.cfg.ntiles && a.cfg.wm == b.cfg.wm;
-  return a.skinny || a.ksplit == b.ksplit;
+  return a.ksplit == b.ksplit;
 }
 
 // Plans pinned per shape (w4_plan_pin); a shape without one takes the
@@ -271,11 +289,22 @@ int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream, int fq 
 }
 
 template <int KIND>
-int launch_skinny(const Plan& P, const MMParams& p, hipStream_t stream) {
-  const dim3 grid(ceil_div(P.ngroups * P.mtiles, 8) * 8);
+int launch_skinny(const Plan& P, MMParams p, void* ws, hipStream_t stream) {
+  p.ksplit = P.ksplit;
+  p.kts = P.kts;
+  p.counters = reinterpret_cast<unsigned*>(ws);
+  p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + P.counters_bytes : nullptr;
+  const dim3 grid(ceil_div(P.ngroups * P.mtiles, 8) * 8, P.ksplit);
   const size_t smem = skinny_smem<KIND>();
-  allow_smem((const void*)&k_skinny<KIND, 8>, smem);
-  hipLaunchKernelGGL((k_skinny<KIND, 8>), grid, dim3(SKINNY_THREADS), smem, stream, p, P.ngroups);
+  if (P.ksplit > 1) {
+    allow_smem((const void*)&k_skinny<KIND, 8, true>, smem);
+    hipLaunchKernelGGL((k_skinny<KIND, 8, true>), grid, dim3(SKINNY_THREADS), smem, stream, p,
+                       P.ngroups);
+  } else {
+    allow_smem((const void*)&k_skinny<KIND, 8>, smem);
+    hipLaunchKernelGGL((k_skinny<KIND, 8>), grid, dim3(SKINNY_THREADS), smem, stream, p,
+                       P.ngroups);
+  }
   return launch_status();
 }
 
@@ -291,7 +320,7 @@ int run(MMParams p, void* ws, size_t ws_bytes, hipStream_t stream) {
   p.KT = g.KT;
   p.KQ = g.KQ;
   if (P.gemm) return launch_gemm<KIND>(p, P.cfg, ws, stream);
-  if (P.skinny) return launch_skinny<KIND>(P, p, stream);
+  if (P.skinny) return launch_skinny<KIND>(P, p, ws, stream);
   return launch_gemv<KIND>(P, p, ws, stream);
 }
 
@@ -594,7 +623,8 @@ inline int candidate_name(int kind, const Candidate& c, int M, int N, int K, cha
     // block tile: 64 rows per m wave group, 16 columns per n tile
     n = snprintf(buf, len, "gemm:%dx%d", 64 * c.cfg.wm, 16 * c.cfg.ntiles);
   } else if (c.path == PATH_SKINNY) {
-    n = snprintf(buf, len, "skinny");
+    const int ks = plan_from(kind, M, N, K, c).ksplit;
+    n = ks > 1 ? snprintf(buf, len, "skinny:ksplit=%d", ks) : snprintf(buf, len, "skinny");
   } else {
     n = snprintf(buf, len, "decode:ksplit=%d", plan_from(kind, M, N, K, c).ksplit);
   }

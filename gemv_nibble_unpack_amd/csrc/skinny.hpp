@@ -3,13 +3,20 @@
 // product above 16 rows.
 //
 // Block = 8 waves = one 16-row activation tile x 8 weight n-tiles (128
-// output columns). Wave w owns n-tile w of the group over the whole K, so no
-// cross-wave reduction is needed; the block stages its activation rows in LDS
-// in k chunks of up to 64 KiB that all 8 waves share, which is what the
-// decode kernel (one n-tile per block) cannot do: there every n-tile re-reads
-// the same rows. Per chunk: the activation loads and the first weight loads
-// are issued together, the rows go to LDS behind one barrier, and each wave
-// then streams its weight tiles MAXT at a time through registers.
+// output columns). Wave w owns n-tile w of the group over the block's k
+// range, so no cross-wave reduction is needed; the block stages its
+// activation rows in LDS in k chunks of up to 64 KiB that all 8 waves share,
+// which is what the decode kernel (one n-tile per block) cannot do: there
+// every n-tile re-reads the same rows. Per chunk: the activation loads and the
+// first weight loads are issued together, the rows go to LDS behind one
+// barrier, and each wave then streams its weight tiles MAXT at a time through
+// registers.
+//
+// Split K (grid.y = ksplit > 1): block y covers k tiles [y kts, (y+1) kts),
+// which gives few-column products enough blocks while every block still
+// shares its activation slice across 8 n-tiles. The blocks of a (row tile,
+// column group) publish 16 x 128 partial sums at device scope; the last to
+// arrive adds them in split order and writes the outputs.
 #pragma once
 
 #include "gemv.hpp"
@@ -30,7 +37,9 @@ constexpr size_t skinny_smem() {
   return (size_t)16 * (skinny_chunk_tiles<KIND>() * AStage<KIND>::TILE_ROWB + 16);
 }
 
-template <int KIND, int MAXT>
+// SPLIT selects the k-split instance; without it the kernel covers the whole K
+// with the staging and epilogue of the unsplit kernel exactly.
+template <int KIND, int MAXT, bool SPLIT = false>
 __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int ngroups) {
   using AS = AStage<KIND>;
   constexpr bool A16 = KIND == KIND_W4A16 || KIND == KIND_W2A16;
@@ -63,18 +72,39 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A);
   const size_t arow_bytes = (size_t)p.K * AS::ESZ;
   const int cpr = ROWB / 16;                         // 16-byte chunks per staged row
+  const int kb = SPLIT ? blockIdx.y * p.kts : 0;     // this block's k tiles [kb, ke)
+  const int ke = SPLIT ? min(p.KT, kb + p.kts) : p.KT;
 
   Acc acc = Acc{};
-  for (int kc = 0; kc < p.KT; kc += CT) {
-    const int ct = min(CT, p.KT - kc);               // k tiles in this chunk
+  for (int kc = kb; kc < ke; kc += CT) {
+    const int ct = min(CT, ke - kc);                 // k tiles in this chunk
     const size_t kbyte0 = (size_t)kc * AS::TILE_ROWB;
-    // ---- activation loads of the chunk (rows past M clamp, k past K zero) --
+    // ---- activation loads of the chunk (rows past M clamp, k past K zero):
+    // 16-byte pieces in row-major order, each row padded to a power-of-two
+    // piece count lg2 >= the ct tiles the chunk holds (a full chunk has no
+    // padding; a short k range per block under a k split would otherwise load
+    // and store a full chunk for a fraction of it). Padding slots re-read
+    // piece 0, so that the loads stay unconditional and the wait counts exact.
+    // (the unsplit kernel deals the full chunk's pieces, zeroing those past
+    // the chunk's tiles)
+    const int cw = ct * (AS::TILE_ROWB / 16);        // pieces per row in use
+    const int lg = cw > 1 ? 32 - __builtin_clz((unsigned)(cw - 1)) : 0;
+    const int need = 16 << lg;
+    auto used = [&](int c) { return c < need && (c & ((1 << lg) - 1)) < cw; };
     u4 stage[APER];
 #pragma unroll
     for (int i = 0; i < APER; ++i) {
       const int c = tid + i * SKINNY_THREADS;
-      const int row = c / cpr, col = c - row * cpr;
-      // past K (or past the chunk's last tile): clamp into the row, zeroed below
+      int row, col;
+      if constexpr (SPLIT) {
+        const int cc = used(c) ? c : 0;
+        row = cc >> lg;
+        col = cc & ((1 << lg) - 1);
+      } else {
+        row = c / cpr;
+        col = c - row * cpr;
+      }
+      // past K (or past the chunk's tiles): clamp into the row, zeroed below
       const size_t off = min(kbyte0 + (size_t)col * 16, arow_bytes - 16);
       const int gm = min(mtile * 16 + row, p.M - 1);
       stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)gm * arow_bytes + off);
@@ -107,11 +137,20 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
 #pragma unroll
         for (int i = 0; i < APER; ++i) {
           const int c = tid + i * SKINNY_THREADS;
-          const int row = c / cpr, col = c - row * cpr;
-          u4 v = stage[i];
-          if (kbyte0 + (size_t)col * 16 >= arow_bytes || col * 16 >= ct * AS::TILE_ROWB)
-            v = u4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u4*>(smem + row * SSTRIDE + col * 16) = v;
+          if constexpr (SPLIT) {
+            if (used(c)) {
+              const int row = c >> lg, col = c & ((1 << lg) - 1);
+              u4 v = stage[i];
+              if (kbyte0 + (size_t)col * 16 >= arow_bytes) v = u4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u4*>(smem + row * SSTRIDE + col * 16) = v;
+            }
+          } else {
+            const int row = c / cpr, col = c - row * cpr;
+            u4 v = stage[i];
+            if (kbyte0 + (size_t)col * 16 >= arow_bytes || col * 16 >= ct * AS::TILE_ROWB)
+              v = u4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u4*>(smem + row * SSTRIDE + col * 16) = v;
+          }
         }
         __syncthreads();
       }
@@ -132,23 +171,67 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   }
 
   // ---- epilogue: lane holds output column (lane & 15), rows 4*(lane >> 4)+e
-  if (!live_tile) return;
   const int n = tile * 16 + r;
-  if (n >= p.N) return;
+  if constexpr (!SPLIT) {
+    if (!live_tile || n >= p.N) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * b + e;
+      if (row >= rows) continue;
+      const int m = mtile * 16 + row;
+      const auto v = acc[e];                         // scalar copy before any bit cast
+      if constexpr (A16) {
+        store_out<KIND>(p, m, n, v, 0, 0.f);
+      } else if constexpr (float_acc<KIND>()) {
+        store_out<KIND>(p, m, n, v, 0, p.a_scale[m]);
+      } else {
+        store_out<KIND>(p, m, n, 0.f, v, p.a_scale[m]);
+      }
+    }
+    return;
+  }
+  auto store = [&](int e, float fv, int iv) {
+    const int m = mtile * 16 + 4 * b + e;
+    if constexpr (A16) store_out<KIND>(p, m, n, fv, 0, 0.f);
+    else store_out<KIND>(p, m, n, fv, iv, p.a_scale[m]);
+  };
+
+  // ---- split K: publish this block's 16 x 128 partial sums (every wave, so
+  // that all of them reach the barriers), the last block adds them up
+  constexpr int NPART = 16 * SKINNY_WAVES * 16;
+  const size_t slot = (size_t)mtile * ngroups + grp;
+  uint32_t* part = reinterpret_cast<uint32_t*>(p.partials) +
+                   ((size_t)mtile * p.ksplit + blockIdx.y) * ngroups * NPART + (size_t)grp * NPART;
+  const int pcol = wave * 16 + r;                    // column within the group
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = 4 * b + e;
-    if (row >= rows) continue;
-    const int m = mtile * 16 + row;
-    const auto v = acc[e];                           // scalar copy before any bit cast
-    if constexpr (A16) {
-      store_out<KIND>(p, m, n, v, 0, 0.f);
-    } else if constexpr (float_acc<KIND>()) {
-      store_out<KIND>(p, m, n, v, 0, p.a_scale[m]);
-    } else {
-      store_out<KIND>(p, m, n, 0.f, v, p.a_scale[m]);
+    const auto v = acc[e];
+    dev_store(&part[(4 * b + e) * (SKINNY_WAVES * 16) + pcol], __builtin_bit_cast(uint32_t, v));
+  }
+  __shared__ int last;
+  stores_done();
+  __syncthreads();
+  if (tid == 0) last = dev_arrive(&p.counters[slot]) == (unsigned)(p.ksplit - 1);
+  __syncthreads();
+  if (!last) return;
+  if (live_tile && n < p.N) {
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(p.partials) +
+                           (size_t)mtile * p.ksplit * ngroups * NPART + (size_t)grp * NPART;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (4 * b + e >= rows) continue;
+      float fs = 0.f;
+      int is = 0;
+      for (int z = 0; z < p.ksplit; ++z) {
+        const uint32_t v = dev_load(&base[(size_t)z * ngroups * NPART +
+                                          (4 * b + e) * (SKINNY_WAVES * 16) + pcol]);
+        if constexpr (float_acc<KIND>()) fs += __builtin_bit_cast(float, v);
+        else is += (int)v;
+      }
+      store(e, fs, is);
     }
   }
+  if (tid == 0) dev_store(&p.counters[slot], 0u);   // leave the workspace zeroed
 }
 
 }  // namespace w4

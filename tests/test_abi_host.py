@@ -165,9 +165,12 @@ def _names(lib, op, M, N, K):
 
 def test_plan_table_candidates():
     lib = G.load()
-    # decode shape: the decode kernel at each k split up to 1024 blocks, then skinny
+    # decode shape: the decode and skinny kernels at each k split up to 1024
+    # blocks (256 decode blocks, 32 skinny blocks unsplit; a skinny split keeps
+    # at least 2 of the 32 k tiles)
     assert _names(lib, L.W4_OP_W4A8, 1, 4096, 4096) == [
-        "decode:ksplit=1", "decode:ksplit=2", "decode:ksplit=4", "skinny"]
+        "decode:ksplit=1", "decode:ksplit=2", "decode:ksplit=4", "skinny", "skinny:ksplit=2",
+        "skinny:ksplit=4", "skinny:ksplit=8", "skinny:ksplit=16"]
     # prefill shape: plus the three GEMM block shapes of the INT4 x INT8 kernel
     assert _names(lib, L.W4_OP_W4A8, 2048, 4096, 4096) == [
         "decode:ksplit=1", "skinny", "gemm:128x256", "gemm:128x352", "gemm:256x352"]
