@@ -161,6 +161,27 @@ __device__ __forceinline__ unsigned dev_arrive(unsigned* c) {
 // compiler from moving memory accesses across the wait
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Sum of `count` partial values `stride` apart, read at device scope and
+// added in index order (float32 or int32 bits). The loads are issued 8 at a
+// time before any is added: each is a round trip to the level all XCDs share,
+// and loaded one per loop turn they would be waited for one after another.
+template <bool FLOAT>
+__device__ __forceinline__ void dev_sum(const uint32_t* base, size_t stride, int count, float& fs,
+                                        int& is) {
+  for (int z0 = 0; z0 < count; z0 += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = dev_load(base + (size_t)min(z0 + j, count - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (z0 + j < count) {
+        if constexpr (FLOAT) fs += __builtin_bit_cast(float, v[j]);
+        else is += (int)v[j];
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even

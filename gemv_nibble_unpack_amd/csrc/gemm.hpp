@@ -399,10 +399,13 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
     for (int t = 0; t < NTW; ++t) {
       const int n = nbase + 16 * t;
       i4 sum = i4{0, 0, 0, 0};
-      for (int z = 0; z < gg.ksplit; ++z) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) sum[e] += (int)dev_load(&part[(size_t)z * plane + (size_t)m * p.N + n + e]);
+      for (int e = 0; e < 4; ++e) {
+        if (n + e >= p.N) continue;
+        float unused = 0.f;
+        int s = 0;
+        dev_sum<false>(part + (size_t)m * p.N + n + e, plane, gg.ksplit, unused, s);
+        sum[e] = s;
       }
       f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
       gemm_col_params<KIND, OUT, BIAS>(p, n, ws, bias);

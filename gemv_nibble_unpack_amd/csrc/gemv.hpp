@@ -661,11 +661,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     if (row >= rows || n >= p.N) continue;
     float fs = 0.f;
     int is = 0;
-    for (int sp = 0; sp < p.ksplit; ++sp) {
-      const uint32_t v = dev_load(&base[(size_t)sp * ngroups * NOUT + idx]);
-      if constexpr (FACC) fs += __builtin_bit_cast(float, v);
-      else is += (int)v;
-    }
+    dev_sum<FACC>(base + idx, (size_t)ngroups * NOUT, p.ksplit, fs, is);
     store_out<KIND>(p, mtile * 16 + row, n, fs, is, row_sa(row));
   }
   if (tid == 0) dev_store(&p.counters[slot], 0u);  // leave the workspace zeroed

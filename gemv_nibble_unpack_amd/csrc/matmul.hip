@@ -130,15 +130,33 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   return P;
 }
 
+constexpr size_t REREAD_MAX = 64ull << 20;   // activation bytes the decode kernel may re-read
+constexpr int SKINNY_TILES = 12;             // k tiles per block aimed at by a skinny split
+
 // The built-in choice: the prefill GEMM when it has enough tiles, the skinny
 // kernel when several activation tiles can share staged rows across enough
-// blocks, else the decode kernel with its own k split.
+// blocks, else the decode kernel with its own k split -- unless the decode
+// kernel cannot stage the rows in LDS and its blocks would re-read more than
+// 64 MiB of them from L2 (e.g. 16 fp16 rows at N = 11008, K = 4096, or at
+// N = 4096, K = 11008: 90 MB); then the skinny kernel, which reads them once
+// per 8 n-tiles, runs with a k split that leaves about 12 k tiles per block
+// (W4A16 M=16 on MI355X: 17.2 -> 13.8 us and 21.2 -> 13.8 us).
 inline Candidate heuristic(int kind, int M, int N, int K) {
   if (use_gemm(kind, M, N)) return Candidate{PATH_GEMM, 0, gemm_cfg(kind, M, N)};
   const Geometry g = geometry(kind_layout(kind), N, K);
   const int mtiles = ceil_div(M, 16);
   if (mtiles > 1 && ceil_div(g.NT, SKINNY_WAVES) * mtiles >= SPLIT_BELOW)
     return Candidate{PATH_SKINNY, 0, {}};
+  const int rows = M < 16 ? M : 16;
+  const size_t row_bytes = (size_t)g.KT * tile_rowb(kind);
+  if (mtiles == 1 && (size_t)rows * row_bytes > (size_t)STAGE_MAX &&
+      (size_t)g.NT * rows * row_bytes > REREAD_MAX) {
+    // nearest power of two to KT / 12
+    const float want = (float)g.KT / SKINNY_TILES;
+    int ks = 1;
+    while (ks * 2 <= 64 && (float)(ks * 2) <= want * 1.41421356f) ks *= 2;
+    return Candidate{PATH_SKINNY, ks, {}};
+  }
   return Candidate{PATH_DECODE, 0, {}};
 }
 

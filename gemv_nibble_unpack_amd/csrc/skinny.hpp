@@ -222,12 +222,8 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
       if (4 * b + e >= rows) continue;
       float fs = 0.f;
       int is = 0;
-      for (int z = 0; z < p.ksplit; ++z) {
-        const uint32_t v = dev_load(&base[(size_t)z * ngroups * NPART +
-                                          (4 * b + e) * (SKINNY_WAVES * 16) + pcol]);
-        if constexpr (float_acc<KIND>()) fs += __builtin_bit_cast(float, v);
-        else is += (int)v;
-      }
+      dev_sum<float_acc<KIND>()>(base + (4 * b + e) * (SKINNY_WAVES * 16) + pcol,
+                                 (size_t)ngroups * NPART, p.ksplit, fs, is);
       store(e, fs, is);
     }
   }
