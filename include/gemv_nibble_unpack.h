@@ -169,7 +169,9 @@ int quantize_a8(const void* A, int in_dtype, int M, int K, int8_t* Aq, float* a_
 /* ---- the matmul ------------------------------------------------------------ */
 
 /*
- * w4_workspace_bytes -- device workspace a matmul call needs (0 if none).
+ * w4_workspace_bytes -- device workspace a matmul call needs (0 if none), for
+ * the op that owns the layout (W4A8, W4A16, W2A8, W8A8); w2a16_gemm and
+ * f8f8_gemm share a layout with another op and use w4_plan_workspace_bytes.
  * The workspace must be zero-filled once before its first use; every call
  * leaves the part it relies on zero again, so the same buffer can be reused
  * by later calls on the same stream, whatever their shapes and plans: its
@@ -188,8 +190,10 @@ size_t w4_workspace_bytes(int layout, int M, int N, int K);
  *   W4_OUT_F16: C = fp16(acc * w_scale[n] * a_scale[m] + bias[n]) (fp16[M,N]).
  *   Aq int8[M,K]; a_scale float32[M]; Wp from prepack_w(W4_LAYOUT_W4A8);
  *   w_scale float32[N]; bias fp16[N] or NULL (ignored for W4_OUT_I32).
- *   K multiple of 16. M <= 16 runs the decode GEMV kernel, larger M the
- *   LDS-tiled MFMA GEMM kernel.
+ *   K multiple of 16. Small M runs the decode GEMV kernel (or the skinny
+ *   kernel, when the rows would be re-read too often), large M the LDS-tiled
+ *   MFMA GEMM kernel; the plan table at the end of this header lists and pins
+ *   the choices per shape.
  */
 int w4a8_gemm(const int8_t* Aq, const float* a_scale, const uint8_t* Wp, const float* w_scale,
               const uint16_t* bias, void* C, int out_dtype, int M, int N, int K,
@@ -228,9 +232,9 @@ int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size, const uint1
  *   buffer w2a8_gemm reads; w_scale16 the per-tensor fp16 scale s (device
  *   pointer); bias fp16[N] or NULL; C fp16[M,N]. K multiple of 16. Runs
  *   the decode kernel over 16-row tiles, or the skinny kernel when many
- *   16-row tiles share few columns. Its workspace size is
- *   w4_plan_workspace_bytes(W4_OP_W2A16, M, N, K); while neither op has a
- *   pinned plan that equals w4_workspace_bytes(W4_LAYOUT_W2A8, M, N, K).
+ *   16-row tiles share few columns or the rows would be re-read too often.
+ *   Its workspace size is w4_plan_workspace_bytes(W4_OP_W2A16, M, N, K) (its
+ *   plan can differ from w2a8_gemm's on the same layout).
  */
 int w2a16_gemm(const uint16_t* A, const uint8_t* Wp, const uint16_t* w_scale16,
                const uint16_t* bias, uint16_t* C, int M, int N, int K, void* workspace,
