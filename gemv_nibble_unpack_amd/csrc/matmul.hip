@@ -26,13 +26,15 @@ enum PlanPath { PATH_DECODE = 0, PATH_SKINNY = 1, PATH_GEMM = 2 };
 
 struct Candidate {
   int path;
-  int ks;           // decode: requested k split (0: chosen from the grid size)
+  int ks;           // decode, skinny: requested k split (0: chosen from the grid size)
   GemmCfg cfg;      // gemm: block shape
+  int mt;           // skinny: 16-row activation tiles per block (0 or 1: one, 2: two)
 };
 
 struct Plan {
   bool gemm;        // prefill kernel instead of the decode kernel
   bool skinny;      // > 16 rows without enough GEMM tiles: 16 rows x 128 columns per block
+  int mtb;          // skinny: 16-row activation tiles per block (1 or 2)
   GemmCfg cfg;      // gemm: block shape
   int ngroups;      // skinny: groups of 8 weight n-tiles
   bool staged;      // activation rows staged in LDS
@@ -83,13 +85,16 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   P.ngroups = ceil_div(g.NT, SKINNY_WAVES);
   if (c.path == PATH_SKINNY) {
     P.skinny = true;
+    P.mtb = c.mt == 2 ? 2 : 1;
+    P.mtiles = ceil_div(M, 16 * P.mtb);            // blocks of 16 mtb rows
     // k split: one counter per (row tile, column group)
     const int ks = c.ks > 1 && P.mtiles * P.ngroups <= WS_COUNTER_SLOTS ? c.ks : 1;
     P.kts = ceil_div(g.KT, ks);
     P.ksplit = ceil_div(g.KT, P.kts);
     if (P.ksplit > 1) {
       P.counters_bytes = WS_COUNTERS;
-      P.ws_bytes = WS_COUNTERS + (size_t)P.mtiles * P.ksplit * P.ngroups * SKINNY_WAVES * 256 * 4;
+      P.ws_bytes = WS_COUNTERS + (size_t)P.mtiles * P.ksplit * P.ngroups * SKINNY_WAVES * 256 *
+                                     P.mtb * 4;
     }
     return P;
   }
@@ -131,6 +136,7 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
 }
 
 constexpr size_t REREAD_MAX = 64ull << 20;   // activation bytes the decode kernel may re-read
+constexpr int SKINNY_RESIDENT = 512;         // skinny blocks resident at once (two per CU)
 constexpr int SKINNY_TILES = 12;             // k tiles per block aimed at by a skinny split
 
 // The built-in choice: the prefill GEMM when it has enough tiles, the skinny
@@ -145,8 +151,11 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   if (use_gemm(kind, M, N)) return Candidate{PATH_GEMM, 0, gemm_cfg(kind, M, N)};
   const Geometry g = geometry(kind_layout(kind), N, K);
   const int mtiles = ceil_div(M, 16);
-  if (mtiles > 1 && ceil_div(g.NT, SKINNY_WAVES) * mtiles >= SPLIT_BELOW)
-    return Candidate{PATH_SKINNY, 0, {}};
+  const int ngroups = ceil_div(g.NT, SKINNY_WAVES);
+  // two 16-row tiles per block once one-tile blocks would need more than the
+  // 512 resident at two per CU
+  if (mtiles > 1 && ngroups * mtiles >= SPLIT_BELOW)
+    return Candidate{PATH_SKINNY, 0, {}, ngroups * mtiles > SKINNY_RESIDENT ? 2 : 1};
   const int rows = M < 16 ? M : 16;
   const size_t row_bytes = (size_t)g.KT * tile_rowb(kind);
   if (mtiles == 1 && (size_t)rows * row_bytes > (size_t)STAGE_MAX &&
@@ -177,16 +186,18 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     last = eff;
     out[n++] = Candidate{PATH_DECODE, ks, {}};
   }
-  // the skinny kernel, whole K and at each distinct k split up to the same
-  // block count
-  const int sblocks = ceil_div(g.NT, SKINNY_WAVES) * ceil_div(M, 16);
-  last = 0;
-  for (int ks = 1; ks <= 64; ks *= 2) {
-    if (ks > 1 && (ceil_div(g.KT, ks) < 2 || sblocks * ks > CAND_MAX_BLOCKS)) break;
-    const int eff = ceil_div(g.KT, ceil_div(g.KT, ks));
-    if (eff == last) continue;
-    last = eff;
-    out[n++] = Candidate{PATH_SKINNY, ks, {}};
+  // the skinny kernel (one, and above 16 rows also two, row tiles per block),
+  // whole K and at each distinct k split up to the same block count
+  for (int mt = 1; mt <= (M > 16 ? 2 : 1); ++mt) {
+    const int sblocks = ceil_div(g.NT, SKINNY_WAVES) * ceil_div(M, 16 * mt);
+    last = 0;
+    for (int ks = 1; ks <= 64; ks *= 2) {
+      if (ks > 1 && (ceil_div(g.KT, ks) < 2 || sblocks * ks > CAND_MAX_BLOCKS)) break;
+      const int eff = ceil_div(g.KT, ceil_div(g.KT, ks));
+      if (eff == last) continue;
+      last = eff;
+      out[n++] = Candidate{PATH_SKINNY, ks, {}, mt};
+    }
   }
   if (M > 16 && kind == KIND_W4A8) {
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{16, 2}};
@@ -201,6 +212,7 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
 inline bool same_plan(const Plan& a, const Plan& b) {
   if (a.gemm != b.gemm || a.skinny != b.skinny) return false;
   if (a.gemm) return a.cfg.ntiles == b.cfg.ntiles && a.cfg.wm == b.cfg.wm;
+  if (a.skinny && a.mtb != b.mtb) return false;
   return a.ksplit == b.ksplit;
 }
 
@@ -313,16 +325,21 @@ int launch_skinny(const Plan& P, MMParams p, void* ws, hipStream_t stream) {
   p.counters = reinterpret_cast<unsigned*>(ws);
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + P.counters_bytes : nullptr;
   const dim3 grid(ceil_div(P.ngroups * P.mtiles, 8) * 8, P.ksplit);
-  const size_t smem = skinny_smem<KIND>();
-  if (P.ksplit > 1) {
-    allow_smem((const void*)&k_skinny<KIND, 8, true>, smem);
-    hipLaunchKernelGGL((k_skinny<KIND, 8, true>), grid, dim3(SKINNY_THREADS), smem, stream, p,
-                       P.ngroups);
+#define W4_SKINNY(SPLIT, MTB)                                                               \
+  do {                                                                                      \
+    const size_t smem = skinny_smem<KIND, MTB>();                                           \
+    allow_smem((const void*)&k_skinny<KIND, 8, SPLIT, MTB>, smem);                          \
+    hipLaunchKernelGGL((k_skinny<KIND, 8, SPLIT, MTB>), grid, dim3(SKINNY_THREADS), smem,   \
+                       stream, p, P.ngroups);                                               \
+  } while (0)
+  if (P.mtb == 2) {
+    if (P.ksplit > 1) W4_SKINNY(true, 2);
+    else W4_SKINNY(false, 2);
   } else {
-    allow_smem((const void*)&k_skinny<KIND, 8>, smem);
-    hipLaunchKernelGGL((k_skinny<KIND, 8>), grid, dim3(SKINNY_THREADS), smem, stream, p,
-                       P.ngroups);
+    if (P.ksplit > 1) W4_SKINNY(true, 1);
+    else W4_SKINNY(false, 1);
   }
+#undef W4_SKINNY
   return launch_status();
 }
 
@@ -641,8 +658,11 @@ inline int candidate_name(int kind, const Candidate& c, int M, int N, int K, cha
     // block tile: 64 rows per m wave group, 16 columns per n tile
     n = snprintf(buf, len, "gemm:%dx%d", 64 * c.cfg.wm, 16 * c.cfg.ntiles);
   } else if (c.path == PATH_SKINNY) {
-    const int ks = plan_from(kind, M, N, K, c).ksplit;
-    n = ks > 1 ? snprintf(buf, len, "skinny:ksplit=%d", ks) : snprintf(buf, len, "skinny");
+    const Plan P = plan_from(kind, M, N, K, c);
+    const char* rows = P.mtb == 2 ? ":rows=32" : "";
+    n = P.ksplit > 1 ? snprintf(buf, len, "skinny%s%sksplit=%d", rows, P.mtb == 2 ? "," : ":",
+                                P.ksplit)
+                     : snprintf(buf, len, "skinny%s", rows);
   } else {
     n = snprintf(buf, len, "decode:ksplit=%d", plan_from(kind, M, N, K, c).ksplit);
   }

@@ -27,29 +27,38 @@ constexpr int SKINNY_WAVES = 8;
 constexpr int SKINNY_THREADS = SKINNY_WAVES * 64;
 constexpr int SKINNY_STAGE = 64 * 1024;            // activation bytes per chunk
 
-template <int KIND>
+// MTB 16-row activation tiles per block (1 or 2): the LDS chunk keeps its
+// size, so a two-tile block stages half the k range per chunk.
+template <int KIND, int MTB = 1>
 __host__ __device__ constexpr int skinny_chunk_tiles() {
-  return SKINNY_STAGE / (16 * AStage<KIND>::TILE_ROWB);
+  return SKINNY_STAGE / (16 * MTB * AStage<KIND>::TILE_ROWB);
 }
 
-template <int KIND>
+template <int KIND, int MTB = 1>
 constexpr size_t skinny_smem() {
-  return (size_t)16 * (skinny_chunk_tiles<KIND>() * AStage<KIND>::TILE_ROWB + 16);
+  return (size_t)16 * MTB * (skinny_chunk_tiles<KIND, MTB>() * AStage<KIND>::TILE_ROWB + 16);
 }
 
 // SPLIT selects the k-split instance; without it the kernel covers the whole K
-// with the staging and epilogue of the unsplit kernel exactly.
-template <int KIND, int MAXT, bool SPLIT = false>
+// with the staging and epilogue of the unsplit kernel exactly. MTB = 2 makes
+// each block cover two 16-row activation tiles: every weight tile a wave
+// loads and unpacks then feeds two MFMA chains, which halves the weight
+// traffic and the block count of many-row products (the ternary M = 128
+// layers at N = 8640 would otherwise need 544 blocks, one more round than the
+// 512 that fit at two per CU).
+template <int KIND, int MAXT, bool SPLIT = false, int MTB = 1>
 __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int ngroups) {
   using AS = AStage<KIND>;
   constexpr bool A16 = KIND == KIND_W4A16 || KIND == KIND_W2A16;
   constexpr bool GRP = KIND == KIND_W4A16;
   constexpr int AC = KindTraits<KIND>::A_CHUNKS;
-  constexpr int CT = skinny_chunk_tiles<KIND>();     // k tiles per staged chunk
+  constexpr int RB = 16 * MTB;                       // activation rows per block
+  constexpr int CT = skinny_chunk_tiles<KIND, MTB>();  // k tiles per staged chunk
   constexpr int ROWB = CT * AS::TILE_ROWB;           // staged bytes per row
   constexpr int SSTRIDE = ROWB + 16;                 // padded: conflict-free fragment reads
-  constexpr int APER = 16 * ROWB / 16 / SKINNY_THREADS;  // 16-byte staging loads per thread
-  static_assert(16 * ROWB % (16 * SKINNY_THREADS) == 0, "staging chunk");
+  constexpr int APER = RB * ROWB / 16 / SKINNY_THREADS;  // 16-byte staging loads per thread
+  static_assert(RB * ROWB % (16 * SKINNY_THREADS) == 0, "staging chunk");
+  static_assert(MTB == 1 || MTB == 2, "row tiles per block");
   typedef typename std::conditional<float_acc<KIND>(), f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -58,9 +67,9 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, b = lane >> 4;
-  // block id -> (n group, m tile): consecutive ids of one XCD walk the m tiles
-  // of one n group, so the group's weight tiles stay in that XCD's L2
-  const int mtiles = (p.M + 15) / 16;
+  // block id -> (n group, m block): consecutive ids of one XCD walk the m
+  // blocks of one n group, so the group's weight tiles stay in that XCD's L2
+  const int mtiles = (p.M + RB - 1) / RB;            // blocks of RB rows
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
   const int per_xcd = (int)(gridDim.x >> 3);         // grid is a multiple of 8
   const int seq = xcd * per_xcd + local;
@@ -68,14 +77,16 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   if (local >= per_xcd || grp >= ngroups) return;    // block-uniform
   const int tile = grp * SKINNY_WAVES + wave;        // this wave's n tile
   const bool live_tile = tile < p.NT;                // wave-uniform
-  const int rows = min(16, p.M - mtile * 16);
+  const int rows = min(RB, p.M - mtile * RB);
   const uint8_t* Ab = reinterpret_cast<const uint8_t*>(p.A);
   const size_t arow_bytes = (size_t)p.K * AS::ESZ;
   const int cpr = ROWB / 16;                         // 16-byte chunks per staged row
   const int kb = SPLIT ? blockIdx.y * p.kts : 0;     // this block's k tiles [kb, ke)
   const int ke = SPLIT ? min(p.KT, kb + p.kts) : p.KT;
 
-  Acc acc = Acc{};
+  Acc acc[MTB];
+#pragma unroll
+  for (int j = 0; j < MTB; ++j) acc[j] = Acc{};
   for (int kc = kb; kc < ke; kc += CT) {
     const int ct = min(CT, ke - kc);                 // k tiles in this chunk
     const size_t kbyte0 = (size_t)kc * AS::TILE_ROWB;
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
     // the chunk's tiles)
     const int cw = ct * (AS::TILE_ROWB / 16);        // pieces per row in use
     const int lg = cw > 1 ? 32 - __builtin_clz((unsigned)(cw - 1)) : 0;
-    const int need = 16 << lg;
+    const int need = RB << lg;
     auto used = [&](int c) { return c < need && (c & ((1 << lg) - 1)) < cw; };
     u4 stage[APER];
 #pragma unroll
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
       }
       // past K (or past the chunk's tiles): clamp into the row, zeroed below
       const size_t off = min(kbyte0 + (size_t)col * 16, arow_bytes - 16);
-      const int gm = min(mtile * 16 + row, p.M - 1);
+      const int gm = min(mtile * RB + row, p.M - 1);
       stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)gm * arow_bytes + off);
     }
     for (int pass = 0; pass * MAXT < ct; ++pass) {
@@ -155,17 +166,19 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
         __syncthreads();
       }
       if (!live_tile) continue;                      // wave-uniform: nothing to multiply
-      const uint8_t* arow = smem + r * SSTRIDE;
 #pragma unroll
       for (int u = 0; u < MAXT; ++u) {
         if (u >= pn) continue;                       // uniform
         const int kl = pass * MAXT + u;              // tile index within the chunk
-        const u4* src = reinterpret_cast<const u4*>(arow + kl * AS::TILE_ROWB +
-                                                    (AS::TILE_ROWB / 4) * b);
-        u4 af[AC];
 #pragma unroll
-        for (int j = 0; j < AC; ++j) af[j] = src[j];
-        tile_mma<KIND>(wv[u], af, sv[u], zv[u], acc);
+        for (int t = 0; t < MTB; ++t) {
+          const u4* src = reinterpret_cast<const u4*>(smem + (16 * t + r) * SSTRIDE +
+                                                      kl * AS::TILE_ROWB + (AS::TILE_ROWB / 4) * b);
+          u4 af[AC];
+#pragma unroll
+          for (int j = 0; j < AC; ++j) af[j] = src[j];
+          tile_mma<KIND>(wv[u], af, sv[u], zv[u], acc[t]);
+        }
       }
     }
   }
@@ -175,38 +188,45 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   if constexpr (!SPLIT) {
     if (!live_tile || n >= p.N) return;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * b + e;
-      if (row >= rows) continue;
-      const int m = mtile * 16 + row;
-      const auto v = acc[e];                         // scalar copy before any bit cast
-      if constexpr (A16) {
-        store_out<KIND>(p, m, n, v, 0, 0.f);
-      } else if constexpr (float_acc<KIND>()) {
-        store_out<KIND>(p, m, n, v, 0, p.a_scale[m]);
-      } else {
-        store_out<KIND>(p, m, n, 0.f, v, p.a_scale[m]);
+    for (int t = 0; t < MTB; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * t + 4 * b + e;
+        if (row >= rows) continue;
+        const int m = mtile * RB + row;
+        const auto v = acc[t][e];                    // scalar copy before any bit cast
+        if constexpr (A16) {
+          store_out<KIND>(p, m, n, v, 0, 0.f);
+        } else if constexpr (float_acc<KIND>()) {
+          store_out<KIND>(p, m, n, v, 0, p.a_scale[m]);
+        } else {
+          store_out<KIND>(p, m, n, 0.f, v, p.a_scale[m]);
+        }
       }
     }
     return;
   }
-  auto store = [&](int e, float fv, int iv) {
-    const int m = mtile * 16 + 4 * b + e;
+  auto store = [&](int row, float fv, int iv) {
+    const int m = mtile * RB + row;
     if constexpr (A16) store_out<KIND>(p, m, n, fv, 0, 0.f);
     else store_out<KIND>(p, m, n, fv, iv, p.a_scale[m]);
   };
 
-  // ---- split K: publish this block's 16 x 128 partial sums (every wave, so
+  // ---- split K: publish this block's RB x 128 partial sums (every wave, so
   // that all of them reach the barriers), the last block adds them up
-  constexpr int NPART = 16 * SKINNY_WAVES * 16;
+  constexpr int NPART = RB * SKINNY_WAVES * 16;
   const size_t slot = (size_t)mtile * ngroups + grp;
   uint32_t* part = reinterpret_cast<uint32_t*>(p.partials) +
                    ((size_t)mtile * p.ksplit + blockIdx.y) * ngroups * NPART + (size_t)grp * NPART;
   const int pcol = wave * 16 + r;                    // column within the group
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const auto v = acc[e];
-    dev_store(&part[(4 * b + e) * (SKINNY_WAVES * 16) + pcol], __builtin_bit_cast(uint32_t, v));
+  for (int t = 0; t < MTB; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto v = acc[t][e];
+      dev_store(&part[(16 * t + 4 * b + e) * (SKINNY_WAVES * 16) + pcol],
+                __builtin_bit_cast(uint32_t, v));
+    }
   }
   __shared__ int last;
   stores_done();
@@ -218,13 +238,17 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
     const uint32_t* base = reinterpret_cast<const uint32_t*>(p.partials) +
                            (size_t)mtile * p.ksplit * ngroups * NPART + (size_t)grp * NPART;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (4 * b + e >= rows) continue;
-      float fs = 0.f;
-      int is = 0;
-      dev_sum<float_acc<KIND>()>(base + (4 * b + e) * (SKINNY_WAVES * 16) + pcol,
-                                 (size_t)ngroups * NPART, p.ksplit, fs, is);
-      store(e, fs, is);
+    for (int t = 0; t < MTB; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * t + 4 * b + e;
+        if (row >= rows) continue;
+        float fs = 0.f;
+        int is = 0;
+        dev_sum<float_acc<KIND>()>(base + row * (SKINNY_WAVES * 16) + pcol,
+                                   (size_t)ngroups * NPART, p.ksplit, fs, is);
+        store(row, fs, is);
+      }
     }
   }
   if (tid == 0) dev_store(&p.counters[slot], 0u);   // leave the workspace zeroed

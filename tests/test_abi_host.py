@@ -173,7 +173,14 @@ def test_plan_table_candidates():
         "skinny:ksplit=4", "skinny:ksplit=8", "skinny:ksplit=16"]
     # prefill shape: plus the three GEMM block shapes of the INT4 x INT8 kernel
     assert _names(lib, L.W4_OP_W4A8, 2048, 4096, 4096) == [
-        "decode:ksplit=1", "skinny", "gemm:128x256", "gemm:128x352", "gemm:256x352"]
+        "decode:ksplit=1", "skinny", "skinny:rows=32", "gemm:128x256", "gemm:128x352",
+        "gemm:256x352"]
+    # above 16 rows the skinny kernel also runs with two row tiles per block
+    # (the built-in choice once one-tile blocks exceed the 512 resident)
+    names = _names(lib, L.W4_OP_W2A8, 128, 8640, 3200)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 8640, 3200)] == "skinny:rows=32"
+    names = _names(lib, L.W4_OP_W2A8, 128, 3200, 3200)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 3200, 3200)] == "skinny"
     assert _names(lib, L.W4_OP_W2A8, 128, 3200, 8640)[-1] == "gemm:128x128"
     # fp16 activations and INT8 weights have no GEMM candidate
     for op in (L.W4_OP_W4A16, L.W4_OP_W2A16, L.W4_OP_W8A8):
