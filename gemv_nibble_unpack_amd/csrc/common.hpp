@@ -140,7 +140,6 @@ __device__ __forceinline__ int sym_code_rcp(float w, float s, float rs, float li
   return (int)fminf(fmaxf(q, -lim), lim);
 }
 
-// fp16 bit pattern <-> float
 // Cross-block exchange of split-K partial sums through the workspace, at
 // device scope. A device-scope fence writes back and invalidates the whole
 // L2 of the XCD (costly once per block); instead the partial sums themselves
@@ -153,6 +152,15 @@ __device__ __forceinline__ void dev_store(uint32_t* a, uint32_t v) {
 }
 __device__ __forceinline__ uint32_t dev_load(const uint32_t* a) {
   return __hip_atomic_load(const_cast<uint32_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// the same for two consecutive 32-bit values (8-byte aligned)
+__device__ __forceinline__ void dev_store2(uint32_t* a, uint32_t lo, uint32_t hi) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(a), (uint64_t)lo | ((uint64_t)hi << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t dev_load2(const uint32_t* a) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<uint32_t*>(a)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ unsigned dev_arrive(unsigned* c) {
   return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -182,6 +190,7 @@ __device__ __forceinline__ void dev_sum(const uint32_t* base, size_t stride, int
   }
 }
 
+// fp16 bit pattern <-> float
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even

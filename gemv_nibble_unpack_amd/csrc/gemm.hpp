@@ -74,9 +74,9 @@ struct GemmShape {
   static constexpr bool LDS_PARAMS = BLOCKS_PER_CU * (PARAM_OFF + PARAM_BYTES) <= 160 * 1024;
   static constexpr int LDS = PARAM_OFF + (LDS_PARAMS ? PARAM_BYTES : 0);
   static_assert(BLOCKS_PER_CU * LDS <= 160 * 1024, "LDS exceeds the CU");
-  // the split-K finish holds every accumulator next to its partial sums;
-  // wider blocks would spill, so they are only planned with ksplit == 1
-  static constexpr bool SPLIT_OK = NTILES <= 16;
+  // the split-K finish holds every accumulator next to a batch of the other
+  // splits' sums; wider blocks would spill, so they only run with ksplit == 1
+  static constexpr bool SPLIT_OK = NTILES <= 8;
 };
 
 struct GemmGrid {
@@ -297,8 +297,76 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     sav[i] = OUT == W4_OUT_I32 ? 0.f : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
+  // ---- split K: exact INT32 partial sums through the workspace; the last
+  // block of the tile to arrive adds the other blocks' sums to its own
+  // accumulators and runs the epilogue below. Integer sums do not depend on
+  // the order of the additions, so the result is bit-identical to one pass.
+  // Every block of a tile holds the same outputs in the same registers, so
+  // the sums are kept in register order: word pair q of thread tid of split z
+  // at ((tile * ksplit + z) * Q + q) * THREADS + tid. A wave instruction then
+  // moves 512 contiguous bytes, and rows past M or columns past N need no
+  // test (their sums are never stored to C).
+  if constexpr (S::SPLIT_OK) {
+    if (gg.ksplit > 1) {
+      constexpr int Q = 8 * NTW;                     // 64-bit words per thread
+      uint32_t* tile_part = reinterpret_cast<uint32_t*>(p.partials) +
+                            (size_t)tix * gg.ksplit * Q * S::THREADS * 2;
+      auto word = [&](int z, int q) {
+        return tile_part + ((size_t)(z * Q + q) * S::THREADS + tid) * 2;
+      };
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const int q = (i * NTW + t) * 2;
+          dev_store2(word(kz, q), (uint32_t)acc[i][t][0], (uint32_t)acc[i][t][1]);
+          dev_store2(word(kz, q + 1), (uint32_t)acc[i][t][2], (uint32_t)acc[i][t][3]);
+        }
+      // every wave's stores are complete before thread 0 counts the block in
+      __shared__ int last;
+      stores_done();
+      __syncthreads();
+      if (tid == 0) last = dev_arrive(&p.counters[tix]) == (unsigned)(gg.ksplit - 1);
+      __syncthreads();
+      if (!last) return;
+      if (tid == 0) dev_store(&p.counters[tix], 0u); // every split has counted in
+      // Add the other splits' sums, 32 words per thread at a time: every load
+      // of a batch is issued before any is added, so a batch costs one round
+      // trip to the level all XCDs share.
+      constexpr int IB = 16 / NTW;                   // fragment rows per batch
+      for (int j = 0; j < gg.ksplit - 1; ++j) {
+        const int z = j + (j >= kz);                 // the other splits in order
+#pragma unroll
+        for (int i0 = 0; i0 < 4; i0 += IB) {
+          // keeps the compiler from hoisting later batches' loads (and their
+          // registers) above this batch's additions
+          asm volatile("" ::: "memory");
+          uint64_t lv[IB][NTW][2];
+#pragma unroll
+          for (int ii = 0; ii < IB; ++ii)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+              const int q = ((i0 + ii) * NTW + t) * 2;
+              lv[ii][t][0] = dev_load2(word(z, q));
+              lv[ii][t][1] = dev_load2(word(z, q + 1));
+            }
+#pragma unroll
+          for (int ii = 0; ii < IB; ++ii)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+              i4& a = acc[i0 + ii][t];
+              a[0] += (int)(uint32_t)lv[ii][t][0];
+              a[1] += (int)(uint32_t)(lv[ii][t][0] >> 32);
+              a[2] += (int)(uint32_t)lv[ii][t][1];
+              a[3] += (int)(uint32_t)(lv[ii][t][1] >> 32);
+            }
+        }
+      }
+    }
+  }
+
   if constexpr (OUT == W4_OUT_F16) {
-    if ((!S::SPLIT_OK || gg.ksplit == 1) && (p.N % 8) == 0) {
+    if ((p.N % 8) == 0) {
       // Stage the wave's fp16 tile in LDS, 32 rows x 16*NTW columns per pass,
       // then store whole 16-byte row chunks (a lane group writes a contiguous
       // row segment). The k loop ended with a barrier, so the stages are
@@ -353,67 +421,17 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
       return;
     }
   }
-  if (!S::SPLIT_OK || gg.ksplit == 1) {
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
-      gemm_col_params<KIND, OUT, BIAS>(p, nbase + 16 * t, ws, bias);
+  for (int t = 0; t < NTW; ++t) {
+    f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
+    gemm_col_params<KIND, OUT, BIAS>(p, nbase + 16 * t, ws, bias);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        gemm_store4<KIND, OUT, BIAS>(p, m0 + 64 * wm + 16 * i + r, nbase + 16 * t, acc[i][t], ws,
-                                     bias, sav[i], vec_ok);
-    }
-    return;
+    for (int i = 0; i < 4; ++i)
+      gemm_store4<KIND, OUT, BIAS>(p, m0 + 64 * wm + 16 * i + r, nbase + 16 * t, acc[i][t], ws,
+                                   bias, sav[i], vec_ok);
   }
-
-  // split K: exact INT32 partial sums, the last block of the tile finishes
-  uint32_t* part = reinterpret_cast<uint32_t*>(p.partials);
-  const size_t plane = (size_t)p.M * p.N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 64 * wm + 16 * i + r;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const int n = nbase + 16 * t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = acc[i][t][e];
-        if (n + e < p.N) dev_store(&part[(size_t)kz * plane + (size_t)m * p.N + n + e], (uint32_t)v);
-      }
-    }
-  }
-  // every wave's partial stores are complete before thread 0 counts the
-  // block in; the last block reads the partials at device scope
-  __shared__ int last;
-  stores_done();
-  __syncthreads();
-  if (tid == 0) last = dev_arrive(&p.counters[tix]) == (unsigned)(gg.ksplit - 1);
-  __syncthreads();
-  if (!last) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 64 * wm + 16 * i + r;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const int n = nbase + 16 * t;
-      i4 sum = i4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (n + e >= p.N) continue;
-        float unused = 0.f;
-        int s = 0;
-        dev_sum<false>(part + (size_t)m * p.N + n + e, plane, gg.ksplit, unused, s);
-        sum[e] = s;
-      }
-      f4 ws = f4{0.f, 0.f, 0.f, 0.f}, bias = f4{0.f, 0.f, 0.f, 0.f};
-      gemm_col_params<KIND, OUT, BIAS>(p, n, ws, bias);
-      gemm_store4<KIND, OUT, BIAS>(p, m, n, sum, ws, bias, sav[i], vec_ok);
-    }
-  }
-  if (tid == 0) dev_store(&p.counters[tix], 0u);
 }
+
 
 // ---------------------------------------------------------------------------
 // planning (host)
@@ -422,6 +440,7 @@ constexpr int GEMM_CUS = 256;
 
 struct GemmCfg {
   int ntiles, wm;
+  int ks = 0;       // requested k split (0: chosen from the tile count)
 };
 
 inline int gemm_tiles(int M, int N, GemmCfg c) {
@@ -463,19 +482,25 @@ inline GemmGrid gemm_grid(int kind, int M, int N, int K, GemmCfg c) {
   gg.mblocks = ceil_div(M, 64 * c.wm);
   gg.nblocks = ceil_div(g.NT, c.ntiles);
   gg.tiles = gg.mblocks * gg.nblocks;
+  // K is split only for blocks of up to 8 weight tiles, with one arrival
+  // counter per tile
   int ks = 1;
-  if (c.ntiles <= 16 && gg.tiles <= WS_COUNTER_SLOTS)
-    while (gg.tiles * ks < 256 && ceil_div(g.KT, ks * 2) >= 2) ks *= 2;
+  if (c.ntiles <= 8 && gg.tiles <= WS_COUNTER_SLOTS) {
+    if (c.ks > 0) ks = c.ks;
+    else
+      while (gg.tiles * ks < 256 && ceil_div(g.KT, ks * 2) >= 2) ks *= 2;
+  }
   gg.kts = ceil_div(g.KT, ks);
   gg.ksplit = ceil_div(g.KT, gg.kts);
   gg.per_xcd = ceil_div(gg.tiles, 8);
   return gg;
 }
 
+// counters, then every split's INT32 sums of every block tile
 inline size_t gemm_workspace_bytes(int kind, int M, int N, int K, GemmCfg c) {
   const GemmGrid gg = gemm_grid(kind, M, N, K, c);
   if (gg.ksplit == 1) return 0;
-  return WS_COUNTERS + (size_t)gg.ksplit * M * N * sizeof(int32_t);
+  return WS_COUNTERS + (size_t)gg.tiles * gg.ksplit * (64 * c.wm) * (16 * c.ntiles) * sizeof(int32_t);
 }
 
 template <int KIND, int NTILES, int WM, int OUT, bool BIAS>

@@ -78,6 +78,7 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   if (c.path == PATH_GEMM) {
     P.gemm = true;
     P.cfg = c.cfg;
+    P.ksplit = gemm_grid(kind, M, N, K, c.cfg).ksplit;
     P.ws_bytes = gemm_workspace_bytes(kind, M, N, K, c.cfg);
     return P;
   }
@@ -204,14 +205,24 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 4}};
   } else if (M > 16 && kind == KIND_W2A8) {
-    out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{8, 2}};
+    // 128 x 128 blocks, whole K and at each distinct k split up to the same
+    // block count
+    const int tiles = gemm_tiles(M, N, GemmCfg{8, 2});
+    last = 0;
+    for (int ks = 1; ks <= 64; ks *= 2) {
+      if (ks > 1 && (ceil_div(g.KT, ks) < 2 || tiles * ks > CAND_MAX_BLOCKS)) break;
+      const int eff = gemm_grid(kind, M, N, K, GemmCfg{8, 2, ks}).ksplit;
+      if (eff == last) continue;
+      last = eff;
+      out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{8, 2, ks}};
+    }
   }
   return n;
 }
 
 inline bool same_plan(const Plan& a, const Plan& b) {
   if (a.gemm != b.gemm || a.skinny != b.skinny) return false;
-  if (a.gemm) return a.cfg.ntiles == b.cfg.ntiles && a.cfg.wm == b.cfg.wm;
+  if (a.gemm) return a.cfg.ntiles == b.cfg.ntiles && a.cfg.wm == b.cfg.wm && a.ksplit == b.ksplit;
   if (a.skinny && a.mtb != b.mtb) return false;
   return a.ksplit == b.ksplit;
 }
@@ -656,7 +667,9 @@ inline int candidate_name(int kind, const Candidate& c, int M, int N, int K, cha
   int n;
   if (c.path == PATH_GEMM) {
     // block tile: 64 rows per m wave group, 16 columns per n tile
-    n = snprintf(buf, len, "gemm:%dx%d", 64 * c.cfg.wm, 16 * c.cfg.ntiles);
+    const int ks = gemm_grid(kind, M, N, K, c.cfg).ksplit;
+    n = ks > 1 ? snprintf(buf, len, "gemm:%dx%d,ksplit=%d", 64 * c.cfg.wm, 16 * c.cfg.ntiles, ks)
+               : snprintf(buf, len, "gemm:%dx%d", 64 * c.cfg.wm, 16 * c.cfg.ntiles);
   } else if (c.path == PATH_SKINNY) {
     const Plan P = plan_from(kind, M, N, K, c);
     const char* rows = P.mtb == 2 ? ":rows=32" : "";

@@ -213,19 +213,25 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   };
 
   // ---- split K: publish this block's RB x 128 partial sums (every wave, so
-  // that all of them reach the barriers), the last block adds them up
-  constexpr int NPART = RB * SKINNY_WAVES * 16;
+  // that all of them reach the barriers), the last block adds them up. The
+  // blocks of a (row tile, column group) hold the same outputs in the same
+  // registers, so the sums are kept in register order: word pair q of thread
+  // tid of split z at ((slot * ksplit + z) * Q2 + q) * THREADS + tid, and a
+  // wave instruction moves 512 contiguous bytes.
+  constexpr int Q2 = 2 * MTB;                        // 64-bit words per thread
   const size_t slot = (size_t)mtile * ngroups + grp;
-  uint32_t* part = reinterpret_cast<uint32_t*>(p.partials) +
-                   ((size_t)mtile * p.ksplit + blockIdx.y) * ngroups * NPART + (size_t)grp * NPART;
-  const int pcol = wave * 16 + r;                    // column within the group
+  uint64_t* slot_part = reinterpret_cast<uint64_t*>(p.partials) +
+                        slot * p.ksplit * Q2 * SKINNY_THREADS;
+  auto word = [&](int z, int q) {
+    return reinterpret_cast<uint32_t*>(slot_part + ((size_t)z * Q2 + q) * SKINNY_THREADS + tid);
+  };
 #pragma unroll
   for (int t = 0; t < MTB; ++t) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const auto v = acc[t][e];
-      dev_store(&part[(16 * t + 4 * b + e) * (SKINNY_WAVES * 16) + pcol],
-                __builtin_bit_cast(uint32_t, v));
+    for (int h = 0; h < 2; ++h) {
+      const auto lo = acc[t][2 * h], hi = acc[t][2 * h + 1];
+      dev_store2(word(blockIdx.y, 2 * t + h), __builtin_bit_cast(uint32_t, lo),
+                 __builtin_bit_cast(uint32_t, hi));
     }
   }
   __shared__ int last;
@@ -234,24 +240,44 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   if (tid == 0) last = dev_arrive(&p.counters[slot]) == (unsigned)(p.ksplit - 1);
   __syncthreads();
   if (!last) return;
-  if (live_tile && n < p.N) {
-    const uint32_t* base = reinterpret_cast<const uint32_t*>(p.partials) +
-                           (size_t)mtile * p.ksplit * ngroups * NPART + (size_t)grp * NPART;
+  if (tid == 0) dev_store(&p.counters[slot], 0u);   // every split has counted in
+  if (!live_tile || n >= p.N) return;
+  // Sum every split's value in split order (float sums then do not depend on
+  // which block finishes), 8 splits per batch: every load of a batch is issued
+  // before any is added, so a batch costs one round trip to the level all
+  // XCDs share.
+  float fs[MTB][4] = {};
+  int is[MTB][4] = {};
+  for (int z0 = 0; z0 < p.ksplit; z0 += 8) {
+    // keeps the compiler from hoisting the next batch's loads (and their
+    // registers) above this batch's additions
+    asm volatile("" ::: "memory");
+    uint64_t v[8][Q2];
 #pragma unroll
-    for (int t = 0; t < MTB; ++t) {
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * t + 4 * b + e;
-        if (row >= rows) continue;
-        float fs = 0.f;
-        int is = 0;
-        dev_sum<float_acc<KIND>()>(base + row * (SKINNY_WAVES * 16) + pcol,
-                                   (size_t)ngroups * NPART, p.ksplit, fs, is);
-        store(row, fs, is);
-      }
+      for (int q = 0; q < Q2; ++q) v[j][q] = dev_load2(word(min(z0 + j, p.ksplit - 1), q));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (z0 + j >= p.ksplit) break;
+#pragma unroll
+      for (int t = 0; t < MTB; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t bits = (uint32_t)(v[j][2 * t + e / 2] >> (32 * (e & 1)));
+          if constexpr (float_acc<KIND>()) fs[t][e] += __builtin_bit_cast(float, bits);
+          else is[t][e] += (int)bits;
+        }
     }
   }
-  if (tid == 0) dev_store(&p.counters[slot], 0u);   // leave the workspace zeroed
+#pragma unroll
+  for (int t = 0; t < MTB; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * t + 4 * b + e;
+      if (row < rows) store(row, fs[t][e], is[t][e]);
+    }
+  }
 }
 
 }  // namespace w4

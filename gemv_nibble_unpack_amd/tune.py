@@ -175,9 +175,15 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--out", default=None, help="write the tuned table here (JSON)")
     ap.add_argument("--reps", type=int, default=50)
+    ap.add_argument("--scheme", action="append", default=None, choices=sorted(OPS),
+                    help="tune only the shapes of this weight/activation scheme (repeatable)")
+    ap.add_argument("--min-m", type=int, default=1, help="tune only shapes with M >= this")
     args = ap.parse_args(argv)
+    want = {OPS[k] for k in args.scheme} if args.scheme else None
     table = []
     for op, M, N, K in workload_shapes():
+        if (want is not None and op not in want) or M < args.min_m:
+            continue
         G.w4_plan_pin(op, M, N, K, -1)
         builtin = candidates(op, M, N, K)[G.w4_plan_current(op, M, N, K)]
         rec = tune_shape(op, M, N, K, reps=args.reps)

@@ -340,7 +340,8 @@ int w2a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
  *
  * Every matmul call runs one of several plans that compute the same result:
  * the decode kernel or the skinny kernel, each at one of its k splits, or
- * (INT8 activations, M > 16) the tiled GEMM at one of its block shapes. Without a
+ * (INT8 activations, M > 16) the tiled GEMM at one of its block shapes (the
+ * ternary 128 x 128 block also at each of its k splits). Without a
  * pin the library picks one from the shape (built-in choice). A caller that
  * has timed the candidates (the Python package's tune module does) pins the
  * fastest per (op, M, N, K); every later call of that op and shape, on any
@@ -363,9 +364,11 @@ int w2a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
 int w4_plan_count(int op, int M, int N, int K);
 
 /* Writes the name of candidate `index` (NUL-terminated, at most len bytes,
- * host memory) to buf: "decode:ksplit=S", "skinny", "skinny:ksplit=S" or
- * "gemm:RxC" (R rows x C columns per block). W4_ERR_NULL for buf NULL; W4_ERR_ARG for an index out
- * of range or a buffer too small. */
+ * host memory) to buf: "decode:ksplit=S", "skinny", "skinny:ksplit=S",
+ * "skinny:rows=32", "skinny:rows=32,ksplit=S", "gemm:RxC" or
+ * "gemm:RxC,ksplit=S" (R rows x C columns per block, K split S ways).
+ * W4_ERR_NULL for buf NULL; W4_ERR_ARG for an index out of range or a buffer
+ * too small. */
 int w4_plan_name(int op, int M, int N, int K, int index, char* buf, size_t len);
 
 /* Pins candidate `index` for the shape; index -1 removes the shape's pin. */

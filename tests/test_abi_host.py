@@ -181,7 +181,17 @@ def test_plan_table_candidates():
     assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 8640, 3200)] == "skinny:rows=32"
     names = _names(lib, L.W4_OP_W2A8, 128, 3200, 3200)
     assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 3200, 3200)] == "skinny"
-    assert _names(lib, L.W4_OP_W2A8, 128, 3200, 8640)[-1] == "gemm:128x128"
+    # ternary weights above 16 rows: the 128 x 128 GEMM blocks, whole K and at
+    # each distinct k split up to 1024 blocks (25 tiles, 34 k tiles)
+    assert [n for n in _names(lib, L.W4_OP_W2A8, 128, 3200, 8640) if n.startswith("gemm")] == [
+        "gemm:128x128"] + [f"gemm:128x128,ksplit={s}" for s in (2, 4, 7, 12, 17)]
+    # splits are planned for blocks of up to 8 weight tiles only: the INT4
+    # GEMM shapes always run over the whole K
+    names = _names(lib, L.W4_OP_W4A8, 1100, 4004, 512)
+    assert names[lib.w4_plan_current(L.W4_OP_W4A8, 1100, 4004, 512)] == "gemm:128x256"
+    assert lib.w4_plan_workspace_bytes(L.W4_OP_W4A8, 1100, 4004, 512) == 0
+    names = _names(lib, L.W4_OP_W2A8, 1100, 2000, 1024)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 1100, 2000, 1024)] == "gemm:128x128,ksplit=2"
     # fp16 activations and INT8 weights have no GEMM candidate
     for op in (L.W4_OP_W4A16, L.W4_OP_W2A16, L.W4_OP_W8A8):
         assert not any(n.startswith("gemm") for n in _names(lib, op, 2048, 4096, 4096))

@@ -143,6 +143,9 @@ class Shape:
 PLAN_SHAPES = [
     ("w4a8", 1, 4096, 4096), ("w4a8", 37, 1000, 1040), ("w4a8", 130, 4100, 528),
     ("w2a8", 1, 16, 131072), ("w2a8", 70, 3000, 2000),
+    # split GEMM finishes over column pairs with a ragged pair (N % 4 == 2)
+    # and over single columns (odd N), with rows past M in the last block
+    ("w2a8", 130, 1002, 1024), ("w2a8", 100, 1001, 768),
     ("w4a16", 16, 4096, 4096), ("w4a16", 33, 1000, 1024),
     ("w2a16", 3, 3200, 8640), ("w2a16", 40, 3000, 2000),
     ("w8a8", 16, 4096, 4096), ("w8a8", 20, 1000, 528),
@@ -158,6 +161,8 @@ def test_every_plan_matches_oracle(g, name, M, N, K):
     s = Shape(g, op, M, N, K, seed=12000 + M + N)
     n = g.w4_plan_count(op, M, N, K)
     assert n >= 2
+    exact = op in (g.W4_OP_W4A8, g.W4_OP_W2A8, g.W4_OP_W8A8)
+    first = None
     try:
         for i in range(n):
             plan = g.w4_plan_name(op, M, N, K, i)
@@ -165,6 +170,14 @@ def test_every_plan_matches_oracle(g, name, M, N, K):
             g.w4_plan_pin(op, M, N, K, i)
             assert g.w4_plan_current(op, M, N, K) == i
             s.check(f"{name} {M}x{N}x{K} {plan}")
+            if exact:
+                # integer sums do not depend on how K is split: every plan
+                # gives the whole INT32 output bit for bit
+                full = s.run(g.W4_OUT_I32)
+                if first is None:
+                    first = full
+                else:
+                    assert np.array_equal(full, first), plan
     finally:
         g.w4_plan_pin(op, M, N, K, -1)
 
@@ -176,11 +189,11 @@ def test_one_workspace_for_any_mix_of_shapes_and_plans(g):
     # result on a fresh workspace, bit for bit.
     say("case shared workspace: decode split 64, gemm split, decode split 4")
     cases = [Shape(g, g.W4_OP_W2A8, 1, 16, 131072, seed=13000),
-             Shape(g, g.W4_OP_W4A8, 1100, 4004, 512, seed=13100),
+             Shape(g, g.W4_OP_W2A8, 1100, 2000, 1024, seed=13100),
              Shape(g, g.W4_OP_W4A8, 1, 4096, 4096, seed=13200)]
     names = [g.w4_plan_name(c.op, c.M, c.N, c.K, g.w4_plan_current(c.op, c.M, c.N, c.K))
              for c in cases[:2]]
-    assert names == ["decode:ksplit=64", "gemm:128x256"]
+    assert names == ["decode:ksplit=64", "gemm:128x128,ksplit=2"]
     try:
         g.w4_plan_pin(g.W4_OP_W4A8, 1, 4096, 4096, 2)
         assert g.w4_plan_name(g.W4_OP_W4A8, 1, 4096, 4096, 2) == "decode:ksplit=4"
