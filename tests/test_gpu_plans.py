@@ -232,3 +232,27 @@ def test_tuner_pins_a_candidate_and_results_hold(g, tmp_path):
         assert names[g.w4_plan_current(op, M, N, K)] == rec["plan"]
     finally:
         g.w4_plan_reset()
+
+
+@pytest.mark.parametrize("name,M,N,K,plan", [
+    ("w4a16", 16, 1024, 4096, "skinny:ksplit=4"),
+    ("w2a16", 40, 1000, 2048, "skinny:rows=32,ksplit=4"),
+    ("w4a16", 1, 512, 8192, "decode:ksplit=4"),
+])
+def test_float_split_sums_do_not_depend_on_arrival_order(g, name, M, N, K, plan):
+    # fp32 partial sums of a k split are added in split order by whichever
+    # block of the tile arrives last, so repeated calls give the same fp16
+    # bits (and match the oracle like any plan)
+    op = getattr(g, "W4_OP_" + name.upper())
+    s = Shape(g, op, M, N, K, seed=14000 + M)
+    names = [g.w4_plan_name(op, M, N, K, i) for i in range(g.w4_plan_count(op, M, N, K))]
+    assert plan in names
+    say(f"case repeat {name} M={M} N={N} K={K} {plan}")
+    try:
+        g.w4_plan_pin(op, M, N, K, names.index(plan))
+        outs = [s.run(g.W4_OUT_F16, bias=True) for _ in range(4)]
+        for o in outs[1:]:
+            assert np.array_equal(o.view(np.uint16), outs[0].view(np.uint16))
+        s.check(f"{name} {M}x{N}x{K} {plan}")
+    finally:
+        g.w4_plan_pin(op, M, N, K, -1)
