@@ -15,10 +15,9 @@
 
 namespace w4 {
 
-constexpr int GEMV_WAVES = 8;
-constexpr int GEMV_THREADS = GEMV_WAVES * 64;
+constexpr int GEMV_WAVES = 8;             // decode block: 8 waves, or 16 for long k runs
 constexpr int SPLIT_BELOW = 64;            // blocks below which K is split
-constexpr int STAGE_MAX = 8 * 16 * GEMV_THREADS;  // activation bytes one block may stage
+constexpr int STAGE_MAX = 64 * 1024;       // activation bytes one block may stage
 
 // The three ways a product can run. Every candidate computes the same
 // result; they differ in how the work is cut into blocks.
@@ -29,6 +28,7 @@ struct Candidate {
   int ks;           // decode, skinny: requested k split (0: chosen from the grid size)
   GemmCfg cfg;      // gemm: block shape
   int mt;           // skinny: 16-row activation tiles per block (0 or 1: one, 2: two)
+  int waves;        // decode: waves per block (0 or 8: eight, 16: sixteen)
 };
 
 struct Plan {
@@ -41,6 +41,7 @@ struct Plan {
   bool wst;         // staged per wave (each wave its own k range, no block barrier)
   int apw;          // wave staging: 16-byte loads per lane
   int ksplit, kts, mtiles, maxt, aper;
+  int waves;        // decode: waves per block (8, or 16 with wave staging)
   size_t smem;
   size_t counters_bytes, ws_bytes;
 };
@@ -102,33 +103,39 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   const int rows = M < 16 ? M : 16;
   const int blocks = g.NT * P.mtiles;
   const int trb = tile_rowb(kind);
+  const int W = c.waves == 16 ? 16 : GEMV_WAVES;
+  P.waves = W;
   int ks = g.NT * P.mtiles <= WS_COUNTER_SLOTS ? c.ks : 1;  // one counter per block slot
   if (ks <= 0) {
     // split K across blocks only when the grid would leave most CUs idle,
     // keeping a tile per wave (larger grids gain little or lose from the
     // partial-sum round trip; the plan table can pin a split per shape)
     ks = 1;
-    while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= GEMV_WAVES) ks *= 2;
+    while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= W) ks *= 2;
   }
   P.kts = ceil_div(g.KT, ks);
   P.ksplit = ceil_div(g.KT, P.kts);
-  const int per = ceil_div(P.kts, GEMV_WAVES);
-  P.maxt = per <= 4 ? 4 : per <= 8 ? 8 : 16;
+  const int per = ceil_div(P.kts, W);
+  P.maxt = per <= 2 && W == 16 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
   // stage the block's activation rows in LDS when they fit, else each lane
   // streams its own fragments from L2
   P.staged = (size_t)rows * P.kts * trb <= (size_t)STAGE_MAX;
   const int chunks = ceil_div(rows * P.kts * trb, 16);
-  const int aper = ceil_div(chunks, GEMV_THREADS);
+  const int aper = ceil_div(chunks, W * 64);
   P.aper = aper <= 1 ? 1 : aper <= 2 ? 2 : aper <= 4 ? 4 : 8;
   // small per-wave ranges (up to 4 loads per lane) are staged by each wave
   // for itself: a wave then starts on its first tile without waiting for the
   // slowest wave of the block
   const int wchunks = rows * per * trb / 16;
   P.wst = P.staged && wchunks <= 4 * 64;
+  // sixteen waves run only with wave staging and up to 8 tiles per wave;
+  // otherwise the plan is the eight-wave one
+  if (W == 16 && (!P.wst || per > 8))
+    return plan_from(kind, M, N, K, Candidate{PATH_DECODE, c.ks, {}, 0, 8});
   P.apw = wchunks <= 64 ? 1 : wchunks <= 128 ? 2 : 4;
   const size_t block_stage = P.staged ? (size_t)rows * (P.kts * trb + 16) : 0;
-  const size_t wave_stage = P.wst ? (size_t)GEMV_WAVES * rows * (per * trb + 16) : 0;
-  P.smem = std::max({block_stage, wave_stage, (size_t)GEMV_WAVES * 1024});
+  const size_t wave_stage = P.wst ? (size_t)W * rows * (per * trb + 16) : 0;
+  P.smem = std::max({block_stage, wave_stage, (size_t)W * 1024});
   if (P.ksplit > 1) {
     P.counters_bytes = WS_COUNTERS;
     P.ws_bytes = WS_COUNTERS + (size_t)P.mtiles * P.ksplit * g.NT * 256 * 4;
@@ -167,10 +174,20 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
     while (ks * 2 <= 64 && (float)(ks * 2) <= want * 1.41421356f) ks *= 2;
     return Candidate{PATH_SKINNY, ks, {}};
   }
+  // long activation rows (K >= 8192) over one block per CU at most and
+  // enough blocks not to split K: sixteen waves, each staging and streaming
+  // half as long a k run (M=1 on MI355X:
+  // W4A16 N=4096 K=11008 9.46 -> 8.63 us, W2A16 N=3200 K=8640 6.18 -> 5.53,
+  // W2A8 N=3200 K=8640 4.54 -> 4.34; at K <= 4096, or with more blocks, the
+  // eight-wave block is as fast or faster)
+  const Candidate wide{PATH_DECODE, 0, {}, 0, 16};
+  if (mtiles == 1 && K >= 8192 && g.NT >= SPLIT_BELOW && g.NT <= 256 &&
+      plan_from(kind, M, N, K, wide).waves == 16)
+    return wide;
   return Candidate{PATH_DECODE, 0, {}};
 }
 
-constexpr int MAX_CANDIDATES = 32;
+constexpr int MAX_CANDIDATES = 64;
 constexpr int CAND_MAX_BLOCKS = 1024;      // decode k splits tried up to this many blocks
 
 // Every plan that may run the shape, in a fixed order: the decode kernel at
@@ -186,6 +203,9 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     if (eff == last) continue;
     last = eff;
     out[n++] = Candidate{PATH_DECODE, ks, {}};
+    // the same split with sixteen waves per block, where that plan exists
+    const Candidate wide{PATH_DECODE, ks, {}, 0, 16};
+    if (plan_from(kind, M, N, K, wide).waves == 16) out[n++] = wide;
   }
   // the skinny kernel (one, and above 16 rows also two, row tiles per block),
   // whole K and at each distinct k split up to the same block count
@@ -224,6 +244,7 @@ inline bool same_plan(const Plan& a, const Plan& b) {
   if (a.gemm != b.gemm || a.skinny != b.skinny) return false;
   if (a.gemm) return a.cfg.ntiles == b.cfg.ntiles && a.cfg.wm == b.cfg.wm && a.ksplit == b.ksplit;
   if (a.skinny && a.mtb != b.mtb) return false;
+  if (!a.skinny && a.waves != b.waves) return false;
   return a.ksplit == b.ksplit;
 }
 
@@ -267,55 +288,65 @@ inline int fq_slots(int rows, int K) {
   return need <= 2 ? 2 : need <= 8 ? 8 : 0;
 }
 
-template <int KIND, int MAXT>
+template <int KIND, int WAVES, int MAXT>
 int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq = 0, int fqc = 0) {
   // x enumerates (n tile, m tile) pairs so that the m tiles of one n tile land
   // on the same XCD (blocks are dealt to the 8 XCDs round-robin by id)
   const int nblk = P.mtiles == 1 ? p.NT : ceil_div(p.NT * P.mtiles, 8) * 8;
   const dim3 grid(nblk, P.ksplit, 1);
-  const dim3 block(GEMV_THREADS);
-#define W4_GEMV_FQ(F, C)                                                                  \
-  do {                                                                                    \
-    allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, 1, true, F, C>, P.smem);      \
-    hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, 1, true, F, C>), grid, block,      \
-                       P.smem, stream, p);                                                \
+  const dim3 block(WAVES * 64);
+#define W4_GEMV_WCASE(A)                                                              \
+  do {                                                                                \
+    allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, A, true, 0, 1, true>, P.smem);  \
+    hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, A, true, 0, 1, true>), grid, block,  \
+                       P.smem, stream, p);                                            \
   } while (0)
-  if constexpr (KIND == KIND_W4A8 || KIND == KIND_W2A8) {
-    if (fq) {
-      if (fq == 1 && fqc == 2) W4_GEMV_FQ(1, 2);
-      else if (fq == 1) W4_GEMV_FQ(1, 8);
-      else if (fqc == 2) W4_GEMV_FQ(2, 2);
-      else W4_GEMV_FQ(2, 8);
-      return launch_status();
-    }
-  }
-#undef W4_GEMV_FQ
-#define W4_GEMV_CASE(A, ST)                                                   \
-  allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>, P.smem);     \
-  hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A, ST>), grid, block, P.smem, stream, p)
-#define W4_GEMV_WCASE(A)                                                                  \
-  do {                                                                                    \
-    allow_smem((const void*)&k_gemv<KIND, GEMV_WAVES, MAXT, A, true, 0, 1, true>, P.smem); \
-    hipLaunchKernelGGL((k_gemv<KIND, GEMV_WAVES, MAXT, A, true, 0, 1, true>), grid, block, \
-                       P.smem, stream, p);                                                \
-  } while (0)
-  if (!P.staged) {
-    W4_GEMV_CASE(1, false);
-  } else if (P.wst) {
+  if constexpr (WAVES == 16) {
+    // sixteen-wave plans always stage per wave and never quantize in the
+    // prologue (the planner guarantees both)
+    if (fq || !P.wst) return W4_ERR_ARG;
     if (P.apw == 1) W4_GEMV_WCASE(1);
     else if (P.apw == 2) W4_GEMV_WCASE(2);
     else W4_GEMV_WCASE(4);
+    return launch_status();
   } else {
-    switch (P.aper) {
-      case 1: W4_GEMV_CASE(1, true); break;
-      case 2: W4_GEMV_CASE(2, true); break;
-      case 4: W4_GEMV_CASE(4, true); break;
-      default: W4_GEMV_CASE(8, true); break;
+#define W4_GEMV_FQ(F, C)                                                              \
+  do {                                                                                \
+    allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, 1, true, F, C>, P.smem);        \
+    hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, 1, true, F, C>), grid, block,        \
+                       P.smem, stream, p);                                            \
+  } while (0)
+    if constexpr (KIND == KIND_W4A8 || KIND == KIND_W2A8) {
+      if (fq) {
+        if (fq == 1 && fqc == 2) W4_GEMV_FQ(1, 2);
+        else if (fq == 1) W4_GEMV_FQ(1, 8);
+        else if (fqc == 2) W4_GEMV_FQ(2, 2);
+        else W4_GEMV_FQ(2, 8);
+        return launch_status();
+      }
     }
-  }
+#undef W4_GEMV_FQ
+#define W4_GEMV_CASE(A, ST)                                                 \
+  allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, A, ST>, P.smem);        \
+  hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, A, ST>), grid, block, P.smem, stream, p)
+    if (!P.staged) {
+      W4_GEMV_CASE(1, false);
+    } else if (P.wst) {
+      if (P.apw == 1) W4_GEMV_WCASE(1);
+      else if (P.apw == 2) W4_GEMV_WCASE(2);
+      else W4_GEMV_WCASE(4);
+    } else {
+      switch (P.aper) {
+        case 1: W4_GEMV_CASE(1, true); break;
+        case 2: W4_GEMV_CASE(2, true); break;
+        case 4: W4_GEMV_CASE(4, true); break;
+        default: W4_GEMV_CASE(8, true); break;
+      }
+    }
 #undef W4_GEMV_CASE
+    return launch_status();
+  }
 #undef W4_GEMV_WCASE
-  return launch_status();
 }
 
 template <int KIND>
@@ -324,9 +355,14 @@ int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream, int fq 
   p.kts = P.kts;
   p.counters = reinterpret_cast<unsigned*>(ws);
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + P.counters_bytes : nullptr;
-  if (P.maxt == 4) return launch_gemv_m<KIND, 4>(P, p, stream, fq, fqc);
-  if (P.maxt == 8) return launch_gemv_m<KIND, 8>(P, p, stream, fq, fqc);
-  return launch_gemv_m<KIND, 16>(P, p, stream, fq, fqc);
+  if (P.waves == 16) {
+    if (P.maxt == 2) return launch_gemv_m<KIND, 16, 2>(P, p, stream, fq, fqc);
+    if (P.maxt == 4) return launch_gemv_m<KIND, 16, 4>(P, p, stream, fq, fqc);
+    return launch_gemv_m<KIND, 16, 8>(P, p, stream, fq, fqc);
+  }
+  if (P.maxt == 4) return launch_gemv_m<KIND, 8, 4>(P, p, stream, fq, fqc);
+  if (P.maxt == 8) return launch_gemv_m<KIND, 8, 8>(P, p, stream, fq, fqc);
+  return launch_gemv_m<KIND, 8, 16>(P, p, stream, fq, fqc);
 }
 
 template <int KIND>
@@ -485,6 +521,10 @@ struct FusedPlan {
 inline FusedPlan fused_plan(int kind, int M, int N, int K) {
   FusedPlan F{};
   F.P = make_plan(kind, M, N, K);
+  // the quantizing prologue runs in eight-wave blocks: a sixteen-wave plan
+  // becomes the eight-wave plan of the same split
+  if (!F.P.gemm && !F.P.skinny && F.P.waves == 16)
+    F.P = plan_from(kind, M, N, K, Candidate{PATH_DECODE, F.P.ksplit, {}, 0, 8});
   F.fqc = (!F.P.gemm && !F.P.skinny && F.P.staged) ? fq_slots(M < 16 ? M : 16, K) : 0;
   if (F.fqc) {
     F.ws_bytes = F.P.ws_bytes;
@@ -677,7 +717,9 @@ inline int candidate_name(int kind, const Candidate& c, int M, int N, int K, cha
                                 P.ksplit)
                      : snprintf(buf, len, "skinny%s", rows);
   } else {
-    n = snprintf(buf, len, "decode:ksplit=%d", plan_from(kind, M, N, K, c).ksplit);
+    const Plan P = plan_from(kind, M, N, K, c);
+    n = P.waves == 16 ? snprintf(buf, len, "decode:ksplit=%d,waves=16", P.ksplit)
+                      : snprintf(buf, len, "decode:ksplit=%d", P.ksplit);
   }
   return n < 0 || (size_t)n >= len ? W4_ERR_ARG : W4_OK;
 }

@@ -165,16 +165,28 @@ def _names(lib, op, M, N, K):
 
 def test_plan_table_candidates():
     lib = G.load()
-    # decode shape: the decode and skinny kernels at each k split up to 1024
-    # blocks (256 decode blocks, 32 skinny blocks unsplit; a skinny split keeps
-    # at least 2 of the 32 k tiles)
+    # decode shape: the decode kernel (8 and 16 waves per block) and the skinny
+    # kernel at each k split up to 1024 blocks (256 decode blocks, 32 skinny
+    # blocks unsplit; a skinny split keeps at least 2 of the 32 k tiles)
     assert _names(lib, L.W4_OP_W4A8, 1, 4096, 4096) == [
-        "decode:ksplit=1", "decode:ksplit=2", "decode:ksplit=4", "skinny", "skinny:ksplit=2",
-        "skinny:ksplit=4", "skinny:ksplit=8", "skinny:ksplit=16"]
+        "decode:ksplit=1", "decode:ksplit=1,waves=16", "decode:ksplit=2",
+        "decode:ksplit=2,waves=16", "decode:ksplit=4", "decode:ksplit=4,waves=16", "skinny",
+        "skinny:ksplit=2", "skinny:ksplit=4", "skinny:ksplit=8", "skinny:ksplit=16"]
+    # 16 waves need per-wave staging and at most 8 tiles per wave: not at
+    # 86 k tiles of 4 rows unsplit (rows too long to stage)
+    assert "decode:ksplit=1,waves=16" not in _names(lib, L.W4_OP_W4A16, 4, 4096, 11008)
+    # built-in: 16 waves for long rows over 64..256 unsplit blocks only
+    for op, M, N, K, want in ((L.W4_OP_W4A16, 1, 4096, 11008, "decode:ksplit=1,waves=16"),
+                              (L.W4_OP_W2A8, 1, 3200, 8640, "decode:ksplit=1,waves=16"),
+                              (L.W4_OP_W4A16, 1, 4096, 4096, "decode:ksplit=1"),
+                              (L.W4_OP_W4A16, 1, 11008, 4096, "decode:ksplit=1"),
+                              (L.W4_OP_W2A8, 1, 8640, 3200, "decode:ksplit=1")):
+        names = _names(lib, op, M, N, K)
+        assert names[lib.w4_plan_current(op, M, N, K)] == want, (op, M, N, K)
     # prefill shape: plus the three GEMM block shapes of the INT4 x INT8 kernel
     assert _names(lib, L.W4_OP_W4A8, 2048, 4096, 4096) == [
-        "decode:ksplit=1", "skinny", "skinny:rows=32", "gemm:128x256", "gemm:128x352",
-        "gemm:256x352"]
+        "decode:ksplit=1", "decode:ksplit=1,waves=16", "skinny", "skinny:rows=32",
+        "gemm:128x256", "gemm:128x352", "gemm:256x352"]
     # above 16 rows the skinny kernel also runs with two row tiles per block
     # (the built-in choice once one-tile blocks exceed the 512 resident)
     names = _names(lib, L.W4_OP_W2A8, 128, 8640, 3200)
@@ -213,18 +225,20 @@ def test_plan_table_pin_and_workspace():
     # the fp16-activation op on the same layout keeps its own (built-in) plan
     assert lib.w4_plan_workspace_bytes(L.W4_OP_W2A16, M, N, K) == 16384 + 64 * 1024
     # the pin is per (op, shape): another op or size keeps its built-in plan
-    assert lib.w4_plan_current(op, M, N, K - 256) == 6
+    names = _names(lib, op, M, N, K - 256)
+    assert names[lib.w4_plan_current(op, M, N, K - 256)] == "decode:ksplit=64"
     assert lib.w4_workspace_bytes(lay, M, N, K - 256) > 0
     # the fused entry points share the W2A8 op's plan: unsplit, the 128 KiB
     # row does not fit the LDS staging, so it is quantized into the workspace
     assert lib.w4_fused_act_workspace_bytes(lay, M, N, K) == 16384 + K + 256
+    builtin = _names(lib, op, M, N, K).index("decode:ksplit=64")
     assert lib.w4_plan_pin(op, M, N, K, -1) == L.W4_OK
-    assert lib.w4_plan_current(op, M, N, K) == 6
+    assert lib.w4_plan_current(op, M, N, K) == builtin
     assert lib.w4_plan_pin(op, M, N, K, 2) == L.W4_OK
     assert lib.w4_plan_pin(L.W4_OP_W4A8, 2048, 4096, 4096, 1) == L.W4_OK
     assert lib.w4_plan_current(L.W4_OP_W4A8, 2048, 4096, 4096) == 1
     assert lib.w4_plan_reset() == L.W4_OK
-    assert lib.w4_plan_current(op, M, N, K) == 6
+    assert lib.w4_plan_current(op, M, N, K) == builtin
     assert lib.w4_plan_current(L.W4_OP_W4A8, 2048, 4096, 4096) != 1
 
 

@@ -143,6 +143,9 @@ class Shape:
 PLAN_SHAPES = [
     ("w4a8", 1, 4096, 4096), ("w4a8", 37, 1000, 1040), ("w4a8", 130, 4100, 528),
     ("w2a8", 1, 16, 131072), ("w2a8", 70, 3000, 2000),
+    # long rows: 16-wave decode plans next to the 8-wave ones (the first two
+    # take 16 waves unsplit as their built-in plan; ragged last n-tile)
+    ("w4a16", 1, 1040, 11008), ("w2a16", 1, 1030, 8640), ("w8a8", 3, 300, 8192),
     # split GEMM finishes over column pairs with a ragged pair (N % 4 == 2)
     # and over single columns (odd N), with rows past M in the last block
     ("w2a8", 130, 1002, 1024), ("w2a8", 100, 1001, 768),
@@ -195,8 +198,10 @@ def test_one_workspace_for_any_mix_of_shapes_and_plans(g):
              for c in cases[:2]]
     assert names == ["decode:ksplit=64", "gemm:128x128,ksplit=2"]
     try:
-        g.w4_plan_pin(g.W4_OP_W4A8, 1, 4096, 4096, 2)
-        assert g.w4_plan_name(g.W4_OP_W4A8, 1, 4096, 4096, 2) == "decode:ksplit=4"
+        split4 = [g.w4_plan_name(g.W4_OP_W4A8, 1, 4096, 4096, i)
+                  for i in range(g.w4_plan_count(g.W4_OP_W4A8, 1, 4096, 4096))].index(
+                      "decode:ksplit=4")
+        g.w4_plan_pin(g.W4_OP_W4A8, 1, 4096, 4096, split4)
         need = max(g.w4_plan_workspace_bytes(c.op, c.M, c.N, c.K) for c in cases)
         assert need > 16384
         shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
