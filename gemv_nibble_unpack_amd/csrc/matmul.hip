@@ -143,6 +143,7 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   return P;
 }
 
+constexpr int CAND_MAX_BLOCKS = 1024;      // k splits tried up to this many blocks
 constexpr size_t REREAD_MAX = 64ull << 20;   // activation bytes the decode kernel may re-read
 constexpr int SKINNY_RESIDENT = 512;         // skinny blocks resident at once (two per CU)
 constexpr int SKINNY_TILES = 12;             // k tiles per block aimed at by a skinny split
@@ -184,11 +185,20 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   if (mtiles == 1 && K >= 8192 && g.NT >= SPLIT_BELOW && g.NT <= 256 &&
       plan_from(kind, M, N, K, wide).waves == 16)
     return wide;
+  // up to 4 rows whose whole k run per wave is too long to stage per wave:
+  // the smallest k split (up to 1024 blocks) that lets every wave stage its
+  // own range (M=4, N=4096, K=11008 on MI355X: 13.27 -> 11.77 us at 4 splits;
+  // 2 splits, still staged per block, took 14.69)
+  if (rows <= 4 && !plan_from(kind, M, N, K, Candidate{PATH_DECODE, 0, {}}).wst) {
+    for (int ks = 2; ks <= 8 && g.NT * ks <= CAND_MAX_BLOCKS; ks *= 2) {
+      const Candidate c{PATH_DECODE, ks, {}};
+      if (plan_from(kind, M, N, K, c).wst) return c;
+    }
+  }
   return Candidate{PATH_DECODE, 0, {}};
 }
 
 constexpr int MAX_CANDIDATES = 64;
-constexpr int CAND_MAX_BLOCKS = 1024;      // decode k splits tried up to this many blocks
 
 // Every plan that may run the shape, in a fixed order: the decode kernel at
 // each distinct k split that keeps a tile per wave, the skinny kernel, then

@@ -180,7 +180,10 @@ def test_plan_table_candidates():
                               (L.W4_OP_W2A8, 1, 3200, 8640, "decode:ksplit=1,waves=16"),
                               (L.W4_OP_W4A16, 1, 4096, 4096, "decode:ksplit=1"),
                               (L.W4_OP_W4A16, 1, 11008, 4096, "decode:ksplit=1"),
-                              (L.W4_OP_W2A8, 1, 8640, 3200, "decode:ksplit=1")):
+                              (L.W4_OP_W2A8, 1, 8640, 3200, "decode:ksplit=1"),
+                              # 4 rows of K=11008: the smallest split that
+                              # lets each wave stage its own range
+                              (L.W4_OP_W4A16, 4, 4096, 11008, "decode:ksplit=4")):
         names = _names(lib, op, M, N, K)
         assert names[lib.w4_plan_current(op, M, N, K)] == want, (op, M, N, K)
     # prefill shape: plus the three GEMM block shapes of the INT4 x INT8 kernel
