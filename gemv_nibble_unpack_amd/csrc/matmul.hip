@@ -178,8 +178,8 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   // long activation rows (K >= 8192) over one block per CU at most and
   // enough blocks not to split K: sixteen waves, each staging and streaming
   // half as long a k run (M=1 on MI355X:
-  // W4A16 N=4096 K=11008 9.46 -> 8.63 us, W2A16 N=3200 K=8640 6.18 -> 5.53,
-  // W2A8 N=3200 K=8640 4.54 -> 4.34; at K <= 4096, or with more blocks, the
+  // W4A16 N=4096 K=11008 9.46 -> 8.54 us, W2A16 N=3200 K=8640 6.38 -> 5.79,
+  // W2A8 N=3200 K=8640 4.78 -> 4.44; at K <= 4096, or with more blocks, the
   // eight-wave block is as fast or faster)
   const Candidate wide{PATH_DECODE, 0, {}, 0, 16};
   if (mtiles == 1 && K >= 8192 && g.NT >= SPLIT_BELOW && g.NT <= 256 &&
@@ -201,8 +201,9 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
 constexpr int MAX_CANDIDATES = 64;
 
 // Every plan that may run the shape, in a fixed order: the decode kernel at
-// each distinct k split that keeps a tile per wave, the skinny kernel, then
-// (INT8 activations, more than 16 rows) each GEMM block shape.
+// each distinct k split that keeps a tile per wave (each followed by its
+// sixteen-wave form where that exists), the skinny kernel, then (INT8
+// activations, more than 16 rows) each GEMM block shape.
 inline int candidates(int kind, int M, int N, int K, Candidate* out) {
   const Geometry g = geometry(kind_layout(kind), N, K);
   const int blocks = g.NT * ceil_div(M, 16);
