@@ -399,7 +399,7 @@ def main():
                          "replaying them from one captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(column/row sharding is described in the design notes, not built).",
               file=sys.stderr)
         sys.exit(2)
