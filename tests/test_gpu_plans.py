@@ -261,3 +261,56 @@ def test_float_split_sums_do_not_depend_on_arrival_order(g, name, M, N, K, plan)
         s.check(f"{name} {M}x{N}x{K} {plan}")
     finally:
         g.w4_plan_pin(op, M, N, K, -1)
+
+
+@pytest.mark.parametrize("name,M,N,K,plan", [
+    ("w4a8", 300, 2000, 1040, "gemm:128x256"),
+    ("w2a8", 1100, 2000, 1024, "gemm:128x128,ksplit=2"),
+    ("w4a16", 16, 1024, 4096, "skinny:ksplit=4"),
+    ("w2a8", 128, 3200, 3200, "skinny:rows=32,ksplit=2"),
+    ("w4a16", 4, 4096, 11008, "decode:ksplit=4"),
+])
+def test_graph_replays_match_eager(g, name, M, N, K, plan):
+    # The GEMM, the skinny kernel and the decode kernel, split and not, are
+    # captured in a HIP graph and replayed three times with eager work in
+    # between; each replay must give the eager call's output bit for bit
+    # (split counters are left zero by each call, no memset is recorded).
+    op = getattr(g, "W4_OP_" + name.upper())
+    s = Shape(g, op, M, N, K, seed=15000 + M)
+    names = [g.w4_plan_name(op, M, N, K, i) for i in range(g.w4_plan_count(op, M, N, K))]
+    assert plan in names
+    say(f"case graph {name} M={M} N={N} K={K} {plan}")
+    try:
+        g.w4_plan_pin(op, M, N, K, names.index(plan))
+        need = g.w4_plan_workspace_bytes(op, M, N, K)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda") if need else None
+        if op == g.W4_OP_W4A16:
+            C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            A = dev(s.A)
+            call = lambda: g.w4a16_gemm(A, s.Wp, N, workspace=ws, C=C)
+        else:
+            C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+            mm = g.w4a8_gemm if op == g.W4_OP_W4A8 else g.w2a8_gemm
+            call = lambda: mm(s.Aq, s.sa, s.Wp, s.scale, N, out_dtype=g.W4_OUT_I32,
+                              workspace=ws, C=C)
+        call()
+        eager = host(C).copy()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        for rep in range(3):
+            C.fill_(0)                                  # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            got = host(C)
+            assert np.array_equal(got.view(np.uint8), eager.view(np.uint8)), rep
+        if need:
+            assert not host(ws[:16384]).any()           # counters zero after the replays
+    finally:
+        g.w4_plan_pin(op, M, N, K, -1)
