@@ -128,9 +128,12 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   // slowest wave of the block
   const int wchunks = rows * per * trb / 16;
   P.wst = P.staged && wchunks <= 4 * 64;
-  // sixteen waves run only with wave staging and up to 8 tiles per wave;
-  // otherwise the plan is the eight-wave one
-  if (W == 16 && (!P.wst || per > 8))
+  // sixteen waves run with wave staging (up to 8 tiles per wave) or without
+  // staging (up to 4, and not for fp16 x 2-bit, whose 8 fragment loads per
+  // tile would not fit the activation ring in 128 registers); otherwise the
+  // plan is the eight-wave one
+  if (W == 16 && ((P.staged && !P.wst) || per > 8 ||
+                  (!P.staged && (per > 4 || kind == KIND_W2A16))))
     return plan_from(kind, M, N, K, Candidate{PATH_DECODE, c.ks, {}, 0, 8});
   P.apw = wchunks <= 64 ? 1 : wchunks <= 128 ? 2 : 4;
   const size_t block_stage = P.staged ? (size_t)rows * (P.kts * trb + 16) : 0;
@@ -175,15 +178,17 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
     while (ks * 2 <= 64 && (float)(ks * 2) <= want * 1.41421356f) ks *= 2;
     return Candidate{PATH_SKINNY, ks, {}};
   }
-  // long activation rows (K >= 8192) over one block per CU at most and
-  // enough blocks not to split K: sixteen waves, each staging and streaming
-  // half as long a k run (M=1 on MI355X:
-  // W4A16 N=4096 K=11008 9.46 -> 8.54 us, W2A16 N=3200 K=8640 6.38 -> 5.79,
-  // W2A8 N=3200 K=8640 4.78 -> 4.44; at K <= 4096, or with more blocks, the
-  // eight-wave block is as fast or faster)
+  // Sixteen waves per block, each with half as long a k run, where the grid
+  // needs no k split and either (a) one row of K >= 8192 is staged per wave
+  // over one block per CU at most (M=1 on MI355X: W4A16 N=4096 K=11008
+  // 9.46 -> 8.54 us, W2A16 N=3200 K=8640 6.38 -> 5.79, W2A8 N=3200 K=8640
+  // 4.78 -> 4.44; at K <= 4096, or with more blocks, eight waves are as fast
+  // or faster at M=1), or (b) 4 to 16 rows of K <= 4096 (W4A16 M=4 4096x4096
+  // 5.33 -> 5.15, M=4 N=11008 9.51 -> 8.97, M=16 4096x4096 8.22 -> 7.93)
   const Candidate wide{PATH_DECODE, 0, {}, 0, 16};
-  if (mtiles == 1 && K >= 8192 && g.NT >= SPLIT_BELOW && g.NT <= 256 &&
-      plan_from(kind, M, N, K, wide).waves == 16)
+  const Plan pw = plan_from(kind, M, N, K, wide);
+  if (mtiles == 1 && g.NT >= SPLIT_BELOW && pw.waves == 16 && pw.ksplit == 1 &&
+      ((K >= 8192 && g.NT <= 256 && pw.wst) || (rows >= 4 && K <= 4096)))
     return wide;
   // up to 4 rows whose whole k run per wave is too long to stage per wave:
   // the smallest k split (up to 1024 blocks) that lets every wave stage its
@@ -313,12 +318,23 @@ int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq =
                        P.smem, stream, p);                                            \
   } while (0)
   if constexpr (WAVES == 16) {
-    // sixteen-wave plans always stage per wave and never quantize in the
-    // prologue (the planner guarantees both)
-    if (fq || !P.wst) return W4_ERR_ARG;
-    if (P.apw == 1) W4_GEMV_WCASE(1);
-    else if (P.apw == 2) W4_GEMV_WCASE(2);
-    else W4_GEMV_WCASE(4);
+    // sixteen-wave plans stage per wave or not at all, and never quantize in
+    // the prologue (the planner guarantees both)
+    if (fq || (P.staged && !P.wst)) return W4_ERR_ARG;
+    if (!P.staged) {
+      if constexpr (MAXT <= 4 && KIND != KIND_W2A16) {
+        allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, 1, false>, P.smem);
+        hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, 1, false>), grid, block, P.smem, stream, p);
+      } else {
+        return W4_ERR_ARG;
+      }
+    } else if (P.apw == 1) {
+      W4_GEMV_WCASE(1);
+    } else if (P.apw == 2) {
+      W4_GEMV_WCASE(2);
+    } else {
+      W4_GEMV_WCASE(4);
+    }
     return launch_status();
   } else {
 #define W4_GEMV_FQ(F, C)                                                              \

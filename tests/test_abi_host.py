@@ -172,8 +172,9 @@ def test_plan_table_candidates():
         "decode:ksplit=1", "decode:ksplit=1,waves=16", "decode:ksplit=2",
         "decode:ksplit=2,waves=16", "decode:ksplit=4", "decode:ksplit=4,waves=16", "skinny",
         "skinny:ksplit=2", "skinny:ksplit=4", "skinny:ksplit=8", "skinny:ksplit=16"]
-    # 16 waves need per-wave staging and at most 8 tiles per wave: not at
-    # 86 k tiles of 4 rows unsplit (rows too long to stage)
+    # 16 waves need per-wave staging and at most 8 tiles per wave, or no
+    # staging and at most 4: not at 86 k tiles of 4 rows unsplit (rows too
+    # long to stage, 6 tiles per wave)
     assert "decode:ksplit=1,waves=16" not in _names(lib, L.W4_OP_W4A16, 4, 4096, 11008)
     # built-in: 16 waves for long rows over 64..256 unsplit blocks only
     for op, M, N, K, want in ((L.W4_OP_W4A16, 1, 4096, 11008, "decode:ksplit=1,waves=16"),
@@ -183,7 +184,11 @@ def test_plan_table_candidates():
                               (L.W4_OP_W2A8, 1, 8640, 3200, "decode:ksplit=1"),
                               # 4 rows of K=11008: the smallest split that
                               # lets each wave stage its own range
-                              (L.W4_OP_W4A16, 4, 4096, 11008, "decode:ksplit=4")):
+                              (L.W4_OP_W4A16, 4, 4096, 11008, "decode:ksplit=4"),
+                              # 4..16 rows of K <= 4096: 16 waves, staged per
+                              # wave (4 rows) or not staged (16 rows)
+                              (L.W4_OP_W4A16, 4, 4096, 4096, "decode:ksplit=1,waves=16"),
+                              (L.W4_OP_W4A16, 16, 4096, 4096, "decode:ksplit=1,waves=16")):
         names = _names(lib, op, M, N, K)
         assert names[lib.w4_plan_current(op, M, N, K)] == want, (op, M, N, K)
     # prefill shape: plus the three GEMM block shapes of the INT4 x INT8 kernel

@@ -146,6 +146,8 @@ PLAN_SHAPES = [
     # long rows: 16-wave decode plans next to the 8-wave ones (the first two
     # take 16 waves unsplit as their built-in plan; ragged last n-tile)
     ("w4a16", 1, 1040, 11008), ("w2a16", 1, 1030, 8640), ("w8a8", 3, 300, 8192),
+    # rows too long to stage: 16-wave plans stream their fragments from L2
+    ("w4a16", 13, 1000, 4096), ("w8a8", 9, 700, 4096),
     # split GEMM finishes over column pairs with a ragged pair (N % 4 == 2)
     # and over single columns (odd N), with rows past M in the last block
     ("w2a8", 130, 1002, 1024), ("w2a8", 100, 1001, 768),
