@@ -103,7 +103,7 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   const int rows = M < 16 ? M : 16;
   const int blocks = g.NT * P.mtiles;
   const int trb = tile_rowb(kind);
-  const int W = c.waves == 16 ? 16 : GEMV_WAVES;
+  const int W = c.waves == 16 ? 16 : c.waves == 4 ? 4 : GEMV_WAVES;
   P.waves = W;
   int ks = g.NT * P.mtiles <= WS_COUNTER_SLOTS ? c.ks : 1;  // one counter per block slot
   if (ks <= 0) {
@@ -135,6 +135,8 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   if (W == 16 && ((P.staged && !P.wst) || per > 8 ||
                   (!P.staged && (per > 4 || kind == KIND_W2A16))))
     return plan_from(kind, M, N, K, Candidate{PATH_DECODE, c.ks, {}, 0, 8});
+  // four waves run only with wave staging
+  if (W == 4 && !P.wst) return plan_from(kind, M, N, K, Candidate{PATH_DECODE, c.ks, {}, 0, 8});
   P.apw = wchunks <= 64 ? 1 : wchunks <= 128 ? 2 : 4;
   const size_t block_stage = P.staged ? (size_t)rows * (P.kts * trb + 16) : 0;
   const size_t wave_stage = P.wst ? (size_t)W * rows * (per * trb + 16) : 0;
@@ -190,6 +192,17 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   if (mtiles == 1 && g.NT >= SPLIT_BELOW && pw.waves == 16 && pw.ksplit == 1 &&
       ((K >= 8192 && g.NT <= 256 && pw.wst) || (rows >= 4 && K <= 4096)))
     return wide;
+  // Four waves per block, each with twice as long a k run, for one row of
+  // INT8 or FP8 activations of K <= 4096 over 64..639 unsplit blocks (M=1 on
+  // MI355X: W2A8 N=8640 K=3200 4.65 -> 4.42 us, N=K=3200 3.43 -> 3.34, W4A8
+  // 4096x4096 4.31 -> 4.24, INT8 and FP8 weights 4096x4096 -1.3%; fp16
+  // activations, or 688 blocks (W4A8 N=11008), lose 2..12%)
+  const bool a8 = kind == KIND_W4A8 || kind == KIND_W2A8 || kind == KIND_W8A8 || kind == KIND_F8F8;
+  const Candidate narrow{PATH_DECODE, 0, {}, 0, 4};
+  if (a8 && rows == 1 && K <= 4096 && g.NT >= SPLIT_BELOW && g.NT < 640) {
+    const Plan pn = plan_from(kind, M, N, K, narrow);
+    if (pn.waves == 4 && pn.ksplit == 1) return narrow;
+  }
   // up to 4 rows whose whole k run per wave is too long to stage per wave:
   // the smallest k split (up to 1024 blocks) that lets every wave stage its
   // own range (M=4, N=4096, K=11008 on MI355X: 13.27 -> 11.77 us at 4 splits;
@@ -219,7 +232,10 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     if (eff == last) continue;
     last = eff;
     out[n++] = Candidate{PATH_DECODE, ks, {}};
-    // the same split with sixteen waves per block, where that plan exists
+    // the same split with four and with sixteen waves per block, where those
+    // plans exist
+    const Candidate narrow{PATH_DECODE, ks, {}, 0, 4};
+    if (plan_from(kind, M, N, K, narrow).waves == 4) out[n++] = narrow;
     const Candidate wide{PATH_DECODE, ks, {}, 0, 16};
     if (plan_from(kind, M, N, K, wide).waves == 16) out[n++] = wide;
   }
@@ -317,12 +333,12 @@ int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq =
     hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, A, true, 0, 1, true>), grid, block,  \
                        P.smem, stream, p);                                            \
   } while (0)
-  if constexpr (WAVES == 16) {
+  if constexpr (WAVES != 8) {
     // sixteen-wave plans stage per wave or not at all, and never quantize in
     // the prologue (the planner guarantees both)
     if (fq || (P.staged && !P.wst)) return W4_ERR_ARG;
     if (!P.staged) {
-      if constexpr (MAXT <= 4 && KIND != KIND_W2A16) {
+      if constexpr (WAVES == 16 && MAXT <= 4 && KIND != KIND_W2A16) {
         allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, 1, false>, P.smem);
         hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, 1, false>), grid, block, P.smem, stream, p);
       } else {
@@ -382,6 +398,11 @@ int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream, int fq 
   p.kts = P.kts;
   p.counters = reinterpret_cast<unsigned*>(ws);
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + P.counters_bytes : nullptr;
+  if (P.waves == 4) {
+    if (P.maxt == 4) return launch_gemv_m<KIND, 4, 4>(P, p, stream, fq, fqc);
+    if (P.maxt == 8) return launch_gemv_m<KIND, 4, 8>(P, p, stream, fq, fqc);
+    return launch_gemv_m<KIND, 4, 16>(P, p, stream, fq, fqc);
+  }
   if (P.waves == 16) {
     if (P.maxt == 2) return launch_gemv_m<KIND, 16, 2>(P, p, stream, fq, fqc);
     if (P.maxt == 4) return launch_gemv_m<KIND, 16, 4>(P, p, stream, fq, fqc);
@@ -550,7 +571,7 @@ inline FusedPlan fused_plan(int kind, int M, int N, int K) {
   F.P = make_plan(kind, M, N, K);
   // the quantizing prologue runs in eight-wave blocks: a sixteen-wave plan
   // becomes the eight-wave plan of the same split
-  if (!F.P.gemm && !F.P.skinny && F.P.waves == 16)
+  if (!F.P.gemm && !F.P.skinny && F.P.waves != 8)
     F.P = plan_from(kind, M, N, K, Candidate{PATH_DECODE, F.P.ksplit, {}, 0, 8});
   F.fqc = (!F.P.gemm && !F.P.skinny && F.P.staged) ? fq_slots(M < 16 ? M : 16, K) : 0;
   if (F.fqc) {
@@ -745,8 +766,8 @@ inline int candidate_name(int kind, const Candidate& c, int M, int N, int K, cha
                      : snprintf(buf, len, "skinny%s", rows);
   } else {
     const Plan P = plan_from(kind, M, N, K, c);
-    n = P.waves == 16 ? snprintf(buf, len, "decode:ksplit=%d,waves=16", P.ksplit)
-                      : snprintf(buf, len, "decode:ksplit=%d", P.ksplit);
+    n = P.waves != 8 ? snprintf(buf, len, "decode:ksplit=%d,waves=%d", P.ksplit, P.waves)
+                     : snprintf(buf, len, "decode:ksplit=%d", P.ksplit);
   }
   return n < 0 || (size_t)n >= len ? W4_ERR_ARG : W4_OK;
 }

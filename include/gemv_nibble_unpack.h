@@ -364,8 +364,8 @@ int w2a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
 int w4_plan_count(int op, int M, int N, int K);
 
 /* Writes the name of candidate `index` (NUL-terminated, at most len bytes,
- * host memory) to buf: "decode:ksplit=S", "decode:ksplit=S,waves=16" (16 waves
- * per block instead of 8), "skinny", "skinny:ksplit=S",
+ * host memory) to buf: "decode:ksplit=S", "decode:ksplit=S,waves=W" (W = 4 or
+ * 16 waves per block instead of 8), "skinny", "skinny:ksplit=S",
  * "skinny:rows=32", "skinny:rows=32,ksplit=S", "gemm:RxC" or
  * "gemm:RxC,ksplit=S" (R rows x C columns per block, K split S ways).
  * W4_ERR_NULL for buf NULL; W4_ERR_ARG for an index out of range or a buffer

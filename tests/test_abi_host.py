@@ -165,12 +165,13 @@ def _names(lib, op, M, N, K):
 
 def test_plan_table_candidates():
     lib = G.load()
-    # decode shape: the decode kernel (8 and 16 waves per block) and the skinny
-    # kernel at each k split up to 1024 blocks (256 decode blocks, 32 skinny
-    # blocks unsplit; a skinny split keeps at least 2 of the 32 k tiles)
+    # decode shape: the decode kernel (8, 4 and 16 waves per block) and the
+    # skinny kernel at each k split up to 1024 blocks (256 decode blocks, 32
+    # skinny blocks unsplit; a skinny split keeps at least 2 of the 32 k tiles)
     assert _names(lib, L.W4_OP_W4A8, 1, 4096, 4096) == [
-        "decode:ksplit=1", "decode:ksplit=1,waves=16", "decode:ksplit=2",
-        "decode:ksplit=2,waves=16", "decode:ksplit=4", "decode:ksplit=4,waves=16", "skinny",
+        "decode:ksplit=1", "decode:ksplit=1,waves=4", "decode:ksplit=1,waves=16",
+        "decode:ksplit=2", "decode:ksplit=2,waves=4", "decode:ksplit=2,waves=16",
+        "decode:ksplit=4", "decode:ksplit=4,waves=4", "decode:ksplit=4,waves=16", "skinny",
         "skinny:ksplit=2", "skinny:ksplit=4", "skinny:ksplit=8", "skinny:ksplit=16"]
     # 16 waves need per-wave staging and at most 8 tiles per wave, or no
     # staging and at most 4: not at 86 k tiles of 4 rows unsplit (rows too
@@ -181,7 +182,8 @@ def test_plan_table_candidates():
                               (L.W4_OP_W2A8, 1, 3200, 8640, "decode:ksplit=1,waves=16"),
                               (L.W4_OP_W4A16, 1, 4096, 4096, "decode:ksplit=1"),
                               (L.W4_OP_W4A16, 1, 11008, 4096, "decode:ksplit=1"),
-                              (L.W4_OP_W2A8, 1, 8640, 3200, "decode:ksplit=1"),
+                              (L.W4_OP_W2A8, 1, 8640, 3200, "decode:ksplit=1,waves=4"),
+                              (L.W4_OP_W4A8, 1, 11008, 4096, "decode:ksplit=1"),
                               # 4 rows of K=11008: the smallest split that
                               # lets each wave stage its own range
                               (L.W4_OP_W4A16, 4, 4096, 11008, "decode:ksplit=4"),

@@ -148,6 +148,8 @@ PLAN_SHAPES = [
     ("w4a16", 1, 1040, 11008), ("w2a16", 1, 1030, 8640), ("w8a8", 3, 300, 8192),
     # rows too long to stage: 16-wave plans stream their fragments from L2
     ("w4a16", 13, 1000, 4096), ("w8a8", 9, 700, 4096),
+    # one INT8 row over 65 n-tiles: 4-wave plans built in (k tail in the second)
+    ("w2a8", 1, 1030, 3200), ("w8a8", 1, 1030, 1008),
     # split GEMM finishes over column pairs with a ragged pair (N % 4 == 2)
     # and over single columns (odd N), with rows past M in the last block
     ("w2a8", 130, 1002, 1024), ("w2a8", 100, 1001, 768),
