@@ -273,12 +273,15 @@ def test_float_split_sums_do_not_depend_on_arrival_order(g, name, M, N, K, plan)
     ("w4a16", 16, 1024, 4096, "skinny:ksplit=4"),
     ("w2a8", 128, 3200, 3200, "skinny:rows=32,ksplit=2"),
     ("w4a16", 4, 4096, 11008, "decode:ksplit=4"),
+    ("w2a8", 1, 8640, 3200, "decode:ksplit=1,waves=4"),
+    ("w4a16", 16, 4096, 4096, "decode:ksplit=1,waves=16"),
 ])
 def test_graph_replays_match_eager(g, name, M, N, K, plan):
-    # The GEMM, the skinny kernel and the decode kernel, split and not, are
-    # captured in a HIP graph and replayed three times with eager work in
-    # between; each replay must give the eager call's output bit for bit
-    # (split counters are left zero by each call, no memset is recorded).
+    # The GEMM, the skinny kernel and the decode kernel (split, and with 4 and
+    # 16 waves per block) are captured in a HIP graph and replayed three
+    # times with eager work in between; each replay must give the eager
+    # call's output bit for bit (split counters are left zero by each call,
+    # no memset is recorded).
     op = getattr(g, "W4_OP_" + name.upper())
     s = Shape(g, op, M, N, K, seed=15000 + M)
     names = [g.w4_plan_name(op, M, N, K, i) for i in range(g.w4_plan_count(op, M, N, K))]
