@@ -121,6 +121,36 @@ def summarize_traffic(fetch_dir, write_dir, out_path, kernel, calib_bytes, cmd,
     return rec
 
 
+def summarize_mfma(util_dir, raw_dir, out_path, kernel, ops, cmds):
+    """Matrix-core evidence for one kernel from two counter passes: the derived
+    MfmaUtil (busy MFMA cycles over all SIMDs / (GPU-active cycles x SIMDs)),
+    and the raw I8 MFMA operation count (x 512) with the busy cycles and the
+    GPU-active cycles (summed over the XCDs). Medians per launch."""
+    def pick(d, counter):
+        vals = [v for name, vs in pmc_values(d, counter).items() if kernel in name for v in vs]
+        if not vals:
+            raise KeyError(f"no {counter} for a dispatch matching {kernel!r}")
+        return statistics.median(vals), len(vals)
+
+    util, n = pick(util_dir, "MfmaUtil")
+    mops, _ = pick(raw_dir, "SQ_INSTS_VALU_MFMA_MOPS_I8")
+    busy, _ = pick(raw_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    active, _ = pick(raw_dir, "GRBM_GUI_ACTIVE")
+    lines = ["# rocprofv3 matrix-core counters", "",
+             f"Kernel: `{kernel}` ({n} launches, medians per launch)", "",
+             "| quantity | value |", "|---|---|",
+             f"| MfmaUtil (busy MFMA cycles / (GPU-active cycles x SIMDs)) | {util:.1f} % |",
+             f"| I8 MFMA operations (SQ_INSTS_VALU_MFMA_MOPS_I8 x 512) | {mops * 512:.4e} |",
+             f"| algorithmic operations 2*M*N*K | {ops:.4e} |",
+             f"| executed / algorithmic (padding of the last block's columns) | {mops * 512 / ops:.4f} |",
+             f"| SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) | {busy:.0f} |",
+             f"| GRBM_GUI_ACTIVE (summed over the XCDs) | {active:.0f} |",
+             "", "Commands:", ""] + [f"* `{c}`" for c in cmds]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
+
+
 def load_traffic(path):
     """The recorded traffic, or None if absent or the kernels changed since."""
     try:
@@ -149,7 +179,17 @@ def main():
     q.add_argument("--calib-kernel", default="bitwise_not",
                    help="name substring of the calibration copy kernel")
     q.add_argument("--cmd", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("util_dir")
+    m.add_argument("raw_dir")
+    m.add_argument("out")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--ops", type=float, required=True, help="algorithmic operations per launch")
+    m.add_argument("--cmd", action="append", required=True)
     a = ap.parse_args()
+    if a.what == "mfma":
+        print(summarize_mfma(a.util_dir, a.raw_dir, a.out, a.kernel, a.ops, a.cmd))
+        return
     if a.what == "trace":
         print(summarize_trace(a.dir, a.out, a.cmd))
     else:
