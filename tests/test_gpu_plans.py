@@ -321,3 +321,24 @@ def test_graph_replays_match_eager(g, name, M, N, K, plan):
             assert not host(ws[:16384]).any()           # counters zero after the replays
     finally:
         g.w4_plan_pin(op, M, N, K, -1)
+
+
+def _random_shapes():
+    # two ragged shapes per kind from one fixed seed: rows 1..16 and
+    # 17..140, columns 1..700 (partial n-tiles), K a required multiple up to
+    # 4096 (k tails)
+    rng = np.random.default_rng(16000)
+    out = []
+    for name, kmult in (("w4a8", 16), ("w2a8", 16), ("w4a16", 128), ("w2a16", 16),
+                        ("w8a8", 16), ("f8f8", 16)):
+        for lo, hi in ((1, 17), (17, 141)):
+            M = int(rng.integers(lo, hi))
+            N = int(rng.integers(1, 701))
+            K = int(rng.integers(1, 4096 // kmult + 1)) * kmult
+            out.append((name, M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("name,M,N,K", _random_shapes())
+def test_random_shapes_every_plan(g, name, M, N, K):
+    test_every_plan_matches_oracle(g, name, M, N, K)
