@@ -182,15 +182,19 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   }
   // Sixteen waves per block, each with half as long a k run, where the grid
   // needs no k split and either (a) one row of K >= 8192 is staged per wave
-  // over one block per CU at most (M=1 on MI355X: W4A16 N=4096 K=11008
-  // 9.46 -> 8.54 us, W2A16 N=3200 K=8640 6.38 -> 5.79, W2A8 N=3200 K=8640
-  // 4.78 -> 4.44; at K <= 4096, or with more blocks, eight waves are as fast
-  // or faster at M=1), or (b) 4 to 16 rows of K <= 4096 (W4A16 M=4 4096x4096
-  // 5.33 -> 5.15, M=4 N=11008 9.51 -> 8.97, M=16 4096x4096 8.22 -> 7.93)
+  // over one block per CU at most, or with more than 8 tiles per wave at
+  // eight waves (whose 16 weight registers per lane would leave one block per
+  // CU) (M=1 on MI355X: W4A16 N=4096 K=11008 9.46 -> 8.54 us, N=K=16384
+  // 39.0 -> 33.7, W2A16 N=3200 K=8640 6.38 -> 5.79, W2A8 N=3200 K=8640
+  // 4.78 -> 4.44; at K <= 4096, or more blocks of at most 8 tiles per wave,
+  // eight waves are as fast or faster at M=1: N=28672 K=8192 26.2 vs 32.1),
+  // or (b) 4 to 16 rows of K <= 4096 (W4A16 M=4 4096x4096 5.33 -> 5.15, M=4
+  // N=11008 9.51 -> 8.97, M=16 4096x4096 8.22 -> 7.93)
   const Candidate wide{PATH_DECODE, 0, {}, 0, 16};
   const Plan pw = plan_from(kind, M, N, K, wide);
+  const bool long_runs = ceil_div(g.KT, GEMV_WAVES) > 8;
   if (mtiles == 1 && g.NT >= SPLIT_BELOW && pw.waves == 16 && pw.ksplit == 1 &&
-      ((K >= 8192 && g.NT <= 256 && pw.wst) || (rows >= 4 && K <= 4096)))
+      ((K >= 8192 && (g.NT <= 256 || long_runs) && pw.wst) || (rows >= 4 && K <= 4096)))
     return wide;
   // Four waves per block, each with twice as long a k run, for one row of
   // INT8 or FP8 activations of K <= 4096 over 64..639 unsplit blocks (M=1 on
@@ -203,11 +207,12 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
     const Plan pn = plan_from(kind, M, N, K, narrow);
     if (pn.waves == 4 && pn.ksplit == 1) return narrow;
   }
-  // up to 4 rows whose whole k run per wave is too long to stage per wave:
-  // the smallest k split (up to 1024 blocks) that lets every wave stage its
-  // own range (M=4, N=4096, K=11008 on MI355X: 13.27 -> 11.77 us at 4 splits;
-  // 2 splits, still staged per block, took 14.69)
-  if (rows <= 4 && !plan_from(kind, M, N, K, Candidate{PATH_DECODE, 0, {}}).wst) {
+  // up to 4 rows too long to stage in LDS at all: the smallest k split (up to
+  // 1024 blocks) that lets every wave stage its own range (M=4, N=4096,
+  // K=11008 on MI355X: 13.27 -> 11.77 us at 4 splits; 2 splits, staged per
+  // block, took 14.69). Rows that the block can stage stay unsplit (M=1,
+  // N=8192, K=28672: 33.9 us unsplit, 39.5 at 2 splits).
+  if (rows <= 4 && !plan_from(kind, M, N, K, Candidate{PATH_DECODE, 0, {}}).staged) {
     for (int ks = 2; ks <= 8 && g.NT * ks <= CAND_MAX_BLOCKS; ks *= 2) {
       const Candidate c{PATH_DECODE, ks, {}};
       if (plan_from(kind, M, N, K, c).wst) return c;

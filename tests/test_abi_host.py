@@ -187,6 +187,11 @@ def test_plan_table_candidates():
                               # 4 rows of K=11008: the smallest split that
                               # lets each wave stage its own range
                               (L.W4_OP_W4A16, 4, 4096, 11008, "decode:ksplit=4"),
+                              # one long row: 16 waves where 8 would need 16
+                              # tiles each; a row the block can stage, unsplit
+                              (L.W4_OP_W4A16, 1, 16384, 16384, "decode:ksplit=1,waves=16"),
+                              (L.W4_OP_W4A16, 1, 28672, 8192, "decode:ksplit=1"),
+                              (L.W4_OP_W4A16, 1, 8192, 28672, "decode:ksplit=1"),
                               # 4..16 rows of K <= 4096: 16 waves, staged per
                               # wave (4 rows) or not staged (16 rows)
                               (L.W4_OP_W4A16, 4, 4096, 4096, "decode:ksplit=1,waves=16"),
