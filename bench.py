@@ -180,20 +180,24 @@ def bench_prefill(args, stream):
     wsp = G.Workspace(dev)
     steps = max(1, args.steps // 4)
 
-    def step(i):
-        G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None), stream=stream)
+    def step(i, st=stream):
+        G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None), stream=st)
         G.w4a8_gemm(Aq, sa, copies[i % R], ws_, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
-                    workspace=wsp, C=C, stream=stream)
+                    workspace=wsp, C=C, stream=st)
 
     def gemm_only(i):
         G.w4a8_gemm(Aq, sa, copies[i % R], ws_, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
                     workspace=wsp, C=C, stream=stream)
 
-    region_ms, _ = time_loop(step, steps, max(1, args.warmup // 4), stream)
+    eager_step_ms, _ = time_loop(step, steps, max(1, args.warmup // 4), stream)
+    # the two launches of a step replayed from one captured graph (stream=None:
+    # the capture stream), as the decode steps are; eager for --eager
+    region_ms = eager_step_ms if args.eager else \
+        time_graph(lambda i: step(i, None), steps, max(1, args.warmup // 4), stream)[0]
     gemm_ms, per_call = time_loop(gemm_only, steps, 1, stream)
     del copies
     torch.cuda.empty_cache()
-    return c, {"step_ms": region_ms, "gemm_region_ms": gemm_ms,
+    return c, {"step_ms": region_ms, "eager_step_ms": eager_step_ms, "gemm_region_ms": gemm_ms,
                "gemm_per_call_median_ms": float(np.median(per_call)), "steps": steps,
                "bytes": prefill_bytes(c.M, c.N, c.K), "copies": R}
 
@@ -472,6 +476,8 @@ def main():
             "metric": "W4A8 GEMM TOPS at M=2048 (quantize_a8 + w4a8_gemm per step)",
             "value": round(step_tops, 2), "unit": "TOPS", "ms_per_step": round(pre["step_ms"], 5),
             "steps": pre["steps"], "dtype": "i8",
+            "timing": "HIP-graph replay of the timed steps" if not args.eager else "eager",
+            "eager_ms_per_step": round(pre["eager_step_ms"], 5),
             "config": {"workload": "w4a8_prefill_gemm", "M": cp.M, "N": cp.N, "K": cp.K,
                        "weights": "int4 sym per-channel", "act": "int8 per-token",
                        "out": "fp16 + bias", "cold_weight_copies": pre["copies"]},
