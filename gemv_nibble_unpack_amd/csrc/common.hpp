@@ -140,6 +140,45 @@ __device__ __forceinline__ int sym_code_rcp(float w, float s, float rs, float li
   return (int)fminf(fmaxf(q, -lim), lim);
 }
 
+// Eight per-token INT8 codes of one chunk, packed little-endian into (lo, hi),
+// and their sum added to `sum`: code = rint(fl(x / s)) clipped to [-127, 127],
+// 0 for s == 0, with s = max|x| / 127 of the row and rs = fl(1 / s) (0 when
+// s == 0). y = fl(x * rs) is rounded to an integer by adding 1.5 * 2^23: for
+// |y| < 2^22 the sum lies in [2^23, 2^24), where the floats are the integers,
+// so the addition itself rounds y to nearest even, and the sum's bits are
+// 0x4B400000 + code, whose low byte is the code in two's complement. A normal
+// s keeps |y| below 127.5, so the clip never acts on this path. A chunk with
+// any y within 2^-14 of a half integer (where y and fl(x / s) may round
+// apart) goes through sym_code_rcp; a subnormal s (whose own rounding error
+// can carry |x / s| past the clip) goes through the division.
+__device__ __forceinline__ void codes8_i8(const float (&x)[8], float s, float rs, uint32_t& lo,
+                                          uint32_t& hi, int& sum) {
+#pragma clang fp contract(off)
+  constexpr float R = 12582912.0f;                   // 1.5 * 2^23
+  constexpr uint32_t RB = 0x4B400000u;               // bits of R
+  uint32_t b[8];
+  float dev = 0.f;                                   // largest |rint(y) - y|, exact
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = x[e] * rs;
+    const float t = y + R;
+    dev = fmaxf(dev, fabsf((t - R) - y));
+    b[e] = __builtin_bit_cast(uint32_t, t);
+  }
+  if (__builtin_expect(dev > 0.5f - 0x1p-14f || (s > 0.f && s < 0x1p-126f), 0)) {
+    const bool sub = s < 0x1p-126f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      b[e] = RB + (uint32_t)(sub ? sym_code_div(x[e], s, 127.f) : sym_code_rcp(x[e], s, rs, 127.f));
+  }
+  // low bytes of b[0..3] and b[4..7]
+  lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                             __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+  hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                             __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+  sum += (int)(b[0] + b[1] + b[2] + b[3] + b[4] + b[5] + b[6] + b[7] - 8u * RB);
+}
+
 // Cross-block exchange of split-K partial sums through the workspace, at
 // device scope. A device-scope fence writes back and invalidates the whole
 // L2 of the XCD (costly once per block); instead the partial sums themselves

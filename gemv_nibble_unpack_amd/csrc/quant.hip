@@ -216,15 +216,8 @@ __global__ __launch_bounds__(QB) void k_quant_a8(const T* __restrict__ A, int K,
   int sum = 0;
   int8_t* out = Aq + (size_t)m * K;
   auto emit = [&](int c, const float (&y)[8]) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = sym_code_rcp(y[i], s, rs, 127.f);
-      sum += q;
-      const uint32_t bq = (uint32_t)(q & 0xFF);
-      if (i < 4) lo |= bq << (8 * i);
-      else hi |= bq << (8 * (i - 4));
-    }
+    uint32_t lo, hi;
+    codes8_i8(y, s, rs, lo, hi, sum);
     *reinterpret_cast<u2*>(out + 8 * c) = u2{lo, hi};
   };
   if constexpr (CPT > 0) {
@@ -240,10 +233,10 @@ __global__ __launch_bounds__(QB) void k_quant_a8(const T* __restrict__ A, int K,
       emit(c, y);
     }
   }
-  sum = block_sum_i(sum, shi);
-  if (threadIdx.x == 0) {
-    a_scale[m] = s;
-    if (rowsum) rowsum[m] = sum;
+  if (threadIdx.x == 0) a_scale[m] = s;
+  if (rowsum) {                                      // uniform: a kernel argument
+    sum = block_sum_i(sum, shi);
+    if (threadIdx.x == 0) rowsum[m] = sum;
   }
 }
 

@@ -134,6 +134,29 @@ def test_quantize_a8_near_ties(g):
     assert np.array_equal(host(rs), rs_ref)
 
 
+def test_quantize_a8_tiny_rows(g):
+    # float32 rows whose scale max|a| / 127 is subnormal or just normal: a
+    # subnormal scale carries its own rounding error (|a / s| can pass 127, so
+    # the clip acts), and its reciprocal can overflow; the codes still follow
+    # rint(fl(a / s)) clipped to [-127, 127]. Also without the row sums.
+    rng = np.random.default_rng(4100)
+    K = 1024
+    rows = []
+    for amax in (1e-37, 2.0 ** -126 * 127, 2.0 ** -126 * 126.9, 3e-39, 7e-44, 2.0 ** -149 * 5):
+        r = (rng.uniform(-1.0, 1.0, K) * amax).astype(np.float32)
+        r[rng.integers(0, K)] = np.float32(amax)
+        rows.append(r)
+    A = np.stack(rows)
+    say(f"case quantize_a8 tiny rows M={A.shape[0]} K={K}")
+    Aq, sa, rs = g.quantize_a8(dev(A))
+    qa_ref, sa_ref, rs_ref = O.quantize_a8(A)
+    assert np.array_equal(host(sa), sa_ref)
+    assert np.array_equal(host(Aq), qa_ref)
+    assert np.array_equal(host(rs), rs_ref)
+    Aq2, sa2, _ = g.quantize_a8(dev(A), with_rowsum=False)
+    assert np.array_equal(host(Aq2), qa_ref) and np.array_equal(host(sa2), sa_ref)
+
+
 @pytest.mark.parametrize("layout,N,K", [(0, 256, 256), (0, 50, 208), (1, 4096, 4096),
                                         (1, 37, 384), (2, 3200, 8640), (2, 19, 48)])
 def test_prepack_roundtrip(g, layout, N, K):
