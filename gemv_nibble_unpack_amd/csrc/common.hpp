@@ -131,7 +131,10 @@ __device__ __forceinline__ int sym_code_div(float w, float s, float lim) {
 // y = fl(w * rs) differs from w / s by at most 128 * (2^-24 + 2^-24) = 2^-16,
 // and fl(w / s) differs from w / s by at most 2^-17, so rint(y) and
 // rint(fl(w / s)) can differ only if y lies within 2^-15 of a half integer.
-// Lanes within 2^-14 of one take the correctly rounded division.
+// Lanes within 2^-14 of one take the correctly rounded division. rs must be
+// finite: below s = 2^-128 (subnormal) it overflows, and the caller divides
+// instead. A subnormal s with a finite reciprocal carries a relative error of
+// at most 2^-21, so |w / s| stays below 127.001 and the bound above holds.
 __device__ __forceinline__ int sym_code_rcp(float w, float s, float rs, float lim) {
   if (!(s > 0.f)) return 0;
   const float y = w * rs;
@@ -149,8 +152,8 @@ __device__ __forceinline__ int sym_code_rcp(float w, float s, float rs, float li
 // 0x4B400000 + code, whose low byte is the code in two's complement. A normal
 // s keeps |y| below 127.5, so the clip never acts on this path. A chunk with
 // any y within 2^-14 of a half integer (where y and fl(x / s) may round
-// apart) goes through sym_code_rcp; a subnormal s (whose own rounding error
-// can carry |x / s| past the clip) goes through the division.
+// apart, see sym_code_rcp), or with a subnormal s (whose own rounding error
+// can carry |x / s| past the clip), takes the correctly rounded division.
 __device__ __forceinline__ void codes8_i8(const float (&x)[8], float s, float rs, uint32_t& lo,
                                           uint32_t& hi, int& sum) {
 #pragma clang fp contract(off)
@@ -166,10 +169,8 @@ __device__ __forceinline__ void codes8_i8(const float (&x)[8], float s, float rs
     b[e] = __builtin_bit_cast(uint32_t, t);
   }
   if (__builtin_expect(dev > 0.5f - 0x1p-14f || (s > 0.f && s < 0x1p-126f), 0)) {
-    const bool sub = s < 0x1p-126f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      b[e] = RB + (uint32_t)(sub ? sym_code_div(x[e], s, 127.f) : sym_code_rcp(x[e], s, rs, 127.f));
+    for (int e = 0; e < 8; ++e) b[e] = RB + (uint32_t)sym_code_div(x[e], s, 127.f);
   }
   // low bytes of b[0..3] and b[4..7]
   lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),

@@ -512,9 +512,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
         const float rs = sa > 0.f ? 1.0f / sa : 0.f;
         float x[8];
         chunk(sl, x);
-        uint32_t lo, hi;
-        int unused = 0;
-        codes8_i8(x, sa, rs, lo, hi, unused);
+        uint32_t lo = 0, hi = 0;
+        auto put = [&](int e, int q) {
+          const uint32_t bq = (uint32_t)(q & 0xFF);
+          if (e < 4) lo |= bq << (8 * e);
+          else hi |= bq << (8 * (e - 4));
+        };
+        if (__builtin_expect(!(rs <= 0x1.fffffep127f), 0)) {  // 1 / sa overflowed
+#pragma unroll
+          for (int e = 0; e < 8; ++e) put(e, sym_code_div(x[e], sa, 127.f));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) put(e, sym_code_rcp(x[e], sa, rs, 127.f));
+        }
         *reinterpret_cast<u2*>(smem + row * sstride + (8 * col - k0)) = u2{lo, hi};
       }
       // k tail past K inside the last staged tile contributes zero

@@ -401,6 +401,31 @@ def test_matmul_m0_is_noop_and_errors(g):
 # ---------------------------------------------------------------------------
 # fused activation quantization (quantize_a8 + matmul in one call)
 # ---------------------------------------------------------------------------
+def test_fused_act_tiny_and_tie_rows(g):
+    # the prologue's code rule at its edges: quotients on and next to half
+    # integers, and float32 rows with subnormal or just-normal scales; one
+    # fused call per row (M=1 decode) against the two-call path
+    ties = _near_tie_rows(K=1024)
+    rng = np.random.default_rng(4200)
+    tiny = []
+    for amax in (1e-37, 2.0 ** -126 * 127, 2.0 ** -126 * 126.9, 3e-39):
+        r = (rng.uniform(-1.0, 1.0, 1024) * amax).astype(np.float32)
+        r[rng.integers(0, 1024)] = np.float32(amax)
+        tiny.append(r)
+    rows = np.concatenate([ties[::3], np.stack(tiny)])
+    N, K = 256, 1024
+    Wp, ws = prep_w4a8(g, WL.weights_f32(N, K, seed=4201))
+    say(f"case fused act edge rows: {rows.shape[0]} rows N={N} K={K}")
+    for m in range(rows.shape[0]):
+        Ad = dev(rows[m:m + 1])
+        Aq, sa, _ = g.quantize_a8(Ad)
+        qa_ref, _, _ = O.quantize_a8(rows[m:m + 1])
+        assert np.array_equal(host(Aq), qa_ref), m
+        ref = host(g.w4a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I32))
+        got = host(g.w4a8_gemm_fused_act(Ad, Wp, ws, N, out_dtype=g.W4_OUT_I32))
+        assert np.array_equal(ref, got), m
+
+
 @pytest.mark.parametrize("scheme,M,N,K,dt", [
     ("w4a8", 1, 256, 256, np.float32),      # the tiny GEMV configuration
     ("w4a8", 1, 4096, 4096, np.float16),
