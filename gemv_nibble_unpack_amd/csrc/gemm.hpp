@@ -161,13 +161,27 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
   constexpr int RC = G::ROW_CHUNKS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  // ---- block -> (m block, n block, k split) with XCD-contiguous n ranges --
+  // ---- block -> (m block, n block, k split) -------------------------------
+  // Each XCD (blocks id, id + 8, ...) takes a contiguous run of the tile
+  // order, which is n-major within each half of the m blocks: at M=2048,
+  // N=11008 (8 x 32 tiles) an XCD covers 4 m blocks x 8 n blocks, so its L2
+  // pulls in half of A and a quarter of W (78.6 MB from memory in all, against
+  // 90 MB when an XCD held all 8 m blocks of 4 n blocks).
   const int id = blockIdx.x;
   const int xcd = id & 7, local = id >> 3;
-  const int tix = xcd * gg.per_xcd + local;          // n-major tile order
+  const int tix = xcd * gg.per_xcd + local;
   if (local >= gg.per_xcd || tix >= gg.tiles) return;
-  const int nb = tix / gg.mblocks;
-  const int mb = tix - nb * gg.mblocks;
+  int nb, mb;
+  if (gg.mblocks % 2 == 0) {
+    const int mh = gg.mblocks / 2;
+    const int half = tix / (gg.nblocks * mh);
+    const int rem = tix - half * gg.nblocks * mh;
+    nb = rem / mh;
+    mb = half * mh + (rem - nb * mh);
+  } else {
+    nb = tix / gg.mblocks;
+    mb = tix - nb * gg.mblocks;
+  }
   const int kz = blockIdx.y;
   const int kb = kz * gg.kts;
   const int ke = min(p.KT, kb + gg.kts);
