@@ -3,10 +3,17 @@
 
 One JSON line on stdout. Headline (``value``): the W4A16 decode GEMV at M=1,
 N=K=4096 (group-128 uINT4 weights, fp16 activations, fp16 output) in GB/s of
-algorithmic bytes. The same line carries the W4A8 prefill GEMM (M=2048,
-N=11008, K=4096) in TOPS under ``prefill``. Every timed step reads its weights
-from a different copy (>= 1 GiB of copies in rotation) so each launch streams
-them from HBM, not from the 256 MB last-level cache.
+algorithmic bytes, timed over exactly ``--steps`` calls replayed from one
+captured HIP graph. The line's ``roofline`` carries the same GEMV at the two
+11008-sized projection shapes and, for each of the three, a plain streaming
+read of the same weight bytes through the same protocol (the achievable
+rate). The W4A8 prefill GEMM (M=2048, N=11008, K=4096) is reported in TOPS
+under ``prefill``.
+
+Cold weights: every call reads its weights from one of R copies (>= 1 GiB in
+rotation), and 1 GiB of other memory is read and written between the untimed
+replay and the timed one, so that no call of the timed region finds its
+weights in the 256 MB last-level cache, whatever the step count.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill]
 """
@@ -16,6 +23,7 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -28,11 +36,16 @@ if ROOT not in sys.path:
 METRIC = "W4 GEMV HBM GB/s (% peak) at M=1; W4A8 GEMM TOPS (% MFMA peak) at M=2048"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 I8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA
+LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 ROTATE_BYTES = 1 << 30         # weight copies in rotation per workload
+FLUSH_BYTES = 1 << 30          # read + written between the untimed and the timed pass
+PREFILL_MIN_STEPS = 50         # the prefill is timed over at least this many calls
 CALIB_BYTES = 256 << 20        # device-to-device copy used to calibrate PMC byte counters
+PROBE_PER = (1, 2, 4, 8)       # 16-byte loads per lane tried by the read probe
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_TRAFFIC = os.path.join(PROFILES, "k_gemv_w4a16_decode_m1_n4096_k4096_traffic.json")
 PREFILL_TRAFFIC = os.path.join(PROFILES, "k_gemm_w4a8_prefill_m2048_n11008_k4096_traffic.json")
+DECODE_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
 
 
 def log(*a):
@@ -52,38 +65,43 @@ def prefill_bytes(M, N, K):
     return N * K // 2 + N * 4 + M * K + M * 4 + N * 2 + M * N * 2
 
 
-def time_loop(fn, steps, warmup, stream):
-    """Warm up, then time `steps` calls with events on `stream`.
-
-    Returns (ms per step over the whole timed region, list of per-call ms
-    from per-call event pairs measured in a second pass)."""
-    import torch
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        fn(warmup + i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    region_ms = t0.elapsed_time(t1) / steps
-    # per-call brackets (kernel time plus event-marker overhead)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        fn(warmup + steps + i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_call = [a.elapsed_time(b) for a, b in evs]
-    return region_ms, per_call
+def rotation(copy_bytes):
+    """Number of weight copies whose total reaches ROTATE_BYTES."""
+    return max(1, math.ceil(ROTATE_BYTES / copy_bytes))
 
 
-def time_graph(fn, steps, warmup, stream):
-    """Capture `steps` calls in one HIP graph, replay it once untimed and once
-    timed; returns (ms per call, per-call list from the eager pass)."""
+def cold_gap_bytes(steps, copies, copy_bytes, flush_bytes=FLUSH_BYTES):
+    """Fewest bytes that pass through memory between two reads of one weight
+    copy inside a timed region of `steps` calls over `copies` copies: the
+    flush before the region for each copy's first read there, the other
+    copies for a read that comes round again. Above the last-level cache
+    size, every timed call reads its weights from HBM."""
+    gap = flush_bytes
+    if steps > copies:
+        gap = min(gap, (copies - 1) * copy_bytes)
+    return gap
+
+
+class Flush:
+    """Reads FLUSH_BYTES / 2 and writes as many (torch's elementwise
+    bitwise_not on uint8), evicting the weights from the last-level cache."""
+
+    def __init__(self, dev):
+        import torch
+        self.src = torch.ones(FLUSH_BYTES // 2, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self, stream):
+        import torch
+        with torch.cuda.stream(stream):
+            torch.bitwise_not(self.src, out=self.dst)
+
+
+def time_graph(fn, steps, warmup, stream, flush):
+    """Capture `steps` calls fn(0..steps-1) in one HIP graph, replay it once
+    untimed, flush the last-level cache, and time one replay with HIP events
+    on `stream`; returns ms per call. The calls take the current stream (the
+    capture stream while capturing)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -93,14 +111,31 @@ def time_graph(fn, steps, warmup, stream):
         for i in range(steps):
             fn(i)
     g.replay()
-    torch.cuda.synchronize()
+    flush(stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     g.replay()
     t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, []
+    return t0.elapsed_time(t1) / steps
+
+
+def time_eager(fn, steps, warmup, stream, flush):
+    """The same calls launched one by one from Python (host launch cost
+    included); returns ms per call."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    flush(stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 def calibration_copy():
@@ -116,14 +151,45 @@ def calibration_copy():
     torch.cuda.synchronize()
 
 
-def bench_decode(args, stream):
+def copies_of(Wp):
+    import torch
+    R = rotation(Wp.numel())
+    return [Wp] + [Wp.clone() for _ in range(R - 1)]
+
+
+def read_probe(copies, steps, warmup, stream, flush):
+    """The plain streaming read of the same weight copies, in the same
+    protocol, at each loads-per-lane setting; the fastest is the achievable
+    rate for a transfer of that size."""
+    import torch
+    import gemv_nibble_unpack_amd as G
+    sink = torch.zeros(1024, dtype=torch.int32, device=copies[0].device)
+    nbytes = copies[0].numel()
+    R = len(copies)
+    runs = {}
+    for per in PROBE_PER:
+        ms = time_graph(lambda i: G.w4_read_probe(copies[i % R], nbytes, per, sink), steps,
+                        warmup, stream, flush)
+        runs[per] = ms
+    per = min(runs, key=runs.get)
+    ms = runs[per]
+    return {"bytes": nbytes, "loads_per_lane": per, "us": round(ms * 1e3, 3),
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "us_by_loads_per_lane": {str(k): round(v * 1e3, 3) for k, v in runs.items()}}
+
+
+def bench_decode_shape(N, K, steps, warmup, stream, flush, eager=False, probe=True):
+    """W4A16 M=1 GEMV at (N, K): graph-replay time per call (cold weights),
+    the eager rate beside it, and the read probe on the same copies."""
     import torch
     import gemv_nibble_unpack_amd as G
     from gemv_nibble_unpack_amd import workloads as WL
-
-    c = WL.W4A16_DECODE
-    d = c.inputs()
     dev = torch.device("cuda:0")
+    if (N, K) == (4096, 4096):
+        c = WL.W4A16_DECODE
+    else:
+        c = next(x for x in WL.W4A16_SWEEP if (x.M, x.N, x.K) == (1, N, K))
+    d = c.inputs()
     W = torch.from_numpy(d["W"]).to(dev)
     A = torch.from_numpy(d["A"]).to(dev)
     t = time.time()
@@ -131,34 +197,38 @@ def bench_decode(args, stream):
     Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, c.N, c.K, s, z)
     torch.cuda.synchronize()
     prep_ms = (time.time() - t) * 1e3
-    R = max(1, math.ceil(ROTATE_BYTES / Wp.numel()))
-    copies = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    del W, Wq, s, z
+    copies = copies_of(Wp)
+    R = len(copies)
     C = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
     ws = G.Workspace(dev)
 
     def step(i):
-        # stream=None: the current stream (the capture stream under --graph)
-        G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C,
-                     stream=None if not args.eager else stream)
+        # stream=None: the current stream (the capture stream under graph capture)
+        G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C)
 
-    eager_ms, per_call = time_loop(step, args.steps, args.warmup, stream) if args.eager else \
-        time_loop(lambda i: G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C, stream=stream),
-                  args.steps, args.warmup, stream)
-    region_ms = eager_ms if args.eager else time_graph(step, args.steps, args.warmup, stream)[0]
+    eager_ms = time_eager(step, steps, warmup, stream, flush)
+    ms = eager_ms if eager else time_graph(step, steps, warmup, stream, flush)
     nbytes = decode_bytes(c.M, c.N, c.K)
-    kern_ms = float(np.median(per_call))
-    out = {
-        "region_ms": region_ms, "eager_region_ms": eager_ms, "graph": not args.eager,
-        "per_call_median_ms": kern_ms,
-        "per_call_mean_ms": float(np.mean(per_call)), "bytes": nbytes, "copies": R,
-        "offline_prep_ms": prep_ms,
-    }
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"N": c.N, "K": c.K, "bytes": nbytes, "us": round(ms * 1e3, 3),
+           "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "eager_us": round(eager_ms * 1e3, 3), "copies": R,
+           "cold_gap_bytes": cold_gap_bytes(steps, R, Wp.numel()),
+           "offline_prep_ms": round(prep_ms, 3), "ms": ms}
+    if probe:
+        pr = read_probe(copies, steps, warmup, stream, flush)
+        out["achievable"] = pr
+        out["frac_of_achievable"] = round(gbs / pr["GBps"], 4)
     del copies
     torch.cuda.empty_cache()
-    return c, out
+    return out
 
 
-def bench_prefill(args, stream):
+def bench_prefill(args, stream, flush):
+    """W4A8 M=2048 N=11008 K=4096 with fp16 output and bias: the GEMM alone,
+    quantize_a8 + GEMM (two calls), and w4a8_gemm_fused_act (one call), each
+    replayed from a captured graph over at least PREFILL_MIN_STEPS calls."""
     import torch
     import gemv_nibble_unpack_amd as G
     from gemv_nibble_unpack_amd import workloads as WL
@@ -169,69 +239,52 @@ def bench_prefill(args, stream):
     W = torch.from_numpy(d["W"]).to(dev)
     A = torch.from_numpy(d["A"]).to(dev)
     bias = torch.from_numpy(d["bias"]).to(dev)
-    Wq, ws_, _ = G.quantize_pack_w4(W, G.W4_SYM_PER_CHANNEL)
+    Wq, wsc, _ = G.quantize_pack_w4(W, G.W4_SYM_PER_CHANNEL)
     Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, c.N, c.K)
     del W, Wq
-    R = max(1, math.ceil(ROTATE_BYTES / Wp.numel()))
-    copies = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    copies = copies_of(Wp)
+    R = len(copies)
     Aq = torch.empty((c.M, c.K), dtype=torch.int8, device=dev)
     sa = torch.empty(c.M, dtype=torch.float32, device=dev)
     C = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
     wsp = G.Workspace(dev)
-    steps = max(1, args.steps // 4)
+    wsf = G.Workspace(dev)
+    steps = max(PREFILL_MIN_STEPS, args.steps // 4)
+    warm = max(2, args.warmup // 4)
+    G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None))
 
-    def step(i, st=stream):
-        G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None), stream=st)
-        G.w4a8_gemm(Aq, sa, copies[i % R], ws_, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
-                    workspace=wsp, C=C, stream=st)
+    def gemm(i):
+        G.w4a8_gemm(Aq, sa, copies[i % R], wsc, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
+                    workspace=wsp, C=C)
 
-    def gemm_only(i):
-        G.w4a8_gemm(Aq, sa, copies[i % R], ws_, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
-                    workspace=wsp, C=C, stream=stream)
+    def two_calls(i):
+        G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None))
+        gemm(i)
 
-    eager_step_ms, _ = time_loop(step, steps, max(1, args.warmup // 4), stream)
-    # the two launches of a step replayed from one captured graph (stream=None:
-    # the capture stream), as the decode steps are; eager for --eager
-    region_ms = eager_step_ms if args.eager else \
-        time_graph(lambda i: step(i, None), steps, max(1, args.warmup // 4), stream)[0]
-    gemm_ms, per_call = time_loop(gemm_only, steps, 1, stream)
+    def fused(i):
+        G.w4a8_gemm_fused_act(A, copies[i % R], wsc, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
+                              workspace=wsf, C=C)
+
+    timer = time_eager if args.eager else time_graph
+    out = {"steps": steps, "copies": R, "bytes": prefill_bytes(c.M, c.N, c.K),
+           "cold_gap_bytes": cold_gap_bytes(steps, R, Wp.numel())}
+    out["gemm_ms"] = timer(gemm, steps, warm, stream, flush)
+    out["two_call_step_ms"] = timer(two_calls, steps, warm, stream, flush)
+    out["fused_step_ms"] = timer(fused, steps, warm, stream, flush)
+    out["quant_only_ms"] = timer(lambda i: G.quantize_a8(A, with_rowsum=False,
+                                                         out=(Aq, sa, None)),
+                                 steps, warm, stream, flush)
     del copies
     torch.cuda.empty_cache()
-    return c, {"step_ms": region_ms, "eager_step_ms": eager_step_ms, "gemm_region_ms": gemm_ms,
-               "gemm_per_call_median_ms": float(np.median(per_call)), "steps": steps,
-               "bytes": prefill_bytes(c.M, c.N, c.K), "copies": R}
+    return c, out
 
 
-def bench_decode_extra(stream, steps):
-    """Context lines at M=1 (graph replay, cold weight copies): the W4A16
-    GEMV at the two 11008-sized projection shapes, and the W4A8 GEMV with
-    activations quantized by a separate kernel versus in the GEMV prologue
-    (w4a8_gemm_fused_act)."""
+def bench_decode_w4a8(stream, steps, flush):
+    """W4A8 M=1 N=K=4096 (fp16 activations): quantize_a8 + w4a8_gemm against
+    w4a8_gemm_fused_act (graph replay, cold weights)."""
     import torch
     import gemv_nibble_unpack_amd as G
-    from gemv_nibble_unpack_amd import workloads as WL
     dev = torch.device("cuda:0")
-    out = {"w4a16_m1": []}
-    for c in WL.W4A16_SWEEP:
-        if c.M != 1 or c.N * c.K == 4096 * 4096:
-            continue
-        d = c.inputs()
-        Wq, s, z = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_ASYM_GROUP)
-        Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, c.N, c.K, s, z)
-        del Wq
-        A = torch.from_numpy(d["A"]).to(dev)
-        R = max(1, math.ceil(ROTATE_BYTES / Wp.numel()))
-        copies = [Wp] + [Wp.clone() for _ in range(R - 1)]
-        C = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
-        ws = G.Workspace(dev)
-        ms, _ = time_graph(lambda i: G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C),
-                           steps, 10, stream)
-        nb = decode_bytes(c.M, c.N, c.K)
-        out["w4a16_m1"].append({"N": c.N, "K": c.K, "us": round(ms * 1e3, 3),
-                                "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
-                                "pct_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
-        del copies
-    # W4A8 M=1 N=K=4096: two launches vs the fused prologue
     N = K = 4096
     rng = np.random.default_rng(700)
     W = torch.from_numpy(rng.normal(0, 0.02, (N, K)).astype(np.float32)).to(dev)
@@ -239,8 +292,8 @@ def bench_decode_extra(stream, steps):
     Wq, wsc, _ = G.quantize_pack_w4(W, G.W4_SYM_PER_CHANNEL)
     Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, N, K)
     del W, Wq
-    R = max(1, math.ceil(ROTATE_BYTES / Wp.numel()))
-    copies = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    copies = copies_of(Wp)
+    R = len(copies)
     C = torch.empty((1, N), dtype=torch.float16, device=dev)
     q = (torch.empty((1, K), dtype=torch.int8, device=dev), torch.empty(1, device=dev), None)
     ws = G.Workspace(dev)
@@ -255,12 +308,11 @@ def bench_decode_extra(stream, steps):
     nb = N * K // 2 + 4 * N + 2 * K + 2 * N
     row = {"N": N, "K": K, "bytes": nb}
     for name, fn in (("two_launch", two), ("fused", fused)):
-        ms, _ = time_graph(fn, steps, 10, stream)
+        ms = time_graph(fn, steps, 10, stream, flush)
         row[name] = {"us": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
-    out["w4a8_m1"] = row
     del copies
     torch.cuda.empty_cache()
-    return out
+    return row
 
 
 def traffic_of(path):
@@ -271,7 +323,7 @@ def traffic_of(path):
     return None if rec is None else round(rec["traffic_bytes_per_launch"])
 
 
-def bench_case(case, steps, warmup, stream):
+def bench_case(case, steps, warmup, stream, flush):
     """Time one workload case (cold weights, steps replayed from one captured
     HIP graph); returns a dict for --sweep."""
     import torch
@@ -287,14 +339,14 @@ def bench_case(case, steps, warmup, stream):
         wsc = G.ternary_scale_f16(torch.from_numpy(d["src"]).to(dev))
         nbytes = N * K // 4 + 2 + 2 * M * K + 2 * M * N
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
-        copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
+        copies = copies_of(Wp)
         fn = lambda i: G.w2a16_gemm(A, copies[i % len(copies)], wsc, N, workspace=ws, C=C)
     elif case.scheme == "w4a16":
         Wq, s, z = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_ASYM_GROUP)
         Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, N, K, s, z)
         nbytes = decode_bytes(M, N, K)
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
-        copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
+        copies = copies_of(Wp)
         fn = lambda i: G.w4a16_gemm(A, copies[i % len(copies)], N, workspace=ws, C=C)
     else:
         Aq, sa, _ = G.quantize_a8(A)
@@ -320,11 +372,10 @@ def bench_case(case, steps, warmup, stream):
             wsc = G.ternary_scale_f16(torch.from_numpy(d["src"]).to(dev))
             mm, wbytes = G.w2a8_gemm, N * K // 4 + 2
         nbytes = wbytes + M * K + 4 * M + M * N * C.element_size()
-        copies = [Wp] + [Wp.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / Wp.numel())) - 1)]
+        copies = copies_of(Wp)
         fn = lambda i: mm(Aq, sa, copies[i % len(copies)], wsc, N, out_dtype=out, workspace=ws,
                           C=C)
-    # the calls use the current stream: the capture stream while capturing
-    ms, _ = time_graph(fn, steps, warmup, stream)
+    ms = time_graph(fn, steps, warmup, stream, flush)
     del copies
     torch.cuda.empty_cache()
     return {"case": case.name, "M": M, "N": N, "K": K, "us": round(ms * 1e3, 3),
@@ -332,54 +383,90 @@ def bench_case(case, steps, warmup, stream):
             "TOPS": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
 
 
-def cpu_threads():
+# ---------------------------------------------------------------------------
+# the oracle on the host CPU
+# ---------------------------------------------------------------------------
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:  # pragma: no cover
-        return 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return platform.processor() or "unknown"
 
 
-def cpu_baseline_decode(c):
+def host_cores():
+    """CPU threads this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _timed_oracle(fn, threads, budget_s, max_reps):
+    """Repeat fn() with the BLAS pool limited to `threads` for about
+    budget_s; returns (reps, seconds)."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=threads, user_api="blas"):
+        fn()                                   # first call outside the clock
+        reps, t = 0, time.time()
+        while True:
+            fn()
+            reps += 1
+            el = time.time() - t
+            if el > budget_s or reps >= max_reps:
+                return reps, el
+
+
+def cpu_baseline_decode(c, budget_s=6.0):
     """The oracle, untuned, on the host: full M=1 N=K=4096 W4A16 calls
-    (dequantise in float64, then A @ W^T), repeated for about 10 s."""
+    (dequantise in float64, then A @ W^T) with one BLAS thread and with all
+    of the process's cores."""
     import oracle as O
     d = c.inputs()
     q, s, z = O.quantize_w4_group(d["W"], 128)
-    reps, t = 0, time.time()
-    while True:
-        O.w4a16_gemm(d["A"], q, s, z, 128)
-        reps += 1
-        el = time.time() - t
-        if el > 10.0 or reps >= 200:
-            break
-    gbs = decode_bytes(c.M, c.N, c.K) * reps / el / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{reps} full oracle calls of the M=1 N=4096 K=4096 W4A16 GEMV "
-                      f"(weights pre-quantised) in {el:.1f} s"}
+    fn = lambda: O.w4a16_gemm(d["A"], q, s, z, 128)
+    nb = decode_bytes(c.M, c.N, c.K)
+    cores = host_cores()
+    out = {}
+    for key, threads in (("single_thread", 1), ("all_cores", cores)):
+        reps, el = _timed_oracle(fn, threads, budget_s, 200)
+        out[key] = {"value": nb * reps / el / 1e9, "unit": "GB/s", "cores": threads,
+                    "ms_per_call": el / reps * 1e3}
+    return {"value": out["all_cores"]["value"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "single_thread": out["single_thread"],
+            "sample": f"full oracle calls of the M=1 N=4096 K=4096 W4A16 GEMV (weights "
+                      f"pre-quantised), ~{budget_s:.0f} s per thread count; all {cores} cores "
+                      f"{out['all_cores']['ms_per_call']:.1f} ms/call, one thread "
+                      f"{out['single_thread']['ms_per_call']:.1f} ms/call"}
 
 
-def cpu_baseline_prefill(c):
-    """The oracle on a row sample of the prefill GEMM: 8 token rows x all
-    11008 outputs x K=4096, INT64 accumulate plus epilogue, for about 10 s."""
+def cpu_baseline_prefill(c, budget_s=6.0, rows=8):
+    """The oracle on a row sample of the prefill GEMM: `rows` of the 2048
+    token rows x all 11008 outputs x K=4096 (INT64 sums plus epilogue, as
+    the oracle computes them), with one thread and with all cores."""
     import oracle as O
     d = c.inputs()
     q, s = O.quantize_w4_sym(d["W"])
-    rows = 8
     A = d["A"][:rows]
-    reps, t = 0, time.time()
-    while True:
+
+    def fn():
         qa, sa, _ = O.quantize_a8(A)
         O.w4a8_gemm(qa, sa, q, s, d["bias"], O.OUT_F16)
-        reps += 1
-        el = time.time() - t
-        if el > 10.0 or reps >= 100:
-            break
-    tops = 2.0 * rows * c.N * c.K * reps / el / 1e12
-    return {"value": tops, "unit": "TOPS", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{reps} oracle calls on {rows} of {c.M} token rows (N=11008, K=4096) "
-                      f"in {el:.1f} s"}
+
+    ops = 2.0 * rows * c.N * c.K
+    cores = host_cores()
+    out = {}
+    for key, threads in (("single_thread", 1), ("all_cores", cores)):
+        reps, el = _timed_oracle(fn, threads, budget_s, 100)
+        out[key] = {"value": ops * reps / el / 1e12, "unit": "TOPS", "cores": threads,
+                    "ms_per_call": el / reps * 1e3}
+    return {"value": out["all_cores"]["value"], "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "single_thread": out["single_thread"],
+            "sample": f"oracle calls on {rows} of {c.M} token rows (N=11008, K=4096), "
+                      f"~{budget_s:.0f} s per thread count"}
 
 
 def main():
@@ -390,7 +477,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=2048 GEMM")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the M=1 context shapes (11008-sized W4A16, fused W4A8)")
+                    help="skip the W4A8 M=1 context (quantize_a8 + GEMV vs the fused call)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="time one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--calib", action="store_true",
@@ -399,8 +486,8 @@ def main():
                     help="time every configured workload shape (graph replay); one JSON line "
                          "per case")
     ap.add_argument("--eager", action="store_true",
-                    help="launch the timed decode steps one by one from Python instead of "
-                         "replaying them from one captured HIP graph")
+                    help="launch the timed steps one by one from Python instead of replaying "
+                         "them from one captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
@@ -413,32 +500,38 @@ def main():
     G.load()
     assert torch.cuda.is_available(), "needs a GPU"
     stream = torch.cuda.current_stream()
+    flush = Flush(torch.device("cuda:0"))
 
     if args.sweep:
         from gemv_nibble_unpack_amd import workloads as WL
         for case in WL.ALL_CASES:
-            print(json.dumps(bench_case(case, max(20, args.steps // 4), args.warmup, stream)),
-                  flush=True)
+            print(json.dumps(bench_case(case, max(20, args.steps // 4), args.warmup, stream,
+                                        flush)), flush=True)
         return
     if args.only == "prefill":
-        cp, pre = bench_prefill(args, stream)
+        cp, pre = bench_prefill(args, stream, flush)
         if args.calib:
             calibration_copy()
         ops = 2.0 * cp.M * cp.N * cp.K
         print(json.dumps({"workload": "w4a8_prefill_gemm", **pre,
-                          "gemm_tops": ops / (pre["gemm_region_ms"] * 1e-3) / 1e12}), flush=True)
+                          "gemm_tops": ops / (pre["gemm_ms"] * 1e-3) / 1e12}), flush=True)
         return
-    log("bench: decode W4A16 M=1 N=4096 K=4096")
-    c, dec = bench_decode(args, stream)
+
+    shapes = DECODE_SHAPES[:1] if args.only == "decode" else DECODE_SHAPES
+    dec = []
+    for (N, K) in shapes:
+        log(f"bench: decode W4A16 M=1 N={N} K={K}")
+        dec.append(bench_decode_shape(N, K, args.steps, args.warmup, stream, flush,
+                                      eager=args.eager, probe=args.only != "decode"))
+        log("bench:", {k: v for k, v in dec[-1].items() if k != "ms"})
+    head = dec[0]
     if args.only == "decode":
         if args.calib:
             calibration_copy()
-        print(json.dumps({"workload": "w4a16_decode_gemv", **dec,
-                          "gbs": dec["bytes"] / (dec["region_ms"] * 1e-3) / 1e9}), flush=True)
+        print(json.dumps({"workload": "w4a16_decode_gemv", **head}), flush=True)
         return
-    log("bench: decode", dec)
-    gbs = dec["bytes"] / (dec["region_ms"] * 1e-3) / 1e9
-    kern_gbs = dec["bytes"] / (dec["per_call_median_ms"] * 1e-3) / 1e9
+
+    gbs = head["bytes"] / (head["ms"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -446,61 +539,73 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dec["region_ms"], 6),
+        "ms_per_step": round(head["ms"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "w4a16_decode_gemv", "M": c.M, "N": c.N, "K": c.K,
+        "config": {"workload": "w4a16_decode_gemv", "M": 1, "N": 4096, "K": 4096,
                    "weights": "uint4 group128 fp16 scale + uint8 zero", "act": "fp16",
                    "out": "fp16", "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                   "cold_weight_copies": dec["copies"],
-                   "timing": "HIP-graph replay of the timed steps" if dec["graph"] else "eager",
-                   "eager_GBps": round(dec["bytes"] / (dec["eager_region_ms"] * 1e-3) / 1e9, 2)},
+                   "cold_weight_copies": head["copies"],
+                   "llc_flush_bytes": FLUSH_BYTES,
+                   "cold_gap_bytes": head["cold_gap_bytes"],
+                   "timing": ("eager launches" if args.eager else
+                              "one HIP-graph replay of the timed steps, after an untimed replay "
+                              "and a last-level-cache flush"),
+                   "eager_GBps": round(head["bytes"] / (head["eager_us"] * 1e-6) / 1e9, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_of(DECODE_TRAFFIC),
-                     "bytes_per_launch": dec["bytes"],
-                     "per_call_event_gbs": round(kern_gbs, 2)},
-        "offline_prep_ms": round(dec["offline_prep_ms"], 3),
+                     "bytes_per_launch": head["bytes"],
+                     "achievable": head["achievable"],
+                     "frac_of_achievable": head["frac_of_achievable"],
+                     "shapes": [{k: v for k, v in x.items() if k not in ("ms",)} for x in dec]},
+        "offline_prep_ms": head["offline_prep_ms"],
     }
     if not args.no_prefill:
         log("bench: prefill W4A8 M=2048 N=11008 K=4096")
-        cp, pre = bench_prefill(args, stream)
+        cp, pre = bench_prefill(args, stream, flush)
         log("bench: prefill", pre)
         ops = 2.0 * cp.M * cp.N * cp.K
-        step_tops = ops / (pre["step_ms"] * 1e-3) / 1e12
-        gemm_tops = ops / (pre["gemm_region_ms"] * 1e-3) / 1e12
+        tops = lambda ms: ops / (ms * 1e-3) / 1e12
         line["prefill"] = {
-            "metric": "W4A8 GEMM TOPS at M=2048 (quantize_a8 + w4a8_gemm per step)",
-            "value": round(step_tops, 2), "unit": "TOPS", "ms_per_step": round(pre["step_ms"], 5),
-            "steps": pre["steps"], "dtype": "i8",
-            "timing": "HIP-graph replay of the timed steps" if not args.eager else "eager",
-            "eager_ms_per_step": round(pre["eager_step_ms"], 5),
+            "metric": "W4A8 GEMM TOPS at M=2048 (the GEMM alone; steps with activation "
+                      "quantization beside it)",
+            "value": round(tops(pre["gemm_ms"]), 2), "unit": "TOPS",
+            "ms_per_step": round(pre["gemm_ms"], 5), "steps": pre["steps"], "dtype": "i8",
+            "timing": ("eager launches" if args.eager else
+                       "one HIP-graph replay per figure, after an untimed replay and a "
+                       "last-level-cache flush"),
+            "two_call_step": {"ms": round(pre["two_call_step_ms"], 5),
+                              "TOPS": round(tops(pre["two_call_step_ms"]), 2),
+                              "what": "quantize_a8 + w4a8_gemm"},
+            "fused_step": {"ms": round(pre["fused_step_ms"], 5),
+                           "TOPS": round(tops(pre["fused_step_ms"]), 2),
+                           "what": "w4a8_gemm_fused_act (fp16 A in, one call)"},
+            "quantize_a8_ms": round(pre["quant_only_ms"], 5),
             "config": {"workload": "w4a8_prefill_gemm", "M": cp.M, "N": cp.N, "K": cp.K,
                        "weights": "int4 sym per-channel", "act": "int8 per-token",
-                       "out": "fp16 + bias", "cold_weight_copies": pre["copies"]},
-            "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2),
-                         "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
-                         "frac": round(gemm_tops / I8_PEAK_TOPS, 4),
+                       "out": "fp16 + bias", "cold_weight_copies": pre["copies"],
+                       "cold_gap_bytes": pre["cold_gap_bytes"]},
+            "roofline": {"bound": "mfma", "achieved": round(tops(pre["gemm_ms"]), 2),
+                         "peak": I8_PEAK_TOPS, "unit": "TOPS",
+                         "frac": round(tops(pre["gemm_ms"]) / I8_PEAK_TOPS, 4),
                          "traffic": traffic_of(PREFILL_TRAFFIC),
-                         "gemm_ms": round(pre["gemm_region_ms"], 5)},
+                         "bytes_per_launch": pre["bytes"]},
         }
     if not args.no_extra:
-        log("bench: decode context shapes")
-        line["decode_context"] = bench_decode_extra(stream, min(args.steps, 100))
+        log("bench: W4A8 M=1 two launches vs fused")
+        line["decode_context"] = {"w4a8_m1": bench_decode_w4a8(stream, min(args.steps, 100),
+                                                               flush)}
     if not args.no_cpu:
+        from gemv_nibble_unpack_amd import workloads as WL
         log("bench: cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline_decode(c)
+        line["cpu_baseline"] = cpu_baseline_decode(WL.W4A16_DECODE)
         if not args.no_prefill:
-            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(WL_prefill())
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(WL.W4A8_PREFILL)
     print(json.dumps(line), flush=True)
-
-
-def WL_prefill():
-    from gemv_nibble_unpack_amd import workloads as WL
-    return WL.W4A8_PREFILL
 
 
 if __name__ == "__main__":

@@ -17,7 +17,7 @@ W4_IN_F16, W4_IN_F32 = 0, 1
 W4_LAYOUT_W4A8, W4_LAYOUT_W4A16, W4_LAYOUT_W2A8, W4_LAYOUT_W8A8 = 0, 1, 2, 3
 W4_OP_W4A8, W4_OP_W4A16, W4_OP_W2A8, W4_OP_W2A16, W4_OP_W8A8, W4_OP_F8F8 = 0, 1, 2, 3, 4, 5
 W4_GROUP_SIZE = 128
-W4_MAX_K = 131072
+W4_MAX_K = 131056
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -52,6 +52,7 @@ SIGNATURES = {
     "w4_plan_current": (_i, [_i, _i, _i, _i]),
     "w4_plan_reset": (_i, []),
     "w4_plan_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "w4_read_probe": (_i, [_p, _sz, _i, _p, _p]),
 }
 
 _LIB = None

@@ -12,10 +12,20 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _tstream(stream):
+    """The torch stream a call runs on (None: the current stream)."""
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    return _tstream(stream).cuda_stream
+
+
+def _empty(shape, dtype, dev, stream):
+    """An output buffer from the caching pool of the stream the kernel runs on,
+    so that the pool hands the memory out again only behind that kernel."""
+    with torch.cuda.stream(_tstream(stream)):
+        return torch.empty(shape, dtype=dtype, device=dev)
 
 
 def _dev(t):
@@ -30,18 +40,34 @@ class Workspace:
     """A zero-filled device workspace that grows on demand.
 
     The matmul kernels leave the part they rely on zero after each call, so
-    one workspace serves any number of calls issued on one stream.
+    one workspace serves any number of calls issued on one stream. The buffer
+    is allocated and zero-filled on the stream of the call that needs it; a
+    call on another stream first waits for the stream that used it last, so
+    calls sharing a workspace never overlap.
     """
 
     def __init__(self, device=None):
         self.device = torch.device(device or "cuda")
         self.buf = None
+        self.stream = None          # the stream that used the buffer last
+        self.alloc_stream = None    # the stream the buffer was allocated on
 
-    def get(self, nbytes):
+    def get(self, nbytes, stream=None):
         if nbytes == 0:
             return None
+        s = _tstream(stream)
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            if self.buf is not None and self.stream is not None and self.stream != s:
+                s.wait_stream(self.stream)      # the old buffer's last user first
+            with torch.cuda.stream(s):
+                self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self.alloc_stream = s
+        elif self.stream is not None and self.stream != s:
+            s.wait_stream(self.stream)
+        if s != self.alloc_stream:
+            # keep the pool from handing the memory out while s may still use it
+            self.buf.record_stream(s)
+        self.stream = s
         return self.buf
 
 
@@ -49,16 +75,16 @@ def quantize_pack_w4(W, scheme=L.W4_SYM_PER_CHANNEL, group_size=None, stream=Non
     """float32 [N,K] -> (Wq uint8 [N,K/2], scales, zeros-or-None)."""
     dev = _dev(W)
     N, K = W.shape
-    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    Wq = _empty((N, K // 2), torch.uint8, dev, stream)
     if scheme == L.W4_SYM_PER_CHANNEL:
         gs = -1 if group_size is None else group_size
-        scales = torch.empty(N, dtype=torch.float32, device=dev)
+        scales = _empty(N, torch.float32, dev, stream)
         zeros = None
     else:
         gs = L.W4_GROUP_SIZE if group_size is None else group_size
         G = K // L.W4_GROUP_SIZE
-        scales = torch.empty((N, G), dtype=torch.float16, device=dev)
-        zeros = torch.empty((N, G), dtype=torch.uint8, device=dev)
+        scales = _empty((N, G), torch.float16, dev, stream)
+        zeros = _empty((N, G), torch.uint8, dev, stream)
     L.check("quantize_pack_w4", L.load().quantize_pack_w4(
         _ptr(W), N, K, scheme, gs, _ptr(Wq), _ptr(scales), _ptr(zeros), _stream(stream)))
     return Wq, scales, zeros
@@ -68,7 +94,7 @@ def quantize_pack_w2(codes, stream=None):
     """int8 codes [N,K] in [-2,1] -> uint8 [N,K/4]."""
     dev = _dev(codes)
     N, K = codes.shape
-    Wq = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    Wq = _empty((N, K // 4), torch.uint8, dev, stream)
     L.check("quantize_pack_w2", L.load().quantize_pack_w2(_ptr(codes), N, K, _ptr(Wq),
                                                           _stream(stream)))
     return Wq
@@ -77,7 +103,7 @@ def quantize_pack_w2(codes, stream=None):
 def ternary_scale_f16(src, stream=None):
     """float32 tensor -> fp16 [1] device tensor holding fp16(mean|src|)."""
     dev = _dev(src)
-    out = torch.empty(1, dtype=torch.float16, device=dev)
+    out = _empty(1, torch.float16, dev, stream)
     L.check("ternary_scale_f16", L.load().ternary_scale_f16(_ptr(src), src.numel(), _ptr(out),
                                                             _stream(stream)))
     return out
@@ -93,7 +119,7 @@ def prepack_w(layout, Wq, N, K, scales=None, zeros=None, stream=None):
     nbytes = prepack_bytes(layout, N, K)
     if nbytes == 0:
         raise L.W4Error("prepack_bytes", L.W4_ERR_SHAPE)
-    Wp = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    Wp = _empty(nbytes, torch.uint8, dev, stream)
     L.check("prepack_w", L.load().prepack_w(layout, _ptr(Wq), _ptr(scales), _ptr(zeros), N, K,
                                             _ptr(Wp), _stream(stream)))
     return Wp
@@ -103,12 +129,12 @@ def unprepack_w(layout, Wp, N, K, stream=None):
     """Inverse of prepack_w -> (Wq, scales-or-None, zeros-or-None)."""
     dev = _dev(Wp)
     rowbytes = {L.W4_LAYOUT_W2A8: K // 4, L.W4_LAYOUT_W8A8: K}.get(layout, K // 2)
-    Wq = torch.empty((N, rowbytes), dtype=torch.uint8, device=dev)
+    Wq = _empty((N, rowbytes), torch.uint8, dev, stream)
     scales = zeros = None
     if layout == L.W4_LAYOUT_W4A16:
         G = K // L.W4_GROUP_SIZE
-        scales = torch.empty((N, G), dtype=torch.float16, device=dev)
-        zeros = torch.empty((N, G), dtype=torch.uint8, device=dev)
+        scales = _empty((N, G), torch.float16, dev, stream)
+        zeros = _empty((N, G), torch.uint8, dev, stream)
     L.check("unprepack_w", L.load().unprepack_w(layout, _ptr(Wp), N, K, _ptr(Wq), _ptr(scales),
                                                 _ptr(zeros), _stream(stream)))
     return Wq, scales, zeros
@@ -125,9 +151,9 @@ def quantize_a8(A, with_rowsum=True, out=None, stream=None):
     else:
         raise ValueError("A must be float16 or float32")
     if out is None:
-        Aq = torch.empty((M, K), dtype=torch.int8, device=dev)
-        sa = torch.empty(M, dtype=torch.float32, device=dev)
-        rs = torch.empty(M, dtype=torch.int32, device=dev) if with_rowsum else None
+        Aq = _empty((M, K), torch.int8, dev, stream)
+        sa = _empty(M, torch.float32, dev, stream)
+        rs = _empty(M, torch.int32, dev, stream) if with_rowsum else None
     else:
         Aq, sa, rs = out
     L.check("quantize_a8", L.load().quantize_a8(_ptr(A), dt, M, K, _ptr(Aq), _ptr(sa), _ptr(rs),
@@ -159,13 +185,13 @@ _OUT_DT = {L.W4_OUT_F16: torch.float16, L.W4_OUT_F32: torch.float32, L.W4_OUT_I3
            L.W4_OUT_I8: torch.int8}
 
 
-def _workspace(ws, op, M, N, K, dev):
+def _workspace(ws, op, M, N, K, dev, stream):
     need = w4_plan_workspace_bytes(op, M, N, K)
     if need == 0:
         return None, 0
     if ws is None:
         ws = Workspace(dev)
-    buf = ws.get(need) if isinstance(ws, Workspace) else ws
+    buf = ws.get(need, stream) if isinstance(ws, Workspace) else ws
     return buf, buf.numel()
 
 
@@ -174,8 +200,8 @@ def w4a8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, wo
     dev = _dev(Aq)
     M, K = Aq.shape
     if C is None:
-        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
-    buf, nb = _workspace(workspace, L.W4_OP_W4A8, M, N, K, dev)
+        C = _empty((M, N), _OUT_DT[out_dtype], dev, stream)
+    buf, nb = _workspace(workspace, L.W4_OP_W4A8, M, N, K, dev, stream)
     L.check("w4a8_gemm", L.load().w4a8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale),
                                             _ptr(bias), _ptr(C), out_dtype, M, N, K, _ptr(buf), nb,
                                             _stream(stream)))
@@ -187,8 +213,8 @@ def w2a8_gemm(Aq, a_scale, Wp, w_scale16, N, bias=None, out_dtype=L.W4_OUT_F16, 
     dev = _dev(Aq)
     M, K = Aq.shape
     if C is None:
-        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
-    buf, nb = _workspace(workspace, L.W4_OP_W2A8, M, N, K, dev)
+        C = _empty((M, N), _OUT_DT[out_dtype], dev, stream)
+    buf, nb = _workspace(workspace, L.W4_OP_W2A8, M, N, K, dev, stream)
     L.check("w2a8_gemm", L.load().w2a8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale16),
                                             _ptr(bias), _ptr(C), out_dtype, M, N, K, _ptr(buf), nb,
                                             _stream(stream)))
@@ -200,8 +226,8 @@ def w4a16_gemm(A, Wp, N, bias=None, workspace=None, C=None, group_size=L.W4_GROU
     dev = _dev(A)
     M, K = A.shape
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=dev)
-    buf, nb = _workspace(workspace, L.W4_OP_W4A16, M, N, K, dev)
+        C = _empty((M, N), torch.float16, dev, stream)
+    buf, nb = _workspace(workspace, L.W4_OP_W4A16, M, N, K, dev, stream)
     L.check("w4a16_gemm", L.load().w4a16_gemm(_ptr(A), _ptr(Wp), group_size, _ptr(bias), _ptr(C),
                                               M, N, K, _ptr(buf), nb, _stream(stream)))
     return C
@@ -212,8 +238,8 @@ def w2a16_gemm(A, Wp, w_scale16, N, bias=None, workspace=None, C=None, stream=No
     dev = _dev(A)
     M, K = A.shape
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=dev)
-    buf, nb = _workspace(workspace, L.W4_OP_W2A16, M, N, K, dev)
+        C = _empty((M, N), torch.float16, dev, stream)
+    buf, nb = _workspace(workspace, L.W4_OP_W2A16, M, N, K, dev, stream)
     L.check("w2a16_gemm", L.load().w2a16_gemm(_ptr(A), _ptr(Wp), _ptr(w_scale16), _ptr(bias),
                                               _ptr(C), M, N, K, _ptr(buf), nb, _stream(stream)))
     return C
@@ -222,8 +248,8 @@ def quantize_pack_w8(W, stream=None):
     """float32 [N,K] -> (Wq int8 [N,K], scales float32 [N]): symmetric INT8 per row."""
     dev = _dev(W)
     N, K = W.shape
-    Wq = torch.empty((N, K), dtype=torch.int8, device=dev)
-    scales = torch.empty(N, dtype=torch.float32, device=dev)
+    Wq = _empty((N, K), torch.int8, dev, stream)
+    scales = _empty(N, torch.float32, dev, stream)
     L.check("quantize_pack_w8", L.load().quantize_pack_w8(_ptr(W), N, K, _ptr(Wq), _ptr(scales),
                                                           _stream(stream)))
     return Wq, scales
@@ -235,8 +261,8 @@ def w8a8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, ou
     dev = _dev(Aq)
     M, K = Aq.shape
     if C is None:
-        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
-    buf, nb = _workspace(workspace, L.W4_OP_W8A8, M, N, K, dev)
+        C = _empty((M, N), _OUT_DT[out_dtype], dev, stream)
+    buf, nb = _workspace(workspace, L.W4_OP_W8A8, M, N, K, dev, stream)
     L.check("w8a8_gemm", L.load().w8a8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale),
                                             _ptr(bias), _ptr(out_scale), _ptr(C), out_dtype, M, N,
                                             K, _ptr(buf), nb, _stream(stream)))
@@ -253,8 +279,8 @@ def quantize_f8(X, stream=None):
         dt = L.W4_IN_F32
     else:
         raise ValueError("X must be float16 or float32")
-    Xq = torch.empty((R, K), dtype=torch.uint8, device=dev)
-    scales = torch.empty(R, dtype=torch.float32, device=dev)
+    Xq = _empty((R, K), torch.uint8, dev, stream)
+    scales = _empty(R, torch.float32, dev, stream)
     L.check("quantize_f8", L.load().quantize_f8(_ptr(X), dt, R, K, _ptr(Xq), _ptr(scales),
                                                 _stream(stream)))
     return Xq, scales
@@ -266,8 +292,8 @@ def f8f8_gemm(Aq, a_scale, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, wo
     dev = _dev(Aq)
     M, K = Aq.shape
     if C is None:
-        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
-    buf, nb = _workspace(workspace, L.W4_OP_F8F8, M, N, K, dev)
+        C = _empty((M, N), _OUT_DT[out_dtype], dev, stream)
+    buf, nb = _workspace(workspace, L.W4_OP_F8F8, M, N, K, dev, stream)
     L.check("f8f8_gemm", L.load().f8f8_gemm(_ptr(Aq), _ptr(a_scale), _ptr(Wp), _ptr(w_scale),
                                             _ptr(bias), _ptr(C), out_dtype, M, N, K, _ptr(buf),
                                             nb, _stream(stream)))
@@ -336,13 +362,13 @@ def _fused(name, layout, A, Wp, scale, N, bias, out_dtype, workspace, C, stream)
     else:
         raise ValueError("A must be float16 or float32")
     if C is None:
-        C = torch.empty((M, N), dtype=_OUT_DT[out_dtype], device=dev)
+        C = _empty((M, N), _OUT_DT[out_dtype], dev, stream)
     need = w4_fused_act_workspace_bytes(layout, M, N, K)
     buf, nb = None, 0
     if need:
         if workspace is None:
             workspace = Workspace(dev)
-        buf = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+        buf = workspace.get(need, stream) if isinstance(workspace, Workspace) else workspace
         nb = buf.numel()
     L.check(name, getattr(L.load(), name)(_ptr(A), dt, _ptr(Wp), _ptr(scale), _ptr(bias), _ptr(C),
                                           out_dtype, M, N, K, _ptr(buf), nb, _stream(stream)))
@@ -361,3 +387,16 @@ def w2a8_gemm_fused_act(A, Wp, w_scale16, N, bias=None, out_dtype=L.W4_OUT_F16, 
     """fp16/float32 A [M,K] -> quantize_a8 + w2a8_gemm in one C call."""
     return _fused("w2a8_gemm_fused_act", L.W4_LAYOUT_W2A8, A, Wp, w_scale16, N, bias, out_dtype,
                   workspace, C, stream)
+
+
+def w4_read_probe(buf, nbytes=None, per=4, sink=None, stream=None):
+    """Read ``nbytes`` (default: all) of the uint8 device tensor ``buf`` once
+    with 16-byte loads: the plain streaming read a weight-streaming kernel of
+    the same size is measured against. ``sink`` is a device uint32 [1024]."""
+    dev = _dev(buf)
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if sink is None:
+        sink = _empty(1024, torch.int32, dev, stream)
+    L.check("w4_read_probe", L.load().w4_read_probe(_ptr(buf), nbytes, per, _ptr(sink),
+                                                    _stream(stream)))
+    return sink

@@ -599,9 +599,11 @@ extern "C" size_t w4_fused_act_workspace_bytes(int layout, int M, int N, int K) 
 extern "C" int quantize_a8(const void* A, int in_dtype, int M, int K, int8_t* Aq, float* a_scale,
                            int32_t* rowsum, hipStream_t stream);
 
-static int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp,
-                        const void* scale, const uint16_t* bias, void* C, int out_dtype, int M,
-                        int N, int K, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace w4 {
+
+// Argument checks of the fused entry points (everything but the workspace).
+int fused_check(int kind, const void* A, int in_dtype, const uint8_t* Wp, const void* scale,
+                const uint16_t* bias, void* C, int out_dtype, int M, int N, int K) {
   if (in_dtype != W4_IN_F16 && in_dtype != W4_IN_F32) return W4_ERR_ARG;
   if (out_dtype != W4_OUT_F16 && out_dtype != W4_OUT_F32 && out_dtype != W4_OUT_I32)
     return W4_ERR_ARG;
@@ -612,6 +614,16 @@ static int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp
   if (!aligned(A, 16) || !aligned(Wp, 16) || !out_aligned(C, out_dtype) ||
       (bias && !aligned(bias, 2)) || !aligned(scale, kind == KIND_W4A8 ? 4 : 2))
     return W4_ERR_ALIGN;
+  return W4_OK;
+}
+
+// The fused call: quantize_a8 into the workspace and the A8 matmul (two
+// launches), or one decode kernel that quantizes in its prologue.
+int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp, const void* scale,
+                 const uint16_t* bias, void* C, int out_dtype, int M, int N, int K, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  const int st = fused_check(kind, A, in_dtype, Wp, scale, bias, C, out_dtype, M, N, K);
+  if (st != W4_OK || M == 0) return st;
   const FusedPlan F = fused_plan(kind, M, N, K);
   if (F.ws_bytes) {
     if (!ws || ws_bytes < F.ws_bytes) return W4_ERR_WORKSPACE;
@@ -644,6 +656,8 @@ static int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp
   return kind == KIND_W4A8 ? launch_gemv<KIND_W4A8>(F.P, p, ws, stream, fq, F.fqc)
                            : launch_gemv<KIND_W2A8>(F.P, p, ws, stream, fq, F.fqc);
 }
+
+}  // namespace w4
 
 extern "C" int w4a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp,
                                    const float* w_scale, const uint16_t* bias, void* C,

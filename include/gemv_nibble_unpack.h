@@ -31,8 +31,13 @@
  *   aligned; small vectors (scales, zeros, bias, a_scale, rowsum) need their
  *   natural alignment.
  * - Sizes: N >= 1, K >= 1, M >= 1 (M = 0 is accepted by the matmul entry
- *   points and returns W4_OK without a launch). K is limited to 131072 so that
- *   INT32 accumulators cannot overflow.
+ *   points and returns W4_OK without a launch). K is limited to W4_MAX_K =
+ *   131056 so that INT32 accumulators cannot overflow for ANY int8 activation
+ *   and ANY stored weight code: the kernels sum products scaled by 16 (4-bit
+ *   codes) or 64 (2-bit codes), whose magnitude is at most 16 * 128 * 8 =
+ *   64 * 128 * 2 = 128 * 128 = 16384, and 16384 * 131056 < 2^31 <= 16384 *
+ *   131072 (the next multiple of 16 would overflow when every activation is
+ *   -128 and every code is -8, -2 or -128).
  */
 #ifndef GEMV_NIBBLE_UNPACK_H
 #define GEMV_NIBBLE_UNPACK_H
@@ -81,7 +86,7 @@ extern "C" {
 #define W4_OP_F8F8  5         /* f8f8_gemm                                    */
 
 #define W4_GROUP_SIZE 128
-#define W4_MAX_K 131072
+#define W4_MAX_K 131056
 
 /* Human-readable text for a status code (static string, never NULL). */
 const char* w4_status_string(int status);
@@ -256,8 +261,8 @@ int quantize_pack_w8(const float* W, int N, int K, int8_t* Wq, float* scales,
  * row INT8 x INT8, INT32 accumulation, INT8 output; INT4 page, Part 1 step 3:
  * the INT32 result either dequantized or handed to a following quantized
  * layer):
- *   acc[m,n] = sum_k Aq[m,k] * q[n,k] (exact INT32; K <= 131072 keeps it in
- *   range), then as w4a8_gemm for W4_OUT_I32 / W4_OUT_F32 / W4_OUT_F16, and
+ *   acc[m,n] = sum_k Aq[m,k] * q[n,k] (exact INT32; K <= W4_MAX_K keeps it
+ *   in range), then as w4a8_gemm for W4_OUT_I32 / W4_OUT_F32 / W4_OUT_F16, and
  *   W4_OUT_I8: v = float32(float32(float32(acc) * w_scale[n]) * a_scale[m]),
  *   C = clip(rint(v / out_scale[0]), -127, 127) (int8[M,N]; float32 division,
  *   half to even; an out_scale of 0 gives 0), bias must be NULL.
@@ -388,6 +393,21 @@ int w4_plan_reset(void);
  * W4_OP_W2A16 needs this query, since it shares the W2A8 layout but not the
  * W2A8 op's pin. */
 size_t w4_plan_workspace_bytes(int op, int M, int N, int K);
+
+/* ---- measurement aid -------------------------------------------------------
+ * w4_read_probe -- read `bytes` of device memory at `buf` once with 16-byte
+ * loads and do nothing else (`per` = 1, 2, 4 or 8 loads per lane, all issued
+ * before any is used; 256 lanes per block; every wave instruction reads 1 KiB
+ * contiguous). Not a step of the matmul: the INT4 page's T4 discussion names
+ * memory bandwidth as what a weight-streaming GEMV is bound by, and this is
+ * the plain streaming read that such a kernel of the same size is measured
+ * against (the read rate the chip reaches for that transfer, launch and drain
+ * included). `sink` is a device uint32[1024]; the kernel writes it only when
+ * the XOR of a block's data equals a fixed constant, which keeps the loads
+ * from being removed. bytes >= 16 and a multiple of 16; buf 16-byte aligned;
+ * W4_ERR_ARG for another `per`.
+ */
+int w4_read_probe(const void* buf, size_t bytes, int per, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

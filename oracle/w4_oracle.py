@@ -83,6 +83,7 @@ __all__ = [
     "quantize_a8",
     "int_accumulate",
     "int_accumulate_entries",
+    "int_accumulate_f64",
     "dequant_epilogue",
     "w4a8_gemm",
     "w2a16_gemm",
@@ -261,6 +262,30 @@ def int_accumulate(qa, qw):
     Computed exactly in int64 and checked to fit int32.
     """
     acc = np.asarray(qa, np.int64) @ np.asarray(qw, np.int64).T
+    if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -(2**31)):
+        raise OverflowError("accumulator exceeds int32")
+    return acc
+
+
+def int_accumulate_f64(qa, qw):
+    """The INT32 accumulators of ``int_accumulate`` through a float64 matrix
+    product of the codes (a library routine, so full-size outputs check in
+    seconds where the int64 product would take minutes).
+
+    Exact: every product of two codes is an integer of magnitude at most
+    max|qa| * max|qw|, and every partial sum, in whatever order the routine
+    adds, is an integer no larger than K times that; below 2^53 float64
+    represents all of them exactly, so no addition rounds. The bound is
+    checked from the inputs before the product is taken.
+    """
+    qa = np.asarray(qa)
+    qw = np.asarray(qw)
+    K = qa.shape[1]
+    amax = int(np.max(np.abs(qa.astype(np.int64)))) if qa.size else 0
+    wmax = int(np.max(np.abs(qw.astype(np.int64)))) if qw.size else 0
+    if K * amax * wmax >= 2**53:
+        raise OverflowError("float64 sums would round")
+    acc = (qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
     if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -(2**31)):
         raise OverflowError("accumulator exceeds int32")
     return acc

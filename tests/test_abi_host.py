@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -68,7 +68,7 @@ def test_sizes():
     assert lib.prepack_bytes(L.W4_LAYOUT_W8A8, 4096, 4096) == 4096 * 4096
     assert lib.prepack_bytes(L.W4_LAYOUT_W8A8, 50, 208) == 4 * 4 * 1024
     assert lib.w4_workspace_bytes(L.W4_LAYOUT_W4A16, 1, 4096, 4096) == 0
-    assert lib.w4_workspace_bytes(L.W4_LAYOUT_W2A8, 1, 16, 131072) > 0
+    assert lib.w4_workspace_bytes(L.W4_LAYOUT_W2A8, 1, 16, 131056) > 0
     # fused activation quantization: decode rows that fit LDS need nothing;
     # 16 rows of 4096 quantize into the workspace first (int8 rows + scales)
     assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A8, 1, 4096, 4096) == 0
@@ -106,14 +106,14 @@ def test_error_paths_before_launch():
     assert lib.w4a8_gemm(None, P, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_NULL
     assert lib.w4a8_gemm(MIS, P, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
     assert lib.w4a8_gemm(None, None, None, None, None, None, 0, 0, 16, 32, None, 0, s) == L.W4_OK
-    assert lib.w2a8_gemm(P, P, P, P, None, P2, 0, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
+    assert lib.w2a8_gemm(P, P, P, P, None, P2, 0, 1, 16, 131056, None, 0, s) == L.W4_ERR_WORKSPACE
     assert lib.w4a16_gemm(P, P, 64, None, P2, 1, 16, 128, None, 0, s) == L.W4_ERR_ARG
     assert lib.w4a16_gemm(P, P, 128, None, P2, 1, 16, 192, None, 0, s) == L.W4_ERR_SHAPE
     assert lib.w2a16_gemm(P, P, P, None, P2, 1, 16, 24, None, 0, s) == L.W4_ERR_SHAPE
     assert lib.w2a16_gemm(P, P, None, None, P2, 1, 16, 32, None, 0, s) == L.W4_ERR_NULL
     assert lib.w2a16_gemm(MIS, P, P, None, P2, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
     assert lib.w2a16_gemm(None, None, None, None, None, 0, 16, 32, None, 0, s) == L.W4_OK
-    assert lib.w2a16_gemm(P, P, P, None, P2, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
+    assert lib.w2a16_gemm(P, P, P, None, P2, 1, 16, 131056, None, 0, s) == L.W4_ERR_WORKSPACE
     # INT8 weights and the INT8-output matmul
     assert lib.quantize_pack_w8(P, 4, 24, P, P2, s) == L.W4_ERR_SHAPE
     assert lib.quantize_pack_w8(None, 4, 32, P, P2, s) == L.W4_ERR_NULL
@@ -139,8 +139,8 @@ def test_error_paths_before_launch():
     assert lib.f8f8_gemm(MIS, P, P, P, None, P2, L.W4_OUT_F16, 1, 16, 32, None, 0,
                          s) == L.W4_ERR_ALIGN
     assert lib.f8f8_gemm(None, None, None, None, None, None, 0, 0, 16, 32, None, 0, s) == L.W4_OK
-    assert lib.f8f8_gemm(*f8, L.W4_OUT_F16, 1, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
-    assert lib.w4_plan_workspace_bytes(L.W4_OP_F8F8, 1, 16, 131072) > 16384
+    assert lib.f8f8_gemm(*f8, L.W4_OUT_F16, 1, 16, 131056, None, 0, s) == L.W4_ERR_WORKSPACE
+    assert lib.w4_plan_workspace_bytes(L.W4_OP_F8F8, 1, 16, 131056) > 16384
     # the other A8 matmuls have no INT8 output
     assert lib.w4a8_gemm(P, P, P, P, None, P2, L.W4_OUT_I8, 1, 16, 32, None, 0, s) == L.W4_ERR_ARG
     # fused activation quantization
@@ -151,7 +151,7 @@ def test_error_paths_before_launch():
         assert fn(None, 0, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_NULL
         assert fn(MIS, 0, P, P, None, P2, 0, 1, 16, 32, None, 0, s) == L.W4_ERR_ALIGN
         assert fn(None, 0, None, None, None, None, 0, 0, 16, 32, None, 0, s) == L.W4_OK
-        assert fn(P, 1, P, P, None, P2, 0, 16, 16, 131072, None, 0, s) == L.W4_ERR_WORKSPACE
+        assert fn(P, 1, P, P, None, P2, 0, 16, 16, 131056, None, 0, s) == L.W4_ERR_WORKSPACE
 
 
 def _names(lib, op, M, N, K):
@@ -161,6 +161,18 @@ def _names(lib, op, M, N, K):
         assert lib.w4_plan_name(op, M, N, K, i, buf, 64) == L.W4_OK
         out.append(buf.value.decode())
     return out
+
+
+def test_read_probe_error_paths():
+    lib = G.load()
+    s = None
+    sink = P2
+    assert lib.w4_read_probe(None, 1024, 4, sink, s) == L.W4_ERR_NULL
+    assert lib.w4_read_probe(P, 1024, 4, None, s) == L.W4_ERR_NULL
+    assert lib.w4_read_probe(P, 0, 4, sink, s) == L.W4_ERR_SHAPE
+    assert lib.w4_read_probe(P, 1000, 4, sink, s) == L.W4_ERR_SHAPE
+    assert lib.w4_read_probe(P, 1024, 3, sink, s) == L.W4_ERR_ARG
+    assert lib.w4_read_probe(MIS, 1024, 4, sink, s) == L.W4_ERR_ALIGN
 
 
 def test_plan_table_candidates():
@@ -223,13 +235,13 @@ def test_plan_table_candidates():
     for op in (L.W4_OP_W4A16, L.W4_OP_W2A16, L.W4_OP_W8A8):
         assert not any(n.startswith("gemm") for n in _names(lib, op, 2048, 4096, 4096))
     # a tiny-N, huge-K decode splits K 64 ways on its own (one output tile)
-    names = _names(lib, L.W4_OP_W2A8, 1, 16, 131072)
-    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 1, 16, 131072)] == "decode:ksplit=64"
+    names = _names(lib, L.W4_OP_W2A8, 1, 16, 131056)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 1, 16, 131056)] == "decode:ksplit=64"
 
 
 def test_plan_table_pin_and_workspace():
     lib = G.load()
-    op, lay, M, N, K = L.W4_OP_W2A8, L.W4_LAYOUT_W2A8, 1, 16, 131072
+    op, lay, M, N, K = L.W4_OP_W2A8, L.W4_LAYOUT_W2A8, 1, 16, 131056
     assert lib.w4_plan_reset() == L.W4_OK
     # built-in: 64-way split, 16 KiB counter area + 64 partial tiles of 1 KiB
     assert lib.w4_workspace_bytes(lay, M, N, K) == 16384 + 64 * 1024
@@ -245,7 +257,7 @@ def test_plan_table_pin_and_workspace():
     assert lib.w4_workspace_bytes(lay, M, N, K - 256) > 0
     # the fused entry points share the W2A8 op's plan: unsplit, the 128 KiB
     # row does not fit the LDS staging, so it is quantized into the workspace
-    assert lib.w4_fused_act_workspace_bytes(lay, M, N, K) == 16384 + K + 256
+    assert lib.w4_fused_act_workspace_bytes(lay, M, N, K) == 16384 + (K + 255) // 256 * 256 + 256
     builtin = _names(lib, op, M, N, K).index("decode:ksplit=64")
     assert lib.w4_plan_pin(op, M, N, K, -1) == L.W4_OK
     assert lib.w4_plan_current(op, M, N, K) == builtin
@@ -274,8 +286,8 @@ def test_plan_table_errors():
     assert lib.w4_plan_pin(L.W4_OP_W4A8, 1, 16, 128, n) == L.W4_ERR_ARG
     assert lib.w4_plan_pin(L.W4_OP_W4A8, 1, 16, 128, -2) == L.W4_ERR_ARG
     assert lib.w4_plan_pin(L.W4_OP_W4A8, 1, 16, 24, 0) == L.W4_ERR_SHAPE
-    assert lib.w4_plan_workspace_bytes(9, 1, 16, 131072) == 0
-    assert lib.w4_plan_workspace_bytes(L.W4_OP_W2A8, 0, 16, 131072) == 0
+    assert lib.w4_plan_workspace_bytes(9, 1, 16, 131056) == 0
+    assert lib.w4_plan_workspace_bytes(L.W4_OP_W2A8, 0, 16, 131056) == 0
 
 
 def test_binding_refuses_host_tensors():

@@ -21,6 +21,22 @@ def test_prefill_bytes_w4a8_2048_11008_4096():
     assert bench.prefill_bytes(2048, 11008, 4096) == 76_096_000
 
 
+def test_timed_calls_read_cold_weights():
+    # Between two reads of one weight copy inside a timed region, more bytes
+    # than the last-level cache holds pass through memory: the flush before
+    # the region, or the other copies when the rotation comes round. This
+    # holds at the driver's step count and at the defaults, for the decode
+    # and the prefill copies.
+    for copy_bytes in (bench.decode_bytes(1, 4096, 4096), 4096 * 11008 // 2 + 3 * 11008 * 32,
+                       11008 * 4096 // 2):
+        R = bench.rotation(copy_bytes)
+        assert R * copy_bytes >= bench.ROTATE_BYTES
+        for steps in (1, 5, 20, 50, 200, 1000):
+            assert bench.cold_gap_bytes(steps, R, copy_bytes) > 2 * bench.LLC_BYTES
+    assert bench.FLUSH_BYTES >= 4 * bench.LLC_BYTES
+    assert bench.PREFILL_MIN_STEPS >= 50
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300, cwd=ROOT)

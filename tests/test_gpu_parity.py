@@ -233,7 +233,8 @@ def test_w4a8_small_shapes_bitexact(g, M, N, K):
            O.w4a8_gemm(qa_ref, sa_ref, q_ref, s_ref, bias, O.OUT_F16), "f16")
 
 
-def test_w4a8_prefill_config_sampled(g):
+def test_w4a8_prefill_config_full(g):
+    # every one of the M x N outputs: INT32 bit for bit, fp16 to the tolerance
     c = WL.W4A8_PREFILL
     say(f"case {c.name}")
     d = c.inputs()
@@ -245,17 +246,20 @@ def test_w4a8_prefill_config_sampled(g):
     q_ref, s_ref = O.quantize_w4_sym(d["W"])
     qa_ref, sa_ref, _ = O.quantize_a8(d["A"])
     assert np.array_equal(host(Aq), qa_ref)
-    rows, cols = sample_indices(c.M, c.N, 4000, seed=7)
-    acc = O.int_accumulate_entries(qa_ref, q_ref, rows, cols)
-    assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
-    ref16 = O.dequant_epilogue(acc, s_ref[cols], sa_ref[rows], bias[cols], O.OUT_F16)
-    tol_ok(C16[rows, cols], ref16, c.name)
+    assert np.array_equal(host(ws), s_ref)
+    acc = O.int_accumulate_f64(qa_ref, q_ref)
+    assert np.array_equal(C32, acc.astype(np.int32))
+    # the float64 route against the int64 sums on a sample
+    rows, cols = sample_indices(c.M, c.N, 2000, seed=7)
+    assert np.array_equal(acc[rows, cols], O.int_accumulate_entries(qa_ref, q_ref, rows, cols))
+    tol_ok(C16, O.dequant_epilogue(acc, s_ref[None, :], sa_ref[:, None], bias[None, :],
+                                   O.OUT_F16), c.name)
 
 
 @pytest.mark.parametrize("scheme,M,N,K", [("w4a8", 2000, 3000, 1040), ("w4a8", 1100, 4004, 512),
                                           ("w4a8", 2000, 11000, 1040), ("w4a8", 1900, 11004, 512),
                                           ("w2a8", 2000, 3000, 1040), ("w2a8", 1030, 4100, 528)])
-def test_gemm_path_ragged_sampled(g, scheme, M, N, K):
+def test_gemm_path_ragged_full(g, scheme, M, N, K):
     # shapes large enough for the tiled prefill GEMM (>= 128 tiles), with
     # ragged M, N (N % 8 != 0 takes the direct epilogue) and K tails; the
     # N ~ 11000 shapes run 22-tile (352-column) blocks, the others 16 or 8
@@ -269,30 +273,20 @@ def test_gemm_path_ragged_sampled(g, scheme, M, N, K):
         Wp, ws = prep_w4a8(g, W)
         qw, s_ref = O.quantize_w4_sym(W)
         mm = g.w4a8_gemm
-        ws_ref = lambda cols: s_ref[cols]
+        ws_ref = s_ref[None, :]
     else:
         codes = WL.ternary_codes(N, K, seed=8003 + N)
         Wp, ws = prep_w2a8(g, codes, WL.weights_f32(N, K, seed=8004 + N))
         qw = codes
         mm = g.w2a8_gemm
-        scale = np.float64(host(ws)[0])
-        ws_ref = lambda cols: np.full(len(cols), scale)
+        ws_ref = np.float64(host(ws)[0])
     C32 = host(mm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I32))
     C16 = host(mm(Aq, sa, Wp, ws, N, bias=f16(bias), out_dtype=g.W4_OUT_F16))
     C32f = host(mm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_F32))
-    rows, cols = sample_indices(M, N, 3000, seed=11)
-    acc = O.int_accumulate_entries(qa, qw, rows, cols)
-    assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
-    tol_ok(C16[rows, cols], O.dequant_epilogue(acc, ws_ref(cols), sa_ref[rows], bias[cols],
-                                               O.OUT_F16), "f16")
-    tol_ok(C32f[rows, cols], O.dequant_epilogue(acc, ws_ref(cols), sa_ref[rows], None,
-                                                O.OUT_F32), "f32")
-    # the last rows and columns (tails) in full
-    tail_r = np.arange(max(0, M - 3), M)
-    tail_c = np.arange(max(0, N - 40), N)
-    rr, cc = np.meshgrid(tail_r, tail_c, indexing="ij")
-    acc_t = O.int_accumulate_entries(qa, qw, rr.ravel(), cc.ravel())
-    assert np.array_equal(C32[rr, cc].ravel(), acc_t.astype(np.int32))
+    acc = O.int_accumulate_f64(qa, qw)
+    assert np.array_equal(C32, acc.astype(np.int32))
+    tol_ok(C16, O.dequant_epilogue(acc, ws_ref, sa_ref[:, None], bias[None, :], O.OUT_F16), "f16")
+    tol_ok(C32f, O.dequant_epilogue(acc, ws_ref, sa_ref[:, None], None, O.OUT_F32), "f32")
 
 
 def _w4a16_case(g, c, full=True):
@@ -345,16 +339,10 @@ def test_w2a8_ternary(g, c):
     C16 = host(g.w2a8_gemm(Aq, sa, Wp, s16, c.N, out_dtype=g.W4_OUT_F16))
     qa, sa_ref, _ = O.quantize_a8(d["A"])
     scale = host(s16)[0]
-    if c.M == 1:
-        acc = O.int_accumulate(qa, d["codes"])
-        assert np.array_equal(C32, acc.astype(np.int32))
-        tol_ok(C16, O.w2a8_gemm(qa, sa_ref, d["codes"], scale, None, O.OUT_F16), c.name)
-    else:
-        rows, cols = sample_indices(c.M, c.N, 3000, seed=9)
-        acc = O.int_accumulate_entries(qa, d["codes"], rows, cols)
-        assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
-        ref = O.dequant_epilogue(acc, np.float64(scale), sa_ref[rows], None, O.OUT_F16)
-        tol_ok(C16[rows, cols], ref, c.name)
+    acc = O.int_accumulate_f64(qa, d["codes"])
+    assert np.array_equal(C32, acc.astype(np.int32))
+    tol_ok(C16, O.dequant_epilogue(acc, np.float64(scale), sa_ref[:, None], None, O.OUT_F16),
+           c.name)
 
 
 @pytest.mark.parametrize("M,N,K", [(65, 24, 48), (200, 130, 1040), (33, 4100, 256)])
@@ -373,17 +361,36 @@ def test_w2a8_ragged_bitexact(g, M, N, K):
     tol_ok(C16, O.w2a8_gemm(qa, sa_ref, codes, host(s16)[0], b, O.OUT_F16), "w2a8 ragged")
 
 
-def test_w2a8_extreme_codes_no_overflow(g):
-    # -2 codes (never produced by quantisation but decodable) times -127 at max K
-    say("case w2a8 extreme K=131072")
-    N, K = 16, 131072
-    codes = np.full((N, K), -2, np.int8)
-    Wp, _ = prep_w2a8(g, codes, np.ones((N, K), np.float32))
-    Aq = dev(np.full((1, K), -127, np.int8))
-    sa = dev(np.ones(1, np.float32))
-    s16 = f16(np.ones(1))
-    C32 = host(g.w2a8_gemm(Aq, sa, Wp, s16, N, out_dtype=g.W4_OUT_I32))
-    assert np.all(C32 == 254 * K)
+@pytest.mark.parametrize("kind", ["w4a8", "w2a8", "w8a8"])
+def test_extreme_codes_at_max_k_no_overflow(g, kind):
+    # The largest products the INT32 accumulators can meet: activation -128
+    # (a valid int8 the quantizer never makes) times the most negative stored
+    # code (-8 INT4, -2 INT2, -128 INT8; none is made by the quantizers but
+    # all decode), summed over the largest K the library accepts: 16384 * K
+    # sits just below 2^31. Row 1 mixes in +127 activations and row 1 of the
+    # weights the largest positive code, so the sums differ per entry.
+    K = g.W4_MAX_K
+    N = 16
+    say(f"case extreme codes {kind} K={K}")
+    qa = np.full((2, K), -128, np.int8)
+    qa[1, ::2] = 127
+    lo, hi = {"w4a8": (-8, 7), "w2a8": (-2, 1), "w8a8": (-128, 127)}[kind]
+    codes = np.full((N, K), lo, np.int8)
+    codes[1, 1::3] = hi
+    if kind == "w4a8":
+        Wq = dev(O.pack_int4(codes))
+        layout, mm, scale = g.W4_LAYOUT_W4A8, g.w4a8_gemm, dev(np.ones(N, np.float32))
+    elif kind == "w2a8":
+        Wq = dev(O.pack_int2(codes))
+        layout, mm, scale = g.W4_LAYOUT_W2A8, g.w2a8_gemm, f16(np.ones(1))
+    else:
+        Wq = dev(codes)
+        layout, mm, scale = g.W4_LAYOUT_W8A8, g.w8a8_gemm, dev(np.ones(N, np.float32))
+    Wp = g.prepack_w(layout, Wq, N, K)
+    C32 = host(mm(dev(qa), dev(np.ones(2, np.float32)), Wp, scale, N, out_dtype=g.W4_OUT_I32))
+    ref = O.int_accumulate(qa, codes)
+    assert ref[0, 0] == 16384 * K
+    assert np.array_equal(C32, ref.astype(np.int32))
 
 
 def test_matmul_m0_is_noop_and_errors(g):
@@ -466,9 +473,7 @@ def test_fused_act_matches_two_calls_and_oracle(g, scheme, M, N, K, dt):
         assert np.array_equal(ref, got), out
         if out == g.W4_OUT_I32:
             qa, _, _ = O.quantize_a8(A)
-            rows, cols = sample_indices(M, N, 2000, seed=13)
-            acc = O.int_accumulate_entries(qa, qw, rows, cols)
-            assert np.array_equal(got[rows, cols], acc.astype(np.int32))
+            assert np.array_equal(got, O.int_accumulate_f64(qa, qw).astype(np.int32))
 
 
 # ---------------------------------------------------------------------------
@@ -478,24 +483,39 @@ def test_decode_chain_graph_replays_match_eager(g):
     # A decode step's chain of GEMVs captured once and replayed: fp16 output
     # of one layer feeds the next (4096 -> 11008 -> 4096 -> 4096 -> 3200
     # columns), mixing W4A16, fused W4A8 and fused W2A8 calls, one of them
-    # split over K (workspace in use). Each replay, with eager work and a
-    # synchronization in between, must equal the eager chain bit for bit.
+    # split over K (workspace in use). Each layer's eager output is checked
+    # against the oracle applied to the GPU's fp16 input of that layer; each
+    # replay, with eager work and a synchronization in between, must equal
+    # the eager chain bit for bit.
     say("case decode chain graph capture")
     dims = [4096, 11008, 4096, 256, 3200]
     kinds = ["w4a16", "w4a8", "w4a16", "w2a8"]
-    layers = []
+    layers, refs = [], []
     for i, kind in enumerate(kinds):
         K, N = dims[i], dims[i + 1]
         W = WL.weights_f32(N, K, seed=9100 + i)
         if kind == "w4a16":
             layers.append((kind, prep_w4a16(g, W), None, N))
+            q, s16, z = O.quantize_w4_group(W, 128)
+            refs.append(lambda x, q=q, s16=s16, z=z: O.w4a16_gemm(x, q, s16, z, 128))
         elif kind == "w4a8":
             Wp, ws = prep_w4a8(g, W)
             layers.append((kind, Wp, ws, N))
+            qw, sw = O.quantize_w4_sym(W)
+
+            def ref_w4a8(x, qw=qw, sw=sw):
+                qa, sa, _ = O.quantize_a8(x)
+                return O.w4a8_gemm(qa, sa, qw, sw, None, O.OUT_F16)
+            refs.append(ref_w4a8)
         else:
             codes = WL.ternary_codes(N, K, seed=9200 + i)
             Wp, ws = prep_w2a8(g, codes, W)
             layers.append((kind, Wp, ws, N))
+
+            def ref_w2a8(x, codes=codes, ws=ws):
+                qa, sa, _ = O.quantize_a8(x)
+                return O.w2a8_gemm(qa, sa, codes, host(ws)[0], None, O.OUT_F16)
+            refs.append(ref_w2a8)
     bufs = [torch.empty((1, d), dtype=torch.float16, device="cuda") for d in dims]
     wss = [g.Workspace("cuda") for _ in layers]
     x0 = dev(WL.activations(1, dims[0], seed=9300, dtype=np.float16))
@@ -514,6 +534,9 @@ def test_decode_chain_graph_replays_match_eager(g):
     torch.cuda.synchronize()
     eager = [host(b) for b in bufs[1:]]
     assert all(np.isfinite(e.astype(np.float32)).all() for e in eager)
+    ins = [host(bufs[0])] + eager[:-1]
+    for i, ref in enumerate(refs):
+        tol_ok(eager[i], ref(ins[i]), f"chain layer {i} ({kinds[i]})")
     # warm the workspaces, then capture on a side stream
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -545,11 +568,7 @@ def test_w2a16_ternary(g, c):
     Wp, ws = prep_w2a8(g, d["codes"], d["src"])
     scale = host(ws)[0]
     C = host(g.w2a16_gemm(dev(d["A"]), Wp, ws, c.N))
-    if c.M == 1:
-        tol_ok(C, O.w2a16_gemm(d["A"], d["codes"], scale), c.name)
-    else:
-        rows, cols = sample_indices(c.M, c.N, 3000, seed=17)
-        tol_ok(C[rows, cols], O.w2a16_entries(d["A"], d["codes"], scale, rows, cols), c.name)
+    tol_ok(C, O.w2a16_gemm(d["A"], d["codes"], scale), c.name)
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 100, 528), (3, 37, 48), (17, 260, 1040), (1, 256, 8640),
@@ -604,22 +623,21 @@ def test_w8a8_outputs(g, M, N, K):
     Aq, sa, _ = g.quantize_a8(dev(A))
     qa, sa_ref, _ = O.quantize_a8(A)
     qw, ws_ref = O.quantize_w8_sym(W)
-    rows, cols = sample_indices(M, N, 3000, seed=19)
-    acc = O.int_accumulate_entries(qa, qw, rows, cols)
+    acc = O.int_accumulate_f64(qa, qw)
     C32 = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I32))
-    assert np.array_equal(C32[rows, cols], acc.astype(np.int32))
+    assert np.array_equal(C32, acc.astype(np.int32))
     # output scale that saturates the largest few codes
-    vmax = float(np.max(np.abs((acc.astype(np.float32) * ws_ref[cols]) * sa_ref[rows])))
+    vmax = float(np.max(np.abs((acc.astype(np.float32) * ws_ref[None, :]) * sa_ref[:, None])))
     so = np.float32(vmax / 100.0)
     C8 = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_I8,
                           out_scale=dev(np.array([so], np.float32))))
-    assert np.array_equal(C8[rows, cols], O.requantize_i8(acc, ws_ref[cols], sa_ref[rows], so))
+    assert np.array_equal(C8, O.requantize_i8(acc, ws_ref[None, :], sa_ref[:, None], so))
     C16 = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, bias=f16(bias), out_dtype=g.W4_OUT_F16))
-    tol_ok(C16[rows, cols], O.dequant_epilogue(acc, ws_ref[cols], sa_ref[rows], bias[cols],
-                                               O.OUT_F16), "f16")
+    tol_ok(C16, O.dequant_epilogue(acc, ws_ref[None, :], sa_ref[:, None], bias[None, :],
+                                   O.OUT_F16), "f16")
     C32f = host(g.w8a8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_F32))
-    tol_ok(C32f[rows, cols], O.dequant_epilogue(acc, ws_ref[cols], sa_ref[rows], None,
-                                                O.OUT_F32), "f32")
+    tol_ok(C32f, O.dequant_epilogue(acc, ws_ref[None, :], sa_ref[:, None], None, O.OUT_F32),
+           "f32")
 
 
 # ---------------------------------------------------------------------------
@@ -695,10 +713,7 @@ def test_f8f8_outputs(g, M, N, K):
     qa, sa_ref = O.quantize_f8(A)
     qw, ws_ref = O.quantize_f8(W)
     assert np.array_equal(host(Aq), qa) and np.array_equal(host(Wq), qw)
-    rows, cols = sample_indices(M, N, 3000, seed=23)
     C16 = host(g.f8f8_gemm(Aq, sa, Wp, ws, N, bias=f16(bias), out_dtype=g.W4_OUT_F16))
-    tol_ok(C16[rows, cols], O.f8f8_entries(qa, sa_ref, qw, ws_ref, rows, cols, bias, O.OUT_F16),
-           "f16")
+    tol_ok(C16, O.f8f8_gemm(qa, sa_ref, qw, ws_ref, bias, O.OUT_F16), "f16")
     C32 = host(g.f8f8_gemm(Aq, sa, Wp, ws, N, out_dtype=g.W4_OUT_F32))
-    tol_ok(C32[rows, cols], O.f8f8_entries(qa, sa_ref, qw, ws_ref, rows, cols, None, O.OUT_F32),
-           "f32")
+    tol_ok(C32, O.f8f8_gemm(qa, sa_ref, qw, ws_ref, None, O.OUT_F32), "f32")

@@ -1,10 +1,10 @@
 """GPU parity of the plan table: every candidate plan of a shape against the
 oracle, one workspace shared by any mix of shapes and plans, and the tuner.
 
-INT32 accumulators and INT8 outputs must be bit-exact for every plan (the
-products are exact integers whatever the k split); fp16 outputs meet the
-same tolerance as the other parity tests, |gpu - ref| <= 2^-9 |ref| +
-1e-3 rms(ref).
+Every output element is checked. INT32 accumulators and INT8 outputs must
+be bit-exact for every plan (the products are exact integers whatever the k
+split); fp16 outputs meet the same tolerance as the other parity tests,
+|gpu - ref| <= 2^-9 |ref| + 1e-3 rms(ref).
 """
 import json
 
@@ -13,7 +13,7 @@ import pytest
 
 import oracle as O
 from gemv_nibble_unpack_amd import workloads as WL
-from tests._helpers import say, sample_indices, tol_ok
+from tests._helpers import say, tol_ok
 
 torch = pytest.importorskip("torch")
 
@@ -51,7 +51,6 @@ class Shape:
         self.g, self.op, self.M, self.N, self.K = g, op, M, N, K
         self.A = WL.activations(M, K, seed=seed, dtype=np.float16)
         self.bias = WL.bias_f16(N, seed=seed + 1)
-        self.rows, self.cols = sample_indices(M, N, 3000, seed=seed + 2)
         a8 = op in (g.W4_OP_W4A8, g.W4_OP_W2A8, g.W4_OP_W8A8)
         if a8:
             self.Aq, self.sa, _ = g.quantize_a8(dev(self.A))
@@ -69,7 +68,7 @@ class Shape:
             self.Wp = g.prepack_w(g.W4_LAYOUT_W2A8, Wq, N, K)
             self.scale = g.ternary_scale_f16(dev(WL.weights_f32(N, K, seed=seed + 4)))
             s = np.float64(host(self.scale)[0])
-            self.qw, self.ws_ref = self.codes, np.full(len(self.cols), s)
+            self.qw, self.ws_ref = self.codes, np.full((1, N), s)
         elif op == g.W4_OP_W4A16:
             W = WL.weights_f32(N, K, seed=seed + 3)
             Wq, s, z = g.quantize_pack_w4(dev(W), g.W4_ASYM_GROUP)
@@ -80,15 +79,15 @@ class Shape:
             Wq, self.scale = g.quantize_pack_w8(dev(W))
             self.Wp = g.prepack_w(g.W4_LAYOUT_W8A8, Wq, N, K)
             self.qw, ws = O.quantize_w8_sym(W)
-            self.ws_ref = ws[self.cols]
+            self.ws_ref = ws[None, :]
         else:
             W = WL.weights_f32(N, K, seed=seed + 3)
             Wq, self.scale, _ = g.quantize_pack_w4(dev(W), g.W4_SYM_PER_CHANNEL)
             self.Wp = g.prepack_w(g.W4_LAYOUT_W4A8, Wq, N, K)
             self.qw, ws = O.quantize_w4_sym(W)
-            self.ws_ref = ws[self.cols]
+            self.ws_ref = ws[None, :]
         if a8:
-            self.acc = O.int_accumulate_entries(self.qa, self.qw, self.rows, self.cols)
+            self.acc = O.int_accumulate_f64(self.qa, self.qw)
 
     def run(self, out_dtype, bias=False, workspace=None, out_scale=None):
         g, N = self.g, self.N
@@ -108,41 +107,41 @@ class Shape:
         return host(mm(self.Aq, self.sa, self.Wp, self.scale, N, bias=b, out_dtype=out_dtype,
                        workspace=workspace))
 
+    def ref_f16(self, bias=True):
+        """The oracle's fp16 output of the whole [M, N] product."""
+        b = self.bias if bias else None
+        if self.op == self.g.W4_OP_W4A16:
+            return O.w4a16_gemm(self.A, self.q, self.s16, self.z, 128, b)
+        if self.op == self.g.W4_OP_W2A16:
+            return O.w2a16_gemm(self.A, self.codes, np.float64(host(self.scale)[0]), b)
+        if self.op == self.g.W4_OP_F8F8:
+            return O.f8f8_gemm(self.qa, self.sa_ref, self.qw, self.sw, b, O.OUT_F16)
+        return O.dequant_epilogue(self.acc, self.ws_ref, self.sa_ref[:, None],
+                                  None if b is None else b[None, :], O.OUT_F16)
+
     def check(self, what):
-        """Every output type of the op against the oracle on the sampled entries."""
-        g, r, c = self.g, self.rows, self.cols
-        if self.op == g.W4_OP_W4A16:
-            ref = O.w4a16_entries(self.A, self.q, self.s16, self.z, r, c, 128, self.bias)
-            tol_ok(self.run(g.W4_OUT_F16, bias=True)[r, c], ref, what)
-            return
-        if self.op == g.W4_OP_W2A16:
-            s = np.float64(host(self.scale)[0])
-            ref = O.w2a16_entries(self.A, self.codes, s, r, c, self.bias)
-            tol_ok(self.run(g.W4_OUT_F16, bias=True)[r, c], ref, what)
-            return
+        """Every output type of the op against the oracle, every element."""
+        g = self.g
+        tol_ok(self.run(g.W4_OUT_F16, bias=True), self.ref_f16(), what)
         if self.op == g.W4_OP_F8F8:
-            for out, bias in ((O.OUT_F16, self.bias), (O.OUT_F32, None)):
-                ref = O.f8f8_entries(self.qa, self.sa_ref, self.qw, self.sw, r, c, bias, out)
-                got = self.run(g.W4_OUT_F16 if out == O.OUT_F16 else g.W4_OUT_F32,
-                               bias=bias is not None)
-                tol_ok(got[r, c], ref, f"{what} {out}")
+            ref = O.f8f8_gemm(self.qa, self.sa_ref, self.qw, self.sw, None, O.OUT_F32)
+            tol_ok(self.run(g.W4_OUT_F32), ref, f"{what} f32")
+        if self.op in (g.W4_OP_W4A16, g.W4_OP_W2A16, g.W4_OP_F8F8):
             return
         C32 = self.run(g.W4_OUT_I32)
-        assert np.array_equal(C32[r, c], self.acc.astype(np.int32)), what
-        ref = O.dequant_epilogue(self.acc, self.ws_ref, self.sa_ref[r], self.bias[c], O.OUT_F16)
-        tol_ok(self.run(g.W4_OUT_F16, bias=True)[r, c], ref, what)
+        assert np.array_equal(C32, self.acc.astype(np.int32)), what
         if self.op == g.W4_OP_W8A8:
             vmax = float(np.max(np.abs((self.acc.astype(np.float32) * self.ws_ref) *
-                                       self.sa_ref[r])))
+                                       self.sa_ref[:, None])))
             so = np.float32(vmax / 100.0)
             C8 = self.run(g.W4_OUT_I8, out_scale=dev(np.array([so], np.float32)))
-            assert np.array_equal(C8[r, c], O.requantize_i8(self.acc, self.ws_ref,
-                                                            self.sa_ref[r], so)), what
+            assert np.array_equal(C8, O.requantize_i8(self.acc, self.ws_ref,
+                                                      self.sa_ref[:, None], so)), what
 
 
 PLAN_SHAPES = [
     ("w4a8", 1, 4096, 4096), ("w4a8", 37, 1000, 1040), ("w4a8", 130, 4100, 528),
-    ("w2a8", 1, 16, 131072), ("w2a8", 70, 3000, 2000),
+    ("w2a8", 1, 16, 131056), ("w2a8", 70, 3000, 2000),
     # long rows: 16-wave decode plans next to the 8-wave ones (the first two
     # take 16 waves unsplit as their built-in plan; ragged last n-tile)
     ("w4a16", 1, 1040, 11008), ("w2a16", 1, 1030, 8640), ("w8a8", 3, 300, 8192),
@@ -195,7 +194,7 @@ def test_one_workspace_for_any_mix_of_shapes_and_plans(g):
     # tiles) then count arrivals in the same buffer. Each must equal its
     # result on a fresh workspace, bit for bit.
     say("case shared workspace: decode split 64, gemm split, decode split 4")
-    cases = [Shape(g, g.W4_OP_W2A8, 1, 16, 131072, seed=13000),
+    cases = [Shape(g, g.W4_OP_W2A8, 1, 16, 131056, seed=13000),
              Shape(g, g.W4_OP_W2A8, 1100, 2000, 1024, seed=13100),
              Shape(g, g.W4_OP_W4A8, 1, 4096, 4096, seed=13200)]
     names = [g.w4_plan_name(c.op, c.M, c.N, c.K, g.w4_plan_current(c.op, c.M, c.N, c.K))
@@ -214,7 +213,7 @@ def test_one_workspace_for_any_mix_of_shapes_and_plans(g):
                 got = c.run(g.W4_OUT_I32, workspace=shared)
                 fresh = c.run(g.W4_OUT_I32)
                 assert np.array_equal(got, fresh), (rep, c.op, c.M, c.N, c.K)
-                assert np.array_equal(got[c.rows, c.cols], c.acc.astype(np.int32))
+                assert np.array_equal(got, c.acc.astype(np.int32))
         # the counter area is zero again after the calls
         assert not host(shared[:16384]).any()
     finally:
@@ -302,6 +301,11 @@ def test_graph_replays_match_eager(g, name, M, N, K, plan):
                               workspace=ws, C=C)
         call()
         eager = host(C).copy()
+        # the eager output itself against the oracle, every element
+        if op == g.W4_OP_W4A16:
+            tol_ok(eager, s.ref_f16(bias=False), f"graph eager {plan}")
+        else:
+            assert np.array_equal(eager, s.acc.astype(np.int32)), plan
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -317,6 +321,11 @@ def test_graph_replays_match_eager(g, name, M, N, K, plan):
             graph.replay()
             got = host(C)
             assert np.array_equal(got.view(np.uint8), eager.view(np.uint8)), rep
+            # and each replay against the oracle directly
+            if op == g.W4_OP_W4A16:
+                tol_ok(got, s.ref_f16(bias=False), f"graph replay {rep} {plan}")
+            else:
+                assert np.array_equal(got, s.acc.astype(np.int32)), (rep, plan)
         if need:
             assert not host(ws[:16384]).any()           # counters zero after the replays
     finally:
@@ -342,3 +351,46 @@ def _random_shapes():
 @pytest.mark.parametrize("name,M,N,K", _random_shapes())
 def test_random_shapes_every_plan(g, name, M, N, K):
     test_every_plan_matches_oracle(g, name, M, N, K)
+
+
+def test_split_plans_on_a_side_stream(g):
+    # Split plans launched on a stream other than the current one, without
+    # switching the current stream: the wrapper's temporary workspace must be
+    # zero-filled on the launch stream (not on the current one), and a shared
+    # Workspace first used on the current stream must be ordered before the
+    # side-stream call. Every result against the oracle, every element.
+    op, M, N, K = g.W4_OP_W2A8, 1, 16, 131056
+    s = Shape(g, op, M, N, K, seed=17000)
+    assert g.w4_plan_name(op, M, N, K, g.w4_plan_current(op, M, N, K)) == "decode:ksplit=64"
+    s16 = Shape(g, g.W4_OP_W4A16, 1, 512, 8192, seed=17100)
+    names = [g.w4_plan_name(g.W4_OP_W4A16, 1, 512, 8192, i)
+             for i in range(g.w4_plan_count(g.W4_OP_W4A16, 1, 512, 8192))]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    say("case side stream: w2a8 decode:ksplit=64 and w4a16 decode:ksplit=4, fresh workspaces")
+    try:
+        g.w4_plan_pin(g.W4_OP_W4A16, 1, 512, 8192, names.index("decode:ksplit=4"))
+        A16 = dev(s16.A)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            # busy the current stream so that unordered work would overlap
+            junk = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+            junk.fill_(0xFF)
+            C = g.w2a8_gemm(s.Aq, s.sa, s.Wp, s.scale, N, out_dtype=g.W4_OUT_I32, stream=side)
+            C16 = g.w4a16_gemm(A16, s16.Wp, 512, stream=side)
+            side.synchronize()
+            assert np.array_equal(C.cpu().numpy(), s.acc.astype(np.int32)), rep
+            tol_ok(C16.cpu().numpy(), s16.ref_f16(bias=False), f"side stream w4a16 {rep}")
+            del junk
+        say("case side stream: one Workspace used on the current stream, then on a side stream")
+        ws = g.Workspace("cuda")
+        Ccur = g.w2a8_gemm(s.Aq, s.sa, s.Wp, s.scale, N, out_dtype=g.W4_OUT_I32, workspace=ws)
+        Cside = g.w2a8_gemm(s.Aq, s.sa, s.Wp, s.scale, N, out_dtype=g.W4_OUT_I32, workspace=ws,
+                            stream=side)
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert np.array_equal(Ccur.cpu().numpy(), s.acc.astype(np.int32))
+        assert np.array_equal(Cside.cpu().numpy(), s.acc.astype(np.int32))
+        assert not ws.buf[:16384].cpu().numpy().any()
+    finally:
+        g.w4_plan_pin(g.W4_OP_W4A16, 1, 512, 8192, -1)

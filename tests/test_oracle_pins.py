@@ -241,6 +241,35 @@ def test_extreme_accumulator_value():
     assert acc[0, 0] == -889 * K
 
 
+def test_f64_accumulate_equals_int64_random_and_extreme():
+    # the float64 product of the codes is the int64 sum exactly: random
+    # INT4, INT2 and INT8 codes on ragged shapes, and the extreme products
+    # (-128 x -8, -128 x -2, -128 x -128) summed over the largest K the
+    # library accepts, where the int32 result sits just below 2^31
+    rng = np.random.default_rng(31)
+    for (M, N, K, lo, hi) in [(7, 13, 48, -8, 8), (33, 17, 1040, -2, 2), (5, 9, 4096, -128, 128),
+                              (64, 80, 528, -128, 128)]:
+        qa = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        qw = rng.integers(lo, hi, size=(N, K)).astype(np.int8)
+        assert np.array_equal(O.int_accumulate_f64(qa, qw), O.int_accumulate(qa, qw))
+    K = 131056
+    qa = np.full((2, K), -128, np.int8)
+    qa[1, ::2] = 127
+    for code in (-8, -2, -128):
+        qw = np.full((3, K), code, np.int8)
+        qw[1, 1::3] = 7 if code == -8 else 1 if code == -2 else 127
+        f = O.int_accumulate_f64(qa, qw)
+        assert np.array_equal(f, O.int_accumulate(qa, qw))
+    assert O.int_accumulate_f64(np.full((1, K), -128, np.int8),
+                                np.full((1, K), -128, np.int8))[0, 0] == 16384 * K
+    assert 16384 * K < 2**31 <= 16384 * (K + 16)
+
+
+def test_f64_accumulate_refuses_rounding_range():
+    with pytest.raises(OverflowError):
+        O.int_accumulate_f64(np.full((1, 2**20), 127, np.int32), np.full((1, 2**20), 2**30, np.int64))
+
+
 def test_epilogue_exact_powers_of_two_and_bias():
     acc = np.array([[3, -5], [1000, 7]], np.int64)
     ws = np.array([0.5, 2.0], np.float32)
