@@ -11,6 +11,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 # status codes and enumerations (mirror include/gemv_nibble_unpack.h)
 W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_ARG, W4_ERR_WORKSPACE, W4_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
+W4_ERR_SCRATCH = -7
+W4_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 W4_SYM_PER_CHANNEL, W4_ASYM_GROUP = 0, 1
 W4_OUT_F16, W4_OUT_F32, W4_OUT_I32, W4_OUT_I8 = 0, 1, 2, 3
 W4_IN_F16, W4_IN_F32 = 0, 1
@@ -46,6 +48,7 @@ SIGNATURES = {
     "w4_fused_act_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "w4a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
     "w2a8_gemm_fused_act": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
+    "w4a8_gemm_fused_act_noalloc": (_i, [_p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _p]),
     "w4_plan_count": (_i, [_i, _i, _i, _i]),
     "w4_plan_name": (_i, [_i, _i, _i, _i, _i, ctypes.c_char_p, _sz]),
     "w4_plan_pin": (_i, [_i, _i, _i, _i, _i]),

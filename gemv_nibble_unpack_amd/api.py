@@ -382,6 +382,26 @@ def w4a8_gemm_fused_act(A, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, wo
                   workspace, C, stream)
 
 
+def w4a8_gemm_fused_act_noalloc(A, Wp, w_scale, N, bias=None, out_dtype=L.W4_OUT_F16, C=None,
+                                stream=None):
+    """w4a8_gemm_fused_act on the library's static per-GPU scratch: no
+    workspace is allocated (pass ``C`` as well to allocate nothing at all)."""
+    dev = _dev(A)
+    M, K = A.shape
+    if A.dtype == torch.float16:
+        dt = L.W4_IN_F16
+    elif A.dtype == torch.float32:
+        dt = L.W4_IN_F32
+    else:
+        raise ValueError("A must be float16 or float32")
+    if C is None:
+        C = _empty((M, N), _OUT_DT[out_dtype], dev, stream)
+    L.check("w4a8_gemm_fused_act_noalloc", L.load().w4a8_gemm_fused_act_noalloc(
+        _ptr(A), dt, _ptr(Wp), _ptr(w_scale), _ptr(bias), _ptr(C), out_dtype, M, N, K,
+        _stream(stream)))
+    return C
+
+
 def w2a8_gemm_fused_act(A, Wp, w_scale16, N, bias=None, out_dtype=L.W4_OUT_F16, workspace=None,
                         C=None, stream=None):
     """fp16/float32 A [M,K] -> quantize_a8 + w2a8_gemm in one C call."""

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["quant.hip", "prepack.hip", "matmul.hip", "probe.hip"]
+SOURCES = ["quant.hip", "prepack.hip", "matmul.hip", "probe.hip", "noalloc.hip"]
 OUT = os.path.join(HERE, "libgemv_nibble_unpack.so")
 ARCH = os.environ.get("W4_OFFLOAD_ARCH", "gfx950")
 

@@ -310,6 +310,9 @@ extern "C" const char* w4_status_string(int status) {
     case W4_ERR_ARG: return "an enumerated argument has an unknown value";
     case W4_ERR_WORKSPACE: return "workspace is NULL or too small";
     case W4_ERR_HIP: return "the HIP runtime rejected the launch";
+    case W4_ERR_SCRATCH:
+      return "the call needs more scratch than the library's static buffer holds "
+             "(W4_NOALLOC_SCRATCH_BYTES); use the entry point that takes a workspace";
     default: return "unknown status";
   }
 }

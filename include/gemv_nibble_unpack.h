@@ -58,6 +58,7 @@ extern "C" {
 #define W4_ERR_ARG       -4   /* an enumerated argument has an unknown value  */
 #define W4_ERR_WORKSPACE -5   /* workspace NULL or smaller than required      */
 #define W4_ERR_HIP       -6   /* the HIP runtime rejected the launch          */
+#define W4_ERR_SCRATCH   -7   /* needs more than the static scratch holds     */
 
 /* ---- enumerations -------------------------------------------------------- */
 /* weight schemes for quantize_pack_w4 */
@@ -87,6 +88,7 @@ extern "C" {
 
 #define W4_GROUP_SIZE 128
 #define W4_MAX_K 131056
+#define W4_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)  /* w4a8_gemm_fused_act_noalloc */
 
 /* Human-readable text for a status code (static string, never NULL). */
 const char* w4_status_string(int status);
@@ -327,6 +329,27 @@ size_t w4_fused_act_workspace_bytes(int layout, int M, int N, int K);
 int w4a8_gemm_fused_act(const void* A, int in_dtype, const uint8_t* Wp, const float* w_scale,
                         const uint16_t* bias, void* C, int out_dtype, int M, int N, int K,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * w4a8_gemm_fused_act_noalloc -- w4a8_gemm_fused_act without a workspace,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments (minus the workspace), same kernels, same outputs bit for bit.
+ * The scratch the call needs (w4_fused_act_workspace_bytes(W4_LAYOUT_W4A8,
+ * M, N, K): split-K counters and partial sums, and for shapes that quantize
+ * in a separate launch the int8 rows and their scales) is a static device
+ * array of W4_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library; every GPU
+ * the library runs on holds its own copy until the process ends. Nothing is
+ * allocated, nothing freed. A shape that needs more scratch than that (e.g.
+ * M * K above about 33.5 million with the two-launch form) returns
+ * W4_ERR_SCRATCH before any GPU work. Every call on one GPU shares that
+ * GPU's array and leaves its counter area zero; calls that overlap in time on
+ * one GPU (several streams, or several threads) race on it and must not be
+ * issued.
+ */
+int w4a8_gemm_fused_act_noalloc(const void* A, int in_dtype, const uint8_t* Wp,
+                                const float* w_scale, const uint16_t* bias, void* C, int out_dtype,
+                                int M, int N, int K, hipStream_t stream);
 
 /*
  * w2a8_gemm_fused_act -- quantize_a8 followed by w2a8_gemm in one call, as

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -35,7 +35,7 @@ def test_header_and_library_agree():
 def test_constants_match_header():
     text = open(HEADER).read()
     for name in ["W4_OK", "W4_ERR_NULL", "W4_ERR_SHAPE", "W4_ERR_ALIGN", "W4_ERR_ARG",
-                 "W4_ERR_WORKSPACE", "W4_ERR_HIP", "W4_SYM_PER_CHANNEL", "W4_ASYM_GROUP",
+                 "W4_ERR_WORKSPACE", "W4_ERR_HIP", "W4_ERR_SCRATCH", "W4_SYM_PER_CHANNEL", "W4_ASYM_GROUP",
                  "W4_OUT_F16", "W4_OUT_F32", "W4_OUT_I32", "W4_OUT_I8", "W4_IN_F16", "W4_IN_F32",
                  "W4_LAYOUT_W4A8", "W4_LAYOUT_W4A16", "W4_LAYOUT_W2A8", "W4_LAYOUT_W8A8",
                  "W4_OP_W4A8", "W4_OP_W4A16", "W4_OP_W2A8", "W4_OP_W2A16", "W4_OP_W8A8",
@@ -49,8 +49,8 @@ def test_constants_match_header():
 
 def test_status_strings():
     lib = G.load()
-    for s in range(-6, 1):
-        assert lib.w4_status_string(s)
+    for s in range(-7, 1):
+        assert lib.w4_status_string(s) != b"unknown status"
     assert lib.w4_status_string(-99) == b"unknown status"
 
 
@@ -161,6 +161,27 @@ def _names(lib, op, M, N, K):
         assert lib.w4_plan_name(op, M, N, K, i, buf, 64) == L.W4_OK
         out.append(buf.value.decode())
     return out
+
+
+def test_noalloc_fused_entry_rejects_before_any_gpu_work():
+    lib = G.load()
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+W4_NOALLOC_SCRATCH_BYTES\s+\((\d+) \* 1024 \* 1024\)", text)
+    assert m and int(m.group(1)) * 1024 * 1024 == L.W4_NOALLOC_SCRATCH_BYTES
+    s = None
+    f = lib.w4a8_gemm_fused_act_noalloc
+    assert f(P, 0, P, P, None, P2, 0, 1, 16, 24, s) == L.W4_ERR_SHAPE
+    assert f(P, 7, P, P, None, P2, 0, 1, 16, 32, s) == L.W4_ERR_ARG
+    assert f(None, 0, P, P, None, P2, 0, 1, 16, 32, s) == L.W4_ERR_NULL
+    assert f(MIS, 0, P, P, None, P2, 0, 1, 16, 32, s) == L.W4_ERR_ALIGN
+    assert f(None, 0, None, None, None, None, 0, 0, 16, 32, s) == L.W4_OK
+    # a shape whose scratch exceeds the static array: the int8 rows of a
+    # two-launch call alone take M * K bytes
+    M, K = 4096, 16384
+    assert lib.w4_fused_act_workspace_bytes(L.W4_LAYOUT_W4A8, M, 4096, K) > \
+        L.W4_NOALLOC_SCRATCH_BYTES
+    assert f(P, 0, P, P, None, P2, 0, M, 4096, K, s) == L.W4_ERR_SCRATCH
+    assert b"static" in lib.w4_status_string(L.W4_ERR_SCRATCH)
 
 
 def test_read_probe_error_paths():
