@@ -13,7 +13,11 @@ under ``prefill``.
 Cold weights: every call reads its weights from one of R copies (>= 1 GiB in
 rotation), and 1 GiB of other memory is read and written between the untimed
 replay and the timed one, so that no call of the timed region finds its
-weights in the 256 MB last-level cache, whatever the step count.
+weights in the 256 MB last-level cache, whatever the step count. Steady
+state: right before the timed replay, a graph of the same calls over a
+separate set of weight copies runs for about WARM_US microseconds, so that
+the timed steps start on a busy, clocked-up GPU and the graph's launch is
+queued behind it.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill]
 """
@@ -42,6 +46,8 @@ FLUSH_BYTES = 1 << 30          # read + written between the untimed and the time
 PREFILL_MIN_STEPS = 50         # the prefill is timed over at least this many calls
 CALIB_BYTES = 256 << 20        # device-to-device copy used to calibrate PMC byte counters
 PROBE_PER = (1, 2, 4, 8)       # 16-byte loads per lane tried by the read probe
+WARM_US = 250.0                # GPU time of the warm-up replay right before a timed one
+WARM_COPIES = 8                # weight copies the warm-up replay cycles through
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_TRAFFIC = os.path.join(PROFILES, "k_gemv_w4a16_decode_m1_n4096_k4096_traffic.json")
 PREFILL_TRAFFIC = os.path.join(PROFILES, "k_gemm_w4a8_prefill_m2048_n11008_k4096_traffic.json")
@@ -83,25 +89,34 @@ def cold_gap_bytes(steps, copies, copy_bytes, flush_bytes=FLUSH_BYTES):
 
 
 class Flush:
-    """Reads FLUSH_BYTES / 2 and writes as many (torch's elementwise
-    bitwise_not on uint8), evicting the weights from the last-level cache."""
+    """Reads FLUSH_BYTES / 2 and writes as many (torch's elementwise neg on
+    int8; a kernel of its own name, apart from the bitwise_not copy that
+    calibrates the byte counters), evicting the weights from the last-level
+    cache."""
 
     def __init__(self, dev):
         import torch
-        self.src = torch.ones(FLUSH_BYTES // 2, dtype=torch.uint8, device=dev)
+        self.src = torch.ones(FLUSH_BYTES // 2, dtype=torch.int8, device=dev)
         self.dst = torch.empty_like(self.src)
 
     def __call__(self, stream):
         import torch
         with torch.cuda.stream(stream):
-            torch.bitwise_not(self.src, out=self.dst)
+            torch.neg(self.src, out=self.dst)
 
 
-def time_graph(fn, steps, warmup, stream, flush):
-    """Capture `steps` calls fn(0..steps-1) in one HIP graph, replay it once
-    untimed, flush the last-level cache, and time one replay with HIP events
-    on `stream`; returns ms per call. The calls take the current stream (the
-    capture stream while capturing)."""
+def warm_steps(step_ms):
+    """Steps of a warm-up replay that lasts about WARM_US."""
+    return max(2, min(400, math.ceil(WARM_US * 1e-3 / max(step_ms, 1e-6))))
+
+
+def time_graph(fn, steps, warmup, stream, flush, warm_fn=None):
+    """Capture `steps` calls fn(0..steps-1) in one HIP graph and replay it
+    once untimed; then flush the last-level cache, replay a warm-up graph of
+    warm_fn calls (over other weight copies, about WARM_US long), and time one
+    replay of the first graph with HIP events on `stream`; returns ms per
+    call. The calls take the current stream (the capture stream while
+    capturing)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -110,10 +125,23 @@ def time_graph(fn, steps, warmup, stream, flush):
     with torch.cuda.graph(g):
         for i in range(steps):
             fn(i)
-    g.replay()
-    flush(stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    gw = None
+    if warm_fn is not None:
+        nw = warm_steps(t0.elapsed_time(t1) / steps)
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw):
+            for i in range(nw):
+                warm_fn(i)
+        gw.replay()
+    flush(stream)
+    if gw is not None:
+        gw.replay()
     t0.record(stream)
     g.replay()
     t1.record(stream)
@@ -152,12 +180,13 @@ def calibration_copy():
 
 
 def copies_of(Wp):
-    import torch
+    """The timed rotation of weight copies (>= ROTATE_BYTES in all), and
+    WARM_COPIES more for the warm-up replays (never read in a timed region)."""
     R = rotation(Wp.numel())
-    return [Wp] + [Wp.clone() for _ in range(R - 1)]
+    return [Wp] + [Wp.clone() for _ in range(R - 1)], [Wp.clone() for _ in range(WARM_COPIES)]
 
 
-def read_probe(copies, steps, warmup, stream, flush):
+def read_probe(copies, warm, steps, warmup, stream, flush):
     """The plain streaming read of the same weight copies, in the same
     protocol, at each loads-per-lane setting; the fastest is the achievable
     rate for a transfer of that size."""
@@ -165,11 +194,12 @@ def read_probe(copies, steps, warmup, stream, flush):
     import gemv_nibble_unpack_amd as G
     sink = torch.zeros(1024, dtype=torch.int32, device=copies[0].device)
     nbytes = copies[0].numel()
-    R = len(copies)
+    R, Wn = len(copies), len(warm)
     runs = {}
     for per in PROBE_PER:
         ms = time_graph(lambda i: G.w4_read_probe(copies[i % R], nbytes, per, sink), steps,
-                        warmup, stream, flush)
+                        warmup, stream, flush,
+                        warm_fn=lambda i: G.w4_read_probe(warm[i % Wn], nbytes, per, sink))
         runs[per] = ms
     per = min(runs, key=runs.get)
     ms = runs[per]
@@ -198,8 +228,8 @@ def bench_decode_shape(N, K, steps, warmup, stream, flush, eager=False, probe=Tr
     torch.cuda.synchronize()
     prep_ms = (time.time() - t) * 1e3
     del W, Wq, s, z
-    copies = copies_of(Wp)
-    R = len(copies)
+    copies, warm = copies_of(Wp)
+    R, Wn = len(copies), len(warm)
     C = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
     ws = G.Workspace(dev)
 
@@ -207,8 +237,11 @@ def bench_decode_shape(N, K, steps, warmup, stream, flush, eager=False, probe=Tr
         # stream=None: the current stream (the capture stream under graph capture)
         G.w4a16_gemm(A, copies[i % R], c.N, workspace=ws, C=C)
 
+    def warm_step(i):
+        G.w4a16_gemm(A, warm[i % Wn], c.N, workspace=ws, C=C)
+
     eager_ms = time_eager(step, steps, warmup, stream, flush)
-    ms = eager_ms if eager else time_graph(step, steps, warmup, stream, flush)
+    ms = eager_ms if eager else time_graph(step, steps, warmup, stream, flush, warm_step)
     nbytes = decode_bytes(c.M, c.N, c.K)
     gbs = nbytes / (ms * 1e-3) / 1e9
     out = {"N": c.N, "K": c.K, "bytes": nbytes, "us": round(ms * 1e3, 3),
@@ -217,10 +250,10 @@ def bench_decode_shape(N, K, steps, warmup, stream, flush, eager=False, probe=Tr
            "cold_gap_bytes": cold_gap_bytes(steps, R, Wp.numel()),
            "offline_prep_ms": round(prep_ms, 3), "ms": ms}
     if probe:
-        pr = read_probe(copies, steps, warmup, stream, flush)
+        pr = read_probe(copies, warm, steps, warmup, stream, flush)
         out["achievable"] = pr
         out["frac_of_achievable"] = round(gbs / pr["GBps"], 4)
-    del copies
+    del copies, warm
     torch.cuda.empty_cache()
     return out
 
@@ -242,39 +275,45 @@ def bench_prefill(args, stream, flush):
     Wq, wsc, _ = G.quantize_pack_w4(W, G.W4_SYM_PER_CHANNEL)
     Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, c.N, c.K)
     del W, Wq
-    copies = copies_of(Wp)
-    R = len(copies)
+    copies, warm = copies_of(Wp)
+    R, Wn = len(copies), len(warm)
     Aq = torch.empty((c.M, c.K), dtype=torch.int8, device=dev)
     sa = torch.empty(c.M, dtype=torch.float32, device=dev)
     C = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
     wsp = G.Workspace(dev)
     wsf = G.Workspace(dev)
     steps = max(PREFILL_MIN_STEPS, args.steps // 4)
-    warm = max(2, args.warmup // 4)
+    warm_n = max(2, args.warmup // 4)
     G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None))
 
-    def gemm(i):
-        G.w4a8_gemm(Aq, sa, copies[i % R], wsc, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
+    def gemm(i, cps=copies):
+        G.w4a8_gemm(Aq, sa, cps[i % len(cps)], wsc, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
                     workspace=wsp, C=C)
 
-    def two_calls(i):
+    def two_calls(i, cps=copies):
         G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None))
-        gemm(i)
+        gemm(i, cps)
 
-    def fused(i):
-        G.w4a8_gemm_fused_act(A, copies[i % R], wsc, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
+    def fused(i, cps=copies):
+        G.w4a8_gemm_fused_act(A, cps[i % len(cps)], wsc, c.N, bias=bias, out_dtype=G.W4_OUT_F16,
                               workspace=wsf, C=C)
 
-    timer = time_eager if args.eager else time_graph
+    def quant(i, cps=None):
+        G.quantize_a8(A, with_rowsum=False, out=(Aq, sa, None))
+
     out = {"steps": steps, "copies": R, "bytes": prefill_bytes(c.M, c.N, c.K),
            "cold_gap_bytes": cold_gap_bytes(steps, R, Wp.numel())}
-    out["gemm_ms"] = timer(gemm, steps, warm, stream, flush)
-    out["two_call_step_ms"] = timer(two_calls, steps, warm, stream, flush)
-    out["fused_step_ms"] = timer(fused, steps, warm, stream, flush)
-    out["quant_only_ms"] = timer(lambda i: G.quantize_a8(A, with_rowsum=False,
-                                                         out=(Aq, sa, None)),
-                                 steps, warm, stream, flush)
-    del copies
+    if args.eager:
+        timer = lambda fn: time_eager(fn, steps, warm_n, stream, flush)
+    else:
+        timer = lambda fn: time_graph(fn, steps, warm_n, stream, flush,
+                                      lambda i: fn(i, warm))
+        timer(gemm)           # the first pass over a process's fresh copies runs slow: settle
+    out["gemm_ms"] = timer(gemm)
+    out["two_call_step_ms"] = timer(two_calls)
+    out["fused_step_ms"] = timer(fused)
+    out["quant_only_ms"] = timer(quant)
+    del copies, warm
     torch.cuda.empty_cache()
     return c, out
 
@@ -292,25 +331,24 @@ def bench_decode_w4a8(stream, steps, flush):
     Wq, wsc, _ = G.quantize_pack_w4(W, G.W4_SYM_PER_CHANNEL)
     Wp = G.prepack_w(G.W4_LAYOUT_W4A8, Wq, N, K)
     del W, Wq
-    copies = copies_of(Wp)
-    R = len(copies)
+    copies, warm = copies_of(Wp)
     C = torch.empty((1, N), dtype=torch.float16, device=dev)
     q = (torch.empty((1, K), dtype=torch.int8, device=dev), torch.empty(1, device=dev), None)
     ws = G.Workspace(dev)
 
-    def two(i):
+    def two(i, cps=copies):
         G.quantize_a8(A, out=q)
-        G.w4a8_gemm(q[0], q[1], copies[i % R], wsc, N, workspace=ws, C=C)
+        G.w4a8_gemm(q[0], q[1], cps[i % len(cps)], wsc, N, workspace=ws, C=C)
 
-    def fused(i):
-        G.w4a8_gemm_fused_act(A, copies[i % R], wsc, N, workspace=ws, C=C)
+    def fused(i, cps=copies):
+        G.w4a8_gemm_fused_act(A, cps[i % len(cps)], wsc, N, workspace=ws, C=C)
 
     nb = N * K // 2 + 4 * N + 2 * K + 2 * N
     row = {"N": N, "K": K, "bytes": nb}
     for name, fn in (("two_launch", two), ("fused", fused)):
-        ms = time_graph(fn, steps, 10, stream, flush)
+        ms = time_graph(fn, steps, 10, stream, flush, lambda i, fn=fn: fn(i, warm))
         row[name] = {"us": round(ms * 1e3, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
-    del copies
+    del copies, warm
     torch.cuda.empty_cache()
     return row
 
@@ -339,15 +377,15 @@ def bench_case(case, steps, warmup, stream, flush):
         wsc = G.ternary_scale_f16(torch.from_numpy(d["src"]).to(dev))
         nbytes = N * K // 4 + 2 + 2 * M * K + 2 * M * N
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
-        copies = copies_of(Wp)
-        fn = lambda i: G.w2a16_gemm(A, copies[i % len(copies)], wsc, N, workspace=ws, C=C)
+        copies, warm = copies_of(Wp)
+        fn = lambda i, cps=copies: G.w2a16_gemm(A, cps[i % len(cps)], wsc, N, workspace=ws, C=C)
     elif case.scheme == "w4a16":
         Wq, s, z = G.quantize_pack_w4(torch.from_numpy(d["W"]).to(dev), G.W4_ASYM_GROUP)
         Wp = G.prepack_w(G.W4_LAYOUT_W4A16, Wq, N, K, s, z)
         nbytes = decode_bytes(M, N, K)
         C = torch.empty((M, N), dtype=torch.float16, device=dev)
-        copies = copies_of(Wp)
-        fn = lambda i: G.w4a16_gemm(A, copies[i % len(copies)], N, workspace=ws, C=C)
+        copies, warm = copies_of(Wp)
+        fn = lambda i, cps=copies: G.w4a16_gemm(A, cps[i % len(cps)], N, workspace=ws, C=C)
     else:
         Aq, sa, _ = G.quantize_a8(A)
         out = G.W4_OUT_F32 if case.out == "f32" else G.W4_OUT_F16
@@ -372,11 +410,11 @@ def bench_case(case, steps, warmup, stream, flush):
             wsc = G.ternary_scale_f16(torch.from_numpy(d["src"]).to(dev))
             mm, wbytes = G.w2a8_gemm, N * K // 4 + 2
         nbytes = wbytes + M * K + 4 * M + M * N * C.element_size()
-        copies = copies_of(Wp)
-        fn = lambda i: mm(Aq, sa, copies[i % len(copies)], wsc, N, out_dtype=out, workspace=ws,
-                          C=C)
-    ms = time_graph(fn, steps, warmup, stream, flush)
-    del copies
+        copies, warm = copies_of(Wp)
+        fn = lambda i, cps=copies: mm(Aq, sa, cps[i % len(cps)], wsc, N, out_dtype=out,
+                                      workspace=ws, C=C)
+    ms = time_graph(fn, steps, warmup, stream, flush, lambda i: fn(i, warm))
+    del copies, warm
     torch.cuda.empty_cache()
     return {"case": case.name, "M": M, "N": N, "K": K, "us": round(ms * 1e3, 3),
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -485,6 +523,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time every configured workload shape (graph replay); one JSON line "
                          "per case")
+    ap.add_argument("--case", default=None,
+                    help="with --sweep: time only the workload cases whose name contains this")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one from Python instead of replaying "
                          "them from one captured HIP graph")
@@ -505,6 +545,8 @@ def main():
     if args.sweep:
         from gemv_nibble_unpack_amd import workloads as WL
         for case in WL.ALL_CASES:
+            if args.case and args.case not in case.name:
+                continue
             print(json.dumps(bench_case(case, max(20, args.steps // 4), args.warmup, stream,
                                         flush)), flush=True)
         return

@@ -8,12 +8,14 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["quant.hip", "prepack.hip", "matmul.hip", "probe.hip", "noalloc.hip"]
+SOURCES = ["quant.hip", "prepack.hip", "matmul.hip", "gemm_launch.hip", "probe.hip", "noalloc.hip"]
 OUT = os.path.join(HERE, "libgemv_nibble_unpack.so")
+OBJ_DIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("W4_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -33,11 +35,7 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=True):
-    """Compile every HIP source into the package's shared library."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = OUT + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,6 +45,24 @@ def build(verbose=True):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose=True, jobs=None):
+    """Compile every HIP source (in parallel, one object each) and link the
+    package's shared library. Each translation unit carries its own device
+    code; no device function is called across units."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cflags = [f for f in FLAGS if f != "-shared"]
+    cmds = [[hipcc(), *cflags, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = OUT + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     undefined_kernels(tmp)
     os.replace(tmp, OUT)
     return OUT

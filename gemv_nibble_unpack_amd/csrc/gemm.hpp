@@ -55,10 +55,12 @@ struct GemmShape {
   static constexpr int A_BYTES = BM * G::TILE_K;                // unpadded, XOR-swizzled rows
   static constexpr int A_LOADS = A_BYTES / TILE_BYTES;          // 1 KiB wave loads per stage
   static constexpr int W_BYTES = NTILES * TILE_BYTES;
-  static constexpr int STAGE = A_BYTES + W_BYTES;
   static_assert(NTILES % 2 == 0, "two waves split the block's columns");
   static constexpr int NTW = NTILES / 2;                        // n subtiles per wave
-  // LDS stages in the ring (two fit the CU's 160 KiB in every configuration)
+  static constexpr int STAGE = A_BYTES + W_BYTES;
+  // LDS stages in the ring (two fit the CU's 160 KiB in every configuration;
+  // a third weight stage, fetching the weights two k tiles ahead, was
+  // measured no faster on the 256 x 352 blocks and is not used)
   static constexpr int STAGES = 2;
   static constexpr int A_PER_WAVE = A_LOADS / WAVES;            // direct loads per wave
   static constexpr int W_PER_WAVE = (NTILES + WAVES - 1) / WAVES;  // last round may be partial
@@ -150,8 +152,158 @@ __device__ __forceinline__ void gemm_col_params(const MMParams& p, int n, f4& ws
   }
 }
 
-template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
-__global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const GemmGrid gg) {
+// ---------------------------------------------------------------------------
+// One-launch fused prefill (FQ = 1: fp16 rows, FQ = 2: float32 rows in
+// p.A_in). Every wave of the grid first takes activation rows from a shared
+// counter, one at a time, and quantizes each whole row with the per-token
+// rule of quantize_a8 (INT4 page, Part 1 step 2: scale = max|a| / 127,
+// code = rint(a / scale)), writing the int8 row to p.A and its scale to
+// p.a_scale, then counts the row in for its m block. A block then waits until
+// its m block's rows are all in before it loads activations. This cannot
+// deadlock whatever the number of resident blocks: a block waits only after
+// the row counter has run out, i.e. when every row has been claimed by a wave
+// that is running and that waits for nothing before it finishes its row. The
+// wait is bounded anyway (FQ_SPIN_LIMIT polls) so that no wave can spin for
+// ever. The counter is polled with an atomic read-modify-write (dev_count):
+// plain loads of it are not guaranteed to see other XCDs' increments. The
+// last block to finish leaves the counters zero for the next call.
+//
+// Visibility across XCDs: the rows and scales are written with device-scope
+// (sc1) stores, which pass through to the memory all XCDs share, and a wave
+// waits for their completion (vmcnt 0) before it counts the row in with a
+// device-scope atomic; the waiting block polls the counter with device-scope
+// atomics, executes a device-scope acquire fence (the L2 and L1 invalidation
+// the AMDGPU memory model prescribes for an agent-scope acquire on gfx950),
+// and reads the rows and scales with device-scope (sc1) loads, the same
+// store / wait / count / load sequence as the split-K partial sums.
+// ---------------------------------------------------------------------------
+constexpr unsigned FQ_SPIN_LIMIT = 1u << 18;    // polls of ~0.5-2 us: under a second
+
+template <int FQ, int BM>
+__device__ __forceinline__ void fq_quantize_rows(const MMParams& p) {
+  constexpr int ESZ = FQ == 2 ? 4 : 2;               // input element bytes
+  constexpr int U = ESZ / 2;                         // 16-byte loads per 8-element chunk
+  constexpr int RC = 8;                              // chunks per lane held in registers
+  const int lane = threadIdx.x & 63;
+  const int K = p.K, nch = K / 8;                    // K % 16 == 0
+  const uint8_t* Ain = reinterpret_cast<const uint8_t*>(p.A_in);
+  uint32_t* qA = reinterpret_cast<uint32_t*>(const_cast<void*>(p.A));
+  uint32_t* sa = reinterpret_cast<uint32_t*>(const_cast<float*>(p.a_scale));
+  auto widen = [&](const u4 (&r)[U], float (&x)[8]) {
+    if constexpr (FQ == 1) {
+      const h8 hv = __builtin_bit_cast(h8, r[0]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (float)hv[e];
+    } else {
+      // whole-vector casts (a bit cast of one ext-vector element reads
+      // element 0 with this compiler)
+      const f4 a0 = __builtin_bit_cast(f4, r[0]);
+      const f4 a1 = __builtin_bit_cast(f4, r[U - 1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = a0[e];
+        x[4 + e] = a1[e];
+      }
+    }
+  };
+  auto load = [&](const uint8_t* src, int c, u4 (&r)[U]) {
+#pragma unroll
+    for (int h = 0; h < U; ++h) r[h] = *reinterpret_cast<const u4*>(src + (size_t)c * 8 * ESZ + 16 * h);
+  };
+  for (;;) {
+    // One claim per wave. The loop holds no lane-dependent branch around a
+    // side effect, and the row is wave-uniform in the compiler's eyes (an
+    // SGPR from readfirstlane): with the claim and the count-in written as
+    // `if (lane == 0) ...` and the row taken from a lane shuffle, the
+    // compiler gave the loop per-lane exits in which lane 0 went back for a
+    // new claim while the 63 others went round again on a stale row, for
+    // ever. Every lane now takes part in the atomics, lane 0 adding 1 and the
+    // others 0.
+    const unsigned one = lane == 0 ? 1u : 0u;
+    const unsigned claim = __hip_atomic_fetch_add(&p.sync[SYNC_NEXT], one, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    const int row = (int)__builtin_amdgcn_readfirstlane(claim);
+    if (row >= p.M) break;                           // uniform
+    const uint8_t* src = Ain + (size_t)row * K * ESZ;
+    uint32_t* dst = qA + (size_t)row * (K / 4);
+    float mx = 0.f, s, rs;
+    int sum = 0;
+    if (nch <= 64 * RC) {
+      // the row in registers: every load issued before the first is used
+      u4 raw[RC][U];
+#pragma unroll
+      for (int j = 0; j < RC; ++j) load(src, min(lane + 64 * j, nch - 1), raw[j]);
+#pragma unroll
+      for (int j = 0; j < RC; ++j) {
+        if (lane + 64 * j < nch) {
+          float x[8];
+          widen(raw[j], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
+        }
+      }
+      mx = wave_max(mx);
+      s = mx / 127.0f;
+      rs = s > 0.f ? 1.0f / s : 0.f;
+#pragma unroll
+      for (int j = 0; j < RC; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nch) {
+          float x[8];
+          widen(raw[j], x);
+          uint32_t lo, hi;
+          codes8_i8(x, s, rs, lo, hi, sum);
+          dev_store2(dst + 2 * c, lo, hi);
+        }
+      }
+    } else {
+      // longer rows: one pass for the maximum, a second (from cache) for the codes
+      for (int c = lane; c < nch; c += 64) {
+        u4 r[U];
+        load(src, c, r);
+        float x[8];
+        widen(r, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
+      }
+      mx = wave_max(mx);
+      s = mx / 127.0f;
+      rs = s > 0.f ? 1.0f / s : 0.f;
+      for (int c = lane; c < nch; c += 64) {
+        u4 r[U];
+        load(src, c, r);
+        float x[8];
+        widen(r, x);
+        uint32_t lo, hi;
+        codes8_i8(x, s, rs, lo, hi, sum);
+        dev_store2(dst + 2 * c, lo, hi);
+      }
+    }
+    dev_store(&sa[row], __builtin_bit_cast(uint32_t, s));   // every lane, the same value
+    stores_done();                                   // the row is out before it is counted in
+    __hip_atomic_fetch_add(&p.sync[SYNC_DONE + row / BM], one, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The last block to finish resets the counters (every block has passed its
+// wait and every wave its row claims by the time it counts itself in).
+template <int BM>
+__device__ __forceinline__ void fq_finish(const MMParams& p) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned total = gridDim.x * gridDim.y;
+    if (dev_arrive(&p.sync[SYNC_FIN]) == total - 1) {
+      const int mblocks = (p.M + BM - 1) / BM;
+      dev_store(&p.sync[SYNC_NEXT], 0u);
+      for (int i = 0; i < mblocks; ++i) dev_store(&p.sync[SYNC_DONE + i], 0u);
+      dev_store(&p.sync[SYNC_FIN], 0u);
+    }
+  }
+}
+
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS, int FQ>
+__device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg) {
   using G = GemmTraits<KIND>;
   using S = GemmShape<KIND, NTILES, WM>;
   static_assert(S::THREADS == 128 * WM, "launch bounds");
@@ -202,9 +354,8 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
   // Rows past M and k past K read clamped addresses: the weight codes there
   // are zero, so those products vanish, and rows past M are never stored.
   const int lrow = lane / RC, lchunk = lane % RC;    // position within one 1 KiB load
-  auto issue = [&](int kt, int st) {
+  auto issue_a = [&](int kt, int st) {
     uint8_t* sa = smem + st * S::STAGE;
-    uint8_t* sw = sa + S::A_BYTES;
 #pragma unroll
     for (int q = 0; q < S::A_PER_WAVE; ++q) {
       const int ld = wave * S::A_PER_WAVE + q;       // 1 KiB load index within the A tile
@@ -212,8 +363,14 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
       const int c = a_chunk<KIND>(row, lchunk);      // logical chunk for this physical slot
       const int gm = min(m0 + row, p.M - 1);
       const int gk = min(kt * TK + 16 * c, p.K - 16);
-      __builtin_amdgcn_global_load_lds(A + (size_t)gm * p.K + gk, sa + ld * TILE_BYTES, 16, 0, 0);
+      // rows quantized by this launch are read at device scope (sc1), like
+      // every other value one block hands to another here
+      __builtin_amdgcn_global_load_lds(A + (size_t)gm * p.K + gk, sa + ld * TILE_BYTES, 16, 0,
+                                       FQ != 0 ? 16 : 0);
     }
+  };
+  auto issue_w = [&](int kt, int st) {
+    uint8_t* sw = smem + st * S::STAGE + S::A_BYTES;
 #pragma unroll
     for (int q = 0; q < S::W_PER_WAVE; ++q) {
       const int tl = q * S::WAVES + wave;            // weight tile within the block
@@ -222,6 +379,10 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
       __builtin_amdgcn_global_load_lds(p.Wt + ((size_t)t * p.KT + kt) * TILE_BYTES + lane * 16,
                                        sw + tl * TILE_BYTES, 16, 0, 0);
     }
+  };
+  auto issue = [&](int kt, int st) {
+    issue_a(kt, st);
+    issue_w(kt, st);
   };
   auto compute = [&](int st, i4 (&acc)[4][NTW]) {
     const uint8_t* sa = smem + st * S::STAGE;
@@ -283,7 +444,24 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
   // Two-stage ring: tile i+1 streams into the other stage while tile i is
   // multiplied; the barrier after the wait publishes it to every wave and
   // frees stage i for tile i+2.
-  if (nk > 0) issue(kb, 0);
+  if constexpr (FQ != 0) {
+    // the first weight tiles do not depend on the activations: they stream
+    // in while the block waits for its m block's quantized rows
+    if (nk > 0) issue_w(kb, 0);
+    if (wave == 0) {
+      if (lane == 0) {
+        const unsigned need = (unsigned)min(S::BM, p.M - m0);
+        unsigned polls = 0;
+        while (dev_count(&p.sync[SYNC_DONE + mb]) < need && ++polls < FQ_SPIN_LIMIT)
+          __builtin_amdgcn_s_sleep(8);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (nk > 0) issue_a(kb, 0);
+  } else {
+    if (nk > 0) issue(kb, 0);
+  }
   constexpr bool LP = S::LDS_PARAMS && OUT == W4_OUT_F16;
   float* lws = reinterpret_cast<float*>(smem + S::PARAM_OFF);
   uint16_t* lbias = reinterpret_cast<uint16_t*>(smem + S::PARAM_OFF + NTILES * 16 * 4);
@@ -310,7 +488,10 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
   float sav[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    sav[i] = OUT == W4_OUT_I32 ? 0.f : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
+    sav[i] = OUT == W4_OUT_I32 ? 0.f
+             : FQ != 0 ? __builtin_bit_cast(float, dev_load(reinterpret_cast<const uint32_t*>(
+                             p.a_scale) + min(m0 + 64 * wm + 16 * i + r, p.M - 1)))
+                       : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
   // ---- split K: exact INT32 partial sums through the workspace; the last
   // block of the tile to arrive adds the other blocks' sums to its own
   // accumulators and runs the epilogue below. Integer sums do not depend on
@@ -446,6 +627,12 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const Ge
   }
 }
 
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS, int FQ = 0>
+__global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const GemmGrid gg) {
+  if constexpr (FQ != 0) fq_quantize_rows<FQ, 64 * WM>(p);
+  gemm_tile<KIND, NTILES, WM, OUT, BIAS, FQ>(p, gg);
+  if constexpr (FQ != 0) fq_finish<64 * WM>(p);
+}
 
 // ---------------------------------------------------------------------------
 // planning (host)
@@ -517,40 +704,48 @@ inline size_t gemm_workspace_bytes(int kind, int M, int N, int K, GemmCfg c) {
   return WS_COUNTERS + (size_t)gg.tiles * gg.ksplit * (64 * c.wm) * (16 * c.ntiles) * sizeof(int32_t);
 }
 
-template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS, int FQ>
 int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
   using S = GemmShape<KIND, NTILES, WM>;
   const dim3 grid(gg.per_xcd * 8, gg.ksplit);
-  allow_smem((const void*)&k_gemm<KIND, NTILES, WM, OUT, BIAS>, S::LDS);
-  hipLaunchKernelGGL((k_gemm<KIND, NTILES, WM, OUT, BIAS>), grid, dim3(S::THREADS), S::LDS,
+  allow_smem((const void*)&k_gemm<KIND, NTILES, WM, OUT, BIAS, FQ>, S::LDS);
+  hipLaunchKernelGGL((k_gemm<KIND, NTILES, WM, OUT, BIAS, FQ>), grid, dim3(S::THREADS), S::LDS,
                      stream, p, gg);
   return launch_status();
 }
 
-template <int KIND, int NTILES, int WM>
-int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream) {
-  p.counters = reinterpret_cast<unsigned*>(ws);
-  p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + WS_COUNTERS : nullptr;
-  if (p.out_dtype == W4_OUT_I32) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I32, false>(p, gg, stream);
-  if (p.out_dtype == W4_OUT_F32) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F32, false>(p, gg, stream);
-  if (p.bias) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, true>(p, gg, stream);
-  return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, false>(p, gg, stream);
+template <int KIND, int NTILES, int WM, int FQ>
+int launch_gemm_f(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
+  if (p.out_dtype == W4_OUT_I32)
+    return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I32, false, FQ>(p, gg, stream);
+  if (p.out_dtype == W4_OUT_F32)
+    return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F32, false, FQ>(p, gg, stream);
+  if (p.bias) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, true, FQ>(p, gg, stream);
+  return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, false, FQ>(p, gg, stream);
 }
 
+// fq: 0 for int8 activations in p.A; 1 (fp16) or 2 (float32) for rows in
+// p.A_in that the kernel quantizes into p.A / p.a_scale first (the caller
+// points those at workspace memory and sets p.sync)
+template <int KIND, int NTILES, int WM>
+int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream, int fq) {
+  p.counters = reinterpret_cast<unsigned*>(ws);
+  p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + WS_COUNTERS : nullptr;
+  if (fq == 1) return launch_gemm_f<KIND, NTILES, WM, 1>(p, gg, stream);
+  if (fq == 2) return launch_gemm_f<KIND, NTILES, WM, 2>(p, gg, stream);
+  return launch_gemm_f<KIND, NTILES, WM, 0>(p, gg, stream);
+}
+
+// Defined in gemm_launch.hip (a translation unit of its own, so that the
+// GEMM instances compile in parallel with the rest of the library).
+int launch_gemm_w4a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
+int launch_gemm_w2a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
+
 template <int KIND>
-int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream) {
-  if constexpr (KIND != KIND_W4A8 && KIND != KIND_W2A8) {
-    return W4_ERR_ARG;
-  } else {
-    const GemmGrid gg = gemm_grid(KIND, p.M, p.N, p.K, c);
-    if constexpr (KIND == KIND_W4A8) {
-      if (c.ntiles == 22 && c.wm == 4) return launch_gemm_t<KIND, 22, 4>(p, gg, ws, stream);
-      if (c.ntiles == 22) return launch_gemm_t<KIND, 22, 2>(p, gg, ws, stream);
-      return launch_gemm_t<KIND, 16, 2>(p, gg, ws, stream);
-    } else {
-      return launch_gemm_t<KIND, 8, 2>(p, gg, ws, stream);
-    }
-  }
+int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq = 0) {
+  if constexpr (KIND == KIND_W4A8) return launch_gemm_w4a8(p, c, ws, stream, fq);
+  else if constexpr (KIND == KIND_W2A8) return launch_gemm_w2a8(p, c, ws, stream, fq);
+  else return W4_ERR_ARG;
 }
 
 }  // namespace w4

@@ -1,0 +1,20 @@
+// The prefill GEMM's kernel instances and their launch (block shape, output
+// type, bias, and the fused activation quantization, chosen at run time).
+
+#include "gemm.hpp"
+
+namespace w4 {
+
+int launch_gemm_w4a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq) {
+  const GemmGrid gg = gemm_grid(KIND_W4A8, p.M, p.N, p.K, c);
+  if (c.ntiles == 22 && c.wm == 4) return launch_gemm_t<KIND_W4A8, 22, 4>(p, gg, ws, stream, fq);
+  if (c.ntiles == 22) return launch_gemm_t<KIND_W4A8, 22, 2>(p, gg, ws, stream, fq);
+  return launch_gemm_t<KIND_W4A8, 16, 2>(p, gg, ws, stream, fq);
+}
+
+int launch_gemm_w2a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq) {
+  const GemmGrid gg = gemm_grid(KIND_W2A8, p.M, p.N, p.K, c);
+  return launch_gemm_t<KIND_W2A8, 8, 2>(p, gg, ws, stream, fq);
+}
+
+}  // namespace w4

@@ -555,22 +555,31 @@ extern "C" int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size,
 // ---------------------------------------------------------------------------
 // fused activation quantization: quantize_a8 + w4a8_gemm / w2a8_gemm in one
 // call. Decode shapes whose activation rows fit the block's LDS staging run
-// one kernel that quantizes in its prologue; everything else quantizes into
-// the workspace first.
+// one kernel that quantizes in its prologue; prefill GEMM shapes run one
+// kernel whose waves quantize whole rows into the workspace before the tiles
+// are multiplied; everything else (the skinny kernel, decode rows too long
+// to stage) quantizes into the workspace with quantize_a8 first.
 // ---------------------------------------------------------------------------
 namespace w4 {
 
+// The one-launch fused prefill (k_gemm with FQ != 0) is switched off: its
+// first GPU runs hung in the row-claim loop (a divergent loop exit, fixed in
+// the kernel since, but not yet run on a GPU again). Until it is, prefill
+// GEMM shapes quantize with quantize_a8 first (two launches).
+constexpr bool FUSED_PREFILL_ONE_LAUNCH = false;
+
 struct FusedPlan {
   Plan P;
-  int fqc;            // prologue slots per lane (0: two launches)
-  size_t q_off;       // two launches: offset of the quantized rows and their scales
+  int fqc;            // decode prologue slots per lane (0: not that form)
+  bool gemm_fq;       // the prefill GEMM quantizes its rows itself (one launch)
+  size_t q_off;       // offset of the quantized rows and their scales
   size_t ws_bytes;    // total workspace
 };
 
-// Two launches: the matmul's own workspace (counters, partial sums) keeps
-// offset 0 and the quantized rows follow it, past the counter area even when
-// the matmul does not split, so the counters of every call stay where they
-// are in every other call.
+// Quantized rows in the workspace: the matmul's own workspace (counters,
+// partial sums) keeps offset 0 and the rows follow it, past the counter area
+// even when the matmul does not split, so the counters of every call stay
+// where they are in every other call.
 inline FusedPlan fused_plan(int kind, int M, int N, int K) {
   FusedPlan F{};
   F.P = make_plan(kind, M, N, K);
@@ -579,6 +588,8 @@ inline FusedPlan fused_plan(int kind, int M, int N, int K) {
   if (!F.P.gemm && !F.P.skinny && F.P.waves != 8)
     F.P = plan_from(kind, M, N, K, Candidate{PATH_DECODE, F.P.ksplit, {}, 0, 8});
   F.fqc = (!F.P.gemm && !F.P.skinny && F.P.staged) ? fq_slots(M < 16 ? M : 16, K) : 0;
+  // one completion counter per m block in the counter area's last KiB
+  F.gemm_fq = FUSED_PREFILL_ONE_LAUNCH && F.P.gemm && ceil_div(M, 64 * F.P.cfg.wm) <= SYNC_MBLOCKS;
   if (F.fqc) {
     F.ws_bytes = F.P.ws_bytes;
   } else {
@@ -630,14 +641,36 @@ int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp, const
     if (!aligned(ws, 256)) return W4_ERR_ALIGN;
   }
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  const Geometry g = geometry(kind_layout(kind), N, K);
+  const int fq = in_dtype == W4_IN_F16 ? 1 : 2;
   if (!F.fqc) {
     int8_t* Aq = reinterpret_cast<int8_t*>(wsb + F.q_off);
     float* sa = reinterpret_cast<float*>(wsb + F.q_off + align256((size_t)M * K));
+    if (F.gemm_fq) {
+      MMParams p{};
+      p.A = Aq;
+      p.a_scale = sa;
+      p.A_in = A;
+      p.sync = reinterpret_cast<unsigned*>(ws) + WS_SYNC_WORD;
+      p.Wt = Wp;
+      p.w_scale = kind == KIND_W4A8 ? (const float*)scale : nullptr;
+      p.w_scale16 = kind == KIND_W2A8 ? (const uint16_t*)scale : nullptr;
+      p.bias = out_dtype == W4_OUT_I32 ? nullptr : bias;
+      p.C = C;
+      p.out_dtype = out_dtype;
+      p.M = M;
+      p.N = N;
+      p.K = K;
+      p.NT = g.NT;
+      p.KT = g.KT;
+      p.KQ = g.KQ;
+      return kind == KIND_W4A8 ? launch_gemm<KIND_W4A8>(p, F.P.cfg, ws, stream, fq)
+                               : launch_gemm<KIND_W2A8>(p, F.P.cfg, ws, stream, fq);
+    }
     const int q = quantize_a8(A, in_dtype, M, K, Aq, sa, nullptr, stream);
     if (q != W4_OK) return q;
     return a8_common(kind, Aq, sa, Wp, scale, bias, C, out_dtype, M, N, K, wsb, F.q_off, stream);
   }
-  const Geometry g = geometry(kind_layout(kind), N, K);
   MMParams p{};
   p.A = A;
   p.Wt = Wp;
@@ -652,7 +685,6 @@ int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp, const
   p.NT = g.NT;
   p.KT = g.KT;
   p.KQ = g.KQ;
-  const int fq = in_dtype == W4_IN_F16 ? 1 : 2;
   return kind == KIND_W4A8 ? launch_gemv<KIND_W4A8>(F.P, p, ws, stream, fq, F.fqc)
                            : launch_gemv<KIND_W2A8>(F.P, p, ws, stream, fq, F.fqc);
 }

@@ -389,7 +389,10 @@ def test_extreme_codes_at_max_k_no_overflow(g, kind):
     Wp = g.prepack_w(layout, Wq, N, K)
     C32 = host(mm(dev(qa), dev(np.ones(2, np.float32)), Wp, scale, N, out_dtype=g.W4_OUT_I32))
     ref = O.int_accumulate(qa, codes)
-    assert ref[0, 0] == 16384 * K
+    # the kernels sum 16 q (4-bit), 64 c (2-bit) or the INT8 code as it is:
+    # the internal accumulator of entry (0, 0) reaches 16384 K < 2^31
+    unpack = {"w4a8": 16, "w2a8": 64, "w8a8": 1}[kind]
+    assert ref[0, 0] * unpack == 16384 * K < 2**31
     assert np.array_equal(C32, ref.astype(np.int32))
 
 
@@ -433,6 +436,15 @@ def test_fused_act_tiny_and_tie_rows(g):
         assert np.array_equal(ref, got), m
 
 
+# The one-launch fused prefill hung twice on the GPU (an endless row-claim
+# loop: the loop exit was divergent in the compiled code; the kernel is fixed
+# since but has not run on a GPU again). Its dispatch is switched off and the
+# cases written for it are skipped until it has.
+SKIP_ONE_LAUNCH = pytest.mark.skip(
+    reason="one-launch fused prefill switched off after two GPU hangs in its row-claim loop "
+           "(divergent loop exit, fixed in the kernel, not yet re-run on a GPU)")
+
+
 @pytest.mark.parametrize("scheme,M,N,K,dt", [
     ("w4a8", 1, 256, 256, np.float32),      # the tiny GEMV configuration
     ("w4a8", 1, 4096, 4096, np.float16),
@@ -443,7 +455,13 @@ def test_fused_act_tiny_and_tie_rows(g):
     ("w4a8", 40, 300, 512, np.float16),     # three 16-row tiles through the prologue
     ("w4a8", 1, 4096, 11008, np.float16),   # long rows: several chunks per lane
     ("w4a8", 16, 4096, 4096, np.float16),   # too wide for the prologue: two launches
-    ("w4a8", 300, 2000, 1040, np.float16),  # prefill GEMM: two launches
+    ("w4a8", 300, 2000, 1040, np.float16),  # skinny kernel: two launches
+    # prefill GEMM, one launch: the waves quantize whole rows first
+    pytest.param("w4a8", 2048, 11008, 4096, np.float16, marks=SKIP_ONE_LAUNCH),  # 256 x 352
+    pytest.param("w4a8", 2000, 3000, 1040, np.float16, marks=SKIP_ONE_LAUNCH),   # 128 x 256
+    pytest.param("w4a8", 1100, 4004, 8208, np.float32, marks=SKIP_ONE_LAUNCH),   # two row passes
+    pytest.param("w2a8", 1100, 2000, 1024, np.float16, marks=SKIP_ONE_LAUNCH),   # split over K
+    pytest.param("w2a8", 1030, 4100, 8240, np.float32, marks=SKIP_ONE_LAUNCH),
     ("w2a8", 1, 3200, 3200, np.float16),
     ("w2a8", 1, 8640, 3200, np.float16),
     ("w2a8", 5, 100, 528, np.float32),
@@ -466,6 +484,10 @@ def test_fused_act_matches_two_calls_and_oracle(g, scheme, M, N, K, dt):
         mm, fused = g.w2a8_gemm, g.w2a8_gemm_fused_act
     Ad = dev(A)
     Aq, sa, _ = g.quantize_a8(Ad)
+    plan = g.w4_plan_name(g.W4_OP_W4A8 if scheme == "w4a8" else g.W4_OP_W2A8, M, N, K,
+                          g.w4_plan_current(g.W4_OP_W4A8 if scheme == "w4a8" else g.W4_OP_W2A8,
+                                            M, N, K))
+    say(f"  plan {plan}")
     for out in (g.W4_OUT_I32, g.W4_OUT_F32, g.W4_OUT_F16):
         b = f16(bias) if out == g.W4_OUT_F16 else None
         ref = host(mm(Aq, sa, Wp, ws, N, bias=b, out_dtype=out))
@@ -474,6 +496,72 @@ def test_fused_act_matches_two_calls_and_oracle(g, scheme, M, N, K, dt):
         if out == g.W4_OUT_I32:
             qa, _, _ = O.quantize_a8(A)
             assert np.array_equal(got, O.int_accumulate_f64(qa, qw).astype(np.int32))
+
+
+@SKIP_ONE_LAUNCH
+def test_fused_prefill_counters_across_calls_graphs_and_shared_workspace(g):
+    # The one-launch fused prefill leaves its row-claim and completion
+    # counters zero: calls of different shapes in a row through one shared
+    # workspace (with a 64-way split decode call between them, whose arrival
+    # counters live in the same counter area), and three replays of a
+    # captured fused call, all equal their results on fresh workspaces and
+    # the oracle.
+    cases = [(2000, 3000, 1040, 0), (1100, 2000, 1024, 2), (600, 11000, 1040, 0)]
+    ops = []
+    for i, (M, N, K, kind) in enumerate(cases):
+        A = WL.activations(M, K, seed=9600 + i, dtype=np.float16)
+        if kind == 0:
+            W = WL.weights_f32(N, K, seed=9610 + i)
+            Wp, ws = prep_w4a8(g, W)
+            qw, _ = O.quantize_w4_sym(W)
+            fn = g.w4a8_gemm_fused_act
+        else:
+            codes = WL.ternary_codes(N, K, seed=9620 + i)
+            Wp, ws = prep_w2a8(g, codes, WL.weights_f32(N, K, seed=9630 + i))
+            qw, fn = codes, g.w2a8_gemm_fused_act
+        qa, _, _ = O.quantize_a8(A)
+        ops.append((dev(A), Wp, ws, N, fn, O.int_accumulate_f64(qa, qw).astype(np.int32)))
+    # the split decode call between them
+    codes = WL.ternary_codes(16, 131056, seed=9640)
+    Wd, wsd = prep_w2a8(g, codes, WL.weights_f32(16, 131056, seed=9641))
+    Ad = dev(WL.activations(1, 131056, seed=9642, dtype=np.float16))
+    qa, sa_d, _ = O.quantize_a8(host(Ad))
+    acc_d = O.int_accumulate_f64(qa, codes).astype(np.int32)
+    Aq_d, sa_dd, _ = g.quantize_a8(Ad)
+    need = max(g.w4_fused_act_workspace_bytes(g.W4_LAYOUT_W4A8 if kind == 0 else
+                                              g.W4_LAYOUT_W2A8, M, N, K)
+               for (M, N, K, kind) in cases)
+    need = max(need, g.w4_plan_workspace_bytes(g.W4_OP_W2A8, 1, 16, 131056))
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    say(f"case fused prefill: shared workspace of {need} bytes, three shapes and a split call")
+    for rep in range(2):
+        for i, (A, Wp, ws, N, fn, acc) in enumerate(ops):
+            got = host(fn(A, Wp, ws, N, out_dtype=g.W4_OUT_I32, workspace=shared))
+            assert np.array_equal(got, acc), (rep, i)
+            assert np.array_equal(got, host(fn(A, Wp, ws, N, out_dtype=g.W4_OUT_I32))), (rep, i)
+            got = host(g.w2a8_gemm(Aq_d, sa_dd, Wd, wsd, 16, out_dtype=g.W4_OUT_I32,
+                                   workspace=shared))
+            assert np.array_equal(got, acc_d), (rep, i)
+        assert not host(shared[:16384]).any()
+    say("case fused prefill: graph capture, three replays")
+    A, Wp, ws, N, fn, acc = ops[0]
+    C = torch.empty((cases[0][0], N), dtype=torch.int32, device="cuda")
+    call = lambda: fn(A, Wp, ws, N, out_dtype=g.W4_OUT_I32, workspace=shared, C=C)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        C.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        assert np.array_equal(host(C), acc), r
+    assert not host(shared[:16384]).any()
 
 
 # ---------------------------------------------------------------------------
