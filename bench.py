@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 I8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA
 LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 ROTATE_BYTES = 1 << 30         # weight copies in rotation per workload
-FLUSH_BYTES = 1 << 30          # read + written between the untimed and the timed pass
+FLUSH_BYTES = 1 << 30          # read between the untimed and the timed pass
 PREFILL_MIN_STEPS = 50         # the prefill is timed over at least this many calls
 CALIB_BYTES = 256 << 20        # device-to-device copy used to calibrate PMC byte counters
 PROBE_PER = (1, 2, 4, 8)       # 16-byte loads per lane tried by the read probe
@@ -89,20 +89,23 @@ def cold_gap_bytes(steps, copies, copy_bytes, flush_bytes=FLUSH_BYTES):
 
 
 class Flush:
-    """Reads FLUSH_BYTES / 2 and writes as many (torch's elementwise neg on
-    int8; a kernel of its own name, apart from the bitwise_not copy that
-    calibrates the byte counters), evicting the weights from the last-level
-    cache."""
+    """Reads FLUSH_BYTES of a buffer of its own with the library's streaming
+    read (w4_read_probe, which stores nothing but a conditional sink word),
+    evicting the weights from the last-level cache. A read-only flush leaves
+    the cache holding clean lines: a flush that wrote would leave dirty ones,
+    whose write-back the next reads would pay for (the timed calls would then
+    move twice their bytes until the dirty data had drained)."""
 
     def __init__(self, dev):
         import torch
-        self.src = torch.ones(FLUSH_BYTES // 2, dtype=torch.int8, device=dev)
-        self.dst = torch.empty_like(self.src)
+        self.buf = torch.ones(FLUSH_BYTES, dtype=torch.int8, device=dev)
+        self.sink = torch.zeros(1024, dtype=torch.int32, device=dev)
 
     def __call__(self, stream):
         import torch
+        import gemv_nibble_unpack_amd as G
         with torch.cuda.stream(stream):
-            torch.neg(self.src, out=self.dst)
+            G.w4_read_probe(self.buf, FLUSH_BYTES, 8, self.sink)
 
 
 def warm_steps(step_ms):
@@ -517,7 +520,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the W4A8 M=1 context (quantize_a8 + GEMV vs the fused call)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
-                    help="time one workload only (for profiler runs); prints its own JSON line")
+                    help="time one workload only (for profiler runs): the decode GEMV at each "
+                         "of its shapes, or the prefill; prints one JSON line per shape")
     ap.add_argument("--calib", action="store_true",
                     help="also run a copy of known size (for PMC byte-counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -559,7 +563,7 @@ def main():
                           "gemm_tops": ops / (pre["gemm_ms"] * 1e-3) / 1e12}), flush=True)
         return
 
-    shapes = DECODE_SHAPES[:1] if args.only == "decode" else DECODE_SHAPES
+    shapes = DECODE_SHAPES
     dec = []
     for (N, K) in shapes:
         log(f"bench: decode W4A16 M=1 N={N} K={K}")
@@ -570,7 +574,8 @@ def main():
     if args.only == "decode":
         if args.calib:
             calibration_copy()
-        print(json.dumps({"workload": "w4a16_decode_gemv", **head}), flush=True)
+        for x in dec:
+            print(json.dumps({"workload": "w4a16_decode_gemv", **x}), flush=True)
         return
 
     gbs = head["bytes"] / (head["ms"] * 1e-3) / 1e9

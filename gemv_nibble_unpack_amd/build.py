@@ -24,6 +24,9 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     # no packed-FP32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive preloaded in SGPRs (up to the
+    # user-SGPR limit) instead of through a kernel-argument fetch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument", *os.environ.get("W4_EXTRA_FLAGS", "").split(),
 ]
 

@@ -106,6 +106,14 @@ inline int launch_status() {
 // device helpers
 // ---------------------------------------------------------------------------
 // Wave-wide reductions (64 lanes) through cross-lane shuffles.
+// c / d for 0 <= c < 2^20 and 1 <= d < 2^24 without an integer division
+// sequence: x = (c + 1/2) / d lies at least 1/(2d) from an integer, while the
+// reciprocal (within 1 ulp) and the product leave an error below x * 2^-22 =
+// (c + 1/2) / d * 2^-22 < 1/(2d), so truncating x gives the exact quotient.
+__device__ __forceinline__ int small_div(int c, int d) {
+  return (int)(((float)c + 0.5f) * __builtin_amdgcn_rcpf((float)d));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -76,6 +76,19 @@ __device__ __forceinline__ h8 unpack_w4_f16(uint32_t w, h2 zlo, h2 zhi) {
   return h8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 }
 
+// W4A16, one activation row: one word (8 codes) -> 8 fp16 values with no
+// arithmetic: 1024 + q in slots 0, 1, 4, 5 (codes in bits 0..3 of a half) and
+// 1024 + 16q in slots 2, 3, 6, 7 (bits 4..7). The staged activations at slots
+// 2, 3, 6, 7 are pre-divided by 16, so every product is a*(1024+q) or
+// (a/16)*(1024+16q) = 64a + aq; the offsets and the zero point are removed
+// per group after the products (see k_gemv, M1).
+__device__ __forceinline__ h8 unpack_w4_off(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  const u4 v = u4{and_or(w, 0x000F000Fu, 0x64006400u), and_or(w, 0x00F000F0u, 0x64006400u),
+                  and_or(w8, 0x000F000Fu, 0x64006400u), and_or(w8, 0x00F000F0u, 0x64006400u)};
+  return __builtin_bit_cast(h8, v);
+}
+
 // W4A8: two words (16 codes) -> one i8 MFMA operand of values 16*q.
 __device__ __forceinline__ i4 unpack_w4_i8(uint32_t w0, uint32_t w1) {
   return i4{(int)((w0 << 4) & 0xF0F0F0F0u), (int)(w0 & 0xF0F0F0F0u),
@@ -284,12 +297,41 @@ struct AStage {
 // scales for the epilogue. Rows <= 8: the waves split into groups of G waves
 // per row; rows > 8: wave w owns rows w and w + 8. Each lane holds up to FQC
 // 8-element chunks of its rows, loaded before the weight tiles.
+//
+// M1 (W4A16, one activation row, wave staging, one pass): the codes go to the
+// matrix core as 1024 + q or 1024 + 16q (unpack_w4_off) against activations
+// whose slots 2, 3, 6, 7 are pre-divided by 16 when staged. A tile's product
+// is then part = 1024*SL + 64*SH + sum(a*q), where SL and SH are the group's
+// activation sums over the two slot classes; its contribution is
+// s * (part - 1024*SL - 64*SH - z*(SL + SH)) = s * sum(a*(q - z)), with the
+// sums formed once per wave from the staged rows. Only the row-0 output of
+// each lane is kept.
+//
+// The fields the first loads depend on come as leading scalar arguments: the
+// library is built with kernel-argument preloading, so they arrive in SGPRs
+// with the wave instead of through a kernel-argument fetch (a memory round
+// trip of a few hundred ns in front of the first weight load); the other
+// fields of p are fetched while the weights stream.
 template <int KIND, int WAVES, int MAXT, int APER, bool STAGED, int FQ = 0, int FQC = 1,
-          bool WST = false>
-__global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
+          bool WST = false, bool M1 = false>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* Wt, const void* A,
+                                                     const uint16_t* St, const uint8_t* Zt, int M,
+                                                     int K, int KT, int KQ, int kts,
+                                                     const MMParams pin) {
   static_assert(FQ == 0 || (STAGED && (KIND == KIND_W4A8 || KIND == KIND_W2A8) && WAVES == 8),
                 "fused quantization");
   static_assert(!WST || (STAGED && FQ == 0), "wave staging");
+  static_assert(!M1 || (KIND == KIND_W4A16 && WST), "one-row offset scheme");
+  MMParams p = pin;
+  p.Wt = Wt;
+  p.A = A;
+  p.St = St;
+  p.Zt = Zt;
+  p.M = M;
+  p.K = K;
+  p.KT = KT;
+  p.KQ = KQ;
+  p.kts = kts;
   using AS = AStage<KIND>;
   constexpr bool A16 = KIND == KIND_W4A16 || KIND == KIND_W2A16;  // fp16 activations
   constexpr bool GRP = KIND == KIND_W4A16;                         // group scales and zeros
@@ -302,7 +344,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   typedef typename std::conditional<FACC, f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  fetch_args(p);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,7 +367,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
   const int rows = min(16, p.M - mtile * 16);
   const int kb = blockIdx.y * p.kts;
   const int ke = min(p.KT, kb + p.kts);
-  const int per = (ke - kb + WAVES - 1) / WAVES;
+  // W4A16 runs start on a group quad (kts is a multiple of 4), so a lane
+  // fetches the scales and zeros of four tiles with one load each
+  const int per = GRP ? ((ke - kb + 3) / 4 + WAVES - 1) / WAVES * 4 : (ke - kb + WAVES - 1) / WAVES;
   const int wb = kb + wave * per;
   const int nt = max(0, min(ke, wb + per) - wb);     // tiles of this wave (uniform)
 
@@ -383,7 +426,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 #pragma unroll
     for (int i = 0; i < APER; ++i) {
       const int c = min(lane + i * 64, wtotal - 1);
-      const int row = c / wcpr, col = c - row * wcpr;
+      const int row = small_div(c, wcpr), col = c - row * wcpr;
       // past the wave's run or past K: clamp into the row, zeroed below
       const size_t off = min(wbyte0 + (size_t)col * 16, arow_bytes - 16);
       stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)(mtile * 16 + row) * arow_bytes + off);
@@ -392,7 +435,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 #pragma unroll
     for (int i = 0; i < (STAGED && FQ == 0 ? APER : 0); ++i) {
       const int c = min(tid + i * NTHR, total - 1);
-      const int row = c / cpr, col = c - row * cpr;
+      const int row = small_div(c, cpr), col = c - row * cpr;
       size_t off = kbyte0 + (size_t)col * 16;
       if constexpr (KTAIL) off = min(off, arow_bytes - 16);  // k tail: clamp, zeroed below
       stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)(mtile * 16 + row) * arow_bytes + off);
@@ -408,6 +451,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
 
   // ---- phase 1b: this wave's weight tiles --------------------------------
   Acc acc = Acc{};
+  // M1: per staged chunk, the float32 activation sums over its two slot
+  // classes; then per tile of the run, the offset 1024*SL + 64*SH and SL + SH
+  float m1_sl[M1 ? APER : 1], m1_sh[M1 ? APER : 1], m1_off[M1 ? MAXT : 1], m1_sum[M1 ? MAXT : 1];
+#pragma unroll
+  for (int i = 0; i < (M1 ? APER : 1); ++i) m1_sl[i] = m1_sh[i] = 0.f;
   for (int pass = 0; pass * MAXT < max(nt, 1); ++pass) {
     const int pb = wb + pass * MAXT;
     const int pn = min(MAXT, nt - pass * MAXT);      // tiles in this pass (uniform)
@@ -425,10 +473,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       // streamed once unless several m tiles share the weight tile through L2
       wv[u] = mtiles == 1 ? __builtin_nontemporal_load(wp) : *wp;
       if constexpr (GRP) {
-        const size_t mi =
-            live ? (((size_t)tile * p.KQ + (kt >> 2)) * TILE_N + r) * 4 + (kt & 3) : 0;
-        sv[u] = p.St[mi];
-        zv[u] = p.Zt[mi];
+        // the run and the pass start on a quad: the row's four group scales
+        // (8 bytes) and zeros (4 bytes) of tiles u..u+3 in one load each (a
+        // quad past the run reads quad 0)
+        if (u % 4 == 0) {
+          const size_t mq = live ? (((size_t)tile * p.KQ + (kt >> 2)) * TILE_N + r) * 4 : 0;
+          const uint64_t s8 = *reinterpret_cast<const uint64_t*>(p.St + mq);
+          const uint32_t z4 = *reinterpret_cast<const uint32_t*>(p.Zt + mq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (u + e < MAXT) {
+              sv[u + e] = (uint16_t)(s8 >> (16 * e));
+              zv[u + e] = (uint8_t)(z4 >> (8 * e));
+            }
+          }
+        }
       }
     }
 
@@ -545,10 +604,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       for (int i = 0; i < APER; ++i) {
         const int c = lane + i * 64;
         if (c < wtotal) {
-          const int row = c / wcpr, col = c - row * wcpr;
+          const int row = small_div(c, wcpr), col = c - row * wcpr;
           u4 v = stage[i];
           if (col * 16 >= nt * AS::TILE_ROWB || wbyte0 + (size_t)col * 16 >= arow_bytes)
             v = u4{0u, 0u, 0u, 0u};
+          if constexpr (M1) {
+            // this chunk's sums over slots 0, 1, 4, 5 (SL) and 2, 3, 6, 7 (SH)
+            // in float32, then slots 2, 3, 6, 7 divided by 16 (exact)
+            const uint32_t e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];
+            const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+            const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+            const h2 x0 = __builtin_bit_cast(h2, e0), x1 = __builtin_bit_cast(h2, e1);
+            const h2 x2 = __builtin_bit_cast(h2, e2), x3 = __builtin_bit_cast(h2, e3);
+            m1_sl[i] = __builtin_amdgcn_fdot2(x0, one, __builtin_amdgcn_fdot2(x2, one, 0.f, false),
+                                              false);
+            m1_sh[i] = __builtin_amdgcn_fdot2(x1, one, __builtin_amdgcn_fdot2(x3, one, 0.f, false),
+                                              false);
+            v[1] = __builtin_bit_cast(uint32_t, x1 * sixteenth);
+            v[3] = __builtin_bit_cast(uint32_t, x3 * sixteenth);
+          }
           *reinterpret_cast<u4*>(smem + wreg + row * wstride + col * 16) = v;
         }
       }
@@ -557,7 +631,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
       for (int i = 0; i < APER; ++i) {
         const int c = tid + i * NTHR;
         if (c < total) {
-          const int row = c / cpr, col = c - row * cpr;
+          const int row = small_div(c, cpr), col = c - row * cpr;
           u4 v = stage[i];
           if constexpr (KTAIL) {
             if (kbyte0 + (size_t)col * 16 >= arow_bytes) v = u4{0u, 0u, 0u, 0u};
@@ -566,6 +640,29 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
         }
       }
       __syncthreads();
+    }
+
+    if constexpr (M1) {
+      // sums over each tile's 16 chunks (16 consecutive lanes), then every
+      // tile's pair broadcast to the wave: tile kl's chunks are 16*kl..16*kl+15
+#pragma unroll
+      for (int i = 0; i < APER; ++i) {
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          m1_sl[i] += __shfl_xor(m1_sl[i], o, 16);
+          m1_sh[i] += __shfl_xor(m1_sh[i], o, 16);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < MAXT; ++u) {
+        const int i = u / 4 < APER ? u / 4 : APER - 1;
+        const float off = fmaf(1024.f, m1_sl[i], 64.f * m1_sh[i]);
+        const float sum = m1_sl[i] + m1_sh[i];
+        m1_off[u] = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, off), 16 * (u & 3)));
+        m1_sum[u] = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 16 * (u & 3)));
+      }
     }
 
     // ---- phase 3: unpack + matrix-core products, tile by tile ------------
@@ -595,22 +692,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
           if ((size_t)kt * AS::TILE_ROWB + (AS::TILE_ROWB / 4) * b + 16 * j >= arow_bytes)
             af[j] = u4{0u, 0u, 0u, 0u};
       }
-      tile_mma<KIND>(wv[u], af, sv[u], zv[u], acc);
+      if constexpr (M1) {
+        f4 part = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t wj = wv[u][j];
+          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, af[j]),
+                                                        unpack_w4_off(wj), part, 0, 0, 0);
+        }
+        const float p0 = part[0];
+        const float t = fmaf(-(float)zv[u], m1_sum[u], p0 - m1_off[u]);
+        acc[0] = fmaf(t, h2f(sv[u]), acc[0]);
+      } else {
+        tile_mma<KIND>(wv[u], af, sv[u], zv[u], acc);
+      }
     }
   }
-
-  // ---- cross-wave reduction through LDS (reuses the staging buffer) -----
-  // MFMA 16x16 output: lane holds column (lane & 15), rows 4*(lane >> 4) + e.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);       // [WAVES][16 rows][16 cols]
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    // copy the element to a scalar first: __builtin_bit_cast applied to an
-    // ext-vector element reads element 0 with this compiler
-    const auto v = acc[e];
-    red[(wave * 16 + 4 * b + e) * 16 + r] = __builtin_bit_cast(float, v);
-  }
-  __syncthreads();
 
   const int ngroups = p.NT;
   const size_t slot = (size_t)mtile * ngroups + tile;
@@ -620,6 +717,40 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const MMParams p) {
     else return p.a_scale[mtile * 16 + row];
   };
   constexpr int NOUT = 256;                          // 16 x 16 outputs of the tile
+
+  // ---- cross-wave reduction through LDS (reuses the staging buffer) -----
+  // MFMA 16x16 output: lane holds column (lane & 15), rows 4*(lane >> 4) + e.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);       // [WAVES][16 rows][16 cols]
+  if (rows == 1 && p.ksplit == 1) {
+    // one row: only row 0 (lanes 0..15, element 0) is an output
+    if (lane < 16) {
+      const auto v = acc[0];
+      red[wave * 16 + lane] = __builtin_bit_cast(float, v);
+    }
+    __syncthreads();
+    const int n = tile * 16 + tid;
+    if (tid < 16 && n < p.N) {
+      float fs = 0.f;
+      int is = 0;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float v = red[w * 16 + tid];
+        if constexpr (FACC) fs += v;
+        else is += __builtin_bit_cast(int, v);
+      }
+      store_out<KIND>(p, mtile * 16, n, fs, is, row_sa(0));
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // copy the element to a scalar first: __builtin_bit_cast applied to an
+    // ext-vector element reads element 0 with this compiler
+    const auto v = acc[e];
+    red[(wave * 16 + 4 * b + e) * 16 + r] = __builtin_bit_cast(float, v);
+  }
+  __syncthreads();
 
   if (p.ksplit == 1) {
     for (int idx = tid; idx < NOUT; idx += NTHR) {

@@ -42,6 +42,7 @@ struct Plan {
   int apw;          // wave staging: 16-byte loads per lane
   int ksplit, kts, mtiles, maxt, aper;
   int waves;        // decode: waves per block (8, or 16 with wave staging)
+  bool m1;          // decode, W4A16, one row: the one-row offset scheme
   size_t smem;
   size_t counters_bytes, ws_bytes;
 };
@@ -113,9 +114,12 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
     ks = 1;
     while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= W) ks *= 2;
   }
-  P.kts = ceil_div(g.KT, ks);
+  // W4A16 cuts K on group quads: every wave's run starts on a quad, and its
+  // four scales and zeros come in one load each
+  const bool quads = kind == KIND_W4A16;
+  P.kts = quads ? 4 * ceil_div(g.KQ, ks) : ceil_div(g.KT, ks);
   P.ksplit = ceil_div(g.KT, P.kts);
-  const int per = ceil_div(P.kts, W);
+  const int per = quads ? 4 * ceil_div(ceil_div(P.kts, 4), W) : ceil_div(P.kts, W);
   P.maxt = per <= 2 && W == 16 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
   // stage the block's activation rows in LDS when they fit, else each lane
   // streams its own fragments from L2
@@ -138,6 +142,8 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   // four waves run only with wave staging
   if (W == 4 && !P.wst) return plan_from(kind, M, N, K, Candidate{PATH_DECODE, c.ks, {}, 0, 8});
   P.apw = wchunks <= 64 ? 1 : wchunks <= 128 ? 2 : 4;
+  // one row, staged per wave in one pass
+  P.m1 = kind == KIND_W4A16 && M == 1 && P.wst && per <= P.maxt;
   const size_t block_stage = P.staged ? (size_t)rows * (P.kts * trb + 16) : 0;
   const size_t wave_stage = P.wst ? (size_t)W * rows * (per * trb + 16) : 0;
   P.smem = std::max({block_stage, wave_stage, (size_t)W * 1024});
@@ -233,7 +239,7 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
   int n = 0, last = 0;
   for (int ks = 1; ks <= 64; ks *= 2) {
     if (ks > 1 && (ceil_div(g.KT, ks) < GEMV_WAVES || blocks * ks > CAND_MAX_BLOCKS)) break;
-    const int eff = ceil_div(g.KT, ceil_div(g.KT, ks));
+    const int eff = plan_from(kind, M, N, K, Candidate{PATH_DECODE, ks, {}}).ksplit;
     if (eff == last) continue;
     last = eff;
     out[n++] = Candidate{PATH_DECODE, ks, {}};
@@ -325,6 +331,16 @@ inline int fq_slots(int rows, int K) {
   return need <= 2 ? 2 : need <= 8 ? 8 : 0;
 }
 
+// Launch one decode-kernel instance: the fields its first loads depend on go
+// as leading scalar arguments, which the build preloads into SGPRs.
+template <typename Kern>
+inline void gemv_go(Kern kern, dim3 grid, dim3 block, size_t smem, hipStream_t stream,
+                    const MMParams& p) {
+  allow_smem((const void*)kern, smem);
+  hipLaunchKernelGGL(kern, grid, block, smem, stream, p.Wt, p.A, p.St, p.Zt, p.M, p.K, p.KT,
+                     p.KQ, p.kts, p);
+}
+
 template <int KIND, int WAVES, int MAXT>
 int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq = 0, int fqc = 0) {
   // x enumerates (n tile, m tile) pairs so that the m tiles of one n tile land
@@ -332,69 +348,66 @@ int launch_gemv_m(const Plan& P, const MMParams& p, hipStream_t stream, int fq =
   const int nblk = P.mtiles == 1 ? p.NT : ceil_div(p.NT * P.mtiles, 8) * 8;
   const dim3 grid(nblk, P.ksplit, 1);
   const dim3 block(WAVES * 64);
-#define W4_GEMV_WCASE(A)                                                              \
-  do {                                                                                \
-    allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, A, true, 0, 1, true>, P.smem);  \
-    hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, A, true, 0, 1, true>), grid, block,  \
-                       P.smem, stream, p);                                            \
-  } while (0)
+  // wave staging; for W4A16 at one row the one-row offset scheme (the
+  // planner sets m1 only for plans it fits)
+  auto wcase = [&](auto aper) {
+    constexpr int A = decltype(aper)::value;
+    if constexpr (KIND == KIND_W4A16) {
+      if (P.m1) {
+        gemv_go(&k_gemv<KIND, WAVES, MAXT, A, true, 0, 1, true, true>, grid, block, P.smem,
+                stream, p);
+        return;
+      }
+    }
+    gemv_go(&k_gemv<KIND, WAVES, MAXT, A, true, 0, 1, true>, grid, block, P.smem, stream, p);
+  };
+  using A1 = std::integral_constant<int, 1>;
+  using A2 = std::integral_constant<int, 2>;
+  using A4 = std::integral_constant<int, 4>;
   if constexpr (WAVES != 8) {
-    // sixteen-wave plans stage per wave or not at all, and never quantize in
-    // the prologue (the planner guarantees both)
+    // sixteen- and four-wave plans stage per wave or not at all, and never
+    // quantize in the prologue (the planner guarantees both)
     if (fq || (P.staged && !P.wst)) return W4_ERR_ARG;
     if (!P.staged) {
       if constexpr (WAVES == 16 && MAXT <= 4 && KIND != KIND_W2A16) {
-        allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, 1, false>, P.smem);
-        hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, 1, false>), grid, block, P.smem, stream, p);
+        gemv_go(&k_gemv<KIND, WAVES, MAXT, 1, false>, grid, block, P.smem, stream, p);
       } else {
         return W4_ERR_ARG;
       }
     } else if (P.apw == 1) {
-      W4_GEMV_WCASE(1);
+      wcase(A1{});
     } else if (P.apw == 2) {
-      W4_GEMV_WCASE(2);
+      wcase(A2{});
     } else {
-      W4_GEMV_WCASE(4);
+      wcase(A4{});
     }
     return launch_status();
   } else {
-#define W4_GEMV_FQ(F, C)                                                              \
-  do {                                                                                \
-    allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, 1, true, F, C>, P.smem);        \
-    hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, 1, true, F, C>), grid, block,        \
-                       P.smem, stream, p);                                            \
-  } while (0)
     if constexpr (KIND == KIND_W4A8 || KIND == KIND_W2A8) {
       if (fq) {
-        if (fq == 1 && fqc == 2) W4_GEMV_FQ(1, 2);
-        else if (fq == 1) W4_GEMV_FQ(1, 8);
-        else if (fqc == 2) W4_GEMV_FQ(2, 2);
-        else W4_GEMV_FQ(2, 8);
+        if (fq == 1 && fqc == 2) gemv_go(&k_gemv<KIND, WAVES, MAXT, 1, true, 1, 2>, grid, block, P.smem, stream, p);
+        else if (fq == 1) gemv_go(&k_gemv<KIND, WAVES, MAXT, 1, true, 1, 8>, grid, block, P.smem, stream, p);
+        else if (fqc == 2) gemv_go(&k_gemv<KIND, WAVES, MAXT, 1, true, 2, 2>, grid, block, P.smem, stream, p);
+        else gemv_go(&k_gemv<KIND, WAVES, MAXT, 1, true, 2, 8>, grid, block, P.smem, stream, p);
         return launch_status();
       }
     }
-#undef W4_GEMV_FQ
-#define W4_GEMV_CASE(A, ST)                                                 \
-  allow_smem((const void*)&k_gemv<KIND, WAVES, MAXT, A, ST>, P.smem);        \
-  hipLaunchKernelGGL((k_gemv<KIND, WAVES, MAXT, A, ST>), grid, block, P.smem, stream, p)
     if (!P.staged) {
-      W4_GEMV_CASE(1, false);
+      gemv_go(&k_gemv<KIND, WAVES, MAXT, 1, false>, grid, block, P.smem, stream, p);
     } else if (P.wst) {
-      if (P.apw == 1) W4_GEMV_WCASE(1);
-      else if (P.apw == 2) W4_GEMV_WCASE(2);
-      else W4_GEMV_WCASE(4);
+      if (P.apw == 1) wcase(A1{});
+      else if (P.apw == 2) wcase(A2{});
+      else wcase(A4{});
     } else {
       switch (P.aper) {
-        case 1: W4_GEMV_CASE(1, true); break;
-        case 2: W4_GEMV_CASE(2, true); break;
-        case 4: W4_GEMV_CASE(4, true); break;
-        default: W4_GEMV_CASE(8, true); break;
+        case 1: gemv_go(&k_gemv<KIND, WAVES, MAXT, 1, true>, grid, block, P.smem, stream, p); break;
+        case 2: gemv_go(&k_gemv<KIND, WAVES, MAXT, 2, true>, grid, block, P.smem, stream, p); break;
+        case 4: gemv_go(&k_gemv<KIND, WAVES, MAXT, 4, true>, grid, block, P.smem, stream, p); break;
+        default: gemv_go(&k_gemv<KIND, WAVES, MAXT, 8, true>, grid, block, P.smem, stream, p); break;
       }
     }
-#undef W4_GEMV_CASE
     return launch_status();
   }
-#undef W4_GEMV_WCASE
 }
 
 template <int KIND>

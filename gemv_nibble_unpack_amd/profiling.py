@@ -45,46 +45,64 @@ def _find(d, suffix):
     return hits[0]
 
 
+def _grid(row):
+    """The launch shape of a dispatch as 'grid x*y*z / block x' (threads)."""
+    return (f"{row['Grid_Size_X']}x{row['Grid_Size_Y']}x{row['Grid_Size_Z']}"
+            f" / {row['Workgroup_Size_X']}")
+
+
 def trace_rows(d):
-    """(kernel name, duration ns) per dispatch from a kernel-trace CSV dir."""
+    """(kernel name, launch shape, duration ns) per dispatch from a
+    kernel-trace CSV dir."""
     path = _find(d, "kernel_trace.csv")
     out = []
     with open(path) as f:
         for row in csv.DictReader(f):
-            out.append((row["Kernel_Name"], int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+            out.append((row["Kernel_Name"], _grid(row),
+                        int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
     return out
 
 
 def summarize_trace(d, out_path, cmd):
+    """Per (kernel, launch shape): one product shape launches one grid, so
+    the shapes of one kernel template are listed apart."""
     rows = trace_rows(d)
     by = defaultdict(list)
-    for name, ns in rows:
-        by[name].append(ns / 1e3)
+    for name, grid, ns in rows:
+        by[(name, grid)].append(ns / 1e3)
     lines = ["# rocprofv3 kernel trace summary", "", f"Command: `{cmd}`", "",
-             "| kernel | calls | mean us | median us | min us |", "|---|---|---|---|---|"]
-    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+             "| kernel | grid / block (threads) | calls | mean us | median us | min us |",
+             "|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         short = name if len(name) < 90 else name[:87] + "..."
-        lines.append(f"| `{short}` | {len(v)} | {statistics.mean(v):.2f} | "
+        lines.append(f"| `{short}` | {grid} | {len(v)} | {statistics.mean(v):.2f} | "
                      f"{statistics.median(v):.2f} | {min(v):.2f} |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out_path
 
 
-def pmc_values(d, counter):
+def pmc_values(d, counter, grid=None, keep="bitwise_not"):
+    """Counter readings per kernel name; with ``grid`` (total threads), only
+    the dispatches of that launch size, and every dispatch of the kernels
+    whose name contains ``keep`` (the calibration copy)."""
     path = _find(d, "counter_collection.csv")
     out = defaultdict(list)
     with open(path) as f:
         for row in csv.DictReader(f):
-            if row["Counter_Name"] == counter:
-                out[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+            if row["Counter_Name"] != counter:
+                continue
+            if grid is not None and int(row["Grid_Size"]) != grid and \
+                    keep not in row["Kernel_Name"]:
+                continue
+            out[row["Kernel_Name"]].append(float(row["Counter_Value"]))
     return out
 
 
 def summarize_traffic(fetch_dir, write_dir, out_path, kernel, calib_bytes, cmd,
-                      calib_kernel="bitwise_not"):
-    fetch = pmc_values(fetch_dir, "FETCH_SIZE")
-    write = pmc_values(write_dir, "WRITE_SIZE")
+                      calib_kernel="bitwise_not", grid=None):
+    fetch = pmc_values(fetch_dir, "FETCH_SIZE", grid, calib_kernel)
+    write = pmc_values(write_dir, "WRITE_SIZE", grid, calib_kernel)
 
     def pick(table, key):
         vals = [v for name, vs in table.items() if key in name for v in vs]
@@ -104,6 +122,7 @@ def summarize_traffic(fetch_dir, write_dir, out_path, kernel, calib_bytes, cmd,
     kf, kw = pick(fetch, kernel), pick(write, kernel)
     rec = {
         "kernel": kernel,
+        "grid_threads": grid,
         "fetch_kib_per_launch": kf, "write_kib_per_launch": kw,
         "calibration": {"copy_kernel": cf, "bytes": calib_bytes,
                         "fetch_kib": statistics.median(fetch[cf]),
@@ -178,6 +197,8 @@ def main():
     q.add_argument("--calib-bytes", type=int, required=True)
     q.add_argument("--calib-kernel", default="bitwise_not",
                    help="name substring of the calibration copy kernel")
+    q.add_argument("--grid", type=int, default=None,
+                   help="only dispatches of this many threads (one product shape)")
     q.add_argument("--cmd", required=True)
     m = sub.add_parser("mfma")
     m.add_argument("util_dir")
@@ -194,7 +215,8 @@ def main():
         print(summarize_trace(a.dir, a.out, a.cmd))
     else:
         print(json.dumps(summarize_traffic(a.fetch_dir, a.write_dir, a.out, a.kernel,
-                                           a.calib_bytes, a.cmd, a.calib_kernel), indent=1))
+                                           a.calib_bytes, a.cmd, a.calib_kernel, a.grid),
+                         indent=1))
 
 
 if __name__ == "__main__":

@@ -8,17 +8,20 @@ import pytest
 
 from gemv_nibble_unpack_amd import profiling as P
 
-HDR = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
-       "Start_Timestamp", "End_Timestamp"]
+HDR = ["Correlation_Id", "Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name",
+       "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 
 
 def _counters(d, rows):
+    """rows: (kernel, counter, value) or (kernel, counter, value, grid threads)."""
     d.mkdir(parents=True)
     with open(d / "run_counter_collection.csv", "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(HDR)
-        for i, (kernel, counter, value) in enumerate(rows):
-            w.writerow([i, i, kernel, counter, value, 1000 * i, 1000 * i + 500])
+        for i, row in enumerate(rows):
+            kernel, counter, value = row[:3]
+            grid = row[3] if len(row) > 3 else 1024
+            w.writerow([i, i, grid, kernel, counter, value, 1000 * i, 1000 * i + 500])
 
 
 def test_trace_summary(tmp_path):
@@ -26,15 +29,18 @@ def test_trace_summary(tmp_path):
     d.mkdir()
     with open(d / "run_kernel_trace.csv", "w", newline="") as f:
         w = csv.writer(f)
-        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z",
+                    "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"])
         for ns in (4000, 5000, 6000):
-            w.writerow(["k_gemv", 0, ns])
-        w.writerow(["copy", 0, 1000])
+            w.writerow(["k_gemv", 131072, 1, 1, 512, 0, ns])
+        w.writerow(["k_gemv", 352256, 1, 1, 512, 0, 7000])     # another shape, listed apart
+        w.writerow(["copy", 512, 1, 1, 512, 0, 1000])
     out = tmp_path / "s.md"
     P.summarize_trace(str(d), str(out), "cmd")
     text = out.read_text()
-    assert "`k_gemv` | 3 | 5.00 | 5.00 | 4.00 |" in text
-    assert text.index("k_gemv") < text.index("copy")           # by total time
+    assert "`k_gemv` | 131072x1x1 / 512 | 3 | 5.00 | 5.00 | 4.00 |" in text
+    assert "`k_gemv` | 352256x1x1 / 512 | 1 | 7.00 | 7.00 | 7.00 |" in text
+    assert text.index("131072x1x1") < text.index("352256x1x1") < text.index("copy")  # by total
     assert "Command: `cmd`" in text
 
 
@@ -59,6 +65,22 @@ def test_traffic_calibration_and_hash(tmp_path, monkeypatch):
     with pytest.raises(KeyError):
         P.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "k_gemm",
                             2048 * 1024, "cmd")
+
+
+def test_traffic_of_one_launch_shape(tmp_path):
+    # two shapes of one kernel: the grid filter keeps one, and the copy
+    _counters(tmp_path / "f", [("bitwise_not copy", "FETCH_SIZE", 1024.0, 65536),
+                               ("k_gemv<1>", "FETCH_SIZE", 100.0, 131072),
+                               ("k_gemv<1>", "FETCH_SIZE", 900.0, 352256)])
+    _counters(tmp_path / "w", [("bitwise_not copy", "WRITE_SIZE", 2048.0, 65536),
+                               ("k_gemv<1>", "WRITE_SIZE", 8.0, 131072),
+                               ("k_gemv<1>", "WRITE_SIZE", 24.0, 352256)])
+    out = tmp_path / "t.json"
+    rec = P.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "k_gemv",
+                              2048 * 1024, "cmd", grid=352256)
+    assert rec["read_bytes_per_launch"] == 900.0 * 2048
+    assert rec["write_bytes_per_launch"] == 24.0 * 1024
+    assert rec["grid_threads"] == 352256
 
 
 def test_mfma_summary(tmp_path):
