@@ -49,7 +49,12 @@ PROBE_PER = (1, 2, 4, 8)       # 16-byte loads per lane tried by the read probe
 WARM_US = 250.0                # GPU time of the warm-up replay right before a timed one
 WARM_COPIES = 8                # weight copies the warm-up replay cycles through
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_TRAFFIC = os.path.join(PROFILES, "k_gemv_w4a16_decode_m1_n4096_k4096_traffic.json")
+def decode_traffic_path(N, K):
+    """The committed PMC traffic summary of the W4A16 M=1 GEMV at (N, K)."""
+    return os.path.join(PROFILES, f"k_gemv_w4a16_decode_m1_n{N}_k{K}_traffic.json")
+
+
+DECODE_TRAFFIC = decode_traffic_path(4096, 4096)
 PREFILL_TRAFFIC = os.path.join(PROFILES, "k_gemm_w4a8_prefill_m2048_n11008_k4096_traffic.json")
 DECODE_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
 
@@ -608,7 +613,9 @@ def main():
                      "bytes_per_launch": head["bytes"],
                      "achievable": head["achievable"],
                      "frac_of_achievable": head["frac_of_achievable"],
-                     "shapes": [{k: v for k, v in x.items() if k not in ("ms",)} for x in dec]},
+                     "shapes": [{**{k: v for k, v in x.items() if k not in ("ms",)},
+                                 "traffic": traffic_of(decode_traffic_path(x["N"], x["K"]))}
+                                for x in dec]},
         "offline_prep_ms": head["offline_prep_ms"],
     }
     if not args.no_prefill:

@@ -184,21 +184,6 @@ __device__ __forceinline__ void store_out(const MMParams& p, int m, int n, float
   }
 }
 
-// Fetch the kernel arguments in one batch at kernel entry. Left to itself the
-// compiler loads the pointers only after the shape fields have arrived and
-// been branched on, which puts two dependent kernel-argument fetches (each a
-// scalar-cache miss of several hundred ns) in front of the first weight load
-// of a kernel that lasts a few microseconds. Naming every field as an SGPR
-// operand of one empty asm statement makes all the loads issue together,
-// followed by a single wait.
-__device__ __forceinline__ void fetch_args(const MMParams& p) {
-  asm volatile("" ::"s"(p.A), "s"(p.a_scale), "s"(p.Wt), "s"(p.St), "s"(p.Zt), "s"(p.w_scale),
-               "s"(p.w_scale16), "s"(p.bias), "s"(p.out_scale), "s"(p.C));
-  asm volatile("" ::"s"(p.out_dtype), "s"(p.M), "s"(p.N), "s"(p.K), "s"(p.NT), "s"(p.KT),
-               "s"(p.KQ), "s"(p.ksplit), "s"(p.kts), "s"(p.counters), "s"(p.partials),
-               "s"(gridDim.x));
-}
-
 // v_and_or_b32: (a & b) | c in one VALU op (the compiler splits the
 // expression into two ops).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
@@ -367,9 +352,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* Wt, const vo
   const int rows = min(16, p.M - mtile * 16);
   const int kb = blockIdx.y * p.kts;
   const int ke = min(p.KT, kb + p.kts);
-  // W4A16 runs start on a group quad (kts is a multiple of 4), so a lane
-  // fetches the scales and zeros of four tiles with one load each
-  const int per = GRP ? ((ke - kb + 3) / 4 + WAVES - 1) / WAVES * 4 : (ke - kb + WAVES - 1) / WAVES;
+  // W4A16 runs start on an even tile (kts is even), so the scales and zeros
+  // of a wave's tiles come in whole quads of groups, one load each
+  const int per = GRP ? ((ke - kb + 1) / 2 + WAVES - 1) / WAVES * 2 : (ke - kb + WAVES - 1) / WAVES;
   const int wb = kb + wave * per;
   const int nt = max(0, min(ke, wb + per) - wb);     // tiles of this wave (uniform)
 
@@ -460,35 +445,64 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* Wt, const vo
     const int pb = wb + pass * MAXT;
     const int pn = min(MAXT, nt - pass * MAXT);      // tiles in this pass (uniform)
     u4 wv[MAXT];
-    uint16_t sv[MAXT];
-    uint8_t zv[MAXT];
+    // W4A16: the pass starts on an even tile, so its tiles' group scales and
+    // zeros lie in the NQ quads from pb / 4 on: one 8-byte scale load and one
+    // 4-byte zero load per quad (a quad past the row's last reads the last).
+    // Quad q is loaded just before tile 4q - 2, in time for a pass that starts
+    // mid-quad (tiles 4q - 2 ..) as well as for one that starts on a quad.
+    constexpr int NQ = GRP ? (MAXT >= 4 ? MAXT / 4 + 1 : 1) : 1;
+    uint64_t sq[NQ];
+    uint32_t zq[NQ];
+    auto quad_load = [&](int q) {
+      const int qq = min((pb >> 2) + q, p.KQ - 1);
+      const size_t mq = (((size_t)tile * p.KQ + qq) * TILE_N + r) * 4;
+      if (MAXT >= 4 && q == NQ - 1) {
+        // only groups 0 and 1 of the last quad can be used: loading no more
+        // leaves no dead register half that the allocator could reuse while
+        // the load is in flight (which would force a wait for it)
+        sq[q] = *reinterpret_cast<const uint32_t*>(p.St + mq);
+        zq[q] = *reinterpret_cast<const uint16_t*>(p.Zt + mq);
+      } else {
+        sq[q] = *reinterpret_cast<const uint64_t*>(p.St + mq);
+        zq[q] = *reinterpret_cast<const uint32_t*>(p.Zt + mq);
+      }
+    };
+    // tile u's scale and zero, taken where they are used, so that the wait
+    // for them covers only the loads issued up to their quad
+    const bool mid = (pb & 2) != 0;                  // the pass starts mid-quad
+    auto scale_of = [&](int u) -> uint16_t {
+      if constexpr (GRP) {
+        const uint16_t s0 = (uint16_t)(sq[u >> 2] >> (16 * (u & 3)));
+        const uint16_t s1 = (uint16_t)(sq[(u + 2) >> 2] >> (16 * ((u + 2) & 3)));
+        return mid ? s1 : s0;
+      } else {
+        return 0;
+      }
+    };
+    auto zero_of = [&](int u) -> uint8_t {
+      if constexpr (GRP) {
+        const uint8_t z0 = (uint8_t)(zq[u >> 2] >> (8 * (u & 3)));
+        const uint8_t z1 = (uint8_t)(zq[(u + 2) >> 2] >> (8 * ((u + 2) & 3)));
+        return mid ? z1 : z0;
+      } else {
+        return 0;
+      }
+    };
     // Unconditional loads keep the wait counts exact: slots past the run
     // read tile 0 (a fixed, cache-resident address) and are skipped below.
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
+      if constexpr (GRP) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          if (u == (q == 0 ? 0 : 4 * q - 2)) quad_load(q);
+      }
       const bool live = u < pn;
       const int kt = pb + u;
       const size_t ti = live ? (size_t)tile * p.KT + kt : 0;
       const u4* wp = reinterpret_cast<const u4*>(p.Wt + ti * TILE_BYTES + lane * 16);
       // streamed once unless several m tiles share the weight tile through L2
       wv[u] = mtiles == 1 ? __builtin_nontemporal_load(wp) : *wp;
-      if constexpr (GRP) {
-        // the run and the pass start on a quad: the row's four group scales
-        // (8 bytes) and zeros (4 bytes) of tiles u..u+3 in one load each (a
-        // quad past the run reads quad 0)
-        if (u % 4 == 0) {
-          const size_t mq = live ? (((size_t)tile * p.KQ + (kt >> 2)) * TILE_N + r) * 4 : 0;
-          const uint64_t s8 = *reinterpret_cast<const uint64_t*>(p.St + mq);
-          const uint32_t z4 = *reinterpret_cast<const uint32_t*>(p.Zt + mq);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (u + e < MAXT) {
-              sv[u + e] = (uint16_t)(s8 >> (16 * e));
-              zv[u + e] = (uint8_t)(z4 >> (8 * e));
-            }
-          }
-        }
-      }
     }
 
     // ---- activation fragments straight from L2 (not STAGED) --------------
@@ -701,10 +715,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* Wt, const vo
                                                         unpack_w4_off(wj), part, 0, 0, 0);
         }
         const float p0 = part[0];
-        const float t = fmaf(-(float)zv[u], m1_sum[u], p0 - m1_off[u]);
-        acc[0] = fmaf(t, h2f(sv[u]), acc[0]);
+        const float t = fmaf(-(float)zero_of(u), m1_sum[u], p0 - m1_off[u]);
+        acc[0] = fmaf(t, h2f(scale_of(u)), acc[0]);
       } else {
-        tile_mma<KIND>(wv[u], af, sv[u], zv[u], acc);
+        tile_mma<KIND>(wv[u], af, scale_of(u), zero_of(u), acc);
       }
     }
   }

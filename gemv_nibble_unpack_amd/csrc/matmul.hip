@@ -114,12 +114,12 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
     ks = 1;
     while (blocks * ks < SPLIT_BELOW && ceil_div(g.KT, ks * 2) >= W) ks *= 2;
   }
-  // W4A16 cuts K on group quads: every wave's run starts on a quad, and its
-  // four scales and zeros come in one load each
-  const bool quads = kind == KIND_W4A16;
-  P.kts = quads ? 4 * ceil_div(g.KQ, ks) : ceil_div(g.KT, ks);
+  // W4A16 cuts K on even tiles: every wave's run starts on an even tile, and
+  // the scales and zeros of its tiles come in whole quads of groups
+  const bool pairs = kind == KIND_W4A16;
+  P.kts = pairs ? 2 * ceil_div(ceil_div(g.KT, 2), ks) : ceil_div(g.KT, ks);
   P.ksplit = ceil_div(g.KT, P.kts);
-  const int per = quads ? 4 * ceil_div(ceil_div(P.kts, 4), W) : ceil_div(P.kts, W);
+  const int per = pairs ? 2 * ceil_div(ceil_div(P.kts, 2), W) : ceil_div(P.kts, W);
   P.maxt = per <= 2 && W == 16 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
   // stage the block's activation rows in LDS when they fit, else each lane
   // streams its own fragments from L2
@@ -443,7 +443,8 @@ int launch_skinny(const Plan& P, MMParams p, void* ws, hipStream_t stream) {
     const size_t smem = skinny_smem<KIND, MTB>();                                           \
     allow_smem((const void*)&k_skinny<KIND, 8, SPLIT, MTB>, smem);                          \
     hipLaunchKernelGGL((k_skinny<KIND, 8, SPLIT, MTB>), grid, dim3(SKINNY_THREADS), smem,   \
-                       stream, p, P.ngroups);                                               \
+                       stream, p.Wt, p.A, p.St, p.Zt, p.M, p.K, p.NT, p.kts, P.ngroups,     \
+                       (int)(grid.x / 8), p);                                               \
   } while (0)
   if (P.mtb == 2) {
     if (P.ksplit > 1) W4_SKINNY(true, 2);

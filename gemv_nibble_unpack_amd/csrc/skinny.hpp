@@ -46,8 +46,16 @@ constexpr size_t skinny_smem() {
 // traffic and the block count of many-row products (the ternary M = 128
 // layers at N = 8640 would otherwise need 544 blocks, one more round than the
 // 512 that fit at two per CU).
+//
+// The fields the first loads depend on come as leading scalar arguments,
+// preloaded into SGPRs (see k_gemv); per_xcd is the grid size / 8, and the
+// k-tile counts follow from K and the kind's tile extent.
 template <int KIND, int MAXT, bool SPLIT = false, int MTB = 1>
-__global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int ngroups) {
+__global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const uint8_t* Wt, const void* A,
+                                                           const uint16_t* St, const uint8_t* Zt,
+                                                           int M, int K, int NT, int kts,
+                                                           int ngroups, int per_xcd,
+                                                           const MMParams pin) {
   using AS = AStage<KIND>;
   constexpr bool A16 = KIND == KIND_W4A16 || KIND == KIND_W2A16;
   constexpr bool GRP = KIND == KIND_W4A16;
@@ -62,7 +70,17 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   typedef typename std::conditional<float_acc<KIND>(), f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  fetch_args(p);
+  MMParams p = pin;
+  p.Wt = Wt;
+  p.A = A;
+  p.St = St;
+  p.Zt = Zt;
+  p.M = M;
+  p.K = K;
+  p.NT = NT;
+  p.kts = kts;
+  p.KT = (K + KindTraits<KIND>::TILE_K - 1) / KindTraits<KIND>::TILE_K;
+  p.KQ = (p.KT + 3) / 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,9 +89,8 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const MMParams p, int
   // blocks of one n group, so the group's weight tiles stay in that XCD's L2
   const int mtiles = (p.M + RB - 1) / RB;            // blocks of RB rows
   const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
-  const int per_xcd = (int)(gridDim.x >> 3);         // grid is a multiple of 8
-  const int seq = xcd * per_xcd + local;
-  const int grp = seq / mtiles, mtile = seq - grp * mtiles;
+  const int seq = xcd * per_xcd + local;             // the grid is 8 * per_xcd blocks
+  const int grp = small_div(seq, mtiles), mtile = seq - grp * mtiles;
   if (local >= per_xcd || grp >= ngroups) return;    // block-uniform
   const int tile = grp * SKINNY_WAVES + wave;        // this wave's n tile
   const bool live_tile = tile < p.NT;                // wave-uniform
