@@ -627,8 +627,27 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
   }
 }
 
+// The fields the block's first loads depend on come as leading scalar
+// arguments, preloaded into SGPRs (see k_gemv).
 template <int KIND, int NTILES, int WM, int OUT, bool BIAS, int FQ = 0>
-__global__ __launch_bounds__(128 * WM, 2) void k_gemm(const MMParams p, const GemmGrid gg) {
+__global__ __launch_bounds__(128 * WM, 2) void k_gemm(const uint8_t* Wt, const void* A, int M,
+                                                      int N, int K, int KT, int mblocks,
+                                                      int nblocks, int tiles, int per_xcd,
+                                                      int kts, const MMParams pin,
+                                                      const GemmGrid gin) {
+  MMParams p = pin;
+  p.Wt = Wt;
+  p.A = A;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.KT = KT;
+  GemmGrid gg = gin;
+  gg.mblocks = mblocks;
+  gg.nblocks = nblocks;
+  gg.tiles = tiles;
+  gg.per_xcd = per_xcd;
+  gg.kts = kts;
   if constexpr (FQ != 0) fq_quantize_rows<FQ, 64 * WM>(p);
   gemm_tile<KIND, NTILES, WM, OUT, BIAS, FQ>(p, gg);
   if constexpr (FQ != 0) fq_finish<64 * WM>(p);
@@ -710,7 +729,8 @@ int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
   const dim3 grid(gg.per_xcd * 8, gg.ksplit);
   allow_smem((const void*)&k_gemm<KIND, NTILES, WM, OUT, BIAS, FQ>, S::LDS);
   hipLaunchKernelGGL((k_gemm<KIND, NTILES, WM, OUT, BIAS, FQ>), grid, dim3(S::THREADS), S::LDS,
-                     stream, p, gg);
+                     stream, p.Wt, p.A, p.M, p.N, p.K, p.KT, gg.mblocks, gg.nblocks, gg.tiles,
+                     gg.per_xcd, gg.kts, p, gg);
   return launch_status();
 }
 
