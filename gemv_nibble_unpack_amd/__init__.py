@@ -21,7 +21,7 @@ from .api import (prepack_bytes, prepack_w, quantize_a8, quantize_pack_w2, quant
                   w4_fused_act_workspace_bytes, w4_workspace_bytes, w4a8_gemm,
                   w4a8_gemm_fused_act, w4a16_gemm, w4_plan_count, w4_plan_current,
                   w4_plan_name, w4_plan_pin, w4_plan_reset, w4_plan_workspace_bytes, Workspace,
-                  w4_read_probe, w4a8_gemm_fused_act_noalloc)
+                  w4_read_probe, w4a8_gemm_fused_act_noalloc, StepGraph)
 
 __all__ = [
     "LibraryMissing", "W4Error", "load", "Workspace",
@@ -35,5 +35,5 @@ __all__ = [
     "w4_plan_count", "w4_plan_name", "w4_plan_pin", "w4_plan_current", "w4_plan_reset",
     "w4_plan_workspace_bytes",
     "W4_OP_W4A8", "W4_OP_W4A16", "W4_OP_W2A8", "W4_OP_W2A16", "W4_OP_W8A8", "W4_OP_F8F8",
-    "quantize_f8", "f8f8_gemm", "w4_read_probe", "w4a8_gemm_fused_act_noalloc",
+    "quantize_f8", "f8f8_gemm", "w4_read_probe", "w4a8_gemm_fused_act_noalloc", "StepGraph",
 ]

@@ -56,6 +56,12 @@ SIGNATURES = {
     "w4_plan_reset": (_i, []),
     "w4_plan_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "w4_read_probe": (_i, [_p, _sz, _i, _p, _p]),
+    "w4_graph_begin": (_i, [_p]),
+    "w4_graph_end": (_i, [_p, ctypes.POINTER(_p)]),
+    "w4_graph_update": (_i, [_p, _p]),
+    "w4_graph_launch": (_i, [_p, _p]),
+    "w4_graph_kernel_nodes": (_i, [_p]),
+    "w4_graph_destroy": (_i, [_p]),
 }
 
 _LIB = None

@@ -420,3 +420,104 @@ def w4_read_probe(buf, nbytes=None, per=4, sink=None, stream=None):
     L.check("w4_read_probe", L.load().w4_read_probe(_ptr(buf), nbytes, per, _ptr(sink),
                                                     _stream(stream)))
     return sink
+
+
+class StepGraph:
+    """A decode step captured once and launched as one HIP graph, its kernels
+    re-pointed at each step's buffers by a kernel-node parameter update (the
+    C calls w4_graph_*; INT4 quantization page, Part 2, steps 2-4)::
+
+        g = StepGraph(stream)            # a torch.cuda.Stream of the caller
+        with g.capture():                # the library calls of one step
+            step(buffers_0)
+        g.launch()
+        with g.update():                 # the same calls, the next buffers
+            step(buffers_1)
+        g.launch()
+
+    Inside ``capture`` and ``update`` the calls run on ``stream`` (it is made
+    the current stream) and are recorded, not run. Outputs and workspaces must
+    be allocated beforehand: nothing may be allocated while capturing.
+    """
+
+    def __init__(self, stream):
+        if stream is None or stream.cuda_stream == 0:
+            raise ValueError("StepGraph needs a stream created by the caller")
+        self.stream = stream
+        self.handle = None
+
+    def _capture(self, name, finish):
+        lib = L.load()
+        parent = self
+
+        class _Ctx:
+            def __enter__(self):
+                self.ctx = torch.cuda.stream(parent.stream)
+                self.ctx.__enter__()
+                try:
+                    L.check("w4_graph_begin", lib.w4_graph_begin(parent.stream.cuda_stream))
+                except BaseException:
+                    self.ctx.__exit__(None, None, None)
+                    raise
+                return parent
+
+            def __exit__(self, et, ev, tb):
+                try:
+                    if et is None:
+                        status = finish(lib)
+                    else:
+                        # the step raised: end the capture and discard it
+                        h = ctypes.c_void_p()
+                        if lib.w4_graph_end(parent.stream.cuda_stream, ctypes.byref(h)) == L.W4_OK:
+                            lib.w4_graph_destroy(h.value)
+                finally:
+                    self.ctx.__exit__(et, ev, tb)
+                if et is None:
+                    L.check(name, status)
+                return False
+        return _Ctx()
+
+    def capture(self):
+        """Context: capture one step and instantiate it."""
+        if self.handle is not None:
+            raise RuntimeError("already captured; use update()")
+
+        def finish(lib):
+            h = ctypes.c_void_p()
+            st = lib.w4_graph_end(self.stream.cuda_stream, ctypes.byref(h))
+            if st == L.W4_OK:
+                self.handle = h.value
+            return st
+        return self._capture("w4_graph_end", finish)
+
+    def update(self):
+        """Context: capture the same step with other buffers and update the
+        instantiated graph's kernel nodes from it (W4Error W4_ERR_ARG if the
+        calls differ in kernels, grids or shapes; the graph is then unchanged)."""
+        if self.handle is None:
+            raise RuntimeError("nothing captured yet")
+        return self._capture(
+            "w4_graph_update",
+            lambda lib: lib.w4_graph_update(self.handle, self.stream.cuda_stream))
+
+    def launch(self, stream=None):
+        """Launch the graph on ``stream`` (default: the capture stream)."""
+        s = self.stream if stream is None else stream
+        L.check("w4_graph_launch", L.load().w4_graph_launch(self.handle, s.cuda_stream))
+
+    def kernel_nodes(self):
+        n = L.load().w4_graph_kernel_nodes(self.handle)
+        if n < 0:
+            L.check("w4_graph_kernel_nodes", n)
+        return n
+
+    def close(self):
+        if self.handle is not None:
+            L.check("w4_graph_destroy", L.load().w4_graph_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,6 +1,6 @@
 // Prefill-side kernel (M > 16): C[M,N] = A[M,K] x W[N,K]^T with INT8
-// activations and 4-bit (or 2-bit ternary) weights on the CDNA4 INT8 matrix
-// cores.
+// activations and 4-bit (or 2-bit ternary, or INT8) weights on the CDNA4 INT8
+// matrix cores.
 //
 // Dataflow (INT4 quantization page, Part 1 step 3, mapped to gfx950): for each
 // k tile, a block copies its activation tile (BM x TILE_K int8) and its
@@ -36,11 +36,13 @@ struct GemmTraits {
 
 // Physical 16-byte chunk of logical chunk c in staged A row `row`: an XOR
 // swizzle that puts the 16 rows of a fragment read on distinct LDS banks
-// (128-byte rows: rows alternate between two 32-bank halves, so the swizzle
-// uses row>>1; 256-byte rows all start on bank 0, so it uses row itself).
+// (64-byte rows: four rows share a 256-byte bank line, so the swizzle uses
+// row>>2; 128-byte rows alternate between two halves, so it uses row>>1;
+// 256-byte rows all start on bank 0, so it uses row itself).
 template <int KIND>
 __device__ __forceinline__ int a_chunk(int row, int c) {
-  if constexpr (GemmTraits<KIND>::ROW_CHUNKS == 8) return c ^ ((row >> 1) & 7);
+  if constexpr (GemmTraits<KIND>::ROW_CHUNKS == 4) return c ^ ((row >> 2) & 3);
+  else if constexpr (GemmTraits<KIND>::ROW_CHUNKS == 8) return c ^ ((row >> 1) & 7);
   else return c ^ (row & 15);
 }
 
@@ -88,7 +90,9 @@ struct GemmGrid {
 // unpack one 16-byte weight fragment into KSTEPS int8 MFMA operands
 template <int KIND>
 __device__ __forceinline__ void unpack_frag(const u4 w, i4 (&bf)[GemmTraits<KIND>::KSTEPS]) {
-  if constexpr (KIND == KIND_W4A8) {
+  if constexpr (KIND == KIND_W8A8) {
+    bf[0] = __builtin_bit_cast(i4, w);               // INT8 weights are the operand
+  } else if constexpr (KIND == KIND_W4A8) {
     bf[0] = unpack_w4_i8(w[0], w[1]);
     bf[1] = unpack_w4_i8(w[2], w[3]);
   } else {
@@ -122,7 +126,13 @@ __device__ __forceinline__ void gemm_store4(const MMParams& p, int m, int n, con
       o[e] = (float)a * ws[e] * sa;
       if constexpr (BIAS && OUT == W4_OUT_F16) o[e] += bias[e];
     }
-    if constexpr (OUT == W4_OUT_F32) {
+    if constexpr (OUT == W4_OUT_I8) {
+      // re-quantized for a following INT8 layer, the code decided in float32
+      // as the decode kernel decides it
+      int8_t* c = reinterpret_cast<int8_t*>(p.C) + (size_t)m * p.N + n;
+      for (int e = 0; e < 4 && n + e < p.N; ++e)
+        c[e] = (int8_t)sym_code_div(o[e], p.out_scale[0], 127.f);
+    } else if constexpr (OUT == W4_OUT_F32) {
       float* c = reinterpret_cast<float*>(p.C) + (size_t)m * p.N + n;
       if (full) {
         *reinterpret_cast<f4*>(c) = f4{o[0], o[1], o[2], o[3]};
@@ -147,7 +157,7 @@ __device__ __forceinline__ void gemm_col_params(const MMParams& p, int n, f4& ws
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int ne = min(n + e, p.N - 1);
-    if constexpr (OUT != W4_OUT_I32) ws[e] = KIND == KIND_W4A8 ? p.w_scale[ne] : h2f(p.w_scale16[0]);
+    if constexpr (OUT != W4_OUT_I32) ws[e] = KIND == KIND_W2A8 ? h2f(p.w_scale16[0]) : p.w_scale[ne];
     if constexpr (BIAS && OUT == W4_OUT_F16) bias[e] = h2f(p.bias[ne]);
   }
 }
@@ -469,7 +479,7 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
 #pragma unroll
     for (int c = tid; c < NTILES * 16; c += S::THREADS) {
       const int n = min(t0 * 16 + c, p.N - 1);
-      lws[c] = KIND == KIND_W4A8 ? p.w_scale[n] : h2f(p.w_scale16[0]);
+      lws[c] = KIND == KIND_W2A8 ? h2f(p.w_scale16[0]) : p.w_scale[n];
       if constexpr (BIAS) lbias[c] = p.bias[n];
     }
   }
@@ -673,7 +683,7 @@ inline int gemm_tiles(int M, int N, GemmCfg c) {
 // 16*ntiles columns in every candidate); the 352-column shapes never split K,
 // so they are only candidates where their grid fills most of the chip.
 inline GemmCfg gemm_cfg(int kind, int M, int N) {
-  if (kind != KIND_W4A8) return GemmCfg{8, 2};
+  if (kind != KIND_W4A8) return GemmCfg{8, 2};       // 2-bit and INT8 weights: 128 x 128
   const GemmCfg narrow{16, 2};
   GemmCfg best = narrow;
   int best_cost = ceil_div(gemm_tiles(M, N, narrow), GEMM_CUS * 2) * 16;
@@ -691,13 +701,16 @@ inline GemmCfg gemm_cfg(int kind, int M, int N) {
 // K much; smaller products run on the decode kernel, one block per (16-row
 // tile, 16-column tile).
 inline bool use_gemm(int kind, int M, int N) {
-  if (kind != KIND_W4A8 && kind != KIND_W2A8) return false;
+  if (kind != KIND_W4A8 && kind != KIND_W2A8 && kind != KIND_W8A8) return false;
   if (M <= 16) return false;
   return gemm_tiles(M, N, gemm_cfg(kind, M, N)) >= 128;
 }
 
 inline GemmGrid gemm_grid(int kind, int M, int N, int K, GemmCfg c) {
-  const Geometry g = geometry(kind == KIND_W2A8 ? W4_LAYOUT_W2A8 : W4_LAYOUT_W4A8, N, K);
+  const Geometry g = geometry(kind == KIND_W2A8   ? W4_LAYOUT_W2A8
+                              : kind == KIND_W8A8 ? W4_LAYOUT_W8A8
+                                                  : W4_LAYOUT_W4A8,
+                              N, K);
   GemmGrid gg{};
   gg.mblocks = ceil_div(M, 64 * c.wm);
   gg.nblocks = ceil_div(g.NT, c.ntiles);
@@ -736,6 +749,10 @@ int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
 
 template <int KIND, int NTILES, int WM, int FQ>
 int launch_gemm_f(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
+  if constexpr (KIND == KIND_W8A8) {
+    if (p.out_dtype == W4_OUT_I8)
+      return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I8, false, FQ>(p, gg, stream);
+  }
   if (p.out_dtype == W4_OUT_I32)
     return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I32, false, FQ>(p, gg, stream);
   if (p.out_dtype == W4_OUT_F32)
@@ -751,8 +768,12 @@ template <int KIND, int NTILES, int WM>
 int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream, int fq) {
   p.counters = reinterpret_cast<unsigned*>(ws);
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + WS_COUNTERS : nullptr;
-  if (fq == 1) return launch_gemm_f<KIND, NTILES, WM, 1>(p, gg, stream);
-  if (fq == 2) return launch_gemm_f<KIND, NTILES, WM, 2>(p, gg, stream);
+  if constexpr (KIND == KIND_W4A8 || KIND == KIND_W2A8) {
+    if (fq == 1) return launch_gemm_f<KIND, NTILES, WM, 1>(p, gg, stream);
+    if (fq == 2) return launch_gemm_f<KIND, NTILES, WM, 2>(p, gg, stream);
+  } else {
+    if (fq) return W4_ERR_ARG;
+  }
   return launch_gemm_f<KIND, NTILES, WM, 0>(p, gg, stream);
 }
 
@@ -760,11 +781,13 @@ int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream, 
 // GEMM instances compile in parallel with the rest of the library).
 int launch_gemm_w4a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
 int launch_gemm_w2a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
+int launch_gemm_w8a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream);
 
 template <int KIND>
 int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq = 0) {
   if constexpr (KIND == KIND_W4A8) return launch_gemm_w4a8(p, c, ws, stream, fq);
   else if constexpr (KIND == KIND_W2A8) return launch_gemm_w2a8(p, c, ws, stream, fq);
+  else if constexpr (KIND == KIND_W8A8) return fq ? W4_ERR_ARG : launch_gemm_w8a8(p, c, ws, stream);
   else return W4_ERR_ARG;
 }
 

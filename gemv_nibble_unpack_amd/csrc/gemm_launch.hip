@@ -17,4 +17,9 @@ int launch_gemm_w2a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream,
   return launch_gemm_t<KIND_W2A8, 8, 2>(p, gg, ws, stream, fq);
 }
 
+int launch_gemm_w8a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream) {
+  const GemmGrid gg = gemm_grid(KIND_W8A8, p.M, p.N, p.K, c);
+  return launch_gemm_t<KIND_W8A8, 8, 2>(p, gg, ws, stream, 0);
+}
+
 }  // namespace w4

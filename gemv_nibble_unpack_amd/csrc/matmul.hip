@@ -267,7 +267,7 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{16, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 4}};
-  } else if (M > 16 && kind == KIND_W2A8) {
+  } else if (M > 16 && (kind == KIND_W2A8 || kind == KIND_W8A8)) {
     // 128 x 128 blocks, whole K and at each distinct k split up to the same
     // block count
     const int tiles = gemm_tiles(M, N, GemmCfg{8, 2});

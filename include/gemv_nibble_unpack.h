@@ -432,6 +432,43 @@ size_t w4_plan_workspace_bytes(int op, int M, int N, int K);
  */
 int w4_read_probe(const void* buf, size_t bytes, int per, uint32_t* sink, hipStream_t stream);
 
+/* ---- decode-step graphs --------------------------------------------------
+ * After the INT4 quantization page, Part 2 (steps 2-4): the kernel launches of
+ * a decode step are captured once from a stream, instantiated, and launched
+ * as one graph per step; before a launch the graph's kernel-node parameters
+ * are updated so that the captured step reads and writes the current step's
+ * buffers (the page's cudaGraphExecKernelNodeSetParams).
+ *
+ * w4_graph_begin starts capturing `stream` (a stream created by the caller;
+ * thread-local capture mode). Matmul calls issued on it are recorded, not run
+ * (their argument checks still run and can fail; a workspace must already be
+ * allocated, since nothing may be allocated while capturing).
+ * w4_graph_end ends the capture and instantiates it into *out (host handle,
+ * owned by the caller until w4_graph_destroy).
+ * w4_graph_update ends a capture begun again with w4_graph_begin, in which
+ * the caller issued the same sequence of calls with other pointers, and gives
+ * every kernel node of `graph` the parameters of the node at the same position
+ * (in dependency order) of the new capture. All nodes must launch the same
+ * kernels with the same grid, block and LDS size (same shapes and plans);
+ * otherwise W4_ERR_ARG and the graph is left as it was. The new capture is
+ * discarded either way.
+ * w4_graph_launch launches the graph on `stream` (any stream of the device).
+ * w4_graph_kernel_nodes returns the number of kernel nodes (>= 0).
+ * w4_graph_destroy frees the graph (NULL is a no-op).
+ * Errors: W4_ERR_NULL for a NULL handle, output pointer or (begin, end,
+ * update) stream; W4_ERR_HIP when the runtime refuses a capture, instantiation
+ * or update (the capture is then ended and discarded). A graph's launches on
+ * one stream run in order; launching it on two streams at once races on its
+ * buffers and workspaces like any other pair of calls.
+ */
+typedef struct w4_graph_s* w4_graph_t;
+int w4_graph_begin(hipStream_t stream);
+int w4_graph_end(hipStream_t stream, w4_graph_t* out);
+int w4_graph_update(w4_graph_t graph, hipStream_t stream);
+int w4_graph_launch(w4_graph_t graph, hipStream_t stream);
+int w4_graph_kernel_nodes(w4_graph_t graph);
+int w4_graph_destroy(w4_graph_t graph);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_and_library_agree():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 34, names
     assert set(names) == set(L.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -252,9 +252,13 @@ def test_plan_table_candidates():
     assert lib.w4_plan_workspace_bytes(L.W4_OP_W4A8, 1100, 4004, 512) == 0
     names = _names(lib, L.W4_OP_W2A8, 1100, 2000, 1024)
     assert names[lib.w4_plan_current(L.W4_OP_W2A8, 1100, 2000, 1024)] == "gemm:128x128,ksplit=2"
-    # fp16 activations and INT8 weights have no GEMM candidate
-    for op in (L.W4_OP_W4A16, L.W4_OP_W2A16, L.W4_OP_W8A8):
+    # fp16 activations and FP8 have no GEMM candidate; INT8 weights take the
+    # 128 x 128 block (built in once 128 blocks fill the chip unsplit)
+    for op in (L.W4_OP_W4A16, L.W4_OP_W2A16, L.W4_OP_F8F8):
         assert not any(n.startswith("gemm") for n in _names(lib, op, 2048, 4096, 4096))
+    names = _names(lib, L.W4_OP_W8A8, 2048, 4096, 4096)
+    assert names[lib.w4_plan_current(L.W4_OP_W8A8, 2048, 4096, 4096)] == "gemm:128x128"
+    assert "gemm:128x128" in _names(lib, L.W4_OP_W8A8, 128, 4096, 4096)
     # a tiny-N, huge-K decode splits K 64 ways on its own (one output tile)
     names = _names(lib, L.W4_OP_W2A8, 1, 16, 131056)
     assert names[lib.w4_plan_current(L.W4_OP_W2A8, 1, 16, 131056)] == "decode:ksplit=64"
@@ -315,3 +319,25 @@ def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         G.quantize_pack_w4(torch.zeros(4, 8))
+
+
+def test_graph_entry_points_reject_null_before_any_hip_call():
+    lib = G.load()
+    assert lib.w4_graph_begin(None) == L.W4_ERR_NULL
+    h = ctypes.c_void_p()
+    assert lib.w4_graph_end(None, ctypes.byref(h)) == L.W4_ERR_NULL
+    assert lib.w4_graph_end(P, None) == L.W4_ERR_NULL
+    assert lib.w4_graph_update(None, P) == L.W4_ERR_NULL
+    assert lib.w4_graph_update(P, None) == L.W4_ERR_NULL
+    assert lib.w4_graph_launch(None, None) == L.W4_ERR_NULL
+    assert lib.w4_graph_kernel_nodes(None) == L.W4_ERR_NULL
+    assert lib.w4_graph_destroy(None) == L.W4_OK
+
+
+def test_step_graph_needs_a_stream_of_its_own():
+    class Default:
+        cuda_stream = 0
+    with pytest.raises(ValueError):
+        G.StepGraph(Default())
+    with pytest.raises(ValueError):
+        G.StepGraph(None)

@@ -698,11 +698,14 @@ def test_quantize_w8_bitexact_and_prepack_roundtrip(g):
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (4, 4096, 4096), (16, 4096, 4096),
                                    (128, 3200, 3200), (3, 130, 208), (1, 256, 8640),
-                                   (40, 300, 512), (300, 2000, 1040)])
+                                   (40, 300, 512), (300, 2000, 1040), (2048, 4096, 4096),
+                                   (1100, 2000, 1040), (1030, 1990, 528)])
 def test_w8a8_outputs(g, M, N, K):
-    # decode (M <= 16), skinny (M = 128, 300) and 16-row-tile (M = 40) kernels,
-    # ragged tails and a split over K; INT32 and INT8 bit-exact, f16/f32 to
-    # the tolerance
+    # decode (M <= 16), skinny (M = 128, 300), 16-row-tile (M = 40) and tiled
+    # GEMM (M >= 1030: 128 x 128 blocks, N % 8 != 0 through the direct
+    # epilogue, K tails of 16 past a 64-k tile) kernels, ragged tails and a
+    # split over K; every output compared: INT32 and INT8 bit-exact, f16/f32
+    # to the tolerance
     say(f"case w8a8 M={M} N={N} K={K}")
     A = WL.activations(M, K, seed=9700 + M, dtype=np.float16)
     W = WL.weights_f32(N, K, seed=9701 + N)
