@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["quant.hip", "prepack.hip", "matmul.hip", "gemm_launch.hip", "probe.hip", "noalloc.hip",
-           "graph.hip"]
+           "graph.hip", "gemm16.hip"]
 OUT = os.path.join(HERE, "libgemv_nibble_unpack.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("W4_OFFLOAD_ARCH", "gfx950")

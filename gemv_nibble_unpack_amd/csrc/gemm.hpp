@@ -683,6 +683,14 @@ inline int gemm_tiles(int M, int N, GemmCfg c) {
 // 16*ntiles columns in every candidate); the 352-column shapes never split K,
 // so they are only candidates where their grid fills most of the chip.
 inline GemmCfg gemm_cfg(int kind, int M, int N) {
+  if (kind == KIND_W4A16) {
+    // fp16 activations (gemm16.hip): 128-row blocks, one per CU, 256 or 352
+    // columns, whichever needs fewer rounds x columns
+    const GemmCfg a{16, 2}, b{22, 2};
+    const int ca = ceil_div(gemm_tiles(M, N, a), GEMM_CUS) * a.ntiles;
+    const int cb = ceil_div(gemm_tiles(M, N, b), GEMM_CUS) * b.ntiles;
+    return cb <= ca ? b : a;
+  }
   if (kind != KIND_W4A8) return GemmCfg{8, 2};       // 2-bit and INT8 weights: 128 x 128
   const GemmCfg narrow{16, 2};
   GemmCfg best = narrow;
@@ -701,7 +709,8 @@ inline GemmCfg gemm_cfg(int kind, int M, int N) {
 // K much; smaller products run on the decode kernel, one block per (16-row
 // tile, 16-column tile).
 inline bool use_gemm(int kind, int M, int N) {
-  if (kind != KIND_W4A8 && kind != KIND_W2A8 && kind != KIND_W8A8) return false;
+  if (kind != KIND_W4A8 && kind != KIND_W2A8 && kind != KIND_W8A8 && kind != KIND_W4A16)
+    return false;
   if (M <= 16) return false;
   return gemm_tiles(M, N, gemm_cfg(kind, M, N)) >= 128;
 }
@@ -718,7 +727,7 @@ inline GemmGrid gemm_grid(int kind, int M, int N, int K, GemmCfg c) {
   // K is split only for blocks of up to 8 weight tiles, with one arrival
   // counter per tile
   int ks = 1;
-  if (c.ntiles <= 8 && gg.tiles <= WS_COUNTER_SLOTS) {
+  if (c.ntiles <= 8 && gg.tiles <= WS_COUNTER_SLOTS && kind != KIND_W4A16) {
     if (c.ks > 0) ks = c.ks;
     else
       while (gg.tiles * ks < 256 && ceil_div(g.KT, ks * 2) >= 2) ks *= 2;
@@ -782,12 +791,14 @@ int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream, 
 int launch_gemm_w4a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
 int launch_gemm_w2a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
 int launch_gemm_w8a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream);
+int launch_gemm_w4a16(const MMParams& p, GemmCfg c, hipStream_t stream);  // gemm16.hip
 
 template <int KIND>
 int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq = 0) {
   if constexpr (KIND == KIND_W4A8) return launch_gemm_w4a8(p, c, ws, stream, fq);
   else if constexpr (KIND == KIND_W2A8) return launch_gemm_w2a8(p, c, ws, stream, fq);
   else if constexpr (KIND == KIND_W8A8) return fq ? W4_ERR_ARG : launch_gemm_w8a8(p, c, ws, stream);
+  else if constexpr (KIND == KIND_W4A16) return fq ? W4_ERR_ARG : launch_gemm_w4a16(p, c, stream);
   else return W4_ERR_ARG;
 }
 

@@ -317,8 +317,24 @@ def test_w4a16_bitblas_example_shape(g):
     _w4a16_case(g, WL.BITBLAS_EXAMPLE)
 
 
-@pytest.mark.parametrize("M,N,K", [(2, 37, 256), (16, 130, 384), (33, 64, 128), (1, 16, 128)])
+def test_w4a16_prefill_gemm_full(g):
+    # M=2048, N=11008, K=4096 with bias: the tiled fp16 GEMM (128 x 352
+    # blocks); every output against the oracle
+    c = WL.W4A16_PREFILL
+    say(f"case {c.name}")
+    d = c.inputs()
+    Wp = prep_w4a16(g, d["W"])
+    C = host(g.w4a16_gemm(dev(d["A"]), Wp, c.N, bias=f16(d["bias"])))
+    q, s, z = O.quantize_w4_group(d["W"], 128)
+    tol_ok(C, O.w4a16_gemm(d["A"], q, s, z, 128, d["bias"]), c.name)
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 37, 256), (16, 130, 384), (33, 64, 128), (1, 16, 128),
+                                   (1030, 4100, 1024), (2000, 3000, 640)])
 def test_w4a16_ragged_with_bias(g, M, N, K):
+    # decode, skinny and (M >= 1030) the tiled fp16 GEMM's 128 x 256 blocks:
+    # N = 4100 has a ragged last column tile and N % 8 != 0 (direct epilogue),
+    # N = 3000 goes through the LDS-staged epilogue; both have rows past M
     say(f"case w4a16 ragged M={M} N={N} K={K}")
     W = WL.weights_f32(N, K, seed=6000 + N)
     A = WL.activations(M, K, seed=6001 + M)

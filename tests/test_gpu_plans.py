@@ -152,7 +152,7 @@ PLAN_SHAPES = [
     # split GEMM finishes over column pairs with a ragged pair (N % 4 == 2)
     # and over single columns (odd N), with rows past M in the last block
     ("w2a8", 130, 1002, 1024), ("w2a8", 100, 1001, 768),
-    ("w4a16", 16, 4096, 4096), ("w4a16", 33, 1000, 1024),
+    ("w4a16", 16, 4096, 4096), ("w4a16", 33, 1000, 1024), ("w4a16", 130, 1003, 512),
     ("w2a16", 3, 3200, 8640), ("w2a16", 40, 3000, 2000),
     ("w8a8", 16, 4096, 4096), ("w8a8", 20, 1000, 528),
     ("f8f8", 16, 4096, 4096), ("f8f8", 20, 1000, 528),
