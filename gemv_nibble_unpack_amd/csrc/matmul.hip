@@ -268,9 +268,10 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 4}};
   } else if (M > 16 && kind == KIND_W4A16) {
-    // fp16 activations: 128 x 256 and 128 x 352 blocks, whole K
+    // fp16 activations: 128 x 256, 128 x 352 and 128 x 384 blocks, whole K
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{16, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 2}};
+    out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{24, 2}};
   } else if (M > 16 && (kind == KIND_W2A8 || kind == KIND_W8A8)) {
     // 128 x 128 blocks, whole K and at each distinct k split up to the same
     // block count

@@ -258,8 +258,9 @@ def test_plan_table_candidates():
     for op in (L.W4_OP_W2A16, L.W4_OP_F8F8):
         assert not any(n.startswith("gemm") for n in _names(lib, op, 2048, 4096, 4096))
     names = _names(lib, L.W4_OP_W4A16, 2048, 11008, 4096)
-    assert [n for n in names if n.startswith("gemm")] == ["gemm:128x256", "gemm:128x352"]
-    assert names[lib.w4_plan_current(L.W4_OP_W4A16, 2048, 11008, 4096)] == "gemm:128x352"
+    assert [n for n in names if n.startswith("gemm")] == ["gemm:128x256", "gemm:128x352",
+                                                          "gemm:128x384"]
+    assert names[lib.w4_plan_current(L.W4_OP_W4A16, 2048, 11008, 4096)] == "gemm:128x384"
     assert names[lib.w4_plan_current(L.W4_OP_W4A16, 2048, 4096, 4096)] == "gemm:128x256"
     assert lib.w4_plan_workspace_bytes(L.W4_OP_W4A16, 2048, 11008, 4096) == 0
     names = _names(lib, L.W4_OP_W4A16, 128, 11008, 4096)

@@ -318,8 +318,8 @@ def test_w4a16_bitblas_example_shape(g):
 
 
 def test_w4a16_prefill_gemm_full(g):
-    # M=2048, N=11008, K=4096 with bias: the tiled fp16 GEMM (128 x 352
-    # blocks); every output against the oracle
+    # M=2048, N=11008, K=4096 with bias: the tiled fp16 GEMM (its built-in
+    # block shape); every output against the oracle
     c = WL.W4A16_PREFILL
     say(f"case {c.name}")
     d = c.inputs()
