@@ -18,6 +18,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef int i4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // prepacked layout geometry
@@ -46,15 +47,9 @@ constexpr int TILE_BYTES = 1024;
 // reuse one workspace (zero-filled once) on one stream: a call's counters never
 // land on bytes an earlier call used as scratch.
 constexpr size_t WS_COUNTERS = 16 * 1024;
-// The last 1 KiB of the counter area holds the one-launch fused prefill's
-// counters (row claims, finished blocks, rows done per m block), which that
-// kernel also leaves zero; split-K arrival counters use the words before it.
-constexpr int WS_SYNC_WORD = 3840;
-constexpr int WS_COUNTER_SLOTS = WS_SYNC_WORD;
-constexpr int SYNC_NEXT = 0;                     // next activation row to claim
-constexpr int SYNC_FIN = 1;                      // blocks that have finished
-constexpr int SYNC_DONE = 4;                     // rows quantized, per m block
-constexpr int SYNC_MBLOCKS = (int)(WS_COUNTERS / sizeof(unsigned)) - WS_SYNC_WORD - SYNC_DONE;
+// Split-K arrival counters (one per output tile of a split launch); the last
+// KiB of the area is left unused.
+constexpr int WS_COUNTER_SLOTS = 3840;
 
 struct Geometry {
   int NT;          // n tiles
@@ -220,14 +215,6 @@ __device__ __forceinline__ uint64_t dev_load2(const uint32_t* a) {
 }
 __device__ __forceinline__ unsigned dev_arrive(unsigned* c) {
   return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The current value of a counter that other XCDs advance with dev_arrive,
-// read as an atomic read-modify-write (adding 0). Counters are only ever read
-// this way: the value an RMW returns is the one at the point where the RMWs
-// of every XCD are performed, while a plain load, even at device scope, may be
-// served from a copy of the line cached before the other XCDs' updates.
-__device__ __forceinline__ unsigned dev_count(unsigned* c) {
-  return __hip_atomic_fetch_add(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // wait until this wave's stores are acknowledged; the clobber keeps the
 // compiler from moving memory accesses across the wait

@@ -1,6 +1,7 @@
 // Prefill-side kernel (M > 16): C[M,N] = A[M,K] x W[N,K]^T with INT8
 // activations and 4-bit (or 2-bit ternary, or INT8) weights on the CDNA4 INT8
-// matrix cores.
+// matrix cores, and FP8 E4M3 x FP8 E4M3 on the FP8 matrix cores
+// (v_mfma_f32_16x16x128_f8f6f4, float32 sums).
 //
 // Dataflow (INT4 quantization page, Part 1 step 3, mapped to gfx950): for each
 // k tile, a block copies its activation tile (BM x TILE_K int8) and its
@@ -29,16 +30,25 @@ namespace w4 {
 
 template <int KIND>
 struct GemmTraits {
-  static constexpr int TILE_K = KindTraits<KIND>::TILE_K;  // k per stage (one weight tile)
+  // weight tiles per n tile per stage: FP8 stages two 64-k tiles, the 128 k
+  // of one v_mfma_f32_16x16x128_f8f6f4; every other kind one tile
+  static constexpr int WT = KIND == KIND_F8F8 ? 2 : 1;
+  static constexpr int TILE_K = KindTraits<KIND>::TILE_K * WT;  // k per stage
   static constexpr int KSTEPS = TILE_K / 64;               // MFMA k steps per lane quarter
   static constexpr int ROW_CHUNKS = TILE_K / 16;           // 16-byte chunks per staged A row
+  using Acc = typename std::conditional<KIND == KIND_F8F8, f4, i4>::type;
 };
 
 // Physical 16-byte chunk of logical chunk c in staged A row `row`: an XOR
-// swizzle that puts the 16 rows of a fragment read on distinct LDS banks
+// swizzle that spreads the 16 rows of a fragment read over the LDS banks
 // (64-byte rows: four rows share a 256-byte bank line, so the swizzle uses
 // row>>2; 128-byte rows alternate between two halves, so it uses row>>1;
-// 256-byte rows all start on bank 0, so it uses row itself).
+// 256-byte rows all start on bank 0, so it uses row itself). On gfx950 a
+// 16-byte read in this layout still costs 4 bank-conflict cycles (rocprofv3
+// SQ_LDS_BANK_CONFLICT on a probe); a chunk-major layout that has none
+// ([row / 16][chunk][row % 16]) needs 16-row x 64-byte direct loads instead of
+// 8-row x 128-byte ones and was measured slower (same box, tuner, 100 calls:
+// W4A8 256 x 352 at M=2048 N=11008 K=4096 +2%, W8A8 128 x 128 +10%).
 template <int KIND>
 __device__ __forceinline__ int a_chunk(int row, int c) {
   if constexpr (GemmTraits<KIND>::ROW_CHUNKS == 4) return c ^ ((row >> 2) & 3);
@@ -56,7 +66,7 @@ struct GemmShape {
   static constexpr int BLOCKS_PER_CU = 4 / WM;                  // two waves per SIMD
   static constexpr int A_BYTES = BM * G::TILE_K;                // unpadded, XOR-swizzled rows
   static constexpr int A_LOADS = A_BYTES / TILE_BYTES;          // 1 KiB wave loads per stage
-  static constexpr int W_BYTES = NTILES * TILE_BYTES;
+  static constexpr int W_BYTES = NTILES * G::WT * TILE_BYTES;
   static_assert(NTILES % 2 == 0, "two waves split the block's columns");
   static constexpr int NTW = NTILES / 2;                        // n subtiles per wave
   static constexpr int STAGE = A_BYTES + W_BYTES;
@@ -65,7 +75,7 @@ struct GemmShape {
   // measured no faster on the 256 x 352 blocks and is not used)
   static constexpr int STAGES = 2;
   static constexpr int A_PER_WAVE = A_LOADS / WAVES;            // direct loads per wave
-  static constexpr int W_PER_WAVE = (NTILES + WAVES - 1) / WAVES;  // last round may be partial
+  static constexpr int W_PER_WAVE = (NTILES * G::WT + WAVES - 1) / WAVES;  // last round may be partial
   // fp16 epilogue staging: per wave and pass, 32 rows of 16*NTW columns
   static constexpr int EPI_ROWS = 32;
   static constexpr int EPI_ROW = NTW * 32 + 16;                 // padded row bytes
@@ -104,13 +114,13 @@ __device__ __forceinline__ void unpack_frag(const u4 w, i4 (&bf)[GemmTraits<KIND
 // Epilogue of one accumulator fragment: 4 consecutive output columns n..n+3
 // of row m (operands are swapped in the MFMA so a lane owns a column run).
 // ws/bias hold the 4 columns' weight scales and biases, sa the row's scale.
-template <int KIND, int OUT, bool BIAS>
-__device__ __forceinline__ void gemm_store4(const MMParams& p, int m, int n, const i4 v,
+template <int KIND, int OUT, bool BIAS, typename V>
+__device__ __forceinline__ void gemm_store4(const MMParams& p, int m, int n, const V v,
                                             const f4 ws, const f4 bias, float sa, bool vec_ok) {
   constexpr int SH = KindTraits<KIND>::SHIFT;
   if (m >= p.M || n >= p.N) return;
   const bool full = vec_ok && n + 3 < p.N;
-  if constexpr (OUT == W4_OUT_I32) {
+  if constexpr (OUT == W4_OUT_I32 && KIND != KIND_F8F8) {
     int32_t* c = reinterpret_cast<int32_t*>(p.C) + (size_t)m * p.N + n;
     const i4 q = i4{v[0] >> SH, v[1] >> SH, v[2] >> SH, v[3] >> SH};
     if (full) {
@@ -122,11 +132,11 @@ __device__ __forceinline__ void gemm_store4(const MMParams& p, int m, int n, con
     float o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int a = v[e] >> SH;
-      o[e] = (float)a * ws[e] * sa;
+      if constexpr (KIND == KIND_F8F8) o[e] = v[e] * ws[e] * sa;
+      else o[e] = (float)(v[e] >> SH) * ws[e] * sa;
       if constexpr (BIAS && OUT == W4_OUT_F16) o[e] += bias[e];
     }
-    if constexpr (OUT == W4_OUT_I8) {
+    if constexpr (OUT == W4_OUT_I8 && KIND != KIND_F8F8) {
       // re-quantized for a following INT8 layer, the code decided in float32
       // as the decode kernel decides it
       int8_t* c = reinterpret_cast<int8_t*>(p.C) + (size_t)m * p.N + n;
@@ -162,157 +172,7 @@ __device__ __forceinline__ void gemm_col_params(const MMParams& p, int n, f4& ws
   }
 }
 
-// ---------------------------------------------------------------------------
-// One-launch fused prefill (FQ = 1: fp16 rows, FQ = 2: float32 rows in
-// p.A_in). Every wave of the grid first takes activation rows from a shared
-// counter, one at a time, and quantizes each whole row with the per-token
-// rule of quantize_a8 (INT4 page, Part 1 step 2: scale = max|a| / 127,
-// code = rint(a / scale)), writing the int8 row to p.A and its scale to
-// p.a_scale, then counts the row in for its m block. A block then waits until
-// its m block's rows are all in before it loads activations. This cannot
-// deadlock whatever the number of resident blocks: a block waits only after
-// the row counter has run out, i.e. when every row has been claimed by a wave
-// that is running and that waits for nothing before it finishes its row. The
-// wait is bounded anyway (FQ_SPIN_LIMIT polls) so that no wave can spin for
-// ever. The counter is polled with an atomic read-modify-write (dev_count):
-// plain loads of it are not guaranteed to see other XCDs' increments. The
-// last block to finish leaves the counters zero for the next call.
-//
-// Visibility across XCDs: the rows and scales are written with device-scope
-// (sc1) stores, which pass through to the memory all XCDs share, and a wave
-// waits for their completion (vmcnt 0) before it counts the row in with a
-// device-scope atomic; the waiting block polls the counter with device-scope
-// atomics, executes a device-scope acquire fence (the L2 and L1 invalidation
-// the AMDGPU memory model prescribes for an agent-scope acquire on gfx950),
-// and reads the rows and scales with device-scope (sc1) loads, the same
-// store / wait / count / load sequence as the split-K partial sums.
-// ---------------------------------------------------------------------------
-constexpr unsigned FQ_SPIN_LIMIT = 1u << 18;    // polls of ~0.5-2 us: under a second
-
-template <int FQ, int BM>
-__device__ __forceinline__ void fq_quantize_rows(const MMParams& p) {
-  constexpr int ESZ = FQ == 2 ? 4 : 2;               // input element bytes
-  constexpr int U = ESZ / 2;                         // 16-byte loads per 8-element chunk
-  constexpr int RC = 8;                              // chunks per lane held in registers
-  const int lane = threadIdx.x & 63;
-  const int K = p.K, nch = K / 8;                    // K % 16 == 0
-  const uint8_t* Ain = reinterpret_cast<const uint8_t*>(p.A_in);
-  uint32_t* qA = reinterpret_cast<uint32_t*>(const_cast<void*>(p.A));
-  uint32_t* sa = reinterpret_cast<uint32_t*>(const_cast<float*>(p.a_scale));
-  auto widen = [&](const u4 (&r)[U], float (&x)[8]) {
-    if constexpr (FQ == 1) {
-      const h8 hv = __builtin_bit_cast(h8, r[0]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (float)hv[e];
-    } else {
-      // whole-vector casts (a bit cast of one ext-vector element reads
-      // element 0 with this compiler)
-      const f4 a0 = __builtin_bit_cast(f4, r[0]);
-      const f4 a1 = __builtin_bit_cast(f4, r[U - 1]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = a0[e];
-        x[4 + e] = a1[e];
-      }
-    }
-  };
-  auto load = [&](const uint8_t* src, int c, u4 (&r)[U]) {
-#pragma unroll
-    for (int h = 0; h < U; ++h) r[h] = *reinterpret_cast<const u4*>(src + (size_t)c * 8 * ESZ + 16 * h);
-  };
-  for (;;) {
-    // One claim per wave. The loop holds no lane-dependent branch around a
-    // side effect, and the row is wave-uniform in the compiler's eyes (an
-    // SGPR from readfirstlane): with the claim and the count-in written as
-    // `if (lane == 0) ...` and the row taken from a lane shuffle, the
-    // compiler gave the loop per-lane exits in which lane 0 went back for a
-    // new claim while the 63 others went round again on a stale row, for
-    // ever. Every lane now takes part in the atomics, lane 0 adding 1 and the
-    // others 0.
-    const unsigned one = lane == 0 ? 1u : 0u;
-    const unsigned claim = __hip_atomic_fetch_add(&p.sync[SYNC_NEXT], one, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-    const int row = (int)__builtin_amdgcn_readfirstlane(claim);
-    if (row >= p.M) break;                           // uniform
-    const uint8_t* src = Ain + (size_t)row * K * ESZ;
-    uint32_t* dst = qA + (size_t)row * (K / 4);
-    float mx = 0.f, s, rs;
-    int sum = 0;
-    if (nch <= 64 * RC) {
-      // the row in registers: every load issued before the first is used
-      u4 raw[RC][U];
-#pragma unroll
-      for (int j = 0; j < RC; ++j) load(src, min(lane + 64 * j, nch - 1), raw[j]);
-#pragma unroll
-      for (int j = 0; j < RC; ++j) {
-        if (lane + 64 * j < nch) {
-          float x[8];
-          widen(raw[j], x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
-        }
-      }
-      mx = wave_max(mx);
-      s = mx / 127.0f;
-      rs = s > 0.f ? 1.0f / s : 0.f;
-#pragma unroll
-      for (int j = 0; j < RC; ++j) {
-        const int c = lane + 64 * j;
-        if (c < nch) {
-          float x[8];
-          widen(raw[j], x);
-          uint32_t lo, hi;
-          codes8_i8(x, s, rs, lo, hi, sum);
-          dev_store2(dst + 2 * c, lo, hi);
-        }
-      }
-    } else {
-      // longer rows: one pass for the maximum, a second (from cache) for the codes
-      for (int c = lane; c < nch; c += 64) {
-        u4 r[U];
-        load(src, c, r);
-        float x[8];
-        widen(r, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
-      }
-      mx = wave_max(mx);
-      s = mx / 127.0f;
-      rs = s > 0.f ? 1.0f / s : 0.f;
-      for (int c = lane; c < nch; c += 64) {
-        u4 r[U];
-        load(src, c, r);
-        float x[8];
-        widen(r, x);
-        uint32_t lo, hi;
-        codes8_i8(x, s, rs, lo, hi, sum);
-        dev_store2(dst + 2 * c, lo, hi);
-      }
-    }
-    dev_store(&sa[row], __builtin_bit_cast(uint32_t, s));   // every lane, the same value
-    stores_done();                                   // the row is out before it is counted in
-    __hip_atomic_fetch_add(&p.sync[SYNC_DONE + row / BM], one, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// The last block to finish resets the counters (every block has passed its
-// wait and every wave its row claims by the time it counts itself in).
-template <int BM>
-__device__ __forceinline__ void fq_finish(const MMParams& p) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned total = gridDim.x * gridDim.y;
-    if (dev_arrive(&p.sync[SYNC_FIN]) == total - 1) {
-      const int mblocks = (p.M + BM - 1) / BM;
-      dev_store(&p.sync[SYNC_NEXT], 0u);
-      for (int i = 0; i < mblocks; ++i) dev_store(&p.sync[SYNC_DONE + i], 0u);
-      dev_store(&p.sync[SYNC_FIN], 0u);
-    }
-  }
-}
-
-template <int KIND, int NTILES, int WM, int OUT, bool BIAS, int FQ>
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
 __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg) {
   using G = GemmTraits<KIND>;
   using S = GemmShape<KIND, NTILES, WM>;
@@ -345,8 +205,9 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
     mb = tix - nb * gg.mblocks;
   }
   const int kz = blockIdx.y;
+  const int KS = (p.KT + G::WT - 1) / G::WT;         // k stages (WT weight tiles each)
   const int kb = kz * gg.kts;
-  const int ke = min(p.KT, kb + gg.kts);
+  const int ke = min(KS, kb + gg.kts);
   const int nk = max(0, ke - kb);
 
   const int tid = threadIdx.x;
@@ -373,20 +234,20 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
       const int c = a_chunk<KIND>(row, lchunk);      // logical chunk for this physical slot
       const int gm = min(m0 + row, p.M - 1);
       const int gk = min(kt * TK + 16 * c, p.K - 16);
-      // rows quantized by this launch are read at device scope (sc1), like
-      // every other value one block hands to another here
-      __builtin_amdgcn_global_load_lds(A + (size_t)gm * p.K + gk, sa + ld * TILE_BYTES, 16, 0,
-                                       FQ != 0 ? 16 : 0);
+      __builtin_amdgcn_global_load_lds(A + (size_t)gm * p.K + gk, sa + ld * TILE_BYTES, 16, 0, 0);
     }
   };
   auto issue_w = [&](int kt, int st) {
     uint8_t* sw = smem + st * S::STAGE + S::A_BYTES;
 #pragma unroll
     for (int q = 0; q < S::W_PER_WAVE; ++q) {
-      const int tl = q * S::WAVES + wave;            // weight tile within the block
-      if (NTILES % S::WAVES != 0 && tl >= NTILES) break;  // wave-uniform
-      const int t = min(t0 + tl, p.NT - 1);
-      __builtin_amdgcn_global_load_lds(p.Wt + ((size_t)t * p.KT + kt) * TILE_BYTES + lane * 16,
+      const int tl = q * S::WAVES + wave;            // weight tile slot within the block
+      if ((NTILES * G::WT) % S::WAVES != 0 && tl >= NTILES * G::WT) break;  // wave-uniform
+      const int t = min(t0 + tl / G::WT, p.NT - 1);
+      // the second tile of a stage past the last weight tile (odd tile
+      // count) re-reads the last one; its products are dropped in compute
+      const int kw = min(kt * G::WT + tl % G::WT, p.KT - 1);
+      __builtin_amdgcn_global_load_lds(p.Wt + ((size_t)t * p.KT + kw) * TILE_BYTES + lane * 16,
                                        sw + tl * TILE_BYTES, 16, 0, 0);
     }
   };
@@ -394,7 +255,39 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
     issue_a(kt, st);
     issue_w(kt, st);
   };
-  auto compute = [&](int st, i4 (&acc)[4][NTW]) {
+  using Acc = typename G::Acc;
+  auto compute_f8 = [&](int st, int kt, auto& acc) {
+    // lane (r, b) holds k = 16 b .. 16 b + 15 of each of the stage's two
+    // weight tiles; its A operand is the same k positions of its row (chunks
+    // b and 4 + b of the 128-byte staged row), so the 128-k product sums the
+    // same terms as the two 64-k halves
+    const uint8_t* sa = smem + st * S::STAGE;
+    const uint8_t* sw = sa + S::A_BYTES;
+    const bool hi_live = kt * 2 + 1 < p.KT;          // uniform
+    v8i af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * wm + 16 * i + r;
+      const u4 lo = *reinterpret_cast<const u4*>(sa + row * TK + 16 * a_chunk<KIND>(row, b));
+      const u4 hi = *reinterpret_cast<const u4*>(sa + row * TK + 16 * a_chunk<KIND>(row, 4 + b));
+      af[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    const uint8_t* swl = sw + wn * NTW * 2 * TILE_BYTES + lane * 16;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const u4 lo = *reinterpret_cast<const u4*>(swl + 2 * t * TILE_BYTES);
+      u4 hi = *reinterpret_cast<const u4*>(swl + (2 * t + 1) * TILE_BYTES);
+      if (!hi_live) hi = u4{0u, 0u, 0u, 0u};
+      const v8i bw = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)   // weights as the row operand: lane owns 4 columns
+        acc[i][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw, af[i], acc[i][t], 0, 0, 0,
+                                                                     0, 0, 0);
+    }
+  };
+  auto compute = [&](int st, auto& acc) {
     const uint8_t* sa = smem + st * S::STAGE;
     const uint8_t* sw = sa + S::A_BYTES;
     i4 af[4][J];
@@ -445,33 +338,16 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
     }
   };
 
-  i4 acc[4][NTW];
+  Acc acc[4][NTW];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) acc[i][t] = i4{0, 0, 0, 0};
+    for (int t = 0; t < NTW; ++t) acc[i][t] = Acc{};
 
   // Two-stage ring: tile i+1 streams into the other stage while tile i is
   // multiplied; the barrier after the wait publishes it to every wave and
   // frees stage i for tile i+2.
-  if constexpr (FQ != 0) {
-    // the first weight tiles do not depend on the activations: they stream
-    // in while the block waits for its m block's quantized rows
-    if (nk > 0) issue_w(kb, 0);
-    if (wave == 0) {
-      if (lane == 0) {
-        const unsigned need = (unsigned)min(S::BM, p.M - m0);
-        unsigned polls = 0;
-        while (dev_count(&p.sync[SYNC_DONE + mb]) < need && ++polls < FQ_SPIN_LIMIT)
-          __builtin_amdgcn_s_sleep(8);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    __syncthreads();
-    if (nk > 0) issue_a(kb, 0);
-  } else {
-    if (nk > 0) issue(kb, 0);
-  }
+  if (nk > 0) issue(kb, 0);
   constexpr bool LP = S::LDS_PARAMS && OUT == W4_OUT_F16;
   float* lws = reinterpret_cast<float*>(smem + S::PARAM_OFF);
   uint16_t* lbias = reinterpret_cast<uint16_t*>(smem + S::PARAM_OFF + NTILES * 16 * 4);
@@ -487,7 +363,8 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) issue(kb + i + 1, (i + 1) & 1);
-    compute(i & 1, acc);
+    if constexpr (KIND == KIND_F8F8) compute_f8(i & 1, kb + i, acc);
+    else compute(i & 1, acc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -498,10 +375,7 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
   float sav[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    sav[i] = OUT == W4_OUT_I32 ? 0.f
-             : FQ != 0 ? __builtin_bit_cast(float, dev_load(reinterpret_cast<const uint32_t*>(
-                             p.a_scale) + min(m0 + 64 * wm + 16 * i + r, p.M - 1)))
-                       : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
+    sav[i] = OUT == W4_OUT_I32 ? 0.f : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
   // ---- split K: exact INT32 partial sums through the workspace; the last
   // block of the tile to arrive adds the other blocks' sums to its own
   // accumulators and runs the epilogue below. Integer sums do not depend on
@@ -511,7 +385,7 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
   // at ((tile * ksplit + z) * Q + q) * THREADS + tid. A wave instruction then
   // moves 512 contiguous bytes, and rows past M or columns past N need no
   // test (their sums are never stored to C).
-  if constexpr (S::SPLIT_OK) {
+  if constexpr (S::SPLIT_OK && KIND != KIND_F8F8) {  // float sums are never split
     if (gg.ksplit > 1) {
       constexpr int Q = 8 * NTW;                     // 64-bit words per thread
       uint32_t* tile_part = reinterpret_cast<uint32_t*>(p.partials) +
@@ -605,7 +479,9 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
             uint32_t hv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              float o = (float)(acc[i][t][e] >> KindTraits<KIND>::SHIFT) * ws[e] * sav[i];
+              float o;
+              if constexpr (KIND == KIND_F8F8) o = acc[i][t][e] * ws[e] * sav[i];
+              else o = (float)(acc[i][t][e] >> KindTraits<KIND>::SHIFT) * ws[e] * sav[i];
               if constexpr (BIAS) o += bias[e];
               hv[e] = f2h(o);
             }
@@ -639,7 +515,7 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
 
 // The fields the block's first loads depend on come as leading scalar
 // arguments, preloaded into SGPRs (see k_gemv).
-template <int KIND, int NTILES, int WM, int OUT, bool BIAS, int FQ = 0>
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
 __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const uint8_t* Wt, const void* A, int M,
                                                       int N, int K, int KT, int mblocks,
                                                       int nblocks, int tiles, int per_xcd,
@@ -658,9 +534,7 @@ __global__ __launch_bounds__(128 * WM, 2) void k_gemm(const uint8_t* Wt, const v
   gg.tiles = tiles;
   gg.per_xcd = per_xcd;
   gg.kts = kts;
-  if constexpr (FQ != 0) fq_quantize_rows<FQ, 64 * WM>(p);
-  gemm_tile<KIND, NTILES, WM, OUT, BIAS, FQ>(p, gg);
-  if constexpr (FQ != 0) fq_finish<64 * WM>(p);
+  gemm_tile<KIND, NTILES, WM, OUT, BIAS>(p, gg);
 }
 
 // ---------------------------------------------------------------------------
@@ -693,7 +567,7 @@ inline GemmCfg gemm_cfg(int kind, int M, int N) {
     // M=2048 N=11008 K=4096 on MI355X, 190.5 against 207.4 us)
     return cb <= ca ? b : a;
   }
-  if (kind != KIND_W4A8) return GemmCfg{8, 2};       // 2-bit and INT8 weights: 128 x 128
+  if (kind != KIND_W4A8) return GemmCfg{8, 2};       // 2-bit, INT8 and FP8 weights: 128 x 128
   const GemmCfg narrow{16, 2};
   GemmCfg best = narrow;
   int best_cost = ceil_div(gemm_tiles(M, N, narrow), GEMM_CUS * 2) * 16;
@@ -711,31 +585,34 @@ inline GemmCfg gemm_cfg(int kind, int M, int N) {
 // K much; smaller products run on the decode kernel, one block per (16-row
 // tile, 16-column tile).
 inline bool use_gemm(int kind, int M, int N) {
-  if (kind != KIND_W4A8 && kind != KIND_W2A8 && kind != KIND_W8A8 && kind != KIND_W4A16)
+  if (kind != KIND_W4A8 && kind != KIND_W2A8 && kind != KIND_W8A8 && kind != KIND_W4A16 &&
+      kind != KIND_F8F8)
     return false;
   if (M <= 16) return false;
   return gemm_tiles(M, N, gemm_cfg(kind, M, N)) >= 128;
 }
 
 inline GemmGrid gemm_grid(int kind, int M, int N, int K, GemmCfg c) {
-  const Geometry g = geometry(kind == KIND_W2A8   ? W4_LAYOUT_W2A8
-                              : kind == KIND_W8A8 ? W4_LAYOUT_W8A8
-                                                  : W4_LAYOUT_W4A8,
+  const Geometry g = geometry(kind == KIND_W2A8                         ? W4_LAYOUT_W2A8
+                              : kind == KIND_W8A8 || kind == KIND_F8F8 ? W4_LAYOUT_W8A8
+                                                                       : W4_LAYOUT_W4A8,
                               N, K);
   GemmGrid gg{};
   gg.mblocks = ceil_div(M, 64 * c.wm);
   gg.nblocks = ceil_div(g.NT, c.ntiles);
   gg.tiles = gg.mblocks * gg.nblocks;
-  // K is split only for blocks of up to 8 weight tiles, with one arrival
-  // counter per tile
+  // k stages: one weight tile each, two for FP8
+  const int stages = kind == KIND_F8F8 ? ceil_div(g.KT, 2) : g.KT;
+  // K is split only for integer sums (exact in any order) over blocks of up
+  // to 8 weight tiles, with one arrival counter per tile
   int ks = 1;
-  if (c.ntiles <= 8 && gg.tiles <= WS_COUNTER_SLOTS && kind != KIND_W4A16) {
+  if (c.ntiles <= 8 && gg.tiles <= WS_COUNTER_SLOTS && kind != KIND_W4A16 && kind != KIND_F8F8) {
     if (c.ks > 0) ks = c.ks;
     else
-      while (gg.tiles * ks < 256 && ceil_div(g.KT, ks * 2) >= 2) ks *= 2;
+      while (gg.tiles * ks < 256 && ceil_div(stages, ks * 2) >= 2) ks *= 2;
   }
-  gg.kts = ceil_div(g.KT, ks);
-  gg.ksplit = ceil_div(g.KT, gg.kts);
+  gg.kts = ceil_div(stages, ks);
+  gg.ksplit = ceil_div(stages, gg.kts);
   gg.per_xcd = ceil_div(gg.tiles, 8);
   return gg;
 }
@@ -747,60 +624,62 @@ inline size_t gemm_workspace_bytes(int kind, int M, int N, int K, GemmCfg c) {
   return WS_COUNTERS + (size_t)gg.tiles * gg.ksplit * (64 * c.wm) * (16 * c.ntiles) * sizeof(int32_t);
 }
 
-template <int KIND, int NTILES, int WM, int OUT, bool BIAS, int FQ>
+template <int KIND, int NTILES, int WM, int OUT, bool BIAS>
 int launch_gemm_o(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
   using S = GemmShape<KIND, NTILES, WM>;
   const dim3 grid(gg.per_xcd * 8, gg.ksplit);
-  allow_smem((const void*)&k_gemm<KIND, NTILES, WM, OUT, BIAS, FQ>, S::LDS);
-  hipLaunchKernelGGL((k_gemm<KIND, NTILES, WM, OUT, BIAS, FQ>), grid, dim3(S::THREADS), S::LDS,
+  allow_smem((const void*)&k_gemm<KIND, NTILES, WM, OUT, BIAS>, S::LDS);
+  hipLaunchKernelGGL((k_gemm<KIND, NTILES, WM, OUT, BIAS>), grid, dim3(S::THREADS), S::LDS,
                      stream, p.Wt, p.A, p.M, p.N, p.K, p.KT, gg.mblocks, gg.nblocks, gg.tiles,
                      gg.per_xcd, gg.kts, p, gg);
   return launch_status();
 }
 
-template <int KIND, int NTILES, int WM, int FQ>
+template <int KIND, int NTILES, int WM>
 int launch_gemm_f(const MMParams& p, const GemmGrid& gg, hipStream_t stream) {
-  if constexpr (KIND == KIND_W8A8) {
-    if (p.out_dtype == W4_OUT_I8)
-      return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I8, false, FQ>(p, gg, stream);
+  if constexpr (KIND == KIND_F8F8) {
+    // float32 sums: fp16 (with or without bias) or float32 outputs only
+    if (p.out_dtype == W4_OUT_F32)
+      return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F32, false>(p, gg, stream);
+    if (p.out_dtype != W4_OUT_F16) return W4_ERR_ARG;
+    if (p.bias) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, true>(p, gg, stream);
+    return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, false>(p, gg, stream);
+  } else {
+    if constexpr (KIND == KIND_W8A8) {
+      if (p.out_dtype == W4_OUT_I8)
+        return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I8, false>(p, gg, stream);
+    }
+    if (p.out_dtype == W4_OUT_I32)
+      return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I32, false>(p, gg, stream);
+    if (p.out_dtype == W4_OUT_F32)
+      return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F32, false>(p, gg, stream);
+    if (p.bias) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, true>(p, gg, stream);
+    return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, false>(p, gg, stream);
   }
-  if (p.out_dtype == W4_OUT_I32)
-    return launch_gemm_o<KIND, NTILES, WM, W4_OUT_I32, false, FQ>(p, gg, stream);
-  if (p.out_dtype == W4_OUT_F32)
-    return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F32, false, FQ>(p, gg, stream);
-  if (p.bias) return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, true, FQ>(p, gg, stream);
-  return launch_gemm_o<KIND, NTILES, WM, W4_OUT_F16, false, FQ>(p, gg, stream);
 }
 
-// fq: 0 for int8 activations in p.A; 1 (fp16) or 2 (float32) for rows in
-// p.A_in that the kernel quantizes into p.A / p.a_scale first (the caller
-// points those at workspace memory and sets p.sync)
 template <int KIND, int NTILES, int WM>
-int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream, int fq) {
+int launch_gemm_t(MMParams p, const GemmGrid& gg, void* ws, hipStream_t stream) {
   p.counters = reinterpret_cast<unsigned*>(ws);
   p.partials = ws ? reinterpret_cast<uint8_t*>(ws) + WS_COUNTERS : nullptr;
-  if constexpr (KIND == KIND_W4A8 || KIND == KIND_W2A8) {
-    if (fq == 1) return launch_gemm_f<KIND, NTILES, WM, 1>(p, gg, stream);
-    if (fq == 2) return launch_gemm_f<KIND, NTILES, WM, 2>(p, gg, stream);
-  } else {
-    if (fq) return W4_ERR_ARG;
-  }
-  return launch_gemm_f<KIND, NTILES, WM, 0>(p, gg, stream);
+  return launch_gemm_f<KIND, NTILES, WM>(p, gg, stream);
 }
 
 // Defined in gemm_launch.hip (a translation unit of its own, so that the
 // GEMM instances compile in parallel with the rest of the library).
-int launch_gemm_w4a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
-int launch_gemm_w2a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq);
+int launch_gemm_w4a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream);
+int launch_gemm_w2a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream);
 int launch_gemm_w8a8(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream);
+int launch_gemm_f8f8(const MMParams& p, GemmCfg c, hipStream_t stream);
 int launch_gemm_w4a16(const MMParams& p, GemmCfg c, hipStream_t stream);  // gemm16.hip
 
 template <int KIND>
-int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream, int fq = 0) {
-  if constexpr (KIND == KIND_W4A8) return launch_gemm_w4a8(p, c, ws, stream, fq);
-  else if constexpr (KIND == KIND_W2A8) return launch_gemm_w2a8(p, c, ws, stream, fq);
-  else if constexpr (KIND == KIND_W8A8) return fq ? W4_ERR_ARG : launch_gemm_w8a8(p, c, ws, stream);
-  else if constexpr (KIND == KIND_W4A16) return fq ? W4_ERR_ARG : launch_gemm_w4a16(p, c, stream);
+int launch_gemm(const MMParams& p, GemmCfg c, void* ws, hipStream_t stream) {
+  if constexpr (KIND == KIND_W4A8) return launch_gemm_w4a8(p, c, ws, stream);
+  else if constexpr (KIND == KIND_W2A8) return launch_gemm_w2a8(p, c, ws, stream);
+  else if constexpr (KIND == KIND_W8A8) return launch_gemm_w8a8(p, c, ws, stream);
+  else if constexpr (KIND == KIND_W4A16) return launch_gemm_w4a16(p, c, stream);
+  else if constexpr (KIND == KIND_F8F8) return launch_gemm_f8f8(p, c, stream);
   else return W4_ERR_ARG;
 }
 

@@ -52,10 +52,6 @@ struct MMParams {
   int ksplit, kts;             // split-K factor and k tiles per split
   unsigned* counters;          // [mtiles * ngroups]  (split-K only)
   void* partials;              // [mtiles][ksplit][ngroups][TN*256] 4-byte
-  // one-launch fused prefill: A_in holds the fp16 / float32 rows, which the
-  // kernel quantizes into A (int8) and a_scale before multiplying
-  const void* A_in;
-  unsigned* sync;              // the fused prefill's counters (WS_SYNC_WORD)
 };
 
 // ---- unpack helpers (word layouts are fixed by prepack) --------------------

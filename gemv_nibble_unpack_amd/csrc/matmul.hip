@@ -272,6 +272,9 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{16, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{22, 2}};
     out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{24, 2}};
+  } else if (M > 16 && kind == KIND_F8F8) {
+    // FP8: 128 x 128 blocks over the whole K (float32 sums are not split)
+    out[n++] = Candidate{PATH_GEMM, 0, GemmCfg{8, 2}};
   } else if (M > 16 && (kind == KIND_W2A8 || kind == KIND_W8A8)) {
     // 128 x 128 blocks, whole K and at each distinct k split up to the same
     // block count
@@ -574,23 +577,15 @@ extern "C" int w4a16_gemm(const uint16_t* A, const uint8_t* Wp, int group_size,
 // ---------------------------------------------------------------------------
 // fused activation quantization: quantize_a8 + w4a8_gemm / w2a8_gemm in one
 // call. Decode shapes whose activation rows fit the block's LDS staging run
-// one kernel that quantizes in its prologue; prefill GEMM shapes run one
-// kernel whose waves quantize whole rows into the workspace before the tiles
-// are multiplied; everything else (the skinny kernel, decode rows too long
-// to stage) quantizes into the workspace with quantize_a8 first.
+// one kernel that quantizes in its prologue; everything else (prefill GEMM
+// and skinny shapes, decode rows too long to stage) quantizes into the
+// workspace with quantize_a8 first and then runs the A8 matmul.
 // ---------------------------------------------------------------------------
 namespace w4 {
-
-// The one-launch fused prefill (k_gemm with FQ != 0) is switched off: its
-// first GPU runs hung in the row-claim loop (a divergent loop exit, fixed in
-// the kernel since, but not yet run on a GPU again). Until it is, prefill
-// GEMM shapes quantize with quantize_a8 first (two launches).
-constexpr bool FUSED_PREFILL_ONE_LAUNCH = false;
 
 struct FusedPlan {
   Plan P;
   int fqc;            // decode prologue slots per lane (0: not that form)
-  bool gemm_fq;       // the prefill GEMM quantizes its rows itself (one launch)
   size_t q_off;       // offset of the quantized rows and their scales
   size_t ws_bytes;    // total workspace
 };
@@ -607,8 +602,6 @@ inline FusedPlan fused_plan(int kind, int M, int N, int K) {
   if (!F.P.gemm && !F.P.skinny && F.P.waves != 8)
     F.P = plan_from(kind, M, N, K, Candidate{PATH_DECODE, F.P.ksplit, {}, 0, 8});
   F.fqc = (!F.P.gemm && !F.P.skinny && F.P.staged) ? fq_slots(M < 16 ? M : 16, K) : 0;
-  // one completion counter per m block in the counter area's last KiB
-  F.gemm_fq = FUSED_PREFILL_ONE_LAUNCH && F.P.gemm && ceil_div(M, 64 * F.P.cfg.wm) <= SYNC_MBLOCKS;
   if (F.fqc) {
     F.ws_bytes = F.P.ws_bytes;
   } else {
@@ -665,27 +658,6 @@ int fused_common(int kind, const void* A, int in_dtype, const uint8_t* Wp, const
   if (!F.fqc) {
     int8_t* Aq = reinterpret_cast<int8_t*>(wsb + F.q_off);
     float* sa = reinterpret_cast<float*>(wsb + F.q_off + align256((size_t)M * K));
-    if (F.gemm_fq) {
-      MMParams p{};
-      p.A = Aq;
-      p.a_scale = sa;
-      p.A_in = A;
-      p.sync = reinterpret_cast<unsigned*>(ws) + WS_SYNC_WORD;
-      p.Wt = Wp;
-      p.w_scale = kind == KIND_W4A8 ? (const float*)scale : nullptr;
-      p.w_scale16 = kind == KIND_W2A8 ? (const uint16_t*)scale : nullptr;
-      p.bias = out_dtype == W4_OUT_I32 ? nullptr : bias;
-      p.C = C;
-      p.out_dtype = out_dtype;
-      p.M = M;
-      p.N = N;
-      p.K = K;
-      p.NT = g.NT;
-      p.KT = g.KT;
-      p.KQ = g.KQ;
-      return kind == KIND_W4A8 ? launch_gemm<KIND_W4A8>(p, F.P.cfg, ws, stream, fq)
-                               : launch_gemm<KIND_W2A8>(p, F.P.cfg, ws, stream, fq);
-    }
     const int q = quantize_a8(A, in_dtype, M, K, Aq, sa, nullptr, stream);
     if (q != W4_OK) return q;
     return a8_common(kind, Aq, sa, Wp, scale, bias, C, out_dtype, M, N, K, wsb, F.q_off, stream);

@@ -3,6 +3,8 @@
     python -m gemv_nibble_unpack_amd.profiling trace <rocprof_dir> <out.md> --cmd "<command>"
     python -m gemv_nibble_unpack_amd.profiling traffic <fetch_dir> <write_dir> <out.json> \
         --kernel <substring> --calib-bytes <bytes> [--calib-kernel <substring>] --cmd "<commands>"
+    python -m gemv_nibble_unpack_amd.profiling counters <out.md> <pmc_dir>... \
+        --kernel <substring> [--grid <threads>] --cmd "<command>" [--cmd ...]
 
 ``trace`` reads a ``--kernel-trace --output-format csv`` directory and writes
 per-kernel call counts and durations. ``traffic`` reads two ``--pmc
@@ -170,6 +172,43 @@ def summarize_mfma(util_dir, raw_dir, out_path, kernel, ops, cmds):
     return out_path
 
 
+def summarize_counters(dirs, out_path, kernel, cmds, grid=None):
+    """Every counter of one or more ``--pmc`` passes for the dispatches of one
+    kernel (name substring) and, with ``grid``, one launch size: the median
+    per launch, and per wave where the pass also counted SQ_WAVES."""
+    per = {}
+    n = 0
+    for d in dirs:
+        path = _find(d, "counter_collection.csv")
+        vals = defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if kernel not in row["Kernel_Name"]:
+                    continue
+                if grid is not None and int(row["Grid_Size"]) != grid:
+                    continue
+                vals[row["Counter_Name"]].append(float(row["Counter_Value"]))
+        if not vals:
+            raise KeyError(f"no dispatch matching {kernel!r} in {d}")
+        n = max(n, max(len(v) for v in vals.values()))
+        per.update({c: statistics.median(v) for c, v in vals.items()})
+    waves = per.get("SQ_WAVES")
+    lines = ["# rocprofv3 counters", "",
+             f"Kernel: `{kernel}`" + (f", {grid} threads per launch" if grid else "") +
+             f" ({n} launches, medians per launch)", "",
+             "| counter | per launch | per wave |", "|---|---|---|"]
+    for c in sorted(per):
+        pw = f"{per[c] / waves:.1f}" if waves else ""
+        lines.append(f"| {c} | {per[c]:.0f} | {pw} |")
+    if "SQ_LDS_BANK_CONFLICT" in per and per.get("SQ_ACTIVE_INST_LDS"):
+        lines += ["", f"LDS bank-conflict cycles / LDS-active cycles: "
+                      f"{per['SQ_LDS_BANK_CONFLICT'] / per['SQ_ACTIVE_INST_LDS']:.2f}"]
+    lines += ["", "Commands:", ""] + [f"* `{c}`" for c in cmds]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return per
+
+
 def load_traffic(path):
     """The recorded traffic, or None if absent or the kernels changed since."""
     try:
@@ -207,7 +246,16 @@ def main():
     m.add_argument("--kernel", required=True)
     m.add_argument("--ops", type=float, required=True, help="algorithmic operations per launch")
     m.add_argument("--cmd", action="append", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("out")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--grid", type=int, default=None)
+    c.add_argument("--cmd", action="append", required=True)
     a = ap.parse_args()
+    if a.what == "counters":
+        print(json.dumps(summarize_counters(a.dirs, a.out, a.kernel, a.cmd, a.grid), indent=1))
+        return
     if a.what == "mfma":
         print(summarize_mfma(a.util_dir, a.raw_dir, a.out, a.kernel, a.ops, a.cmd))
         return

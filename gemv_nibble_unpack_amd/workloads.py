@@ -117,14 +117,16 @@ def _ternary_a16():
 W2A16_TERNARY = _ternary_a16()
 
 # The table's INT8 x INT8 row (INT8 weights with the page's /127 formula,
-# INT8 per-token activations) on the 4096 x 4096 projection, M in {1, 16, 128}.
+# INT8 per-token activations) on the 4096 x 4096 projection, M in {1, 16, 128,
+# 2048}.
 W8A8_CASES = [Case(f"w8a8_M{M}_N4096_K4096", "w8a8", M, 4096, 4096, seed=900 + M)
               for M in (1, 16, 128, 2048)]
 
 # The table's FP8_E4M3 x FP8_E4M3 row (per-row E4M3 quantization of the same
-# float32 weights and fp16 activations) on the 4096 x 4096 projection.
+# float32 weights and fp16 activations) on the 4096 x 4096 projection, M in
+# {1, 16, 128, 2048}.
 F8F8_CASES = [Case(f"f8f8_M{M}_N4096_K4096", "f8f8", M, 4096, 4096, seed=950 + M)
-              for M in (1, 16, 128)]
+              for M in (1, 16, 128, 2048)]
 
 # The fp16-activation prefill: W4A16 at the prefill GEMM's shape, on the tiled
 # fp16 matrix-core GEMM (the north star's "(or fp16)" prefill path), a "next"

@@ -298,8 +298,9 @@ int quantize_f8(const void* X, int in_dtype, int rows, int K, uint8_t* Xq, float
  * Aq uint8 [M,K] E4M3 codes and a_scale float32 [M] from quantize_f8; Wp
  * from prepack_w(W4_LAYOUT_W8A8) of E4M3 weight codes, w_scale float32 [N].
  * out_dtype W4_OUT_F16 (bias applied) or W4_OUT_F32 (bias ignored). K
- * multiple of 16. M <= 16 (and small grids) run the decode kernel, more rows
- * the skinny or 16-row-tile kernels; there is no tiled GEMM for this row.
+ * multiple of 16. M <= 16 (and small grids) run the decode kernel; more rows
+ * run the tiled GEMM (128 x 128 blocks on v_mfma_f32_16x16x128_f8f6f4, the
+ * whole K per block) once it has at least 128 blocks, else the skinny kernel.
  * Workspace: w4_plan_workspace_bytes(W4_OP_F8F8, M, N, K). Errors as
  * w8a8_gemm.
  */

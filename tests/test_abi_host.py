@@ -252,11 +252,15 @@ def test_plan_table_candidates():
     assert lib.w4_plan_workspace_bytes(L.W4_OP_W4A8, 1100, 4004, 512) == 0
     names = _names(lib, L.W4_OP_W2A8, 1100, 2000, 1024)
     assert names[lib.w4_plan_current(L.W4_OP_W2A8, 1100, 2000, 1024)] == "gemm:128x128,ksplit=2"
-    # 2-bit fp16-activation and FP8 products have no GEMM candidate; INT8
-    # weights take the 128 x 128 block (built in once 128 blocks fill the chip
+    # 2-bit fp16-activation products have no GEMM candidate; FP8 takes the
+    # 128 x 128 block over the whole K (float32 sums are never split), INT8
+    # weights the 128 x 128 block (built in once 128 blocks fill the chip
     # unsplit); W4A16 the fp16 GEMM's 128 x 256 or 128 x 352 block
-    for op in (L.W4_OP_W2A16, L.W4_OP_F8F8):
-        assert not any(n.startswith("gemm") for n in _names(lib, op, 2048, 4096, 4096))
+    assert not any(n.startswith("gemm") for n in _names(lib, L.W4_OP_W2A16, 2048, 4096, 4096))
+    names = _names(lib, L.W4_OP_F8F8, 2048, 4096, 4096)
+    assert [n for n in names if n.startswith("gemm")] == ["gemm:128x128"]
+    assert names[lib.w4_plan_current(L.W4_OP_F8F8, 2048, 4096, 4096)] == "gemm:128x128"
+    assert lib.w4_plan_workspace_bytes(L.W4_OP_F8F8, 2048, 4096, 4096) == 0
     names = _names(lib, L.W4_OP_W4A16, 2048, 11008, 4096)
     assert [n for n in names if n.startswith("gemm")] == ["gemm:128x256", "gemm:128x352",
                                                           "gemm:128x384"]

@@ -452,15 +452,6 @@ def test_fused_act_tiny_and_tie_rows(g):
         assert np.array_equal(ref, got), m
 
 
-# The one-launch fused prefill hung twice on the GPU (an endless row-claim
-# loop: the loop exit was divergent in the compiled code; the kernel is fixed
-# since but has not run on a GPU again). Its dispatch is switched off and the
-# cases written for it are skipped until it has.
-SKIP_ONE_LAUNCH = pytest.mark.skip(
-    reason="one-launch fused prefill switched off after two GPU hangs in its row-claim loop "
-           "(divergent loop exit, fixed in the kernel, not yet re-run on a GPU)")
-
-
 @pytest.mark.parametrize("scheme,M,N,K,dt", [
     ("w4a8", 1, 256, 256, np.float32),      # the tiny GEMV configuration
     ("w4a8", 1, 4096, 4096, np.float16),
@@ -472,12 +463,12 @@ SKIP_ONE_LAUNCH = pytest.mark.skip(
     ("w4a8", 1, 4096, 11008, np.float16),   # long rows: several chunks per lane
     ("w4a8", 16, 4096, 4096, np.float16),   # too wide for the prologue: two launches
     ("w4a8", 300, 2000, 1040, np.float16),  # skinny kernel: two launches
-    # prefill GEMM, one launch: the waves quantize whole rows first
-    pytest.param("w4a8", 2048, 11008, 4096, np.float16, marks=SKIP_ONE_LAUNCH),  # 256 x 352
-    pytest.param("w4a8", 2000, 3000, 1040, np.float16, marks=SKIP_ONE_LAUNCH),   # 128 x 256
-    pytest.param("w4a8", 1100, 4004, 8208, np.float32, marks=SKIP_ONE_LAUNCH),   # two row passes
-    pytest.param("w2a8", 1100, 2000, 1024, np.float16, marks=SKIP_ONE_LAUNCH),   # split over K
-    pytest.param("w2a8", 1030, 4100, 8240, np.float32, marks=SKIP_ONE_LAUNCH),
+    # prefill GEMM shapes: quantize_a8 into the workspace, then the GEMM
+    ("w4a8", 2048, 11008, 4096, np.float16),  # 256 x 352 blocks
+    ("w4a8", 2000, 3000, 1040, np.float16),   # 128 x 256
+    ("w4a8", 1100, 4004, 8208, np.float32),   # float32 rows
+    ("w2a8", 1100, 2000, 1024, np.float16),   # split over K
+    ("w2a8", 1030, 4100, 8240, np.float32),
     ("w2a8", 1, 3200, 3200, np.float16),
     ("w2a8", 1, 8640, 3200, np.float16),
     ("w2a8", 5, 100, 528, np.float32),
@@ -514,10 +505,8 @@ def test_fused_act_matches_two_calls_and_oracle(g, scheme, M, N, K, dt):
             assert np.array_equal(got, O.int_accumulate_f64(qa, qw).astype(np.int32))
 
 
-@SKIP_ONE_LAUNCH
-def test_fused_prefill_counters_across_calls_graphs_and_shared_workspace(g):
-    # The one-launch fused prefill leaves its row-claim and completion
-    # counters zero: calls of different shapes in a row through one shared
+def test_fused_prefill_shared_workspace_across_calls_and_graphs(g):
+    # Fused prefill calls of different shapes in a row through one shared
     # workspace (with a 64-way split decode call between them, whose arrival
     # counters live in the same counter area), and three replays of a
     # captured fused call, all equal their results on fresh workspaces and
@@ -806,10 +795,14 @@ def test_f8_every_code_through_the_matrix_core(g):
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (1, 4096, 4096), (16, 4096, 4096),
                                    (128, 3200, 3200), (3, 130, 208), (1, 256, 8640),
-                                   (40, 300, 512), (300, 2000, 1040)])
+                                   (40, 300, 512), (300, 2000, 1040), (2048, 4096, 4096),
+                                   (1100, 2000, 1088), (1030, 2055, 1040)])
 def test_f8f8_outputs(g, M, N, K):
     # decode (M <= 16), skinny (M = 128, 300) and 16-row-tile (M = 40)
-    # kernels, ragged tails and a split over K (N = 256, K = 8640)
+    # kernels, ragged tails and a split over K (N = 256, K = 8640); the tiled
+    # GEMM (M = 2048; M = 1100 over an odd count of 64-k weight tiles, whose
+    # last 128-k stage has one live half; M = 1030 with ragged rows, columns
+    # and a k tail)
     say(f"case f8f8 M={M} N={N} K={K}")
     A = WL.activations(M, K, seed=9900 + M, dtype=np.float16)
     W = WL.weights_f32(N, K, seed=9901 + N)

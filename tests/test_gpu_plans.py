@@ -156,6 +156,9 @@ PLAN_SHAPES = [
     ("w2a16", 3, 3200, 8640), ("w2a16", 40, 3000, 2000),
     ("w8a8", 16, 4096, 4096), ("w8a8", 20, 1000, 528),
     ("f8f8", 16, 4096, 4096), ("f8f8", 20, 1000, 528),
+    # the FP8 GEMM candidate with ragged rows, columns and an odd count of
+    # 64-k weight tiles with a k tail
+    ("f8f8", 130, 1003, 1040),
 ]
 
 

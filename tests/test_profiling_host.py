@@ -96,3 +96,25 @@ def test_mfma_summary(tmp_path):
     assert "| 50.0 % |" in text                                  # median of the gemm launches
     assert "| 5.2429e+05 |" in text and "| 2.0000 |" in text     # executed = 2 x algorithmic
     assert "* `c1`" in text and "* `c2`" in text
+
+
+def test_counter_summary(tmp_path):
+    # two passes; medians per launch, per wave from SQ_WAVES, launch-size filter
+    _counters(tmp_path / "a", [("k_skinny<2>", "SQ_WAVES", 1600.0, 102400),
+                               ("k_skinny<2>", "SQ_WAVES", 1600.0, 102400),
+                               ("k_skinny<2>", "SQ_INSTS_VALU", 1600.0 * 500, 102400),
+                               ("k_skinny<2>", "SQ_INSTS_VALU", 1600.0 * 700, 102400),
+                               ("k_skinny<2>", "SQ_INSTS_VALU", 9.0, 4096),      # other shape
+                               ("other", "SQ_WAVES", 5.0, 102400)])
+    _counters(tmp_path / "b", [("k_skinny<2>", "SQ_LDS_BANK_CONFLICT", 300.0, 102400),
+                               ("k_skinny<2>", "SQ_ACTIVE_INST_LDS", 150.0, 102400)])
+    out = tmp_path / "c.md"
+    per = P.summarize_counters([str(tmp_path / "a"), str(tmp_path / "b")], str(out), "k_skinny",
+                               ["cmd a", "cmd b"], grid=102400)
+    assert per["SQ_INSTS_VALU"] == 1600.0 * 600
+    text = out.read_text()
+    assert "| SQ_INSTS_VALU | 960000 | 600.0 |" in text
+    assert "LDS bank-conflict cycles / LDS-active cycles: 2.00" in text
+    assert "* `cmd b`" in text
+    with pytest.raises(KeyError):
+        P.summarize_counters([str(tmp_path / "b")], str(out), "k_gemm", ["c"])
