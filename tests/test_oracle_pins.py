@@ -489,6 +489,47 @@ def test_requantize_i8_exact_cases():
     assert q.tolist() == [[64, 64]]                              # 2^24/2^18, (2^24+4)/2^18
 
 
+def test_requantize_i8_against_exact_rationals():
+    # Independent of the float32 formula: the code is the exact quotient
+    # acc * ws * sa / out_scale (the float32 inputs taken as exact binary
+    # fractions) rounded half to even and clipped. Three float32 roundings
+    # (product, product, quotient; the accumulators stay below 2^24 here, so
+    # their conversion is exact) move the quotient by at most 3 * 2^-24 of
+    # itself, so the float32 code may differ from the exact one only where the
+    # exact quotient lies that close to a half integer, and then only to its
+    # other neighbour. A dropped scale, a swapped division or the INT4 /7 or
+    # an unscaled clip fails this at once.
+    from fractions import Fraction
+    rng = np.random.default_rng(4242)
+    M, N = 40, 60
+    acc = rng.integers(-2 ** 23, 2 ** 23, (M, N)).astype(np.int64)
+    ws = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    sa = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    # an output scale that puts the median |value| near 60: most codes in
+    # range, a tail clipped at +-127
+    so = np.float32(np.median(np.abs(acc * ws[None, :].astype(np.float64) * sa[:, None])) / 60)
+    q = O.requantize_i8(acc, ws[None, :], sa[:, None], so)
+    near = 0
+    for m in range(M):
+        for n in range(N):
+            x = Fraction(int(acc[m, n])) * Fraction(float(ws[n])) * Fraction(float(sa[m])) \
+                / Fraction(float(so))
+            fl = x.numerator // x.denominator
+            frac = x - fl
+            exact = fl + (1 if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2) else 0)
+            exact = max(-127, min(127, exact))
+            if q[m, n] == exact:
+                continue
+            # only a near-tie may round the other way
+            dist = abs(frac - Fraction(1, 2))
+            assert dist <= abs(x) * Fraction(3, 2 ** 24) + Fraction(1, 2 ** 30), (m, n, float(x))
+            assert abs(int(q[m, n]) - exact) == 1, (m, n)
+            near += 1
+    assert near <= 2                                  # near-ties are rare at these magnitudes
+    # outputs spread over the whole code range, clipped at +-127 on both sides
+    assert q.max() == 127 and q.min() == -127 and len(np.unique(q)) > 200
+
+
 def test_w8a8_one_hot_and_bruteforce():
     rng = np.random.default_rng(42)
     N, K = 5, 32
