@@ -446,13 +446,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* Wt, const vo
     // 4-byte zero load per quad (a quad past the row's last reads the last).
     // Quad q is loaded just before tile 4q - 2, in time for a pass that starts
     // mid-quad (tiles 4q - 2 ..) as well as for one that starts on a quad.
-    constexpr int NQ = GRP ? (MAXT >= 4 ? MAXT / 4 + 1 : 1) : 1;
+    // A pass covers group positions 0 .. MAXT + 1 (mid-quad: shifted by 2).
+    constexpr int NQ = GRP ? (MAXT >= 4 ? (MAXT + 1) / 4 + 1 : 1) : 1;
     uint64_t sq[NQ];
     uint32_t zq[NQ];
     auto quad_load = [&](int q) {
       const int qq = min((pb >> 2) + q, p.KQ - 1);
       const size_t mq = (((size_t)tile * p.KQ + qq) * TILE_N + r) * 4;
-      if (MAXT >= 4 && q == NQ - 1) {
+      if (MAXT >= 4 && MAXT % 4 == 0 && q == NQ - 1) {
         // only groups 0 and 1 of the last quad can be used: loading no more
         // leaves no dead register half that the allocator could reuse while
         // the load is in flight (which would force a wait for it)

@@ -120,7 +120,13 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   P.kts = pairs ? 2 * ceil_div(ceil_div(g.KT, 2), ks) : ceil_div(g.KT, ks);
   P.ksplit = ceil_div(g.KT, P.kts);
   const int per = pairs ? 2 * ceil_div(ceil_div(P.kts, 2), W) : ceil_div(P.kts, W);
-  P.maxt = per <= 2 && W == 16 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+  // (six tiles: W4A16 runs of 5..6 tiles at sixteen waves, e.g. K = 11008,
+  // which eight slots would pad with two dead loads per wave)
+  P.maxt = per <= 2 && W == 16                               ? 2
+           : per <= 4                                        ? 4
+           : per <= 6 && W == 16 && kind == KIND_W4A16       ? 6
+           : per <= 8                                        ? 8
+                                                             : 16;
   // stage the block's activation rows in LDS when they fit, else each lane
   // streams its own fragments from L2
   P.staged = (size_t)rows * P.kts * trb <= (size_t)STAGE_MAX;
@@ -432,6 +438,9 @@ int launch_gemv(const Plan& P, MMParams p, void* ws, hipStream_t stream, int fq 
   if (P.waves == 16) {
     if (P.maxt == 2) return launch_gemv_m<KIND, 16, 2>(P, p, stream, fq, fqc);
     if (P.maxt == 4) return launch_gemv_m<KIND, 16, 4>(P, p, stream, fq, fqc);
+    if constexpr (KIND == KIND_W4A16) {
+      if (P.maxt == 6) return launch_gemv_m<KIND, 16, 6>(P, p, stream, fq, fqc);
+    }
     return launch_gemv_m<KIND, 16, 8>(P, p, stream, fq, fqc);
   }
   if (P.maxt == 4) return launch_gemv_m<KIND, 8, 4>(P, p, stream, fq, fqc);
