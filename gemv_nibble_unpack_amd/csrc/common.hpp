@@ -109,20 +109,57 @@ __device__ __forceinline__ int small_div(int c, int d) {
   return (int)(((float)c + 0.5f) * __builtin_amdgcn_rcpf((float)d));
 }
 
+// Wave max with the row-local steps on DPP (quad swaps, then the 8- and
+// 16-lane mirrors; each lane of a row of 16 ends with the row's max) and the
+// four row maxima read into scalars: a handful of VALU cycles instead of a
+// chain of six LDS crossbar permutes. A max does not depend on the order it is
+// taken in, so the result is the same value as a shuffle tree's. Every lane
+// of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));                      // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f<0x4E>(v));                      // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f<0x141>(v));                     // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));                     // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Sum over each row of 16 lanes, left in every lane of the row (the same
+// DPP steps; a float sum in this fixed order, every lane of a row holding the
+// identical value). Every lane active.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
   return v;
+}
+
+// The same for an integer sum (exact in any order). Every lane active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<0xB1>(v);                               // quad_perm [1, 0, 3, 2]
+  v += dpp_i<0x4E>(v);                               // quad_perm [2, 3, 0, 1]
+  v += dpp_i<0x141>(v);                              // row_half_mirror
+  v += dpp_i<0x140>(v);                              // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll

@@ -658,11 +658,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* Wt, const vo
       // tile's pair broadcast to the wave: tile kl's chunks are 16*kl..16*kl+15
 #pragma unroll
       for (int i = 0; i < APER; ++i) {
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          m1_sl[i] += __shfl_xor(m1_sl[i], o, 16);
-          m1_sh[i] += __shfl_xor(m1_sh[i], o, 16);
-        }
+        m1_sl[i] = row_sum16(m1_sl[i]);
+        m1_sh[i] = row_sum16(m1_sh[i]);
       }
 #pragma unroll
       for (int u = 0; u < MAXT; ++u) {

@@ -190,12 +190,15 @@ __global__ __launch_bounds__(QB) void k_quant_a8(const T* __restrict__ A, int K,
   float mx = 0.f;
   float x[CPT > 0 ? CPT : 1][8];
   if constexpr (CPT > 0) {
+    // every chunk load is issued before any is used: unconditional (chunks
+    // past the row re-read its last chunk and are zeroed after the loads), as
+    // a load inside a branch would be waited for inside it, one chunk after
+    // the other
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) load8<T>(row + 8 * min((int)threadIdx.x + i * QB, nch - 1), x[i]);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * QB;
-      if (c < nch) {
-        load8<T>(row + 8 * c, x[i]);
-      } else {
+      if ((int)threadIdx.x + i * QB >= nch) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
       }
