@@ -80,11 +80,12 @@ struct GemmShape {
   static constexpr int EPI_ROWS = 32;
   static constexpr int EPI_ROW = NTW * 32 + 16;                 // padded row bytes
   static constexpr int EPI = WAVES * EPI_ROWS * EPI_ROW;
-  // the block's column scales (f32) and biases (f16) sit in LDS behind the
-  // stages when two blocks still fit a CU's 160 KiB, so that the epilogue
-  // does not hold them in registers next to every accumulator
+  // the block's column scales (f32) and biases (f16), and its row scales
+  // (f32), sit in LDS behind the stages when the blocks of a CU still fit its
+  // 160 KiB, so that the epilogue neither holds them in registers next to
+  // every accumulator nor waits for a load of them after the k loop
   static constexpr int PARAM_OFF = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
-  static constexpr int PARAM_BYTES = NTILES * 16 * 6;
+  static constexpr int PARAM_BYTES = NTILES * 16 * 6 + BM * 4;
   static constexpr bool LDS_PARAMS = BLOCKS_PER_CU * (PARAM_OFF + PARAM_BYTES) <= 160 * 1024;
   static constexpr int LDS = PARAM_OFF + (LDS_PARAMS ? PARAM_BYTES : 0);
   static_assert(BLOCKS_PER_CU * LDS <= 160 * 1024, "LDS exceeds the CU");
@@ -351,6 +352,7 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
   constexpr bool LP = S::LDS_PARAMS && OUT == W4_OUT_F16;
   float* lws = reinterpret_cast<float*>(smem + S::PARAM_OFF);
   uint16_t* lbias = reinterpret_cast<uint16_t*>(smem + S::PARAM_OFF + NTILES * 16 * 4);
+  float* lsa = reinterpret_cast<float*>(smem + S::PARAM_OFF + NTILES * 16 * 6);
   if constexpr (LP) {
 #pragma unroll
     for (int c = tid; c < NTILES * 16; c += S::THREADS) {
@@ -358,6 +360,8 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
       lws[c] = KIND == KIND_W2A8 ? h2f(p.w_scale16[0]) : p.w_scale[n];
       if constexpr (BIAS) lbias[c] = p.bias[n];
     }
+#pragma unroll
+    for (int c = tid; c < S::BM; c += S::THREADS) lsa[c] = p.a_scale[min(m0 + c, p.M - 1)];
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -375,7 +379,9 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
   float sav[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    sav[i] = OUT == W4_OUT_I32 ? 0.f : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
+    sav[i] = OUT == W4_OUT_I32 ? 0.f
+             : LP              ? lsa[64 * wm + 16 * i + r]
+                               : p.a_scale[min(m0 + 64 * wm + 16 * i + r, p.M - 1)];
   // ---- split K: exact INT32 partial sums through the workspace; the last
   // block of the tile to arrive adds the other blocks' sums to its own
   // accumulators and runs the epilogue below. Integer sums do not depend on
