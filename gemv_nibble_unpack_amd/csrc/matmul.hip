@@ -27,14 +27,14 @@ struct Candidate {
   int path;
   int ks;           // decode, skinny: requested k split (0: chosen from the grid size)
   GemmCfg cfg;      // gemm: block shape
-  int mt;           // skinny: 16-row activation tiles per block (0 or 1: one, 2: two)
+  int mt;           // skinny: 16-row activation tiles per block (0 or 1: one, up to 4)
   int waves;        // decode: waves per block (0 or 8: eight, 16: sixteen)
 };
 
 struct Plan {
   bool gemm;        // prefill kernel instead of the decode kernel
   bool skinny;      // > 16 rows without enough GEMM tiles: 16 rows x 128 columns per block
-  int mtb;          // skinny: 16-row activation tiles per block (1 or 2)
+  int mtb;          // skinny: 16-row activation tiles per block (1 to 4)
   GemmCfg cfg;      // gemm: block shape
   int ngroups;      // skinny: groups of 8 weight n-tiles
   bool staged;      // activation rows staged in LDS
@@ -88,7 +88,7 @@ inline Plan plan_from(int kind, int M, int N, int K, const Candidate& c) {
   P.ngroups = ceil_div(g.NT, SKINNY_WAVES);
   if (c.path == PATH_SKINNY) {
     P.skinny = true;
-    P.mtb = c.mt == 2 ? 2 : 1;
+    P.mtb = c.mt >= 2 && c.mt <= 4 ? c.mt : 1;
     P.mtiles = ceil_div(M, 16 * P.mtb);            // blocks of 16 mtb rows
     // k split: one counter per (row tile, column group)
     const int ks = c.ks > 1 && P.mtiles * P.ngroups <= WS_COUNTER_SLOTS ? c.ks : 1;
@@ -178,10 +178,14 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   const Geometry g = geometry(kind_layout(kind), N, K);
   const int mtiles = ceil_div(M, 16);
   const int ngroups = ceil_div(g.NT, SKINNY_WAVES);
-  // two 16-row tiles per block once one-tile blocks would need more than the
-  // 512 resident at two per CU
-  if (mtiles > 1 && ngroups * mtiles >= SPLIT_BELOW)
-    return Candidate{PATH_SKINNY, 0, {}, ngroups * mtiles > SKINNY_RESIDENT ? 2 : 1};
+  // more row tiles per block once one-tile blocks would need more than the
+  // 512 resident at two per CU: three where that leaves one block per CU at
+  // most, else two (M=128 N=8640 K=3200 on MI355X: W2A8 13.8 -> 13.5 us,
+  // W2A16 22.9 -> 20.6 us at three; four tiles, 136 blocks, 16.4 and 25.6)
+  if (mtiles > 1 && ngroups * mtiles >= SPLIT_BELOW) {
+    if (ngroups * mtiles <= SKINNY_RESIDENT) return Candidate{PATH_SKINNY, 0, {}, 1};
+    return Candidate{PATH_SKINNY, 0, {}, ngroups * ceil_div(M, 48) <= GEMM_CUS ? 3 : 2};
+  }
   const int rows = M < 16 ? M : 16;
   const size_t row_bytes = (size_t)g.KT * tile_rowb(kind);
   if (mtiles == 1 && (size_t)rows * row_bytes > (size_t)STAGE_MAX &&
@@ -258,7 +262,7 @@ inline int candidates(int kind, int M, int N, int K, Candidate* out) {
   }
   // the skinny kernel (one, and above 16 rows also two, row tiles per block),
   // whole K and at each distinct k split up to the same block count
-  for (int mt = 1; mt <= (M > 16 ? 2 : 1); ++mt) {
+  for (int mt = 1; mt <= std::min(4, ceil_div(M, 16)); ++mt) {
     const int sblocks = ceil_div(g.NT, SKINNY_WAVES) * ceil_div(M, 16 * mt);
     last = 0;
     for (int ks = 1; ks <= 64; ks *= 2) {
@@ -463,7 +467,13 @@ int launch_skinny(const Plan& P, MMParams p, void* ws, hipStream_t stream) {
                        stream, p.Wt, p.A, p.St, p.Zt, p.M, p.K, p.NT, p.kts, P.ngroups,     \
                        (int)(grid.x / 8), p);                                               \
   } while (0)
-  if (P.mtb == 2) {
+  if (P.mtb == 4) {
+    if (P.ksplit > 1) W4_SKINNY(true, 4);
+    else W4_SKINNY(false, 4);
+  } else if (P.mtb == 3) {
+    if (P.ksplit > 1) W4_SKINNY(true, 3);
+    else W4_SKINNY(false, 3);
+  } else if (P.mtb == 2) {
     if (P.ksplit > 1) W4_SKINNY(true, 2);
     else W4_SKINNY(false, 2);
   } else {
@@ -811,8 +821,9 @@ inline int candidate_name(int kind, const Candidate& c, int M, int N, int K, cha
                : snprintf(buf, len, "gemm:%dx%d", 64 * c.cfg.wm, 16 * c.cfg.ntiles);
   } else if (c.path == PATH_SKINNY) {
     const Plan P = plan_from(kind, M, N, K, c);
-    const char* rows = P.mtb == 2 ? ":rows=32" : "";
-    n = P.ksplit > 1 ? snprintf(buf, len, "skinny%s%sksplit=%d", rows, P.mtb == 2 ? "," : ":",
+    char rows[16] = "";
+    if (P.mtb > 1) snprintf(rows, sizeof(rows), ":rows=%d", 16 * P.mtb);
+    n = P.ksplit > 1 ? snprintf(buf, len, "skinny%s%sksplit=%d", rows, P.mtb > 1 ? "," : ":",
                                 P.ksplit)
                      : snprintf(buf, len, "skinny%s", rows);
   } else {

@@ -27,11 +27,15 @@ constexpr int SKINNY_WAVES = 8;
 constexpr int SKINNY_THREADS = SKINNY_WAVES * 64;
 constexpr int SKINNY_STAGE = 64 * 1024;            // activation bytes per chunk
 
-// MTB 16-row activation tiles per block (1 or 2): the LDS chunk keeps its
-// size, so a two-tile block stages half the k range per chunk.
+// MTB 16-row activation tiles per block (1 to 4): the LDS chunk keeps its
+// size at most, so a block of more row tiles stages a shorter k range per
+// chunk: the largest power of two of k tiles that fits (a split block pads
+// each row's piece count to a power of two, so a row's pieces must be one).
 template <int KIND, int MTB = 1>
 __host__ __device__ constexpr int skinny_chunk_tiles() {
-  return SKINNY_STAGE / (16 * MTB * AStage<KIND>::TILE_ROWB);
+  int ct = 1;
+  while (2 * ct * 16 * MTB * AStage<KIND>::TILE_ROWB <= SKINNY_STAGE) ct *= 2;
+  return ct;
 }
 
 template <int KIND, int MTB = 1>
@@ -40,12 +44,12 @@ constexpr size_t skinny_smem() {
 }
 
 // SPLIT selects the k-split instance; without it the kernel covers the whole K
-// with the staging and epilogue of the unsplit kernel exactly. MTB = 2 makes
-// each block cover two 16-row activation tiles: every weight tile a wave
-// loads and unpacks then feeds two MFMA chains, which halves the weight
-// traffic and the block count of many-row products (the ternary M = 128
-// layers at N = 8640 would otherwise need 544 blocks, one more round than the
-// 512 that fit at two per CU).
+// with the staging and epilogue of the unsplit kernel exactly. MTB > 1 makes
+// each block cover MTB 16-row activation tiles: every weight tile a wave
+// loads and unpacks then feeds MTB MFMA chains, which divides the weight
+// traffic and the block count of many-row products by MTB (the ternary
+// M = 128 layers at N = 8640 need 544 one-tile blocks, 272 two-tile blocks,
+// or 204 three-tile blocks, the only count of these within one block per CU).
 //
 // The fields the first loads depend on come as leading scalar arguments,
 // preloaded into SGPRs (see k_gemv); per_xcd is the grid size / 8, and the
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const uint8_t* Wt, co
   constexpr int SSTRIDE = ROWB + 16;                 // padded: conflict-free fragment reads
   constexpr int APER = RB * ROWB / 16 / SKINNY_THREADS;  // 16-byte staging loads per thread
   static_assert(RB * ROWB % (16 * SKINNY_THREADS) == 0, "staging chunk");
-  static_assert(MTB == 1 || MTB == 2, "row tiles per block");
+  static_assert(MTB >= 1 && MTB <= 4, "row tiles per block");
   typedef typename std::conditional<float_acc<KIND>(), f4, i4>::type Acc;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 

@@ -234,11 +234,22 @@ def test_plan_table_candidates():
     # prefill shape: plus the three GEMM block shapes of the INT4 x INT8 kernel
     assert _names(lib, L.W4_OP_W4A8, 2048, 4096, 4096) == [
         "decode:ksplit=1", "decode:ksplit=1,waves=16", "skinny", "skinny:rows=32",
-        "gemm:128x256", "gemm:128x352", "gemm:256x352"]
-    # above 16 rows the skinny kernel also runs with two row tiles per block
-    # (the built-in choice once one-tile blocks exceed the 512 resident)
+        "skinny:rows=48", "skinny:rows=64", "gemm:128x256", "gemm:128x352", "gemm:256x352"]
+    # above 16 rows the skinny kernel also runs with two to four row tiles per
+    # block (three the built-in choice once one-tile blocks exceed the 512
+    # resident and three-tile blocks fit one per CU, else two)
     names = _names(lib, L.W4_OP_W2A8, 128, 8640, 3200)
-    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 8640, 3200)] == "skinny:rows=32"
+    assert [n for n in names if n.startswith("skinny") and "ksplit" not in n] == [
+        "skinny", "skinny:rows=32", "skinny:rows=48", "skinny:rows=64"]
+    assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 8640, 3200)] == "skinny:rows=48"
+    names = _names(lib, L.W4_OP_W2A16, 128, 8640, 3200)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A16, 128, 8640, 3200)] == "skinny:rows=48"
+    # 40 rows: three row tiles at most
+    assert not any("rows=64" in n for n in _names(lib, L.W4_OP_W2A16, 40, 1000, 2048))
+    # 2048 rows x 16 column groups: 128 x 16 one-tile blocks exceed 512,
+    # three-tile blocks (43 x 16) do not fit one per CU either: two tiles
+    names = _names(lib, L.W4_OP_W2A16, 2048, 2048, 2048)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A16, 2048, 2048, 2048)] == "skinny:rows=32"
     names = _names(lib, L.W4_OP_W2A8, 128, 3200, 3200)
     assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 3200, 3200)] == "skinny"
     # ternary weights above 16 rows: the 128 x 128 GEMM blocks, whole K and at
