@@ -180,8 +180,8 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   const int ngroups = ceil_div(g.NT, SKINNY_WAVES);
   // more row tiles per block once one-tile blocks would need more than the
   // 512 resident at two per CU: three where that leaves one block per CU at
-  // most, else two (M=128 N=8640 K=3200 on MI355X: W2A8 13.8 -> 13.5 us,
-  // W2A16 22.9 -> 20.6 us at three; four tiles, 136 blocks, 16.4 and 25.6)
+  // most, else two (M=128 N=8640 K=3200 on MI355X: W2A8 13.8 -> 12.9 us,
+  // W2A16 22.9 -> 19.6 us at three; four tiles, 136 blocks, 15.4 and 23.6)
   if (mtiles > 1 && ngroups * mtiles >= SPLIT_BELOW) {
     if (ngroups * mtiles <= SKINNY_RESIDENT) return Candidate{PATH_SKINNY, 0, {}, 1};
     return Candidate{PATH_SKINNY, 0, {}, ngroups * ceil_div(M, 48) <= GEMM_CUS ? 3 : 2};

@@ -108,28 +108,35 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const uint8_t* Wt, co
   Acc acc[MTB];
 #pragma unroll
   for (int j = 0; j < MTB; ++j) acc[j] = Acc{};
-  for (int kc = kb; kc < ke; kc += CT) {
-    const int ct = min(CT, ke - kc);                 // k tiles in this chunk
-    const size_t kbyte0 = (size_t)kc * AS::TILE_ROWB;
-    // ---- activation loads of the chunk (rows past M clamp, k past K zero):
-    // 16-byte pieces in row-major order, each row padded to a power-of-two
-    // piece count lg2 >= the ct tiles the chunk holds (a full chunk has no
-    // padding; a short k range per block under a k split would otherwise load
-    // and store a full chunk for a fraction of it). Padding slots re-read
-    // piece 0, so that the loads stay unconditional and the wait counts exact.
-    // (the unsplit kernel deals the full chunk's pieces, zeroing those past
-    // the chunk's tiles)
-    const int cw = ct * (AS::TILE_ROWB / 16);        // pieces per row in use
-    const int lg = cw > 1 ? 32 - __builtin_clz((unsigned)(cw - 1)) : 0;
+  // ---- activation loads of the chunk at kc (rows past M clamp, k past K
+  // zero): 16-byte pieces in row-major order, each row padded to a
+  // power-of-two piece count lg2 >= the ct tiles the chunk holds (a full chunk
+  // has no padding; a short k range per block under a k split would otherwise
+  // load and store a full chunk for a fraction of it). Padding slots re-read
+  // piece 0, so that the loads stay unconditional and the wait counts exact.
+  // (the unsplit kernel deals the full chunk's pieces, zeroing those past
+  // the chunk's tiles). A chunk at kc >= ke (the prefetch after the last one)
+  // reads the first 16 bytes of A in every slot: always in range, one cache
+  // line, and the count of loads in flight stays the same on every path.
+  auto chunk_geo = [&](int kc, int& ct, int& cw, int& lg) {
+    ct = min(CT, ke - kc);                           // k tiles in this chunk
+    cw = ct * (AS::TILE_ROWB / 16);                  // pieces per row in use
+    lg = cw > 1 ? 32 - __builtin_clz((unsigned)(cw - 1)) : 0;
+  };
+  u4 stage[APER];
+  auto load_chunk = [&](int kc) {
+    const bool live = kc < ke;                       // block-uniform
+    int ct, cw, lg;
+    chunk_geo(live ? kc : kb, ct, cw, lg);
     const int need = RB << lg;
-    auto used = [&](int c) { return c < need && (c & ((1 << lg) - 1)) < cw; };
-    u4 stage[APER];
+    const size_t kbyte0 = (size_t)kc * AS::TILE_ROWB;
 #pragma unroll
     for (int i = 0; i < APER; ++i) {
       const int c = tid + i * SKINNY_THREADS;
       int row, col;
       if constexpr (SPLIT) {
-        const int cc = used(c) ? c : 0;
+        const bool u = c < need && (c & ((1 << lg) - 1)) < cw;
+        const int cc = u ? c : 0;
         row = cc >> lg;
         col = cc & ((1 << lg) - 1);
       } else {
@@ -139,8 +146,24 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const uint8_t* Wt, co
       // past K (or past the chunk's tiles): clamp into the row, zeroed below
       const size_t off = min(kbyte0 + (size_t)col * 16, arow_bytes - 16);
       const int gm = min(mtile * RB + row, p.M - 1);
-      stage[i] = *reinterpret_cast<const u4*>(Ab + (size_t)gm * arow_bytes + off);
+      const size_t at = live ? (size_t)gm * arow_bytes + off : 0;
+      stage[i] = *reinterpret_cast<const u4*>(Ab + at);
     }
+  };
+  // Blocks of three or four row tiles (one per CU, several chunks per block)
+  // load each next chunk while the current one is multiplied; smaller blocks
+  // run two per CU, where the registers that prefetch holds would cost
+  // occupancy (M=128 N=8640 K=3200 on MI355X: W2A8 at three tiles 13.5 ->
+  // 12.9 us with it, W2A16 20.6 -> 19.6; at one tile W2A8 13.8 -> 17.7 us).
+  constexpr bool PF = MTB >= 3;
+  if constexpr (PF) load_chunk(kb);
+  for (int kc = kb; kc < ke; kc += CT) {
+    if constexpr (!PF) load_chunk(kc);
+    int ct, cw, lg;
+    chunk_geo(kc, ct, cw, lg);
+    const size_t kbyte0 = (size_t)kc * AS::TILE_ROWB;
+    const int need = RB << lg;
+    auto used = [&](int c) { return c < need && (c & ((1 << lg) - 1)) < cw; };
     for (int pass = 0; pass * MAXT < ct; ++pass) {
       const int pn = min(MAXT, ct - pass * MAXT);    // tiles in this pass (uniform)
       // ---- this wave's weight tiles (unconditional: dead slots re-read tile 0)
@@ -184,6 +207,10 @@ __global__ __launch_bounds__(SKINNY_THREADS) void k_skinny(const uint8_t* Wt, co
             *reinterpret_cast<u4*>(smem + row * SSTRIDE + col * 16) = v;
           }
         }
+        // (prefetch) the next chunk's rows stream in while this one is multiplied (its
+        // loads are issued after this pass's weight loads, so the matrix
+        // cores of this pass do not wait for them)
+        if constexpr (PF) load_chunk(kc + CT);
         __syncthreads();
       }
       if (!live_tile) continue;                      // wave-uniform: nothing to multiply
