@@ -69,11 +69,18 @@ struct GemmShape {
   static constexpr int W_BYTES = NTILES * G::WT * TILE_BYTES;
   static_assert(NTILES % 2 == 0, "two waves split the block's columns");
   static constexpr int NTW = NTILES / 2;                        // n subtiles per wave
-  static constexpr int STAGE = A_BYTES + W_BYTES;
-  // LDS stages in the ring (two fit the CU's 160 KiB in every configuration;
-  // a third weight stage, fetching the weights two k tiles ahead, was
-  // measured no faster on the 256 x 352 blocks and is not used)
-  static constexpr int STAGES = 2;
+  // LDS rings: two weight stages and two or three activation stages. A third
+  // activation stage (the activation tile two k tiles ahead) is used where it
+  // fits the CU's 160 KiB beside the rest: the INT8-weight 128 x 128 blocks
+  // (M=2048 N=K=4096 on MI355X: 47.5 -> 44.2 us) and the 256 x 352 INT4
+  // blocks (M=2048 N=11008 K=4096: 75.6 against 75.3 us without it, means of
+  // four alternating runs on one box, i.e. no change); a third weight stage
+  // alone was measured no faster there.
+  static constexpr int PARAM_BYTES = NTILES * 16 * 6 + BM * 4;
+  static constexpr int A_STAGES =
+      BLOCKS_PER_CU * (3 * A_BYTES + 2 * W_BYTES + PARAM_BYTES) <= 160 * 1024 ? 3 : 2;
+  static constexpr int W_OFF = A_STAGES * A_BYTES;             // weight ring after the activations
+  static constexpr int RING = W_OFF + 2 * W_BYTES;
   static constexpr int A_PER_WAVE = A_LOADS / WAVES;            // direct loads per wave
   static constexpr int W_PER_WAVE = (NTILES * G::WT + WAVES - 1) / WAVES;  // last round may be partial
   // fp16 epilogue staging: per wave and pass, 32 rows of 16*NTW columns
@@ -84,8 +91,7 @@ struct GemmShape {
   // (f32), sit in LDS behind the stages when the blocks of a CU still fit its
   // 160 KiB, so that the epilogue neither holds them in registers next to
   // every accumulator nor waits for a load of them after the k loop
-  static constexpr int PARAM_OFF = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
-  static constexpr int PARAM_BYTES = NTILES * 16 * 6 + BM * 4;
+  static constexpr int PARAM_OFF = RING > EPI ? RING : EPI;
   static constexpr bool LDS_PARAMS = BLOCKS_PER_CU * (PARAM_OFF + PARAM_BYTES) <= 160 * 1024;
   static constexpr int LDS = PARAM_OFF + (LDS_PARAMS ? PARAM_BYTES : 0);
   static_assert(BLOCKS_PER_CU * LDS <= 160 * 1024, "LDS exceeds the CU");
@@ -227,7 +233,7 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
   // are zero, so those products vanish, and rows past M are never stored.
   const int lrow = lane / RC, lchunk = lane % RC;    // position within one 1 KiB load
   auto issue_a = [&](int kt, int st) {
-    uint8_t* sa = smem + st * S::STAGE;
+    uint8_t* sa = smem + st * S::A_BYTES;
 #pragma unroll
     for (int q = 0; q < S::A_PER_WAVE; ++q) {
       const int ld = wave * S::A_PER_WAVE + q;       // 1 KiB load index within the A tile
@@ -239,7 +245,7 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
     }
   };
   auto issue_w = [&](int kt, int st) {
-    uint8_t* sw = smem + st * S::STAGE + S::A_BYTES;
+    uint8_t* sw = smem + S::W_OFF + st * S::W_BYTES;
 #pragma unroll
     for (int q = 0; q < S::W_PER_WAVE; ++q) {
       const int tl = q * S::WAVES + wave;            // weight tile slot within the block
@@ -252,18 +258,14 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
                                        sw + tl * TILE_BYTES, 16, 0, 0);
     }
   };
-  auto issue = [&](int kt, int st) {
-    issue_a(kt, st);
-    issue_w(kt, st);
-  };
   using Acc = typename G::Acc;
-  auto compute_f8 = [&](int st, int kt, auto& acc) {
+  auto compute_f8 = [&](int ast, int wst, int kt, auto& acc) {
     // lane (r, b) holds k = 16 b .. 16 b + 15 of each of the stage's two
     // weight tiles; its A operand is the same k positions of its row (chunks
     // b and 4 + b of the 128-byte staged row), so the 128-k product sums the
     // same terms as the two 64-k halves
-    const uint8_t* sa = smem + st * S::STAGE;
-    const uint8_t* sw = sa + S::A_BYTES;
+    const uint8_t* sa = smem + ast * S::A_BYTES;
+    const uint8_t* sw = smem + S::W_OFF + wst * S::W_BYTES;
     const bool hi_live = kt * 2 + 1 < p.KT;          // uniform
     v8i af[4];
 #pragma unroll
@@ -288,9 +290,9 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
                                                                      0, 0, 0);
     }
   };
-  auto compute = [&](int st, auto& acc) {
-    const uint8_t* sa = smem + st * S::STAGE;
-    const uint8_t* sw = sa + S::A_BYTES;
+  auto compute = [&](int ast, int wst, auto& acc) {
+    const uint8_t* sa = smem + ast * S::A_BYTES;
+    const uint8_t* sw = smem + S::W_OFF + wst * S::W_BYTES;
     i4 af[4][J];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -345,10 +347,20 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[i][t] = Acc{};
 
-  // Two-stage ring: tile i+1 streams into the other stage while tile i is
-  // multiplied; the barrier after the wait publishes it to every wave and
-  // frees stage i for tile i+2.
-  if (nk > 0) issue(kb, 0);
+  // Rings: weight tile i+1 streams into the other weight stage while tile i
+  // is multiplied; the activation tile runs two k tiles ahead where there are
+  // three activation stages (A3), else one. The wait at the end of step i
+  // leaves only the activation loads of tile i+2 in flight (the youngest this
+  // wave issued; every wave issues A_PER_WAVE of them), and the barrier
+  // publishes tile i+1 and frees the stages of tile i. The barrier is a bare
+  // s_barrier after the LDS wait: __syncthreads() would also wait for every
+  // copy in flight.
+  constexpr bool A3 = S::A_STAGES == 3;
+  if (nk > 0) {
+    issue_a(kb, 0);
+    issue_w(kb, 0);
+  }
+  if (A3 && nk > 1) issue_a(kb + 1, 1);
   constexpr bool LP = S::LDS_PARAMS && OUT == W4_OUT_F16;
   float* lws = reinterpret_cast<float*>(smem + S::PARAM_OFF);
   uint16_t* lbias = reinterpret_cast<uint16_t*>(smem + S::PARAM_OFF + NTILES * 16 * 4);
@@ -363,14 +375,24 @@ __device__ __forceinline__ void gemm_tile(const MMParams& p, const GemmGrid& gg)
 #pragma unroll
     for (int c = tid; c < S::BM; c += S::THREADS) lsa[c] = p.a_scale[min(m0 + c, p.M - 1)];
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  auto wait_next = [&](bool a_ahead) {              // a_ahead: block-uniform
+    if (A3 && a_ahead) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::A_PER_WAVE) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  wait_next(nk > 1);
+  int ast = 0;                                       // activation stage of tile i
   for (int i = 0; i < nk; ++i) {
-    if (i + 1 < nk) issue(kb + i + 1, (i + 1) & 1);
-    if constexpr (KIND == KIND_F8F8) compute_f8(i & 1, kb + i, acc);
-    else compute(i & 1, acc);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    if (i + 1 < nk) issue_w(kb + i + 1, (i + 1) & 1);
+    if constexpr (A3) {
+      if (i + 2 < nk) issue_a(kb + i + 2, ast == 0 ? 2 : ast - 1);
+    } else {
+      if (i + 1 < nk) issue_a(kb + i + 1, (i + 1) & 1);
+    }
+    if constexpr (KIND == KIND_F8F8) compute_f8(ast, i & 1, kb + i, acc);
+    else compute(ast, i & 1, acc);
+    wait_next(i + 2 < nk);
+    ast = A3 ? (ast == 2 ? 0 : ast + 1) : (ast ^ 1);
   }
 
   // ---- epilogue: lane owns columns n..n+3 of row m for each fragment -------
