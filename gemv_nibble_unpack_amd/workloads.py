@@ -129,8 +129,9 @@ F8F8_CASES = [Case(f"f8f8_M{M}_N4096_K4096", "f8f8", M, 4096, 4096, seed=950 + M
               for M in (1, 16, 128, 2048)]
 
 # The fp16-activation prefill: W4A16 at the prefill GEMM's shape, on the tiled
-# fp16 matrix-core GEMM (the north star's "(or fp16)" prefill path), a "next"
-# row beyond the five families.
+# fp16 matrix-core GEMM (the 4-bit codes widened to fp16 instead of INT8; the
+# FP16 x INT4 row of the BitBLAS page's data-type table), a case beyond the
+# five workload families.
 W4A16_PREFILL = Case("w4a16_prefill_2048x11008x4096", "w4a16", 2048, 11008, 4096,
                      bias=True, seed=450)
 
