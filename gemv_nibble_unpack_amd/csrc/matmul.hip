@@ -183,6 +183,18 @@ inline Candidate heuristic(int kind, int M, int N, int K) {
   // most, else two (M=128 N=8640 K=3200 on MI355X: W2A8 13.8 -> 12.9 us,
   // W2A16 22.9 -> 19.6 us at three; four tiles, 136 blocks, 15.4 and 23.6)
   if (mtiles > 1 && ngroups * mtiles >= SPLIT_BELOW) {
+    // fp16 x 2-bit rows over 24 or more k tiles: two row tiles per block (the
+    // crumb unpack, VALU-bound, is shared by both) and the power-of-two k
+    // split nearest to 5 k tiles per block (M=128 N=3200 K=8640 on MI355X:
+    // one-tile blocks 24.5 us, two-tile blocks split 4 / 7 ways 22.4 / 21.6)
+    if (kind == KIND_W2A16 && g.KT >= 24) {
+      const float want = (float)g.KT / 5.0f;
+      int ks = 1;
+      while (ks * 2 <= 64 && (float)(ks * 2) <= want * 1.41421356f) ks *= 2;
+      const Candidate c{PATH_SKINNY, ks, {}, 2};
+      const Plan pc = plan_from(kind, M, N, K, c);
+      if (pc.ksplit > 1 && ngroups * ceil_div(M, 32) * pc.ksplit <= CAND_MAX_BLOCKS) return c;
+    }
     if (ngroups * mtiles <= SKINNY_RESIDENT) return Candidate{PATH_SKINNY, 0, {}, 1};
     return Candidate{PATH_SKINNY, 0, {}, ngroups * ceil_div(M, 48) <= GEMM_CUS ? 3 : 2};
   }

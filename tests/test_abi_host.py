@@ -244,6 +244,9 @@ def test_plan_table_candidates():
     assert names[lib.w4_plan_current(L.W4_OP_W2A8, 128, 8640, 3200)] == "skinny:rows=48"
     names = _names(lib, L.W4_OP_W2A16, 128, 8640, 3200)
     assert names[lib.w4_plan_current(L.W4_OP_W2A16, 128, 8640, 3200)] == "skinny:rows=48"
+    # fp16 x 2-bit rows over 34 k tiles: two row tiles per block, split 7 ways
+    names = _names(lib, L.W4_OP_W2A16, 128, 3200, 8640)
+    assert names[lib.w4_plan_current(L.W4_OP_W2A16, 128, 3200, 8640)] == "skinny:rows=32,ksplit=7"
     # 40 rows: three row tiles at most
     assert not any("rows=64" in n for n in _names(lib, L.W4_OP_W2A16, 40, 1000, 2048))
     # 2048 rows x 16 column groups: 128 x 16 one-tile blocks exceed 512,
